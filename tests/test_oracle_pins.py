@@ -1,0 +1,476 @@
+"""Pins of the CPU oracle to things other than itself (no GPU needed).
+
+Each check is tied to a fixed point that does not come from the oracle:
+hand-derived fixtures (tests/golden), closed forms of special cases, torch's
+scaled_dot_product_attention in float64 (a library routine), a pool whose
+every element encodes its own coordinates, and the invariants the pages fix
+(paging changes where K/V live, not the result; shared prefix blocks equal
+unshared copies; softmax rows sum to one).  ``test_planted_mistakes`` plants
+plausible mistakes in the oracle and checks that some pin catches each.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import paged_attention as opa
+from paged_attention_kv_block_amd import inputs
+from tests.oracle_setup import OracleSide
+
+
+# ---------------------------------------------------------------------------
+# closed forms and golden fixtures
+# ---------------------------------------------------------------------------
+def _golden(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+def test_block_bytes_golden(golden_dir):
+    g = _golden(golden_dir, "closed_forms.json")["block_bytes"]
+    for c in g["cases"]:
+        assert oracle.kv_block_bytes(c["block_size"], c["num_kv_heads"], c["head_size"],
+                                     c["dtype_bytes"]) == c["bytes"], c["what"]
+
+
+def test_blocks_for_budget_golden(golden_dir):
+    g = _golden(golden_dir, "closed_forms.json")["blocks_for_budget"]
+    for c in g["cases"]:
+        assert oracle.num_blocks_for_budget(c["budget"], c["block_bytes"], c["num_layers"]) == c["blocks"]
+
+
+def test_slot_mapping_golden(golden_dir):
+    g = _golden(golden_dir, "closed_forms.json")["slot_mapping"]
+    for c in g["cases"]:
+        got = oracle.slot_mapping(g["row"], c["start"], c["n"], g["block_size"])
+        assert got.tolist() == c["slots"]
+
+
+def run_allocator_trace(make, trace):
+    """Replays a golden trace on an allocator built by ``make`` and returns a
+    list of mismatches (empty when the allocator follows the trace)."""
+    a = make(trace["num_blocks"], trace["initial_order"])
+    bad = []
+    for i, st in enumerate(trace["steps"]):
+        err = None
+        try:
+            if st["op"] == "allocate":
+                got = a.allocate(st["n"])
+                if got != st["expect_ids"]:
+                    bad.append((i, "ids", got))
+            elif st["op"] == "share":
+                a.share(st["ids"])
+            else:
+                a.free(st["ids"])
+        except oracle.NoFreeBlocks:
+            err = "no_blocks"
+        except oracle.InvalidArgument:
+            err = "invalid"
+        if err != st.get("expect_error"):
+            bad.append((i, "error", err))
+        q, rc = a.export()
+        if q != st["queue"] or rc != st["refcount"]:
+            bad.append((i, "state", q, rc))
+    return bad
+
+
+def test_allocator_golden_trace(golden_dir):
+    trace = _golden(golden_dir, "allocator_fifo_trace_n8.json")
+    assert run_allocator_trace(oracle.OracleAllocator, trace) == []
+
+
+def test_allocator_counts_closed_form():
+    """num_free == N - number of distinct blocks with a live reference, and
+    every block is either queued once or referenced, never both."""
+    rng = np.random.default_rng(5)
+    N = 64
+    a = oracle.OracleAllocator(N, rng.permutation(N))
+    held = []
+    for _ in range(400):
+        r = rng.random()
+        if r < 0.4:
+            n = int(rng.integers(0, 6))
+            try:
+                held.append(a.allocate(n))
+            except oracle.NoFreeBlocks:
+                assert n > a.num_free
+        elif r < 0.6 and held:
+            ids = held[int(rng.integers(len(held)))]
+            a.share(ids)
+            held.append(list(ids))
+        elif held:
+            a.free(held.pop(int(rng.integers(len(held)))))
+        q, rc = a.export()
+        live = {i for i in range(N) if rc[i] > 0}
+        assert a.num_free == N - len(live)
+        assert set(q).isdisjoint(live) and len(set(q)) == len(q)
+        assert set(q) | live == set(range(N))
+
+
+def test_allocator_stats_tail_waste():
+    a = oracle.OracleAllocator(10)
+    a.allocate(3)
+    # lengths 16 (no waste), 17 (15 wasted), 1 (15 wasted)
+    assert a.stats([16, 17, 1], 16) == (3, 30)
+
+
+# ---------------------------------------------------------------------------
+# layout: a pool whose elements encode their coordinates
+# ---------------------------------------------------------------------------
+def _code(blk, kv, head, off, d):
+    return float(blk * 100000 + kv * 10000 + head * 1000 + off * 10 + d)
+
+
+def test_gather_reads_stated_layout():
+    N, Hkv, bs, D = 5, 3, 4, 7
+    pool = np.zeros((N, 2, Hkv, bs, D), dtype=np.float64)
+    for blk in range(N):
+        for kv in range(2):
+            for h in range(Hkv):
+                for off in range(bs):
+                    for d in range(D):
+                        pool[blk, kv, h, off, d] = _code(blk, kv, h, off, d)
+    row = [4, 0, 2]
+    L = 10
+    K, V = oracle.gather_kv(pool, row, L)
+    for t in range(L):
+        for h in range(Hkv):
+            for d in range(D):
+                assert K[t, h, d] == _code(row[t // bs], 0, h, t % bs, d)
+                assert V[t, h, d] == _code(row[t // bs], 1, h, t % bs, d)
+
+
+def test_reshape_and_cache_writes_stated_layout():
+    N, Hkv, bs, D = 4, 2, 4, 3
+    pool = np.full((N, 2, Hkv, bs, D), -1.0)
+    T = 5
+    key = np.array([[[t * 100 + h * 10 + d for d in range(D)] for h in range(Hkv)] for t in range(T)], float)
+    val = -key - 7
+    slots = np.array([13, 2, -1, 7, 0])
+    oracle.reshape_and_cache(pool, key, val, slots)
+    for t, s in enumerate(slots):
+        if s < 0:
+            continue
+        np.testing.assert_array_equal(pool[s // bs, 0, :, s % bs, :], key[t])
+        np.testing.assert_array_equal(pool[s // bs, 1, :, s % bs, :], val[t])
+    touched = {(int(s) // bs, int(s) % bs) for s in slots if s >= 0}
+    for blk in range(N):
+        for off in range(bs):
+            if (blk, off) not in touched:
+                assert np.all(pool[blk, :, :, off, :] == -1.0)
+
+
+def test_reshape_and_cache_rejects_duplicate_slots():
+    pool = np.zeros((2, 2, 1, 4, 2))
+    kv = np.zeros((2, 1, 2))
+    with pytest.raises(AssertionError):
+        oracle.reshape_and_cache(pool, kv, kv, np.array([3, 3]))
+
+
+def test_bf16_decode_exact():
+    # 1.0 = 0x3F80, -2.0 = 0xC000, 0.5 = 0x3F00, smallest normal 2^-126 = 0x0080
+    bits = np.array([0x3F80, 0xC000, 0x3F00, 0x0080], dtype=np.uint16)
+    np.testing.assert_array_equal(oracle.to_f64(bits), [1.0, -2.0, 0.5, 2.0 ** -126])
+
+
+# ---------------------------------------------------------------------------
+# attention against a library routine and closed forms
+# ---------------------------------------------------------------------------
+def _sdpa(q, K, V, scale, mask=None, causal=False):
+    """torch SDPA in float64 on CPU. q [H, Lq, D], K/V [H, Lk, D]."""
+    with torch.no_grad():
+        return torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[None], torch.from_numpy(K)[None], torch.from_numpy(V)[None],
+            attn_mask=None if mask is None else torch.from_numpy(mask)[None],
+            is_causal=causal, scale=float(scale))[0].numpy()
+
+
+def check_decode_vs_sdpa(decode_fn, d, scale=None):
+    side = OracleSide(d)
+    wl = d.wl
+    sc = wl.scale if scale is None else scale
+    out, _ = decode_fn(d.query(), side.pool, side.block_tables, d.seq_lens, sc)
+    G = wl.num_q_heads // wl.num_kv_heads
+    q = oracle.to_f64(d.query())
+    worst = 0.0
+    for b in range(wl.num_seqs):
+        k, v = d.kv(b)
+        K = np.repeat(oracle.to_f64(k).transpose(1, 0, 2), G, axis=0)   # [H_q, L, D]
+        V = np.repeat(oracle.to_f64(v).transpose(1, 0, 2), G, axis=0)
+        ref = _sdpa(q[b][:, None, :], K, V, sc)[:, 0, :]
+        worst = max(worst, float(np.max(np.abs(out[b] - ref))))
+    return worst
+
+
+DECODE_SHAPES = [
+    dict(seq_lens=(7, 19), num_q_heads=4, num_kv_heads=2, head_size=64, dtype="f32"),
+    dict(seq_lens=(1, 16, 17, 33, 48), num_q_heads=8, num_kv_heads=1, head_size=64),
+    dict(seq_lens=(5, 40), num_q_heads=3, num_kv_heads=3, head_size=128),
+    dict(seq_lens=(31, 2, 64), num_q_heads=16, num_kv_heads=2, head_size=64),
+]
+
+
+@pytest.mark.parametrize("shape", DECODE_SHAPES)
+def test_decode_matches_sdpa(shape):
+    d = inputs.custom(kind="decode", **shape)
+    assert check_decode_vs_sdpa(oracle.decode, d) <= 1e-12
+
+
+def test_decode_matches_sdpa_tiny_workload():
+    assert check_decode_vs_sdpa(oracle.decode, inputs.draw(0)) <= 1e-12
+
+
+def check_prefill_vs_sdpa(prefill_fn, d):
+    side = OracleSide(d)
+    wl = d.wl
+    qsl = side.query_start_loc()
+    out, _ = prefill_fn(d.query(), qsl, side.pool, side.block_tables, d.seq_lens, wl.scale)
+    G = wl.num_q_heads // wl.num_kv_heads
+    q = oracle.to_f64(d.query())
+    worst = 0.0
+    for b in range(wl.num_seqs):
+        lo, hi = int(qsl[b]), int(qsl[b + 1])
+        C, L = hi - lo, int(d.seq_lens[b])
+        if C == 0:
+            continue
+        k, v = d.kv(b)
+        K = np.repeat(oracle.to_f64(k).transpose(1, 0, 2), G, axis=0)
+        V = np.repeat(oracle.to_f64(v).transpose(1, 0, 2), G, axis=0)
+        # bottom-right aligned causal mask: query i sits at position L - C + i
+        mask = np.arange(L)[None, :] <= (L - C + np.arange(C))[:, None]
+        ref = _sdpa(q[lo:hi].transpose(1, 0, 2), K, V, wl.scale, mask=mask)
+        worst = max(worst, float(np.max(np.abs(out[lo:hi] - ref.transpose(1, 0, 2)))))
+    return worst
+
+
+PREFILL_SHAPES = [
+    dict(seq_lens=(20, 37), chunk_lens=(5, 17), num_q_heads=4, num_kv_heads=2, head_size=64),
+    dict(seq_lens=(16, 1, 50), chunk_lens=(16, 1, 3), num_q_heads=8, num_kv_heads=2, head_size=128),
+    dict(seq_lens=(9,), chunk_lens=(0,), num_q_heads=2, num_kv_heads=1, head_size=64),
+]
+
+
+@pytest.mark.parametrize("shape", PREFILL_SHAPES)
+def test_prefill_matches_sdpa_bottom_right_mask(shape):
+    d = inputs.custom(kind="prefill", **shape)
+    assert check_prefill_vs_sdpa(oracle.prefill_chunk, d) <= 1e-12
+
+
+def test_prefill_whole_sequence_is_causal_sdpa():
+    """Empty prefix, chunk = whole sequence: torch's is_causal (top-left and
+    bottom-right alignment coincide when the query and key counts agree)."""
+    d = inputs.custom(kind="prefill", seq_lens=(23,), chunk_lens=(23,), num_q_heads=2,
+                      num_kv_heads=1, head_size=64)
+    side = OracleSide(d)
+    out, _ = side.prefill()
+    k, v = d.kv(0)
+    K = np.repeat(oracle.to_f64(k).transpose(1, 0, 2), 2, axis=0)
+    V = np.repeat(oracle.to_f64(v).transpose(1, 0, 2), 2, axis=0)
+    ref = _sdpa(oracle.to_f64(d.query()).transpose(1, 0, 2), K, V, d.wl.scale, causal=True)
+    assert np.max(np.abs(out - ref.transpose(1, 0, 2))) <= 1e-12
+
+
+def test_worked_example_three_keys():
+    """q = e1, keys along e1 at 0, 1, 2, scale 1: logits (0, 1, 2), so the
+    weights are (1, e, e^2) / (1 + e + e^2) and lse = ln(1 + e + e^2)."""
+    q = np.array([[1.0, 0.0]])
+    K = np.array([[0.0, 0.0], [1.0, 0.0], [2.0, 0.0]])
+    V = np.array([[1.0, 0.0], [0.0, 1.0], [0.0, 0.0]])
+    o, lse = oracle.attention(q, K, V, 1.0)
+    z = 1.0 + math.e + math.e ** 2
+    np.testing.assert_allclose(o[0], [1.0 / z, math.e / z], rtol=0, atol=1e-15)
+    assert abs(lse[0] - math.log(z)) <= 1e-14
+
+
+def test_closed_form_single_token():
+    rng = np.random.default_rng(1)
+    q, K, V = rng.standard_normal((3, 16)), rng.standard_normal((1, 16)), rng.standard_normal((1, 16))
+    o, lse = oracle.attention(q, K, V, 0.25)
+    np.testing.assert_array_equal(o, np.repeat(V, 3, axis=0))
+    np.testing.assert_allclose(lse, 0.25 * (q @ K[0]), rtol=0, atol=1e-14)
+
+
+def test_closed_form_zero_query_is_mean():
+    rng = np.random.default_rng(2)
+    K, V = rng.standard_normal((9, 8)), rng.standard_normal((9, 8))
+    o, lse = oracle.attention(np.zeros((2, 8)), K, V, 0.3)
+    np.testing.assert_allclose(o, np.repeat(V.mean(axis=0, keepdims=True), 2, axis=0), atol=1e-15)
+    np.testing.assert_allclose(lse, math.log(9), atol=1e-15)
+
+
+def test_closed_form_equal_keys_is_mean():
+    rng = np.random.default_rng(3)
+    k = rng.standard_normal(8)
+    V = rng.standard_normal((5, 8))
+    o, _ = oracle.attention(rng.standard_normal((1, 8)), np.tile(k, (5, 1)), V, 1.0)
+    np.testing.assert_allclose(o[0], V.mean(axis=0), atol=1e-15)
+
+
+def test_closed_form_unit_values():
+    rng = np.random.default_rng(4)
+    o, _ = oracle.attention(rng.standard_normal((4, 32)), rng.standard_normal((50, 32)),
+                            np.ones((50, 32)), 0.2)
+    np.testing.assert_allclose(o, 1.0, atol=1e-15)
+
+
+def test_dominant_key_selects_its_value_without_overflow():
+    """Logits around 1e4 overflow exp() unless the row max is subtracted."""
+    K = np.zeros((6, 4))
+    K[3, 0] = 100.0
+    V = np.arange(24, dtype=float).reshape(6, 4)
+    q = np.array([[100.0, 0, 0, 0]])
+    o, lse = oracle.attention(q, K, V, 1.0)
+    np.testing.assert_allclose(o[0], V[3], atol=1e-12)
+    assert abs(lse[0] - 1e4) < 1e-9
+
+
+def test_empty_sequence_gives_zero_and_minus_inf():
+    o, lse = oracle.attention(np.ones((2, 4)), np.zeros((0, 4)), np.zeros((0, 4)), 1.0)
+    assert np.all(o == 0) and np.all(lse == -np.inf)
+
+
+# ---------------------------------------------------------------------------
+# reductions between entry points and invariants the pages fix
+# ---------------------------------------------------------------------------
+def test_prefill_chunk_of_one_equals_decode():
+    d = inputs.custom(kind="prefill", seq_lens=(18, 33), chunk_lens=(1, 1), num_q_heads=4,
+                      num_kv_heads=2, head_size=64, dtype="f32")
+    side = OracleSide(d)
+    p_out, p_lse = side.prefill()
+    q = d.query()
+    d_out, d_lse = oracle.decode(q, side.pool, side.block_tables, d.seq_lens, d.wl.scale)
+    np.testing.assert_array_equal(p_out, d_out)
+    np.testing.assert_array_equal(p_lse, d_lse)
+
+
+def test_mha_is_gqa_with_group_one():
+    """H_q == H_kv: each query head reads its own KV head."""
+    d = inputs.custom(kind="decode", seq_lens=(21,), num_q_heads=3, num_kv_heads=3, head_size=64)
+    side = OracleSide(d)
+    out, _ = side.decode()
+    k, v = d.kv(0)
+    q = oracle.to_f64(d.query())[0]
+    for h in range(3):
+        o, _ = oracle.attention(q[h:h + 1], oracle.to_f64(k[:, h]), oracle.to_f64(v[:, h]), d.wl.scale)
+        np.testing.assert_array_equal(out[0, h], o[0])
+
+
+def test_block_size_one_is_plain_gather():
+    """With one token per block the pool is a permuted token array."""
+    rng = np.random.default_rng(9)
+    L, Hkv, D = 6, 2, 8
+    perm = rng.permutation(L)
+    K = rng.standard_normal((L, Hkv, D))
+    V = rng.standard_normal((L, Hkv, D))
+    pool = np.zeros((L, 2, Hkv, 1, D))
+    pool[perm, 0, :, 0, :] = K
+    pool[perm, 1, :, 0, :] = V
+    K2, V2 = oracle.gather_kv(pool, perm, L)
+    np.testing.assert_array_equal(K2, K)
+    np.testing.assert_array_equal(V2, V)
+
+
+def test_permutation_of_physical_blocks_is_invisible():
+    d = inputs.draw(0)
+    a = OracleSide(d)
+    out_a, lse_a = a.decode()
+    d2 = inputs.draw(0)
+    d2.pool_order = d2.pool_order[::-1].copy()
+    b = OracleSide(d2)
+    assert not np.array_equal(a.block_tables, b.block_tables)
+    out_b, lse_b = b.decode()
+    np.testing.assert_array_equal(out_a, out_b)
+    np.testing.assert_array_equal(lse_a, lse_b)
+
+
+def _small_prefix_workload():
+    wl = inputs.Workload(50, "small-prefix", "prefill", "bf16", 3, 4, 2, 64,
+                         prefix_tokens=32, private_tokens=9, chunk_tokens=7,
+                         fixed_num_blocks=12)   # room for unshared prefix copies
+    return inputs.Draw(wl)
+
+
+def test_shared_prefix_equals_unshared_copies():
+    d = _small_prefix_workload()
+    shared = OracleSide(d, share_prefix=True)
+    copies = OracleSide(d, share_prefix=False)
+    q, rc = shared.alloc.export()
+    assert max(rc) == 3                              # prefix blocks held by all 3
+    assert len(set(copies.block_tables[:, :2].ravel())) == 6
+    o1, l1 = shared.prefill()
+    o2, l2 = copies.prefill()
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+# ---------------------------------------------------------------------------
+# the pins catch plausible mistakes planted in the oracle
+# ---------------------------------------------------------------------------
+def _mutant_decode_head_mod(query, pool, bt, seq_lens, scale):
+    B, Hq, D = query.shape
+    Hkv = pool.shape[2]
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        K, V = oracle.gather_kv(pool, bt[b], int(seq_lens[b]))
+        for h in range(Hq):
+            out[b, h] = oracle.attention(oracle.to_f64(query[b, h:h + 1]), K[:, h % Hkv], V[:, h % Hkv], scale)[0][0]
+    return out, None
+
+
+def _mutant_decode_swapped_kv(query, pool, bt, seq_lens, scale):
+    return oracle.decode(query, pool[:, ::-1], bt, seq_lens, scale)
+
+
+def _mutant_decode_drops_last_token(query, pool, bt, seq_lens, scale):
+    return oracle.decode(query, pool, bt, np.asarray(seq_lens) - 1, scale)
+
+
+def _mutant_decode_no_scale(query, pool, bt, seq_lens, scale):
+    return oracle.decode(query, pool, bt, seq_lens, 1.0)
+
+
+def _mutant_prefill_strict_causal(query, qsl, pool, bt, seq_lens, scale):
+    out = np.zeros(query.shape)
+    Hkv = pool.shape[2]
+    G = query.shape[1] // Hkv
+    for b in range(len(seq_lens)):
+        lo, hi = int(qsl[b]), int(qsl[b + 1])
+        L = int(seq_lens[b])
+        K, V = oracle.gather_kv(pool, bt[b], L)
+        for i in range(hi - lo):
+            pos = L - (hi - lo) + i
+            for g in range(Hkv):
+                n = max(pos, 1)                     # sees 0..pos-1 (itself excluded)
+                out[lo + i, g * G:(g + 1) * G] = oracle.attention(
+                    oracle.to_f64(query[lo + i, g * G:(g + 1) * G]), K[:n, g], V[:n, g], scale)[0]
+    return out, None
+
+
+@pytest.mark.parametrize("mutant", [_mutant_decode_head_mod, _mutant_decode_swapped_kv,
+                                    _mutant_decode_drops_last_token, _mutant_decode_no_scale])
+def test_planted_decode_mistakes_are_caught(mutant):
+    worst = max(check_decode_vs_sdpa(mutant, inputs.custom(kind="decode", **s)) for s in DECODE_SHAPES)
+    assert worst > 1e-3
+
+
+def test_planted_prefill_mistake_is_caught():
+    worst = max(check_prefill_vs_sdpa(_mutant_prefill_strict_causal, inputs.custom(kind="prefill", **s))
+                for s in PREFILL_SHAPES[:2])
+    assert worst > 1e-3
+
+
+def test_planted_allocator_mistake_is_caught(golden_dir):
+    """A LIFO queue (free pushes to the head) breaks the golden FIFO trace."""
+    class Lifo(oracle.OracleAllocator):
+        def free(self, ids):
+            super().free(ids)
+            q = self.free_block_queue
+            # move blocks just appended to the front, as a LIFO would
+            for _ in range(sum(1 for i in ids if self.refcount[int(i)] == 0)):
+                q.rotate(1)
+    trace = _golden(golden_dir, "allocator_fifo_trace_n8.json")
+    assert run_allocator_trace(Lifo, trace) != []
