@@ -1,0 +1,232 @@
+/*
+ * pa.h -- C ABI of libpa.so, MI355X (gfx950) paged attention.
+ *
+ * Paged attention keeps each sequence's keys and values in fixed-size blocks
+ * of a shared pool; a per-sequence block table maps the sequence's logical
+ * blocks to physical ones, so the storage need not be contiguous.
+ *   - "Inside vLLM: Anatomy of a High-Throughput LLM Inference System",
+ *     section "LLM Engine & Engine Core": the KV-cache manager keeps a
+ *     free_block_queue, and blocks are the index from a sequence's tokens to
+ *     their KV-cache blocks.  Section "LLM Engine constructor": block bytes
+ *     = 2 * block_size * num_kv_heads * head_size * dtype_num_bytes; the
+ *     CPU-side input batch holds the block tables; the cache is allocated
+ *     once, reshaped and bound to the attention layers; attention metadata
+ *     is prepared on the host and consumed by the kernels.
+ *   - "Im Inneren von vLLM: Anatomie eines Hochdurchsatz-LLM-Inferenzsystems",
+ *     sections "Paged Attention & KV-Cache" and "Fortgeschrittene Funktionen"
+ *     (chunked prefill, prefix caching).
+ *   - "vLLM: Ein tiefer Einblick ... auf Basis von PagedAttention", section
+ *     "Tiefenanalyse": non-contiguous KV storage modelled on OS paging.
+ *
+ * Conventions used by every entry point
+ *   Status: every int-returning call returns a pa_status; on failure
+ *   pa_last_error() returns a message (thread-local, valid until the next
+ *   failing call on that thread).  Arguments are validated on the host
+ *   before anything is enqueued, so a failed call has no device effect.
+ *
+ *   Pool layout (the pages give only the byte count; this is the reading):
+ *     kv_cache[num_blocks][2][num_kv_heads][block_size][head_size]
+ *   index 0 of the second axis holds keys, 1 holds values; one block is
+ *   exactly pa_kv_block_bytes() contiguous bytes.  Element type is fp32 or
+ *   bf16 (pa_dtype); queries and outputs use the same element type.
+ *
+ *   Token position p of a sequence lives at slot
+ *     block_tables[b][p / block_size] * block_size + p % block_size.
+ *   Query head h reads KV head h / (H_q / H_kv).
+ *
+ *   Device pointers are device memory owned by the caller (e.g. allocated by
+ *   torch).  The library never allocates or frees device memory and never
+ *   synchronises: device work is enqueued on `stream` (a hipStream_t; NULL
+ *   is the default stream) and returns immediately.  Device-side contents
+ *   (block ids, slots, seq_lens) are the caller's contract: block ids must be
+ *   in [0, num_blocks), seq_lens[b] <= max_seq_len, slots unique.  Out-of-
+ *   range block ids are clamped to block 0 (wrong result, no fault).
+ *   Nothing here is thread-safe per allocator handle.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_EINVAL = 1,     /* bad argument (shape, pointer, refcount, ...) */
+  PA_ENOBLOCKS = 2,  /* allocator: not enough free blocks; state unchanged */
+  PA_ENOTSUP = 3,    /* valid but unsupported (head size, block size, dtype) */
+  PA_EHIP = 4        /* the HIP runtime reported an error at launch */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int pa_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Closed forms ("Inside vLLM", section "LLM Engine constructor")
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of one block: 2 (key and value) * block_size * num_kv_heads *
+ * head_size * dtype_bytes.  Returns 0 if any argument is <= 0. */
+size_t pa_kv_block_bytes(int32_t block_size, int32_t num_kv_heads,
+                         int32_t head_size, int32_t dtype_bytes);
+
+/* Blocks that fit in budget_bytes when each of num_layers layers needs one
+ * block per block id: floor(budget / (block_bytes * num_layers)).
+ * Returns -1 if block_bytes or num_layers is 0 / negative. */
+int64_t pa_num_blocks_for_budget(uint64_t budget_bytes, size_t block_bytes,
+                                 int32_t num_layers);
+
+/* ---------------------------------------------------------------------------
+ * Host block allocator: the free_block_queue ("Inside vLLM", section
+ * "LLM Engine & Engine Core").  The pages name the queue but not its policy;
+ * this one is FIFO: allocate pops from the head, a block goes back to the
+ * tail when its reference count drops to zero (in the order the ids are
+ * given).  Prefix caching ("Im Inneren von vLLM", "Fortgeschrittene
+ * Funktionen") shares blocks by reference count.  Host memory only; every
+ * pointer argument is host memory owned by the caller.
+ * ------------------------------------------------------------------------- */
+typedef struct pa_allocator pa_allocator;
+
+/* Creates an allocator over block ids 0..num_blocks-1.  initial_order
+ * (nullable: 0..N-1) gives the initial queue order and must be a
+ * permutation.  *out receives an opaque handle owned by the library. */
+int pa_allocator_create(int32_t num_blocks, const int32_t* initial_order,
+                        pa_allocator** out);
+void pa_allocator_destroy(pa_allocator* a);
+
+/* Pops n ids from the head into out_ids[0..n) and sets their reference
+ * counts to 1.  All-or-nothing: PA_ENOBLOCKS if fewer than n are free, with
+ * no state change.  n == 0 is a no-op; n < 0 is PA_EINVAL. */
+int pa_allocator_allocate(pa_allocator* a, int32_t n, int32_t* out_ids);
+
+/* Adds one reference to each listed (allocated) block.  PA_EINVAL, with no
+ * state change, if any id is out of range or free. */
+int pa_allocator_share(pa_allocator* a, const int32_t* ids, int32_t n);
+
+/* Drops one reference per listed id (an id may repeat); a block whose count
+ * reaches zero is pushed to the tail, in list order.  PA_EINVAL, with no
+ * state change, if any id is out of range or would drop below zero. */
+int pa_allocator_free(pa_allocator* a, const int32_t* ids, int32_t n);
+
+int32_t pa_allocator_num_free(const pa_allocator* a);
+int32_t pa_allocator_num_blocks(const pa_allocator* a);
+
+/* Whole state: queue_out[0..num_free) = queue head..tail (nullable),
+ * refcount_out[0..num_blocks) (nullable). */
+int pa_allocator_export(const pa_allocator* a, int32_t* queue_out,
+                        int32_t* refcount_out);
+
+/* Fragmentation stats: *used_blocks = blocks with a live reference;
+ * *tail_waste_tokens = sum over the B sequences of ceil(L/bs)*bs - L (the
+ * unused slots of each last block). */
+int pa_allocator_stats(const pa_allocator* a, const int32_t* seq_lens,
+                       int32_t B, int32_t block_size, int64_t* used_blocks,
+                       int64_t* tail_waste_tokens);
+
+/* ---------------------------------------------------------------------------
+ * Token -> slot ("Inside vLLM", section "LLM Engine & Engine Core": blocks
+ * map tokens to their KV-cache blocks).  Host memory.
+ * For each sequence b (in order) and i in [0, num_tokens[b]):
+ *   p = start_pos[b] + i
+ *   out[k++] = block_tables[b*max_blocks_per_seq + p/bs] * bs + p % bs
+ * Returns PA_EINVAL if a needed table entry is negative or p/bs is beyond
+ * max_blocks_per_seq.  *total (nullable) receives the number of slots.
+ * ------------------------------------------------------------------------- */
+int pa_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* start_pos, const int32_t* num_tokens,
+                    int32_t B, int32_t block_size, int64_t* out,
+                    int64_t* total);
+
+/* ---------------------------------------------------------------------------
+ * Device operations
+ * ------------------------------------------------------------------------- */
+
+/* Writes new keys/values into the cache ("Inside vLLM", section "LLM Engine
+ * constructor": KV tensors bound to the layers; section "LLM Engine & Engine
+ * Core": tokens map to their blocks).
+ *   key, value   [num_tokens][num_kv_heads][head_size], dtype, device
+ *   slot_mapping [num_tokens] int64, device; slot < 0 skips the token;
+ *                slots must be unique and < num_blocks*block_size
+ *   kv_cache     pool layout above, device
+ * Values are copied bit for bit.  block_size must be 16; head_size 64 or
+ * 128 (PA_ENOTSUP otherwise).  num_tokens == 0 enqueues nothing. */
+int pa_reshape_and_cache(const void* key, const void* value,
+                         const int64_t* slot_mapping, int32_t num_tokens,
+                         void* kv_cache, int32_t num_blocks,
+                         int32_t block_size, int32_t num_kv_heads,
+                         int32_t head_size, int32_t dtype, void* stream);
+
+/* Device workspace pa_decode needs for split-K partials, in bytes (0 when
+ * partition_size == 0 or one partition covers max_seq_len). */
+size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads,
+                                 int32_t head_size, int32_t max_seq_len,
+                                 int32_t partition_size);
+
+/* Decode attention: one query token per sequence, the last of its seq_len
+ * cached tokens (already written), attends to all of them through its block
+ * table; grouped-query heads share KV heads.  The attention itself is the
+ * standard transformer's ("Inside vLLM", "LLM Engine & Engine Core"):
+ *   o = softmax(scale * q K^T) V,  lse = ln sum exp(scale * q K^T).
+ *   out          [B][H_q][D] dtype, device (written)
+ *   lse_out      [B][H_q] fp32, device, nullable (natural log; -inf and
+ *                out = 0 for seq_len 0)
+ *   query        [B][H_q][D] dtype, device
+ *   block_tables [B][max_blocks_per_seq] int32, device
+ *   seq_lens     [B] int32, device, each in [0, max_seq_len]
+ *   partition_size  0: one pass per (sequence, KV head); otherwise a
+ *                multiple of block_size: the context is split into
+ *                partitions of that many tokens, each processed by its own
+ *                workgroup, and a second kernel combines the partials with
+ *                a log-sum-exp weighted sum (split-K).
+ *   workspace    device, >= pa_decode_workspace_bytes(...) bytes (nullable
+ *                when that is 0), owned by the caller; contents need no
+ *                initialisation and are scratch after the call.
+ * Supported: block_size 16; head_size 64 or 128; H_q % H_kv == 0 with
+ * G = H_q/H_kv in {1, 2, 4, 8} (and 16 for head_size 64). */
+int pa_decode(void* out, float* lse_out, const void* query,
+              const void* kv_cache, int32_t num_blocks,
+              const int32_t* block_tables, int32_t max_blocks_per_seq,
+              const int32_t* seq_lens, int32_t B, int32_t max_seq_len,
+              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
+              int32_t block_size, float scale, int32_t partition_size,
+              void* workspace, size_t workspace_bytes, int32_t dtype,
+              void* stream);
+
+/* Chunked prefill ("Im Inneren von vLLM", "Fortgeschrittene Funktionen":
+ * long prompts are split into chunks; "Inside vLLM", "Generate function":
+ * the batch is flattened into one sequence of tokens).  Sequence b owns the
+ * packed query rows [query_start_loc[b], query_start_loc[b+1]); its C_b
+ * queries are its last C_b tokens (keys/values already written), and query
+ * i at position seq_lens[b] - C_b + i attends causally to tokens
+ * 0..position, reading the cached prefix (possibly blocks shared with other
+ * sequences) and its own keys through its block table.
+ *   out, query      [total_query_tokens][H_q][D] bf16, device
+ *   lse_out         [total_query_tokens][H_q] fp32, device, nullable
+ *   query_start_loc [B+1] int32, device, non-decreasing, [0] = 0,
+ *                   [B] = total_query_tokens, every C_b <= max_query_len
+ *   seq_lens        [B] int32, device, C_b <= seq_lens[b] <= max_seq_len
+ * Supported: bf16 only; block_size 16; head_size 128 or 64; G in
+ * {1, 2, 4, 8}. */
+int pa_prefill_chunk(void* out, float* lse_out, const void* query,
+                     const int32_t* query_start_loc, int32_t max_query_len,
+                     int32_t total_query_tokens, const void* kv_cache,
+                     int32_t num_blocks, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                     int32_t B, int32_t max_seq_len, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_size,
+                     int32_t block_size, float scale, int32_t dtype,
+                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,564 @@
+// pa_decode: one query token per sequence attending to its paged KV cache,
+// grouped-query heads, optional split-K over context partitions with a
+// log-sum-exp reduce pass.
+//
+// What is computed ("Inside vLLM: Anatomy of a High-Throughput LLM Inference
+// System", section "LLM Engine & Engine Core": paged attention over blocks
+// that map tokens to their KV-cache blocks; the attention is the standard
+// transformer's): for sequence b and query head h with KV head g = h / G,
+//   s_t = scale * <q[b,h], K_b[t,g]>,  o = sum_t softmax(s)_t V_b[t,g],
+//   lse = ln sum_t exp(s_t),  t = 0 .. seq_len[b]-1,
+// with K_b[t] / V_b[t] read from physical block block_tables[b][t/16],
+// offset t%16.  Paging only moves where keys/values live ("vLLM: Ein tiefer
+// Einblick ...", section "Tiefenanalyse"), so results do not depend on the
+// physical block ids: the arithmetic order below depends only on logical
+// token positions.
+//
+// Design (gfx950, HBM-bound: 4-8 flop per byte of KV):
+//   * one workgroup of 4 waves per (partition, KV head, sequence); the G
+//     query heads of a KV head share every K/V byte loaded, so each byte of
+//     the cache is read from HBM once per step;
+//   * wave w of the workgroup takes logical blocks w, w+4, ... of its
+//     partition and keeps its own online-softmax state; the four states are
+//     merged through LDS at the end (split of the context inside the
+//     workgroup), and partitions are merged by the reduce kernel;
+//   * K tile (16 tokens x D): one coalesced global load per lane into
+//     registers, prefetched one block ahead, written to a padded LDS tile,
+//     read back as (token, head group, d-part) per lane, so q.k needs no
+//     cross-lane reduction beyond the d-parts; bf16 q.k uses v_dot2_f32_bf16;
+//   * softmax max over the 16 tokens of a block is a DPP butterfly in each
+//     16-lane row; scores are kept in the log2 domain (exp2);
+//   * P goes to LDS as packed bf16 token pairs; V is loaded straight from
+//     global memory with each lane owning one column pair, and P.V is again
+//     v_dot2_f32_bf16 over token pairs after a byte permute;
+//   * the denominator sums the same bf16-rounded P that multiplies V.
+#include "pa.h"
+#include "pa_common.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+constexpr int kDecodeWaves = 4;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <int D, int G, bool BF16>
+struct DecodeCfg {
+  static constexpr int ES = BF16 ? 2 : 4;          // element bytes
+  static constexpr int RB = D * ES;                // bytes per K/V row
+  static constexpr int CPR = RB / 16;              // 16-byte chunks per row
+  static constexpr int TILE_VEC = 16 * CPR;        // 16-byte vectors per tile
+  static constexpr int LOADS = TILE_VEC / kWave;   // vector loads per lane per tile
+  static constexpr int HG = G >= 4 ? 4 : G;        // head groups across lanes
+  static constexpr int HPL = G / HG;               // heads per lane
+  static constexpr int QCH_NEED = HPL * CPR;       // q chunks a lane would need with DP = 1
+  static constexpr int DP_Q = QCH_NEED <= 16 ? 1 : QCH_NEED / 16;  // keep q <= 16 chunks
+  static constexpr int DP_MIN = 4 / HG;
+  static constexpr int DP = DP_Q > DP_MIN ? DP_Q : DP_MIN;  // lanes sharing one token row
+  static constexpr int TPP = kWave / (HG * DP);    // tokens per pass
+  static constexpr int NPASS = 16 / TPP;
+  static constexpr int CPL = CPR / DP;             // chunks per lane per row
+  static constexpr int LDS_ROW = RB + 16;          // padded row (bank spread)
+  static constexpr int LDS_TILE = 16 * LDS_ROW;
+  // P.V layout: lanes own columns; bf16 D=64 splits the 16 rows over 2 halves
+  static constexpr int DPL = BF16 ? 2 : D / kWave;  // output columns per lane
+  static constexpr int HALVES = (BF16 && D == 64) ? 2 : 1;
+  static constexpr int ROWS = 16 / HALVES;         // V rows per lane
+  static constexpr int VW = BF16 ? 1 : DPL;        // V dwords per row per lane
+  static constexpr int P_BYTES = BF16 ? G * 8 * 4 : G * 16 * 4;
+  static_assert(CPR % DP == 0 && TPP >= 1 && 16 % TPP == 0, "bad decode lane split");
+  static_assert(HG * DP * TPP == kWave, "lane split must cover the wave");
+  static_assert(TILE_VEC % kWave == 0, "tile must be a whole number of wave loads");
+  static_assert(!BF16 || D == 64 || D == 128, "bf16 head sizes 64/128");
+};
+
+// q.k partial over one 16-byte chunk
+template <bool BF16>
+__device__ __forceinline__ float chunk_dot(const uint4& q, const uint4& k, float acc) {
+  if constexpr (BF16) {
+    acc = dot2_bf16(q.x, k.x, acc);
+    acc = dot2_bf16(q.y, k.y, acc);
+    acc = dot2_bf16(q.z, k.z, acc);
+    acc = dot2_bf16(q.w, k.w, acc);
+  } else {
+    acc = fmaf(__uint_as_float(q.x), __uint_as_float(k.x), acc);
+    acc = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
+    acc = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
+    acc = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
+  }
+  return acc;
+}
+
+template <int D, int G, bool BF16>
+__global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(
+    void* __restrict__ out, float* __restrict__ lse_out, const void* __restrict__ query,
+    const uint8_t* __restrict__ cache, int num_blocks, const int* __restrict__ block_tables,
+    int max_blocks_per_seq, const int* __restrict__ seq_lens, int max_seq_len, int num_kv_heads,
+    float scale_log2, int part_blocks, int max_parts, float* __restrict__ ws_m,
+    float* __restrict__ ws_l, float* __restrict__ ws_o) {
+  using C = DecodeCfg<D, G, BF16>;
+  const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int H_q = num_kv_heads * G;
+  int L = seq_lens[b];
+  L = L < 0 ? 0 : (L > max_seq_len ? max_seq_len : L);
+  const int nblk = (L + 15) >> 4;
+  const int pb = part_blocks > 0 ? part_blocks : (nblk > 0 ? nblk : 1);
+  const int nparts = (nblk + pb - 1) / pb;
+  if (part > 0 && part >= nparts) return;
+  const int blk_lo = part * pb;
+  const int blk_hi = min(blk_lo + pb, nblk);
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // QK lane roles
+  const int dp = lane % C::DP;
+  const int tq = (lane / C::DP) % C::TPP;
+  const int hg = lane / (C::DP * C::TPP);
+
+  // K tiles during the loop; afterwards the per-wave outputs [wave][G][D] fp32
+  constexpr int kTiles = kDecodeWaves * C::LDS_TILE;
+  constexpr int kOStage = kDecodeWaves * G * D * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t smem_k[kTiles > kOStage ? kTiles : kOStage];
+  __shared__ __attribute__((aligned(16))) uint32_t smem_p[kDecodeWaves][C::P_BYTES / 4];
+  __shared__ float smem_alpha[kDecodeWaves][G];
+  __shared__ float smem_m[kDecodeWaves][G];
+  __shared__ float smem_l[kDecodeWaves][G];
+
+  // ---- query chunks for this lane: heads hg*HPL + hh, chunks dp*CPL + c
+  uint4 q[C::HPL][C::CPL];
+  {
+    const uint4* qb = reinterpret_cast<const uint4*>(query) + int64_t(b) * H_q * C::CPR;
+#pragma unroll
+    for (int hh = 0; hh < C::HPL; ++hh) {
+      const int h = g * G + hg * C::HPL + hh;
+#pragma unroll
+      for (int c = 0; c < C::CPL; ++c) q[hh][c] = qb[h * C::CPR + dp * C::CPL + c];
+    }
+  }
+
+  const int64_t tile_bytes = int64_t(16) * C::RB;
+  const int64_t block_bytes = int64_t(2) * num_kv_heads * tile_bytes;
+  const int* bt_row = block_tables + int64_t(b) * max_blocks_per_seq;
+
+  // online-softmax state (log2 domain)
+  float m_run[C::HPL];     // running max per lane head (uniform across the 16-lane row)
+  float l_part[C::HPL];    // this lane's share of the denominator
+#pragma unroll
+  for (int hh = 0; hh < C::HPL; ++hh) { m_run[hh] = -INFINITY; l_part[hh] = 0.f; }
+  float o[G][C::DPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int j = 0; j < C::DPL; ++j) o[h][j] = 0.f;
+
+  // P.V lane roles
+  const int half = C::HALVES == 2 ? (lane >> 5) : 0;
+  const int col = C::HALVES == 2 ? (lane & 31) : lane;  // dword column within the row
+
+  auto tile_base = [&](int j, int kv) -> const uint8_t* {
+    int phys = bt_row[j];
+    phys = (phys < 0 || phys >= num_blocks) ? 0 : phys;
+    return cache + int64_t(phys) * block_bytes + int64_t(kv * num_kv_heads + g) * tile_bytes;
+  };
+
+  uint4 kreg[C::LOADS];
+  uint32_t vreg[C::ROWS][C::VW];
+  auto load_block = [&](int j) {
+    const uint4* kt = reinterpret_cast<const uint4*>(tile_base(j, 0));
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) kreg[i] = kt[i * kWave + lane];
+    const uint32_t* vt = reinterpret_cast<const uint32_t*>(tile_base(j, 1));
+#pragma unroll
+    for (int r = 0; r < C::ROWS; ++r) {
+      const int row = half * C::ROWS + r;
+#pragma unroll
+      for (int w = 0; w < C::VW; ++w) vreg[r][w] = vt[row * (C::RB / 4) + col * C::VW + w];
+    }
+  };
+
+  uint8_t* kt_lds = smem_k + wave * C::LDS_TILE;
+  uint32_t* p_lds = smem_p[wave];
+
+  int j = blk_lo + wave;
+  if (j < blk_hi) load_block(j);
+  for (; j < blk_hi; j += kDecodeWaves) {
+    // current block's registers, then prefetch the next one
+    uint4 kcur[C::LOADS];
+    uint32_t vcur[C::ROWS][C::VW];
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) kcur[i] = kreg[i];
+#pragma unroll
+    for (int r = 0; r < C::ROWS; ++r)
+#pragma unroll
+      for (int w = 0; w < C::VW; ++w) vcur[r][w] = vreg[r][w];
+    if (j + kDecodeWaves < blk_hi) load_block(j + kDecodeWaves);
+
+    const int valid = min(16, L - j * 16);  // tokens of this block inside the sequence
+
+    // K tile -> LDS (padded rows)
+    wave_lds_sync();  // previous block's reads of the tile are done
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int v = i * kWave + lane;
+      const int row = v / C::CPR, ch = v % C::CPR;
+      *reinterpret_cast<uint4*>(kt_lds + row * C::LDS_ROW + ch * 16) = kcur[i];
+    }
+    wave_lds_sync();
+
+    // ---- scores for this lane's token(s) and heads
+    float s[C::NPASS][C::HPL];
+#pragma unroll
+    for (int ps = 0; ps < C::NPASS; ++ps) {
+      const int row = ps * C::TPP + tq;
+      const uint4* kr = reinterpret_cast<const uint4*>(kt_lds + row * C::LDS_ROW) + dp * C::CPL;
+#pragma unroll
+      for (int hh = 0; hh < C::HPL; ++hh) s[ps][hh] = 0.f;
+#pragma unroll
+      for (int c = 0; c < C::CPL; ++c) {
+        const uint4 kv = kr[c];
+#pragma unroll
+        for (int hh = 0; hh < C::HPL; ++hh) s[ps][hh] = chunk_dot<BF16>(q[hh][c], kv, s[ps][hh]);
+      }
+#pragma unroll
+      for (int hh = 0; hh < C::HPL; ++hh) {
+        float x = allreduce_sum<0, ilog2(C::DP)>(s[ps][hh]);
+        x *= scale_log2;
+        s[ps][hh] = (row < valid) ? x : -INFINITY;
+      }
+    }
+
+    // ---- online softmax per head (max over the block's 16 tokens)
+    float alpha[C::HPL];
+#pragma unroll
+    for (int hh = 0; hh < C::HPL; ++hh) {
+      float mb = s[0][hh];
+#pragma unroll
+      for (int ps = 1; ps < C::NPASS; ++ps) mb = fmaxf(mb, s[ps][hh]);
+      mb = allreduce_max<ilog2(C::DP), ilog2(C::DP * C::TPP)>(mb);
+      const float m_new = fmaxf(m_run[hh], mb);  // finite: token 0 of the block is valid
+      alpha[hh] = exp2f(m_run[hh] - m_new);
+      m_run[hh] = m_new;
+      l_part[hh] *= alpha[hh];
+    }
+
+    // ---- P to LDS
+#pragma unroll
+    for (int ps = 0; ps < C::NPASS; ++ps) {
+      const int row = ps * C::TPP + tq;
+#pragma unroll
+      for (int hh = 0; hh < C::HPL; ++hh) {
+        const int h = hg * C::HPL + hh;
+        const float p = exp2f(s[ps][hh] - m_run[hh]);
+        if constexpr (BF16) {
+          const uint32_t pb16 = f32_to_bf16_rne(p);
+          l_part[hh] += (dp == 0) ? __uint_as_float(pb16 << 16) : 0.f;
+          const uint32_t nb = dpp_u<0x100 + C::DP>(pb16);  // row_shl: lane + DP = token + 1
+          if (dp == 0 && (row & 1) == 0) p_lds[h * 8 + (row >> 1)] = pb16 | (nb << 16);
+        } else {
+          l_part[hh] += (dp == 0) ? p : 0.f;
+          if (dp == 0) reinterpret_cast<float*>(p_lds)[h * 16 + row] = p;
+        }
+      }
+    }
+    if (tq == 0 && dp == 0) {
+#pragma unroll
+      for (int hh = 0; hh < C::HPL; ++hh) smem_alpha[wave][hg * C::HPL + hh] = alpha[hh];
+    }
+    wave_lds_sync();
+
+    // ---- rescale and accumulate P.V
+    if (valid < 16) {  // tail block: rows past the sequence may hold anything
+#pragma unroll
+      for (int r = 0; r < C::ROWS; ++r)
+#pragma unroll
+        for (int w = 0; w < C::VW; ++w)
+          vcur[r][w] = (half * C::ROWS + r < valid) ? vcur[r][w] : 0u;
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float a = smem_alpha[wave][h];
+#pragma unroll
+      for (int jj = 0; jj < C::DPL; ++jj) o[h][jj] *= a;
+    }
+    if constexpr (BF16) {
+      // token pairs (2k, 2k+1) of this lane's rows
+      constexpr int PAIRS = C::ROWS / 2;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        uint32_t pw[PAIRS];
+#pragma unroll
+        for (int k4 = 0; k4 < PAIRS; k4 += 4) {
+          const uint4 t4 = *reinterpret_cast<const uint4*>(p_lds + h * 8 + half * PAIRS + k4);
+          pw[k4] = t4.x; pw[k4 + 1] = t4.y; pw[k4 + 2] = t4.z; pw[k4 + 3] = t4.w;
+        }
+#pragma unroll
+        for (int k = 0; k < PAIRS; ++k) {
+          const uint32_t v0 = vcur[2 * k][0], v1 = vcur[2 * k + 1][0];
+          const uint32_t xlo = __builtin_amdgcn_perm(v1, v0, 0x05040100u);  // (v0.lo, v1.lo)
+          const uint32_t xhi = __builtin_amdgcn_perm(v1, v0, 0x07060302u);  // (v0.hi, v1.hi)
+          o[h][0] = dot2_bf16(xlo, pw[k], o[h][0]);
+          o[h][1] = dot2_bf16(xhi, pw[k], o[h][1]);
+        }
+      }
+    } else {
+      const float* pf = reinterpret_cast<const float*>(p_lds);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = pf[h * 16 + r];
+#pragma unroll
+          for (int w = 0; w < C::VW; ++w) o[h][w] = fmaf(p, __uint_as_float(vcur[r][w]), o[h][w]);
+        }
+      }
+    }
+  }
+
+  // ---- merge: this wave's denominator, then the 4 waves of the workgroup
+#pragma unroll
+  for (int hh = 0; hh < C::HPL; ++hh) {
+    // sum over token lanes of the row (d-part replicas contributed 0)
+    float lsum = l_part[hh];
+#pragma unroll
+    for (int bit = ilog2(C::DP); bit < ilog2(C::DP * C::TPP); ++bit)
+      lsum += __shfl_xor(lsum, 1 << bit, kWave);
+    if (tq == 0 && dp == 0) {
+      smem_m[wave][hg * C::HPL + hh] = m_run[hh];
+      smem_l[wave][hg * C::HPL + hh] = lsum;
+    }
+  }
+  if constexpr (C::HALVES == 2) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int jj = 0; jj < C::DPL; ++jj) o[h][jj] += __shfl_xor(o[h][jj], 32, kWave);
+  }
+  __syncthreads();  // all waves done with their tiles: reuse smem_k for o
+  float* o_lds = reinterpret_cast<float*>(smem_k);  // [wave][G][D]
+  if (C::HALVES == 1 || half == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int jj = 0; jj < C::DPL; ++jj)
+        o_lds[(wave * G + h) * D + col * C::DPL + jj] = o[h][jj];
+  }
+  __syncthreads();
+
+  const bool single = nparts <= 1;
+  for (int e = threadIdx.x; e < G * D; e += kDecodeWaves * kWave) {
+    const int h = e / D, d = e % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, smem_m[w][h]);
+    float lsum = 0.f, acc = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kDecodeWaves; ++w) {
+        const float wt = exp2f(smem_m[w][h] - M);  // 0 for a wave with no tokens
+        lsum += wt * smem_l[w][h];
+        acc += wt * o_lds[(w * G + h) * D + d];
+      }
+    }
+    const int hq = g * G + h;
+    const int64_t row = int64_t(b) * H_q + hq;
+    if (single) {
+      const float val = lsum > 0.f ? acc / lsum : 0.f;
+      if constexpr (BF16)
+        reinterpret_cast<uint16_t*>(out)[row * D + d] = uint16_t(f32_to_bf16_rne(val));
+      else
+        reinterpret_cast<float*>(out)[row * D + d] = val;
+      if (lse_out && d == 0) lse_out[row] = lsum > 0.f ? M * kLn2 + logf(lsum) : -INFINITY;
+    } else {
+      const int64_t prow = row * max_parts + part;
+      ws_o[prow * D + d] = lsum > 0.f ? acc / lsum : 0.f;
+      if (d == 0) {
+        ws_m[prow] = M;
+        ws_l[prow] = lsum;
+      }
+    }
+  }
+}
+
+// Combines the partition partials of every (sequence, query head) with more
+// than one partition: M = max m_p, w_p = 2^(m_p - M) l_p,
+// O = sum w_p o_p / sum w_p, lse = ln2 * M + ln sum w_p.  One wave per row.
+template <int D, bool BF16>
+__global__ __launch_bounds__(kWave) void decode_reduce_kernel(
+    void* __restrict__ out, float* __restrict__ lse_out, const int* __restrict__ seq_lens,
+    int max_seq_len, int H_q, int part_tokens, int max_parts, const float* __restrict__ ws_m,
+    const float* __restrict__ ws_l, const float* __restrict__ ws_o) {
+  const int hq = blockIdx.x, b = blockIdx.y;
+  int L = seq_lens[b];
+  L = L < 0 ? 0 : (L > max_seq_len ? max_seq_len : L);
+  const int nparts = (L + part_tokens - 1) / part_tokens;
+  if (nparts <= 1) return;  // written by the partition kernel
+  const int lane = threadIdx.x;
+  const int64_t row = int64_t(b) * H_q + hq;
+  const float* m = ws_m + row * max_parts;
+  const float* l = ws_l + row * max_parts;
+  float M = -INFINITY;
+  for (int p = lane; p < nparts; p += kWave) M = fmaxf(M, m[p]);
+  M = allreduce_max<0, 6>(M);
+  constexpr int DPL = D / kWave;
+  float acc[DPL] = {};
+  float wsum = 0.f;
+  for (int p = 0; p < nparts; ++p) {
+    const float wt = exp2f(m[p] - M) * l[p];
+    wsum += wt;
+    const float* op = ws_o + (row * max_parts + p) * D;
+#pragma unroll
+    for (int jj = 0; jj < DPL; ++jj) acc[jj] = fmaf(wt, op[jj * kWave + lane], acc[jj]);
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+  for (int jj = 0; jj < DPL; ++jj) {
+    const float val = acc[jj] * inv;
+    const int d = jj * kWave + lane;
+    if constexpr (BF16)
+      reinterpret_cast<uint16_t*>(out)[row * D + d] = uint16_t(f32_to_bf16_rne(val));
+    else
+      reinterpret_cast<float*>(out)[row * D + d] = val;
+  }
+  if (lse_out && lane == 0) lse_out[row] = wsum > 0.f ? M * kLn2 + logf(wsum) : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+struct DecodeArgs {
+  void* out;
+  float* lse;
+  const void* q;
+  const uint8_t* cache;
+  int num_blocks;
+  const int* bt;
+  int max_blocks;
+  const int* seq_lens;
+  int B, max_seq_len, H_kv;
+  float scale_log2;
+  int part_blocks, max_parts;
+  float *ws_m, *ws_l, *ws_o;
+  hipStream_t s;
+};
+
+template <int D, int G, bool BF16>
+static void launch_decode(const DecodeArgs& a) {
+  dim3 grid(a.max_parts, a.H_kv, a.B);
+  hipLaunchKernelGGL((decode_partition_kernel<D, G, BF16>), grid, dim3(kDecodeWaves * kWave), 0,
+                     a.s, a.out, a.lse, a.q, a.cache, a.num_blocks, a.bt, a.max_blocks, a.seq_lens,
+                     a.max_seq_len, a.H_kv, a.scale_log2, a.part_blocks, a.max_parts, a.ws_m,
+                     a.ws_l, a.ws_o);
+  if (a.max_parts > 1)
+    hipLaunchKernelGGL((decode_reduce_kernel<D, BF16>), dim3(a.H_kv * G, a.B), dim3(kWave), 0, a.s,
+                       a.out, a.lse, a.seq_lens, a.max_seq_len, a.H_kv * G, a.part_blocks * 16,
+                       a.max_parts, a.ws_m, a.ws_l, a.ws_o);
+}
+
+template <int D, bool BF16>
+static bool dispatch_g(int G, const DecodeArgs& a) {
+  switch (G) {
+    case 1: launch_decode<D, 1, BF16>(a); return true;
+    case 2: launch_decode<D, 2, BF16>(a); return true;
+    case 4: launch_decode<D, 4, BF16>(a); return true;
+    case 8: launch_decode<D, 8, BF16>(a); return true;
+    case 16:
+      if constexpr (D == 64) { launch_decode<D, 16, BF16>(a); return true; }
+      return false;
+    default: return false;
+  }
+}
+
+static int64_t parts_for(int max_seq_len, int partition_size) {
+  if (partition_size <= 0 || max_seq_len <= 0) return 1;
+  return (int64_t(max_seq_len) + partition_size - 1) / partition_size;
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_size,
+                                            int32_t max_seq_len, int32_t partition_size) {
+  if (B <= 0 || num_q_heads <= 0 || head_size <= 0) return 0;
+  const int64_t P = parts_for(max_seq_len, partition_size);
+  if (P <= 1) return 0;
+  const int64_t rows = int64_t(B) * num_q_heads * P;
+  const int64_t mbytes = (rows * 4 + 255) / 256 * 256;
+  return size_t(2 * mbytes + rows * head_size * 4);
+}
+
+extern "C" int pa_decode(void* out, float* lse_out, const void* query, const void* kv_cache,
+                         int32_t num_blocks, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t B,
+                         int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_size, int32_t block_size, float scale,
+                         int32_t partition_size, void* workspace, size_t workspace_bytes,
+                         int32_t dtype, void* stream) {
+  if (B < 0 || num_blocks < 0 || max_seq_len < 0 || max_blocks_per_seq < 0)
+    return fail(PA_EINVAL, "pa_decode: negative size");
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
+    return fail(PA_EINVAL, "pa_decode: H_q %d not a multiple of H_kv %d", num_q_heads, num_kv_heads);
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_EINVAL, "pa_decode: unknown dtype %d", dtype);
+  if (block_size != kBlockSize) return fail(PA_ENOTSUP, "pa_decode: block_size %d (only 16)", block_size);
+  if (head_size != 64 && head_size != 128)
+    return fail(PA_ENOTSUP, "pa_decode: head_size %d (64 or 128)", head_size);
+  if (partition_size < 0 || partition_size % kBlockSize)
+    return fail(PA_EINVAL, "pa_decode: partition_size %d must be a multiple of 16", partition_size);
+  if (int64_t(max_blocks_per_seq) * kBlockSize < max_seq_len)
+    return fail(PA_EINVAL, "pa_decode: max_seq_len %d exceeds the table (%d blocks)", max_seq_len,
+                max_blocks_per_seq);
+  if (!(scale == scale)) return fail(PA_EINVAL, "pa_decode: scale is NaN");
+  if (B == 0) return PA_OK;
+  if (!out || !query || !block_tables || !seq_lens || (!kv_cache && num_blocks > 0))
+    return fail(PA_EINVAL, "pa_decode: NULL pointer");
+  if ((uintptr_t(out) | uintptr_t(query) | uintptr_t(kv_cache)) & 15)
+    return fail(PA_EINVAL, "pa_decode: out/query/cache must be 16-byte aligned");
+  if ((uintptr_t(block_tables) | uintptr_t(seq_lens) | uintptr_t(lse_out)) & 3)
+    return fail(PA_EINVAL, "pa_decode: int/float arrays must be 4-byte aligned");
+  if (num_blocks == 0 && max_seq_len > 0)
+    return fail(PA_EINVAL, "pa_decode: empty pool but max_seq_len %d", max_seq_len);
+  const int G = num_q_heads / num_kv_heads;
+  const int64_t P = parts_for(max_seq_len, partition_size);
+  if (P > 65535) return fail(PA_EINVAL, "pa_decode: too many partitions (%lld)", (long long)P);
+  if (num_kv_heads > 65535 || B > 65535) return fail(PA_ENOTSUP, "pa_decode: grid too large");
+  const size_t need = pa_decode_workspace_bytes(B, num_q_heads, head_size, max_seq_len, partition_size);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PA_EINVAL, "pa_decode: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (need > 0 && (uintptr_t(workspace) & 255))
+    return fail(PA_EINVAL, "pa_decode: workspace must be 256-byte aligned");
+
+  DecodeArgs a{};
+  a.out = out;
+  a.lse = lse_out;
+  a.q = query;
+  a.cache = static_cast<const uint8_t*>(kv_cache);
+  a.num_blocks = num_blocks;
+  a.bt = block_tables;
+  a.max_blocks = max_blocks_per_seq;
+  a.seq_lens = seq_lens;
+  a.B = B;
+  a.max_seq_len = max_seq_len;
+  a.H_kv = num_kv_heads;
+  a.scale_log2 = scale * kLog2e;
+  a.part_blocks = P > 1 ? partition_size / kBlockSize : 0;
+  a.max_parts = int(P);
+  if (P > 1) {
+    const int64_t rows = int64_t(B) * num_q_heads * P;
+    const int64_t mbytes = (rows * 4 + 255) / 256 * 256;
+    uint8_t* w = static_cast<uint8_t*>(workspace);
+    a.ws_m = reinterpret_cast<float*>(w);
+    a.ws_l = reinterpret_cast<float*>(w + mbytes);
+    a.ws_o = reinterpret_cast<float*>(w + 2 * mbytes);
+  }
+  a.s = reinterpret_cast<hipStream_t>(stream);
+
+  bool ok;
+  if (dtype == PA_BF16)
+    ok = head_size == 64 ? dispatch_g<64, true>(G, a) : dispatch_g<128, true>(G, a);
+  else
+    ok = head_size == 64 ? dispatch_g<64, false>(G, a) : dispatch_g<128, false>(G, a);
+  if (!ok) return fail(PA_ENOTSUP, "pa_decode: group size %d with head_size %d", G, head_size);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_EHIP, "pa_decode: launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}

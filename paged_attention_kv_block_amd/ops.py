@@ -1,0 +1,283 @@
+"""ctypes binding of libpa.so: argument marshalling only.
+
+Every computation runs in the library: the host entry points (allocator, slot
+mapping, closed forms) in its C++ part and the device entry points in its HIP
+kernels.  Device arguments are torch tensors on the GPU; their data pointers
+and the current torch stream are handed to the C ABI unchanged.  There is no
+CPU fallback: if libpa.so is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpa.so")
+
+PA_OK, PA_EINVAL, PA_ENOBLOCKS, PA_ENOTSUP, PA_EHIP = 0, 1, 2, 3, 4
+PA_F32, PA_BF16 = 0, 1
+_STATUS = {PA_EINVAL: "EINVAL", PA_ENOBLOCKS: "ENOBLOCKS", PA_ENOTSUP: "ENOTSUP", PA_EHIP: "EHIP"}
+
+# name -> (restype, argtypes); mirrors include/pa.h
+_c_int, _c_i32, _c_i64, _c_u64, _c_sz = ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t
+_vp, _f = ctypes.c_void_p, ctypes.c_float
+SIGNATURES = {
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_version": (_c_int, []),
+    "pa_kv_block_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32]),
+    "pa_num_blocks_for_budget": (_c_i64, [_c_u64, _c_sz, _c_i32]),
+    "pa_allocator_create": (_c_int, [_c_i32, _vp, ctypes.POINTER(_vp)]),
+    "pa_allocator_destroy": (None, [_vp]),
+    "pa_allocator_allocate": (_c_int, [_vp, _c_i32, _vp]),
+    "pa_allocator_share": (_c_int, [_vp, _vp, _c_i32]),
+    "pa_allocator_free": (_c_int, [_vp, _vp, _c_i32]),
+    "pa_allocator_num_free": (_c_i32, [_vp]),
+    "pa_allocator_num_blocks": (_c_i32, [_vp]),
+    "pa_allocator_export": (_c_int, [_vp, _vp, _vp]),
+    "pa_allocator_stats": (_c_int, [_vp, _vp, _c_i32, _c_i32, _vp, _vp]),
+    "pa_slot_mapping": (_c_int, [_vp, _c_i32, _vp, _vp, _c_i32, _c_i32, _vp, _vp]),
+    "pa_reshape_and_cache": (_c_int, [_vp, _vp, _vp, _c_i32, _vp, _c_i32, _c_i32, _c_i32,
+                                      _c_i32, _c_i32, _vp]),
+    "pa_decode_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "pa_decode": (_c_int, [_vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _vp, _c_i32, _c_i32,
+                           _c_i32, _c_i32, _c_i32, _c_i32, _f, _c_i32, _vp, _c_sz, _c_i32, _vp]),
+    "pa_prefill_chunk": (_c_int, [_vp, _vp, _vp, _vp, _c_i32, _c_i32, _vp, _c_i32, _vp, _c_i32,
+                                  _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _f,
+                                  _c_i32, _vp]),
+}
+
+_lib = None
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def lib(path: Optional[str] = None) -> ctypes.CDLL:
+    """Loads libpa.so (built in-tree by paged_attention_kv_block_amd.build)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with "
+                           "`python -m paged_attention_kv_block_amd.build` (no CPU fallback)")
+    L = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != PA_OK:
+        raise PAError(status, lib().pa_last_error().decode())
+
+
+def _np_ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+# ---------------------------------------------------------------------------
+# host entry points
+# ---------------------------------------------------------------------------
+def kv_block_bytes(block_size: int, num_kv_heads: int, head_size: int, dtype_bytes: int) -> int:
+    return int(lib().pa_kv_block_bytes(block_size, num_kv_heads, head_size, dtype_bytes))
+
+
+def num_blocks_for_budget(budget_bytes: int, block_bytes: int, num_layers: int) -> int:
+    n = int(lib().pa_num_blocks_for_budget(budget_bytes, block_bytes, num_layers))
+    if n < 0:
+        raise PAError(PA_EINVAL, "block_bytes and num_layers must be positive")
+    return n
+
+
+class NoFreeBlocks(PAError):
+    pass
+
+
+class Allocator:
+    """The free_block_queue allocator of libpa (FIFO, ref-counted)."""
+
+    def __init__(self, num_blocks: int, initial_order: Optional[Sequence[int]] = None):
+        self._h = ctypes.c_void_p()
+        order = None if initial_order is None else np.ascontiguousarray(initial_order, dtype=np.int32)
+        _check(lib().pa_allocator_create(int(num_blocks), None if order is None else _np_ptr(order),
+                                         ctypes.byref(self._h)))
+
+    def close(self):
+        if self._h:
+            lib().pa_allocator_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def allocate(self, n: int) -> list:
+        out = np.empty(max(int(n), 1), dtype=np.int32)
+        st = lib().pa_allocator_allocate(self._h, int(n), _np_ptr(out))
+        if st == PA_ENOBLOCKS:
+            raise NoFreeBlocks(st, lib().pa_last_error().decode())
+        _check(st)
+        return out[:max(int(n), 0)].tolist()
+
+    def share(self, ids) -> None:
+        a = np.ascontiguousarray(ids, dtype=np.int32)
+        _check(lib().pa_allocator_share(self._h, _np_ptr(a), a.size))
+
+    def free(self, ids) -> None:
+        a = np.ascontiguousarray(ids, dtype=np.int32)
+        _check(lib().pa_allocator_free(self._h, _np_ptr(a), a.size))
+
+    @property
+    def num_free(self) -> int:
+        return int(lib().pa_allocator_num_free(self._h))
+
+    @property
+    def num_blocks(self) -> int:
+        return int(lib().pa_allocator_num_blocks(self._h))
+
+    def export(self):
+        q = np.empty(max(self.num_free, 1), dtype=np.int32)
+        rc = np.empty(max(self.num_blocks, 1), dtype=np.int32)
+        _check(lib().pa_allocator_export(self._h, _np_ptr(q), _np_ptr(rc)))
+        return q[:self.num_free].tolist(), rc[:self.num_blocks].tolist()
+
+    def stats(self, seq_lens, block_size: int):
+        sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        used, waste = ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().pa_allocator_stats(self._h, _np_ptr(sl), sl.size, int(block_size),
+                                        ctypes.byref(used), ctypes.byref(waste)))
+        return used.value, waste.value
+
+
+def slot_mapping(block_tables: np.ndarray, start_pos, num_tokens, block_size: int) -> np.ndarray:
+    """Slots (int64) of positions start_pos[b] .. +num_tokens[b] for every b."""
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    if bt.ndim == 1:
+        bt = bt[None]
+    sp = np.ascontiguousarray(np.broadcast_to(start_pos, (bt.shape[0],)), dtype=np.int32)
+    nt = np.ascontiguousarray(np.broadcast_to(num_tokens, (bt.shape[0],)), dtype=np.int32)
+    out = np.empty(max(int(nt.sum()), 1), dtype=np.int64)
+    total = ctypes.c_int64()
+    _check(lib().pa_slot_mapping(_np_ptr(bt), bt.shape[1], _np_ptr(sp), _np_ptr(nt), bt.shape[0],
+                                 int(block_size), _np_ptr(out), ctypes.byref(total)))
+    return out[:total.value]
+
+
+# ---------------------------------------------------------------------------
+# device entry points (torch tensors on the GPU)
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    if t.dtype == torch.float32:
+        return PA_F32
+    raise PAError(PA_ENOTSUP, f"element type {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise PAError(PA_EINVAL, "device arguments must be GPU tensors")
+
+
+def reshape_and_cache(key, value, slot_mapping, kv_cache, stream=None) -> None:
+    """key/value [T, H_kv, D]; slot_mapping int64 [T]; kv_cache [N, 2, H_kv, 16, D]."""
+    _need_gpu(key, value, slot_mapping, kv_cache)
+    for t in (key, value, slot_mapping, kv_cache):
+        if not t.is_contiguous():
+            raise PAError(PA_EINVAL, "tensors must be contiguous")
+    N, two, Hkv, bs, D = kv_cache.shape
+    if two != 2 or key.shape != value.shape or tuple(key.shape[1:]) != (Hkv, D) \
+            or key.dtype != kv_cache.dtype or value.dtype != kv_cache.dtype:
+        raise PAError(PA_EINVAL, "shape/dtype mismatch between key/value and kv_cache")
+    if slot_mapping.dtype != _torch().int64 or slot_mapping.numel() != key.shape[0]:
+        raise PAError(PA_EINVAL, "slot_mapping must be int64 [T]")
+    _check(lib().pa_reshape_and_cache(_ptr(key), _ptr(value), _ptr(slot_mapping), key.shape[0],
+                                      _ptr(kv_cache), N, bs, Hkv, D, _dtype_code(kv_cache),
+                                      _stream(stream)))
+
+
+def decode_workspace_bytes(B: int, num_q_heads: int, head_size: int, max_seq_len: int,
+                           partition_size: int) -> int:
+    return int(lib().pa_decode_workspace_bytes(B, num_q_heads, head_size, max_seq_len,
+                                               partition_size))
+
+
+def decode(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int, scale: float,
+           partition_size: int = 0, workspace=None, lse=None, stream=None) -> None:
+    """out/query [B, H_q, D]; kv_cache [N, 2, H_kv, 16, D]; block_tables int32
+    [B, max_blocks]; seq_lens int32 [B]; lse fp32 [B, H_q] or None;
+    workspace a uint8 GPU tensor of decode_workspace_bytes(...) bytes."""
+    _need_gpu(out, query, kv_cache, block_tables, seq_lens, workspace, lse)
+    torch = _torch()
+    N, _, Hkv, bs, D = kv_cache.shape
+    B, Hq, Dq = query.shape
+    if Dq != D or tuple(out.shape) != (B, Hq, D) or out.dtype != kv_cache.dtype \
+            or query.dtype != kv_cache.dtype:
+        raise PAError(PA_EINVAL, "shape/dtype mismatch between out/query and kv_cache")
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32 \
+            or block_tables.shape[0] != B or seq_lens.numel() != B:
+        raise PAError(PA_EINVAL, "block_tables/seq_lens must be int32 with B rows")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq)):
+        raise PAError(PA_EINVAL, "lse must be fp32 [B, H_q]")
+    for t in (out, query, kv_cache, block_tables, seq_lens, workspace, lse):
+        if t is not None and not t.is_contiguous():
+            raise PAError(PA_EINVAL, "tensors must be contiguous")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode(_ptr(out), _ptr(lse), _ptr(query), _ptr(kv_cache), N,
+                           _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), B,
+                           int(max_seq_len), Hq, Hkv, D, bs, float(scale), int(partition_size),
+                           _ptr(workspace), ws_bytes, _dtype_code(kv_cache), _stream(stream)))
+
+
+def prefill_chunk(out, query, query_start_loc, max_query_len: int, kv_cache, block_tables,
+                  seq_lens, max_seq_len: int, scale: float, lse=None, stream=None) -> None:
+    """out/query packed [T, H_q, D] bf16; query_start_loc int32 [B+1]."""
+    _need_gpu(out, query, query_start_loc, kv_cache, block_tables, seq_lens, lse)
+    torch = _torch()
+    N, _, Hkv, bs, D = kv_cache.shape
+    T, Hq, Dq = query.shape
+    B = seq_lens.numel()
+    if Dq != D or tuple(out.shape) != (T, Hq, D) or out.dtype != kv_cache.dtype \
+            or query.dtype != kv_cache.dtype:
+        raise PAError(PA_EINVAL, "shape/dtype mismatch between out/query and kv_cache")
+    if query_start_loc.dtype != torch.int32 or query_start_loc.numel() != B + 1:
+        raise PAError(PA_EINVAL, "query_start_loc must be int32 [B+1]")
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32 or block_tables.shape[0] != B:
+        raise PAError(PA_EINVAL, "block_tables/seq_lens must be int32 with B rows")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (T, Hq)):
+        raise PAError(PA_EINVAL, "lse must be fp32 [T, H_q]")
+    _check(lib().pa_prefill_chunk(_ptr(out), _ptr(lse), _ptr(query), _ptr(query_start_loc),
+                                  int(max_query_len), T, _ptr(kv_cache), N, _ptr(block_tables),
+                                  block_tables.shape[1], _ptr(seq_lens), B, int(max_seq_len), Hq,
+                                  Hkv, D, bs, float(scale), _dtype_code(kv_cache),
+                                  _stream(stream)))
