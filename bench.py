@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1]
+
+One step is the device half of a decode step of the engine for a batch of
+sequences: pa_reshape_and_cache writes the new token's key/value of every
+sequence into its cache slot, then pa_decode attends from that token over the
+whole cached context (one launch; with split-K the partials are merged inside
+the same launch).  Host metadata (block tables from the free_block_queue
+allocator, slot mapping) is built once before timing, as the engine's CPU
+side does ahead of the step, and its cost is reported separately.
+
+Inputs are seeded synthetic draws (paged_attention_kv_block_amd.inputs) that
+are resident in HBM before timing.  The default workload is the
+TinyLlama-1.1B-shaped batch (64 sequences, 32/4 heads, head size 64, lengths
+uniform in [128, 2048], bf16).  Its pool (~79 MB) fits in the 256 MB
+Infinity Cache, so the step rotates over enough identical pool copies (>= 768
+MB) that each step reads its pool from HBM, as a real model's next visit to
+the same layer would.
+
+Prints one JSON line: metric/value (algorithmic GB/s of the whole step),
+the HBM roofline of the dominant kernel (decode), and the fp64 CPU oracle
+timed on this host as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+METRIC = "paged-attn decode KV GB/s (% of HBM peak) + context-tokens/s, 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+DECODE_SOURCES = ["paged_attention_kv_block_amd/csrc/pa_decode.hip",
+                  "paged_attention_kv_block_amd/csrc/pa_common.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def default_partition(wl) -> int:
+    if wl.partition_size:
+        return wl.partition_size
+    return 256 if wl.head_size == 64 else 512
+
+
+def decode_bytes(wl, seq_lens) -> int:
+    """Algorithmic bytes of one decode launch: valid K/V of every context
+    token, query in, output out, the used block-table entries, seq_lens."""
+    db = wl.dtype_bytes
+    kv = int(sum(int(L) for L in seq_lens)) * 2 * wl.num_kv_heads * wl.head_size * db
+    qo = 2 * wl.num_seqs * wl.num_q_heads * wl.head_size * db
+    bt = sum((int(L) + wl.block_size - 1) // wl.block_size for L in seq_lens) * 4
+    return kv + qo + bt + 4 * wl.num_seqs
+
+
+def cache_write_bytes(wl) -> int:
+    """pa_reshape_and_cache of one new token per sequence: read K and V rows,
+    write them, read the slot."""
+    row = wl.num_kv_heads * wl.head_size * wl.dtype_bytes
+    return wl.num_seqs * (4 * row + 8)
+
+
+def load_traffic(kernel_hash: str, launches_per_step: int):
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_hash:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(d, min_seconds: float):
+    """The fp64 oracle (as it stands) on this host: the same step (write the
+    new tokens, decode) repeated until min_seconds of CPU time; BLAS limited
+    to one thread so `cores` is what it used."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from tests.oracle_setup import OracleSide
+
+    wl = d.wl
+    side = OracleSide(d)   # allocator, tables and the full cache (setup, untimed)
+    q = d.query()
+    new_k, new_v, slots = [], [], []
+    for b in range(wl.num_seqs):
+        L = int(d.seq_lens[b])
+        k, v = d.kv(b)
+        new_k.append(k[L - 1])
+        new_v.append(v[L - 1])
+        slots.append(oracle.slot_mapping(side.block_tables[b], L - 1, 1, wl.block_size)[0])
+    new_k, new_v, slots = np.stack(new_k), np.stack(new_v), np.array(slots)
+    reps, t0 = 0, time.perf_counter()
+    with threadpool_limits(1):
+        while True:
+            oracle.reshape_and_cache(side.pool, new_k, new_v, slots)
+            oracle.decode(q, side.pool, side.block_tables, d.seq_lens, wl.scale)
+            reps += 1
+            if time.perf_counter() - t0 >= min_seconds:
+                break
+    dt = (time.perf_counter() - t0) / reps
+    return dt, reps
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=1, help="decode workload index (1, 2, 4; 0 = tiny)")
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="split-K partition in tokens (default: workload's, else 256/512)")
+    ap.add_argument("--rotate-mb", type=int, default=768,
+                    help="total size of rotated pool copies (defeats the 256 MB Infinity Cache)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for counter calibration)")
+    a = ap.parse_args(argv)
+
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; multi-GPU sharding is not "
+              "implemented (--gpus must be 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from paged_attention_kv_block_amd import host, inputs, ops
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda", 0)
+
+    if a.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 5 copies of {n} bytes")
+        return 0
+
+    wl = inputs.workload(a.workload)
+    if wl.kind != "decode":
+        print("bench.py: the benchmarked step is decode; pick a decode workload", file=sys.stderr)
+        return 2
+    d = inputs.draw(a.workload)
+    B, Hq, Hkv, D, bs = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_size, wl.block_size
+    P = default_partition(wl) if a.partition_size is None else a.partition_size
+    seq_lens = d.seq_lens
+    msl = int(seq_lens.max())
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+    def dev_tensor(arr):
+        if wl.dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(arr)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    # ---- host metadata (engine CPU side), timed separately
+    t0 = time.perf_counter()
+    alloc = ops.Allocator(d.num_blocks, d.pool_order)
+    bt = host.decode_block_tables(alloc, seq_lens, bs)
+    new_slots = ops.slot_mapping(bt, seq_lens - 1, 1, bs)
+    host_us = (time.perf_counter() - t0) * 1e6
+
+    # ---- device inputs: cache holds tokens 0..L-2; the step writes token L-1
+    pool_shape = (d.num_blocks, 2, Hkv, bs, D)
+    pool0 = torch.zeros(pool_shape, dtype=tdt, device=dev)
+    ks, vs, sl = [], [], []
+    new_k, new_v = [], []
+    for b in range(B):
+        L = int(seq_lens[b])
+        k, v = d.kv(b)
+        ks.append(k[:L - 1])
+        vs.append(v[:L - 1])
+        sl.append(ops.slot_mapping(bt[b], 0, L - 1, bs))
+        new_k.append(k[L - 1])
+        new_v.append(v[L - 1])
+    ops.reshape_and_cache(dev_tensor(np.concatenate(ks)), dev_tensor(np.concatenate(vs)),
+                          torch.from_numpy(np.concatenate(sl)).to(dev), pool0)
+    del ks, vs
+    pool_bytes = pool0.numel() * pool0.element_size()
+    R = max(1, -(-a.rotate_mb * (1 << 20) // pool_bytes))
+    pools = [pool0] + [pool0.clone() for _ in range(R - 1)]
+    q = dev_tensor(d.query())
+    nk, nv = dev_tensor(np.stack(new_k)), dev_tensor(np.stack(new_v))
+    slots_dev = torch.from_numpy(new_slots).to(dev)
+    bt_dev = torch.from_numpy(bt).to(dev)
+    sl_dev = torch.from_numpy(np.ascontiguousarray(seq_lens, dtype=np.int32)).to(dev)
+    out = torch.empty_like(q)
+    ws_bytes = ops.decode_workspace_bytes(B, Hq, D, msl, P)
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    scale = float(wl.scale)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        pool = pools[i % R]
+        ops.reshape_and_cache(nk, nv, slots_dev, pool)
+        if ev is not None:
+            ev[0].record()
+        ops.decode(out, q, pool, bt_dev, sl_dev, msl, scale, P, ws)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(a.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(a.steps):
+        step(a.warmup + i, evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / a.steps
+    dec_us = sum(e0.elapsed_time(e1) for e0, e1 in evs) / a.steps * 1e3
+
+    ctx = int(seq_lens.sum())
+    dbytes = decode_bytes(wl, seq_lens)
+    step_bytes = dbytes + cache_write_bytes(wl)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = dbytes / (dec_us * 1e-6) / 1e9
+    khash = source_hash(DECODE_SOURCES)
+    traffic = load_traffic(khash, 1)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) keys/values/queries; no weights)",
+        "config": {
+            "workload": wl.name, "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
+            "head_size": D, "block_size": bs, "context_tokens": ctx, "max_seq_len": msl,
+            "partition_size": P, "pool_blocks": d.num_blocks, "pool_copies_rotated": R,
+            "parallelism": "none (1 GPU)",
+        },
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "context_tokens_per_s": round(ctx / (ms_step * 1e-3), 1),
+        "host_metadata_us": round(host_us, 1),
+        "roofline": {
+            "kernel": "pa_decode (decode_partition_kernel)",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": dbytes,
+            "avg_launch_us": round(dec_us, 3),
+            "kernel_source_hash": khash,
+        },
+    }
+    if not a.no_cpu_baseline:
+        dt, reps = cpu_baseline(d, a.cpu_seconds)
+        res["cpu_baseline"] = {
+            "value": round(step_bytes / dt / 1e9, 4),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"the whole {wl.name} step (write {B} new tokens, decode {B} sequences, "
+                      f"{ctx} context tokens) repeated {reps}x; fp64 numpy, BLAS 1 thread; "
+                      f"{dt * 1e3:.1f} ms per step",
+        }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -10,6 +10,9 @@ constexpr int kWave = 64;
 constexpr int kBlockSize = 16;  // tokens per KV-cache block supported by the kernels
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// Native 4 x 32-bit vector (a first-class LLVM vector, unlike HIP's uint4
+// struct, so arrays of it stay in registers).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

@@ -74,7 +74,7 @@ struct DecodeCfg {
 
 // q.k partial over one 16-byte chunk
 template <bool BF16>
-__device__ __forceinline__ float chunk_dot(const uint4& q, const uint4& k, float acc) {
+__device__ __forceinline__ float chunk_dot(const u32x4& q, const u32x4& k, float acc) {
   if constexpr (BF16) {
     acc = dot2_bf16(q.x, k.x, acc);
     acc = dot2_bf16(q.y, k.y, acc);
@@ -87,6 +87,194 @@ __device__ __forceinline__ float chunk_dot(const uint4& q, const uint4& k, float
     acc = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
   }
   return acc;
+}
+
+// Registers of one block: the K tile as coalesced 16-byte vectors (lane i
+// holds vectors i, i+64, ...) and this lane's V column(s) of each row.
+template <class C>
+struct BlockRegs {
+  u32x4 k[C::LOADS];
+  uint32_t v[C::ROWS][C::VW];
+};
+
+template <class C>
+__device__ __forceinline__ BlockRegs<C> load_block_regs(const uint8_t* __restrict__ cache, int phys,
+                                                        int64_t block_bytes, int g,
+                                                        int num_kv_heads, int64_t tile_bytes,
+                                                        int lane, int half, int col) {
+  const uint8_t* kbase = cache + int64_t(phys) * block_bytes + int64_t(g) * tile_bytes;
+  const uint8_t* vbase = kbase + int64_t(num_kv_heads) * tile_bytes;
+  BlockRegs<C> r;
+  const u32x4* kt = reinterpret_cast<const u32x4*>(kbase);
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) r.k[i] = kt[i * kWave + lane];
+  const uint32_t* vt = reinterpret_cast<const uint32_t*>(vbase);
+#pragma unroll
+  for (int rr = 0; rr < C::ROWS; ++rr) {
+    const int row = half * C::ROWS + rr;
+#pragma unroll
+    for (int w = 0; w < C::VW; ++w) r.v[rr][w] = vt[row * (C::RB / 4) + col * C::VW + w];
+  }
+  return r;
+}
+
+// Online-softmax state of one wave: running max and denominator share per
+// lane head (log2 domain), and the unnormalised output columns of this lane.
+template <class C, int G>
+struct DecodeState {
+  float m_run[C::HPL];
+  float l_part[C::HPL];
+  float o[G][C::DPL];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int hh = 0; hh < C::HPL; ++hh) { m_run[hh] = -INFINITY; l_part[hh] = 0.f; }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int j = 0; j < C::DPL; ++j) o[h][j] = 0.f;
+  }
+};
+
+// Ids of up to 64 of a wave's blocks: lane i gets the id of logical block
+// first + 4 * (chunk * 64 + i) (clamped into the pool; lanes past the wave's
+// last block read nothing).
+__device__ __forceinline__ int load_ids(const int* __restrict__ bt_row, int first, int nmine,
+                                        int chunk, int lane, int num_blocks) {
+  const int k = chunk * kWave + lane;
+  int id = k < nmine ? bt_row[first + k * kDecodeWaves] : 0;
+  return (id < 0 || id >= num_blocks) ? 0 : id;  // out-of-range ids read block 0
+}
+
+// One 16-token block: K tile through LDS, scores, online softmax, P to LDS,
+// P.V into the lane's output columns.  `valid` tokens of the block are inside
+// the sequence (>= 1).
+template <int D, int G, bool BF16>
+__device__ __forceinline__ void process_block(BlockRegs<DecodeCfg<D, G, BF16>>& cur, int valid,
+                                            const u32x4 (&q)[DecodeCfg<D, G, BF16>::HPL]
+                                                            [DecodeCfg<D, G, BF16>::CPL],
+                                            DecodeState<DecodeCfg<D, G, BF16>, G>& st,
+                                            uint8_t* kt_lds, uint32_t* p_lds, float* alpha_lds,
+                                            float scale_log2, int dp, int tq, int hg, int half) {
+  using C = DecodeCfg<D, G, BF16>;
+  const int lane = threadIdx.x & (kWave - 1);
+
+  // K tile -> LDS (padded rows)
+  wave_lds_sync();  // previous block's reads of the tile are done
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int v = i * kWave + lane;
+    const int row = v / C::CPR, ch = v % C::CPR;
+    *reinterpret_cast<u32x4*>(kt_lds + row * C::LDS_ROW + ch * 16) = cur.k[i];
+  }
+  wave_lds_sync();
+
+  // ---- scores for this lane's token(s) and heads
+  float s[C::NPASS][C::HPL];
+#pragma unroll
+  for (int ps = 0; ps < C::NPASS; ++ps) {
+    const int row = ps * C::TPP + tq;
+    const u32x4* kr = reinterpret_cast<const u32x4*>(kt_lds + row * C::LDS_ROW) + dp * C::CPL;
+#pragma unroll
+    for (int hh = 0; hh < C::HPL; ++hh) s[ps][hh] = 0.f;
+#pragma unroll
+    for (int c = 0; c < C::CPL; ++c) {
+      const u32x4 kv = kr[c];
+#pragma unroll
+      for (int hh = 0; hh < C::HPL; ++hh) s[ps][hh] = chunk_dot<BF16>(q[hh][c], kv, s[ps][hh]);
+    }
+#pragma unroll
+    for (int hh = 0; hh < C::HPL; ++hh) {
+      float x = allreduce_sum<0, ilog2(C::DP)>(s[ps][hh]);
+      x *= scale_log2;
+      s[ps][hh] = (row < valid) ? x : -INFINITY;
+    }
+  }
+
+  // ---- online softmax per head (max over the block's 16 tokens)
+  float alpha[C::HPL];
+#pragma unroll
+  for (int hh = 0; hh < C::HPL; ++hh) {
+    float mb = s[0][hh];
+#pragma unroll
+    for (int ps = 1; ps < C::NPASS; ++ps) mb = fmaxf(mb, s[ps][hh]);
+    mb = allreduce_max<ilog2(C::DP), ilog2(C::DP * C::TPP)>(mb);
+    const float m_new = fmaxf(st.m_run[hh], mb);  // finite: token 0 of the block is valid
+    alpha[hh] = exp2f(st.m_run[hh] - m_new);
+    st.m_run[hh] = m_new;
+    st.l_part[hh] *= alpha[hh];
+  }
+
+  // ---- P to LDS
+#pragma unroll
+  for (int ps = 0; ps < C::NPASS; ++ps) {
+    const int row = ps * C::TPP + tq;
+#pragma unroll
+    for (int hh = 0; hh < C::HPL; ++hh) {
+      const int h = hg * C::HPL + hh;
+      const float p = exp2f(s[ps][hh] - st.m_run[hh]);
+      if constexpr (BF16) {
+        const uint32_t pb16 = f32_to_bf16_rne(p);
+        st.l_part[hh] += (dp == 0) ? __uint_as_float(pb16 << 16) : 0.f;
+        const uint32_t nb = dpp_u<0x100 + C::DP>(pb16);  // row_shl: lane + DP = token + 1
+        if (dp == 0 && (row & 1) == 0) p_lds[h * 8 + (row >> 1)] = pb16 | (nb << 16);
+      } else {
+        st.l_part[hh] += (dp == 0) ? p : 0.f;
+        if (dp == 0) reinterpret_cast<float*>(p_lds)[h * 16 + row] = p;
+      }
+    }
+  }
+  if (tq == 0 && dp == 0) {
+#pragma unroll
+    for (int hh = 0; hh < C::HPL; ++hh) alpha_lds[hg * C::HPL + hh] = alpha[hh];
+  }
+  wave_lds_sync();
+
+  // ---- rescale and accumulate P.V
+  if (valid < 16) {  // tail block: rows past the sequence may hold anything
+#pragma unroll
+    for (int r = 0; r < C::ROWS; ++r)
+#pragma unroll
+      for (int w = 0; w < C::VW; ++w)
+        cur.v[r][w] = (half * C::ROWS + r < valid) ? cur.v[r][w] : 0u;
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float a = alpha_lds[h];
+#pragma unroll
+    for (int jj = 0; jj < C::DPL; ++jj) st.o[h][jj] *= a;
+  }
+  if constexpr (BF16) {
+    // token pairs (2k, 2k+1) of this lane's rows
+    constexpr int PAIRS = C::ROWS / 2;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      uint32_t pw[PAIRS];
+#pragma unroll
+      for (int k4 = 0; k4 < PAIRS; k4 += 4) {
+        const u32x4 t4 = *reinterpret_cast<const u32x4*>(p_lds + h * 8 + half * PAIRS + k4);
+        pw[k4] = t4.x; pw[k4 + 1] = t4.y; pw[k4 + 2] = t4.z; pw[k4 + 3] = t4.w;
+      }
+#pragma unroll
+      for (int k = 0; k < PAIRS; ++k) {
+        const uint32_t v0 = cur.v[2 * k][0], v1 = cur.v[2 * k + 1][0];
+        const uint32_t xlo = __builtin_amdgcn_perm(v1, v0, 0x05040100u);  // (v0.lo, v1.lo)
+        const uint32_t xhi = __builtin_amdgcn_perm(v1, v0, 0x07060302u);  // (v0.hi, v1.hi)
+        st.o[h][0] = dot2_bf16(xlo, pw[k], st.o[h][0]);
+        st.o[h][1] = dot2_bf16(xhi, pw[k], st.o[h][1]);
+      }
+    }
+  } else {
+    const float* pf = reinterpret_cast<const float*>(p_lds);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = pf[h * 16 + r];
+#pragma unroll
+        for (int w = 0; w < C::VW; ++w) st.o[h][w] = fmaf(p, __uint_as_float(cur.v[r][w]), st.o[h][w]);
+      }
+    }
+  }
 }
 
 template <int D, int G, bool BF16>
@@ -125,9 +313,9 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(
   __shared__ float smem_l[kDecodeWaves][G];
 
   // ---- query chunks for this lane: heads hg*HPL + hh, chunks dp*CPL + c
-  uint4 q[C::HPL][C::CPL];
+  u32x4 q[C::HPL][C::CPL];
   {
-    const uint4* qb = reinterpret_cast<const uint4*>(query) + int64_t(b) * H_q * C::CPR;
+    const u32x4* qb = reinterpret_cast<const u32x4*>(query) + int64_t(b) * H_q * C::CPR;
 #pragma unroll
     for (int hh = 0; hh < C::HPL; ++hh) {
       const int h = g * G + hg * C::HPL + hh;
@@ -140,190 +328,49 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(
   const int64_t block_bytes = int64_t(2) * num_kv_heads * tile_bytes;
   const int* bt_row = block_tables + int64_t(b) * max_blocks_per_seq;
 
-  // online-softmax state (log2 domain)
-  float m_run[C::HPL];     // running max per lane head (uniform across the 16-lane row)
-  float l_part[C::HPL];    // this lane's share of the denominator
-#pragma unroll
-  for (int hh = 0; hh < C::HPL; ++hh) { m_run[hh] = -INFINITY; l_part[hh] = 0.f; }
-  float o[G][C::DPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int j = 0; j < C::DPL; ++j) o[h][j] = 0.f;
+  DecodeState<C, G> st;
+  st.init();
 
   // P.V lane roles
   const int half = C::HALVES == 2 ? (lane >> 5) : 0;
   const int col = C::HALVES == 2 ? (lane & 31) : lane;  // dword column within the row
 
-  auto tile_base = [&](int j, int kv) -> const uint8_t* {
-    int phys = bt_row[j];
-    phys = (phys < 0 || phys >= num_blocks) ? 0 : phys;
-    return cache + int64_t(phys) * block_bytes + int64_t(kv * num_kv_heads + g) * tile_bytes;
-  };
-
-  uint4 kreg[C::LOADS];
-  uint32_t vreg[C::ROWS][C::VW];
-  auto load_block = [&](int j) {
-    const uint4* kt = reinterpret_cast<const uint4*>(tile_base(j, 0));
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) kreg[i] = kt[i * kWave + lane];
-    const uint32_t* vt = reinterpret_cast<const uint32_t*>(tile_base(j, 1));
-#pragma unroll
-    for (int r = 0; r < C::ROWS; ++r) {
-      const int row = half * C::ROWS + r;
-#pragma unroll
-      for (int w = 0; w < C::VW; ++w) vreg[r][w] = vt[row * (C::RB / 4) + col * C::VW + w];
-    }
-  };
-
   uint8_t* kt_lds = smem_k + wave * C::LDS_TILE;
   uint32_t* p_lds = smem_p[wave];
 
-  int j = blk_lo + wave;
-  if (j < blk_hi) load_block(j);
-  for (; j < blk_hi; j += kDecodeWaves) {
-    // current block's registers, then prefetch the next one
-    uint4 kcur[C::LOADS];
-    uint32_t vcur[C::ROWS][C::VW];
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) kcur[i] = kreg[i];
-#pragma unroll
-    for (int r = 0; r < C::ROWS; ++r)
-#pragma unroll
-      for (int w = 0; w < C::VW; ++w) vcur[r][w] = vreg[r][w];
-    if (j + kDecodeWaves < blk_hi) load_block(j + kDecodeWaves);
-
-    const int valid = min(16, L - j * 16);  // tokens of this block inside the sequence
-
-    // K tile -> LDS (padded rows)
-    wave_lds_sync();  // previous block's reads of the tile are done
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int v = i * kWave + lane;
-      const int row = v / C::CPR, ch = v % C::CPR;
-      *reinterpret_cast<uint4*>(kt_lds + row * C::LDS_ROW + ch * 16) = kcur[i];
+  // Block ids of this wave's blocks (lane i holds the id of block
+  // blk_lo + wave + 4 * (chunk * 64 + i)), read per block with v_readlane.
+  const int first = blk_lo + wave;
+  const int nmine = blk_hi > first ? (blk_hi - first + kDecodeWaves - 1) / kDecodeWaves : 0;
+  if (nmine > 0) {
+    int ids = load_ids(bt_row, first, nmine, 0, lane, num_blocks);
+    BlockRegs<C> nxt = load_block_regs<C>(cache, __builtin_amdgcn_readlane(ids, 0), block_bytes,
+                                          g, num_kv_heads, tile_bytes, lane, half, col);
+    for (int k = 0; k + 1 < nmine; ++k) {
+      if (((k + 1) & (kWave - 1)) == 0) ids = load_ids(bt_row, first, nmine, (k + 1) >> 6, lane, num_blocks);
+      const int id_next = __builtin_amdgcn_readlane(ids, (k + 1) & (kWave - 1));
+      BlockRegs<C> cur = nxt;
+      nxt = load_block_regs<C>(cache, id_next, block_bytes, g, num_kv_heads, tile_bytes, lane,
+                               half, col);
+      const int j = first + k * kDecodeWaves;
+      process_block<D, G, BF16>(cur, min(16, L - j * 16), q, st, kt_lds, p_lds, smem_alpha[wave],
+                                scale_log2, dp, tq, hg, half);
     }
-    wave_lds_sync();
-
-    // ---- scores for this lane's token(s) and heads
-    float s[C::NPASS][C::HPL];
-#pragma unroll
-    for (int ps = 0; ps < C::NPASS; ++ps) {
-      const int row = ps * C::TPP + tq;
-      const uint4* kr = reinterpret_cast<const uint4*>(kt_lds + row * C::LDS_ROW) + dp * C::CPL;
-#pragma unroll
-      for (int hh = 0; hh < C::HPL; ++hh) s[ps][hh] = 0.f;
-#pragma unroll
-      for (int c = 0; c < C::CPL; ++c) {
-        const uint4 kv = kr[c];
-#pragma unroll
-        for (int hh = 0; hh < C::HPL; ++hh) s[ps][hh] = chunk_dot<BF16>(q[hh][c], kv, s[ps][hh]);
-      }
-#pragma unroll
-      for (int hh = 0; hh < C::HPL; ++hh) {
-        float x = allreduce_sum<0, ilog2(C::DP)>(s[ps][hh]);
-        x *= scale_log2;
-        s[ps][hh] = (row < valid) ? x : -INFINITY;
-      }
-    }
-
-    // ---- online softmax per head (max over the block's 16 tokens)
-    float alpha[C::HPL];
-#pragma unroll
-    for (int hh = 0; hh < C::HPL; ++hh) {
-      float mb = s[0][hh];
-#pragma unroll
-      for (int ps = 1; ps < C::NPASS; ++ps) mb = fmaxf(mb, s[ps][hh]);
-      mb = allreduce_max<ilog2(C::DP), ilog2(C::DP * C::TPP)>(mb);
-      const float m_new = fmaxf(m_run[hh], mb);  // finite: token 0 of the block is valid
-      alpha[hh] = exp2f(m_run[hh] - m_new);
-      m_run[hh] = m_new;
-      l_part[hh] *= alpha[hh];
-    }
-
-    // ---- P to LDS
-#pragma unroll
-    for (int ps = 0; ps < C::NPASS; ++ps) {
-      const int row = ps * C::TPP + tq;
-#pragma unroll
-      for (int hh = 0; hh < C::HPL; ++hh) {
-        const int h = hg * C::HPL + hh;
-        const float p = exp2f(s[ps][hh] - m_run[hh]);
-        if constexpr (BF16) {
-          const uint32_t pb16 = f32_to_bf16_rne(p);
-          l_part[hh] += (dp == 0) ? __uint_as_float(pb16 << 16) : 0.f;
-          const uint32_t nb = dpp_u<0x100 + C::DP>(pb16);  // row_shl: lane + DP = token + 1
-          if (dp == 0 && (row & 1) == 0) p_lds[h * 8 + (row >> 1)] = pb16 | (nb << 16);
-        } else {
-          l_part[hh] += (dp == 0) ? p : 0.f;
-          if (dp == 0) reinterpret_cast<float*>(p_lds)[h * 16 + row] = p;
-        }
-      }
-    }
-    if (tq == 0 && dp == 0) {
-#pragma unroll
-      for (int hh = 0; hh < C::HPL; ++hh) smem_alpha[wave][hg * C::HPL + hh] = alpha[hh];
-    }
-    wave_lds_sync();
-
-    // ---- rescale and accumulate P.V
-    if (valid < 16) {  // tail block: rows past the sequence may hold anything
-#pragma unroll
-      for (int r = 0; r < C::ROWS; ++r)
-#pragma unroll
-        for (int w = 0; w < C::VW; ++w)
-          vcur[r][w] = (half * C::ROWS + r < valid) ? vcur[r][w] : 0u;
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float a = smem_alpha[wave][h];
-#pragma unroll
-      for (int jj = 0; jj < C::DPL; ++jj) o[h][jj] *= a;
-    }
-    if constexpr (BF16) {
-      // token pairs (2k, 2k+1) of this lane's rows
-      constexpr int PAIRS = C::ROWS / 2;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        uint32_t pw[PAIRS];
-#pragma unroll
-        for (int k4 = 0; k4 < PAIRS; k4 += 4) {
-          const uint4 t4 = *reinterpret_cast<const uint4*>(p_lds + h * 8 + half * PAIRS + k4);
-          pw[k4] = t4.x; pw[k4 + 1] = t4.y; pw[k4 + 2] = t4.z; pw[k4 + 3] = t4.w;
-        }
-#pragma unroll
-        for (int k = 0; k < PAIRS; ++k) {
-          const uint32_t v0 = vcur[2 * k][0], v1 = vcur[2 * k + 1][0];
-          const uint32_t xlo = __builtin_amdgcn_perm(v1, v0, 0x05040100u);  // (v0.lo, v1.lo)
-          const uint32_t xhi = __builtin_amdgcn_perm(v1, v0, 0x07060302u);  // (v0.hi, v1.hi)
-          o[h][0] = dot2_bf16(xlo, pw[k], o[h][0]);
-          o[h][1] = dot2_bf16(xhi, pw[k], o[h][1]);
-        }
-      }
-    } else {
-      const float* pf = reinterpret_cast<const float*>(p_lds);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = pf[h * 16 + r];
-#pragma unroll
-          for (int w = 0; w < C::VW; ++w) o[h][w] = fmaf(p, __uint_as_float(vcur[r][w]), o[h][w]);
-        }
-      }
-    }
+    const int j = first + (nmine - 1) * kDecodeWaves;
+    process_block<D, G, BF16>(nxt, min(16, L - j * 16), q, st, kt_lds, p_lds, smem_alpha[wave],
+                              scale_log2, dp, tq, hg, half);
   }
 
   // ---- merge: this wave's denominator, then the 4 waves of the workgroup
 #pragma unroll
   for (int hh = 0; hh < C::HPL; ++hh) {
     // sum over token lanes of the row (d-part replicas contributed 0)
-    float lsum = l_part[hh];
+    float lsum = st.l_part[hh];
 #pragma unroll
     for (int bit = ilog2(C::DP); bit < ilog2(C::DP * C::TPP); ++bit)
       lsum += __shfl_xor(lsum, 1 << bit, kWave);
     if (tq == 0 && dp == 0) {
-      smem_m[wave][hg * C::HPL + hh] = m_run[hh];
+      smem_m[wave][hg * C::HPL + hh] = st.m_run[hh];
       smem_l[wave][hg * C::HPL + hh] = lsum;
     }
   }
@@ -331,7 +378,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int jj = 0; jj < C::DPL; ++jj) o[h][jj] += __shfl_xor(o[h][jj], 32, kWave);
+      for (int jj = 0; jj < C::DPL; ++jj) st.o[h][jj] += __shfl_xor(st.o[h][jj], 32, kWave);
   }
   __syncthreads();  // all waves done with their tiles: reuse smem_k for o
   float* o_lds = reinterpret_cast<float*>(smem_k);  // [wave][G][D]
@@ -340,7 +387,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int jj = 0; jj < C::DPL; ++jj)
-        o_lds[(wave * G + h) * D + col * C::DPL + jj] = o[h][jj];
+        o_lds[(wave * G + h) * D + col * C::DPL + jj] = st.o[h][jj];
   }
   __syncthreads();
 

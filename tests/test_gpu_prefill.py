@@ -1,0 +1,120 @@
+"""GPU parity of pa_prefill_chunk (and the chunk's pa_reshape_and_cache)
+against the fp64 oracle, plus the prefix-sharing invariant.
+
+Bars: bit-exact cache contents, block tables and allocator state; max |error|
+<= 2e-2 on bf16 outputs and on lse."""
+import numpy as np
+import pytest
+import torch
+
+from paged_attention_kv_block_amd import inputs
+from tests.conftest import gpu_available
+from tests.oracle_setup import OracleSide
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+TOL = 2e-2
+
+
+def _f64(t):
+    import oracle
+    from tests.gpu_setup import from_device
+    return oracle.to_f64(from_device(t))
+
+
+def run_prefill_case(d, seqs=None, check_pool=True):
+    from tests.gpu_setup import GpuSide, from_device
+    o = OracleSide(d, seqs=seqs)
+    g = GpuSide(d)
+    np.testing.assert_array_equal(g.block_tables, o.block_tables)
+    assert g.alloc.export() == o.alloc.export()
+    if check_pool and seqs is None:
+        np.testing.assert_array_equal(from_device(g.pool), o.pool)
+    out, lse = g.prefill()
+    ref, ref_lse = o.prefill(seqs=seqs)
+    qsl = o.query_start_loc()
+    rows = np.concatenate([np.arange(qsl[b], qsl[b + 1]) for b in
+                           (range(d.wl.num_seqs) if seqs is None else seqs)]).astype(int)
+    got = _f64(out)[rows]
+    assert np.all(np.isfinite(got))
+    err = np.max(np.abs(got - ref[rows])) if rows.size else 0.0
+    lerr = np.max(np.abs(lse.cpu().numpy().astype(np.float64)[rows] - ref_lse[rows])) if rows.size else 0.0
+    assert err <= TOL, f"max abs error {err}"
+    assert lerr <= TOL, f"lse max abs error {lerr}"
+    return err, out, lse, g
+
+
+CASES = [
+    ("g4-d128-ragged", dict(seq_lens=(20, 37, 100, 64), chunk_lens=(5, 17, 100, 33), num_q_heads=8,
+                            num_kv_heads=2, head_size=128)),
+    ("g8-d128", dict(seq_lens=(300, 45), chunk_lens=(40, 16), num_q_heads=16, num_kv_heads=2,
+                     head_size=128)),
+    ("g1-d128-long-chunk", dict(seq_lens=(260,), chunk_lens=(200,), num_q_heads=2, num_kv_heads=2,
+                                head_size=128)),
+    ("g2-d64", dict(seq_lens=(50, 90, 1), chunk_lens=(50, 7, 1), num_q_heads=4, num_kv_heads=2,
+                    head_size=64)),
+    ("g4-d64-chunk1", dict(seq_lens=(33, 64, 17), chunk_lens=(1, 1, 1), num_q_heads=16,
+                           num_kv_heads=4, head_size=64)),
+    ("g8-d64-empty-chunk", dict(seq_lens=(40, 70), chunk_lens=(0, 70), num_q_heads=8,
+                                num_kv_heads=1, head_size=64)),
+]
+
+
+@pytest.mark.parametrize("name,kw", CASES, ids=[c[0] for c in CASES])
+def test_prefill_shapes(name, kw):
+    run_prefill_case(inputs.custom(kind="prefill", **kw))
+
+
+def _small_prefix_workload(prefix=64, private=23, chunk=37, n=5, G=4, D=128):
+    wl = inputs.Workload(60, "small-prefix", "prefill", "bf16", n, 2 * G, 2, D,
+                         prefix_tokens=prefix, private_tokens=private, chunk_tokens=chunk,
+                         fixed_num_blocks=n * ((prefix + private + chunk) // 16 + 2))
+    return inputs.Draw(wl)
+
+
+def test_small_shared_prefix_parity():
+    run_prefill_case(_small_prefix_workload())
+
+
+def test_shared_prefix_equals_unshared_copies_bit_exact():
+    from tests.gpu_setup import GpuSide
+    d = _small_prefix_workload()
+    shared = GpuSide(d, share_prefix=True)
+    copies = GpuSide(d, share_prefix=False)
+    _, rc = shared.alloc.export()
+    assert max(rc) == d.wl.num_seqs
+    assert not np.array_equal(shared.block_tables, copies.block_tables)
+    o1, l1 = shared.prefill()
+    o2, l2 = copies.prefill()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_chunked_prefill_workload_sampled():
+    """The 16-sequence shared-prefix workload at full size; the oracle checks
+    the first and last sequence (all 256 queries, all heads)."""
+    run_prefill_case(inputs.draw(3), seqs=[0, 15])
+
+
+def test_chunked_prefill_workload_shared_vs_copies():
+    from tests.gpu_setup import GpuSide
+    d = inputs.draw(3)
+    d.num_blocks = 16 * 176 + 8          # room for unshared copies of the prefix
+    d.pool_order = np.random.default_rng(5).permutation(d.num_blocks).astype(np.int32)
+    a = GpuSide(d, share_prefix=True)
+    b = GpuSide(d, share_prefix=False)
+    oa, la = a.prefill()
+    ob, lb = b.prefill()
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
+    assert torch.equal(la, lb)
+
+
+def test_unit_values_give_unit_output():
+    from tests.gpu_setup import GpuSide
+    d = inputs.custom(kind="prefill", seq_lens=(70, 33), chunk_lens=(40, 33), num_q_heads=8,
+                      num_kv_heads=2, head_size=128)
+    g = GpuSide(d)
+    g.pool[:, 1] = 1.0
+    out, _ = g.prefill()
+    np.testing.assert_array_equal(_f64(out), 1.0)
