@@ -211,8 +211,7 @@ def main(argv=None):
     bt_dev = torch.from_numpy(bt).to(dev)
     sl_dev = torch.from_numpy(np.ascontiguousarray(seq_lens, dtype=np.int32)).to(dev)
     out = torch.empty_like(q)
-    ws_bytes = ops.decode_workspace_bytes(B, Hq, D, msl, P)
-    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    ws = ops.decode_workspace(B, Hq, Hkv, D, msl, P, dev)
     scale = float(wl.scale)
     torch.cuda.synchronize()
 

@@ -164,11 +164,23 @@ int pa_reshape_and_cache(const void* key, const void* value,
                          int32_t block_size, int32_t num_kv_heads,
                          int32_t head_size, int32_t dtype, void* stream);
 
-/* Device workspace pa_decode needs for split-K partials, in bytes (0 when
- * partition_size == 0 or one partition covers max_seq_len). */
+/* Device workspace pa_decode needs for split-K, in bytes: a fixed region of
+ * 65536 arrival counters (one per (sequence, KV head), so B * H_kv <= 65536
+ * with split-K) followed by the per-partition partials (max, denominator,
+ * normalised output; fp32).  0 when partition_size == 0 or one partition
+ * covers max_seq_len.  A workspace sized for the largest shape serves calls
+ * of any smaller shape. */
 size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads,
-                                 int32_t head_size, int32_t max_seq_len,
-                                 int32_t partition_size);
+                                 int32_t num_kv_heads, int32_t head_size,
+                                 int32_t max_seq_len, int32_t partition_size);
+
+/* Zero-fills a decode workspace on `stream` (a fill kernel, no memset).  A
+ * workspace must be zero before its first pa_decode; every completed
+ * pa_decode leaves it reusable (its counters return to zero), so one
+ * initialisation serves any number of calls, including graph replays.
+ * workspace: device, 256-byte aligned; bytes a multiple of 4. */
+int pa_decode_workspace_init(void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* Decode attention: one query token per sequence, the last of its seq_len
  * cached tokens (already written), attends to all of them through its block
@@ -184,11 +196,14 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads,
  *   partition_size  0: one pass per (sequence, KV head); otherwise a
  *                multiple of block_size: the context is split into
  *                partitions of that many tokens, each processed by its own
- *                workgroup, and a second kernel combines the partials with
- *                a log-sum-exp weighted sum (split-K).
+ *                workgroup; the last workgroup of a (sequence, KV head) to
+ *                finish combines the partials with a log-sum-exp weighted
+ *                sum (split-K, one kernel launch).
  *   workspace    device, >= pa_decode_workspace_bytes(...) bytes (nullable
- *                when that is 0), owned by the caller; contents need no
- *                initialisation and are scratch after the call.
+ *                when that is 0), owned by the caller, zeroed once by
+ *                pa_decode_workspace_init (or any zero fill) before first
+ *                use.  Two pa_decode calls sharing a workspace must not run
+ *                concurrently.
  * Supported: block_size 16; head_size 64 or 128; H_q % H_kv == 0 with
  * G = H_q/H_kv in {1, 2, 4, 8} (and 16 for head_size 64). */
 int pa_decode(void* out, float* lse_out, const void* query,

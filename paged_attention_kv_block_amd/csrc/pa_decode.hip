@@ -72,6 +72,23 @@ struct DecodeCfg {
   static_assert(!BF16 || D == 64 || D == 128, "bf16 head sizes 64/128");
 };
 
+// Agent-scope relaxed accesses: coherent across the L2 caches of all XCDs
+// (they bypass a possibly stale local L2 line), used for split-K partials.
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
+  if constexpr (BF16)
+    reinterpret_cast<uint16_t*>(out)[idx] = uint16_t(f32_to_bf16_rne(v));
+  else
+    reinterpret_cast<float*>(out)[idx] = v;
+}
+
 // q.k partial over one 16-byte chunk
 template <bool BF16>
 __device__ __forceinline__ float chunk_dot(const u32x4& q, const u32x4& k, float acc) {
@@ -282,8 +299,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(
     void* __restrict__ out, float* __restrict__ lse_out, const void* __restrict__ query,
     const uint8_t* __restrict__ cache, int num_blocks, const int* __restrict__ block_tables,
     int max_blocks_per_seq, const int* __restrict__ seq_lens, int max_seq_len, int num_kv_heads,
-    float scale_log2, int part_blocks, int max_parts, float* __restrict__ ws_m,
-    float* __restrict__ ws_l, float* __restrict__ ws_o) {
+    float scale_log2, int part_blocks, int max_parts, int* __restrict__ ws_count,
+    float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o) {
   using C = DecodeCfg<D, G, BF16>;
   const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int H_q = num_kv_heads * G;
@@ -392,7 +409,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(
   __syncthreads();
 
   const bool single = nparts <= 1;
-  for (int e = threadIdx.x; e < G * D; e += kDecodeWaves * kWave) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < G * D; e += kDecodeWaves * kWave) {
     const int h = e / D, d = e % D;
     float M = -INFINITY;
 #pragma unroll
@@ -406,67 +424,101 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(
         acc += wt * o_lds[(w * G + h) * D + d];
       }
     }
-    const int hq = g * G + h;
-    const int64_t row = int64_t(b) * H_q + hq;
+    const int64_t row = int64_t(b) * H_q + g * G + h;
     if (single) {
       const float val = lsum > 0.f ? acc / lsum : 0.f;
-      if constexpr (BF16)
-        reinterpret_cast<uint16_t*>(out)[row * D + d] = uint16_t(f32_to_bf16_rne(val));
-      else
-        reinterpret_cast<float*>(out)[row * D + d] = val;
+      store_out<BF16>(out, row * D + d, val);
       if (lse_out && d == 0) lse_out[row] = lsum > 0.f ? M * kLn2 + logf(lsum) : -INFINITY;
     } else {
       const int64_t prow = row * max_parts + part;
-      ws_o[prow * D + d] = lsum > 0.f ? acc / lsum : 0.f;
+      coherent_store(ws_o + prow * D + d, lsum > 0.f ? acc / lsum : 0.f);
       if (d == 0) {
-        ws_m[prow] = M;
-        ws_l[prow] = lsum;
+        coherent_store(ws_m + prow, M);
+        coherent_store(ws_l + prow, lsum);
       }
+    }
+  }
+  if (single) return;
+
+  // ---- split-K: the last workgroup of this (sequence, KV head) to finish
+  // merges all partitions.  Partials are written and read with accesses that
+  // are coherent across the XCDs' L2 caches (agent scope), and this
+  // workgroup's writes have completed before its arrival is counted, so the
+  // workgroup that counts last sees every partial.  No L2 flush is needed.
+  __shared__ int s_last;
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
+  __syncthreads();
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(&ws_count[b * num_kv_heads + g], 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    s_last = old == nparts - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  if (tid == 0)  // ready for the next call
+    __hip_atomic_store(&ws_count[b * num_kv_heads + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // per head: M = max_p m_p and W = sum_p 2^(m_p - M) l_p (one wave per head)
+  __shared__ float s_M[G], s_W[G];
+  for (int h = wave; h < G; h += kDecodeWaves) {
+    const int64_t row = int64_t(b) * H_q + g * G + h;
+    const float* m = ws_m + row * max_parts;
+    const float* l = ws_l + row * max_parts;
+    float M = -INFINITY;
+    for (int p = lane; p < nparts; p += kWave) M = fmaxf(M, coherent_load(m + p));
+    M = allreduce_max<0, 6>(M);
+    float W = 0.f;
+    for (int p = lane; p < nparts; p += kWave)
+      W += exp2f(coherent_load(m + p) - M) * coherent_load(l + p);
+    W = allreduce_sum<0, 6>(W);
+    if (lane == 0) { s_M[h] = M; s_W[h] = W; }
+  }
+  __syncthreads();
+  // O = sum_p w_p o_p / W, the weights staged through LDS in chunks
+  constexpr int EPT = (G * D + kDecodeWaves * kWave - 1) / (kDecodeWaves * kWave);
+  constexpr int WCAP = int(sizeof(smem_k) / sizeof(float)) / G;  // weights per head per chunk
+  float* wbuf = reinterpret_cast<float*>(smem_k);
+  float acc[EPT];
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) acc[k] = 0.f;
+  for (int p0 = 0; p0 < nparts; p0 += WCAP) {
+    const int pc = min(WCAP, nparts - p0);
+    for (int idx = tid; idx < G * pc; idx += kDecodeWaves * kWave) {
+      const int h = idx / pc, pp = idx % pc;
+      const int64_t prow = (int64_t(b) * H_q + g * G + h) * max_parts + p0 + pp;
+      wbuf[h * WCAP + pp] = exp2f(coherent_load(ws_m + prow) - s_M[h]) * coherent_load(ws_l + prow);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const int e = tid + k * kDecodeWaves * kWave;
+      if (e < G * D) {
+        const int h = e / D, d = e % D;
+        const float* op = ws_o + ((int64_t(b) * H_q + g * G + h) * max_parts + p0) * D + d;
+        float a = acc[k];
+        for (int pp = 0; pp < pc; ++pp)
+          a = fmaf(wbuf[h * WCAP + pp], coherent_load(op + int64_t(pp) * D), a);
+        acc[k] = a;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int e = tid + k * kDecodeWaves * kWave;
+    if (e < G * D) {
+      const int h = e / D, d = e % D;
+      const int64_t row = int64_t(b) * H_q + g * G + h;
+      store_out<BF16>(out, row * D + d, acc[k] / s_W[h]);
+      if (lse_out && d == 0) lse_out[row] = s_M[h] * kLn2 + logf(s_W[h]);
     }
   }
 }
 
-// Combines the partition partials of every (sequence, query head) with more
-// than one partition: M = max m_p, w_p = 2^(m_p - M) l_p,
-// O = sum w_p o_p / sum w_p, lse = ln2 * M + ln sum w_p.  One wave per row.
-template <int D, bool BF16>
-__global__ __launch_bounds__(kWave) void decode_reduce_kernel(
-    void* __restrict__ out, float* __restrict__ lse_out, const int* __restrict__ seq_lens,
-    int max_seq_len, int H_q, int part_tokens, int max_parts, const float* __restrict__ ws_m,
-    const float* __restrict__ ws_l, const float* __restrict__ ws_o) {
-  const int hq = blockIdx.x, b = blockIdx.y;
-  int L = seq_lens[b];
-  L = L < 0 ? 0 : (L > max_seq_len ? max_seq_len : L);
-  const int nparts = (L + part_tokens - 1) / part_tokens;
-  if (nparts <= 1) return;  // written by the partition kernel
-  const int lane = threadIdx.x;
-  const int64_t row = int64_t(b) * H_q + hq;
-  const float* m = ws_m + row * max_parts;
-  const float* l = ws_l + row * max_parts;
-  float M = -INFINITY;
-  for (int p = lane; p < nparts; p += kWave) M = fmaxf(M, m[p]);
-  M = allreduce_max<0, 6>(M);
-  constexpr int DPL = D / kWave;
-  float acc[DPL] = {};
-  float wsum = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float wt = exp2f(m[p] - M) * l[p];
-    wsum += wt;
-    const float* op = ws_o + (row * max_parts + p) * D;
-#pragma unroll
-    for (int jj = 0; jj < DPL; ++jj) acc[jj] = fmaf(wt, op[jj * kWave + lane], acc[jj]);
-  }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-#pragma unroll
-  for (int jj = 0; jj < DPL; ++jj) {
-    const float val = acc[jj] * inv;
-    const int d = jj * kWave + lane;
-    if constexpr (BF16)
-      reinterpret_cast<uint16_t*>(out)[row * D + d] = uint16_t(f32_to_bf16_rne(val));
-    else
-      reinterpret_cast<float*>(out)[row * D + d] = val;
-  }
-  if (lse_out && lane == 0) lse_out[row] = wsum > 0.f ? M * kLn2 + logf(wsum) : -INFINITY;
+// Zero-fills a decode workspace (its arrival counters must start at zero).
+__global__ void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -484,6 +536,7 @@ struct DecodeArgs {
   int B, max_seq_len, H_kv;
   float scale_log2;
   int part_blocks, max_parts;
+  int* ws_count;
   float *ws_m, *ws_l, *ws_o;
   hipStream_t s;
 };
@@ -493,12 +546,8 @@ static void launch_decode(const DecodeArgs& a) {
   dim3 grid(a.max_parts, a.H_kv, a.B);
   hipLaunchKernelGGL((decode_partition_kernel<D, G, BF16>), grid, dim3(kDecodeWaves * kWave), 0,
                      a.s, a.out, a.lse, a.q, a.cache, a.num_blocks, a.bt, a.max_blocks, a.seq_lens,
-                     a.max_seq_len, a.H_kv, a.scale_log2, a.part_blocks, a.max_parts, a.ws_m,
-                     a.ws_l, a.ws_o);
-  if (a.max_parts > 1)
-    hipLaunchKernelGGL((decode_reduce_kernel<D, BF16>), dim3(a.H_kv * G, a.B), dim3(kWave), 0, a.s,
-                       a.out, a.lse, a.seq_lens, a.max_seq_len, a.H_kv * G, a.part_blocks * 16,
-                       a.max_parts, a.ws_m, a.ws_l, a.ws_o);
+                     a.max_seq_len, a.H_kv, a.scale_log2, a.part_blocks, a.max_parts, a.ws_count,
+                     a.ws_m, a.ws_l, a.ws_o);
 }
 
 template <int D, bool BF16>
@@ -520,18 +569,58 @@ static int64_t parts_for(int max_seq_len, int partition_size) {
   return (int64_t(max_seq_len) + partition_size - 1) / partition_size;
 }
 
+// Workspace layout (all offsets 256-byte aligned):
+//   [arrival counters: kCounterCap int32][m: rows][l: rows][o: rows * D]
+// with rows = B * H_q * partitions.  Counter (b, g) sits at index
+// b * H_kv + g of a region of fixed size, so calls of any shape can share
+// one workspace without their partials overlapping another shape's
+// counters.  Only the counters need a defined initial value (zero); every
+// completed call leaves them at zero.
+constexpr int64_t kCounterCap = 65536;
+struct WsLayout {
+  int64_t count_off, m_off, l_off, o_off, total;
+};
+static inline int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
+static WsLayout ws_layout(int64_t B, int64_t H_q, int64_t H_kv, int64_t D, int64_t P) {
+  WsLayout w{};
+  const int64_t rows = B * H_q * P;
+  (void)H_kv;
+  w.count_off = 0;
+  w.m_off = kCounterCap * 4;
+  w.l_off = w.m_off + round256(rows * 4);
+  w.o_off = w.l_off + round256(rows * 4);
+  w.total = w.o_off + rows * D * 4;
+  return w;
+}
+
 }  // namespace pa
 
 using namespace pa;
 
-extern "C" size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_size,
-                                            int32_t max_seq_len, int32_t partition_size) {
-  if (B <= 0 || num_q_heads <= 0 || head_size <= 0) return 0;
+extern "C" size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                                            int32_t head_size, int32_t max_seq_len,
+                                            int32_t partition_size) {
+  if (B <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_size <= 0) return 0;
   const int64_t P = parts_for(max_seq_len, partition_size);
   if (P <= 1) return 0;
-  const int64_t rows = int64_t(B) * num_q_heads * P;
-  const int64_t mbytes = (rows * 4 + 255) / 256 * 256;
-  return size_t(2 * mbytes + rows * head_size * 4);
+  return size_t(ws_layout(B, num_q_heads, num_kv_heads, head_size, P).total);
+}
+
+extern "C" int pa_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace_bytes == 0) return PA_OK;
+  if (!workspace) return fail(PA_EINVAL, "pa_decode_workspace_init: NULL workspace");
+  if ((uintptr_t(workspace) & 255) || (workspace_bytes & 3))
+    return fail(PA_EINVAL, "pa_decode_workspace_init: workspace must be 256-byte aligned, "
+                           "size a multiple of 4");
+  const int64_t n = int64_t(workspace_bytes / 4);
+  const int64_t grid = (n + 255) / 256;
+  if (grid > 0x7FFFFFFF) return fail(PA_EINVAL, "pa_decode_workspace_init: too large");
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), static_cast<uint32_t*>(workspace), n);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(PA_EHIP, "pa_decode_workspace_init: launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
 }
 
 extern "C" int pa_decode(void* out, float* lse_out, const void* query, const void* kv_cache,
@@ -568,7 +657,11 @@ extern "C" int pa_decode(void* out, float* lse_out, const void* query, const voi
   const int64_t P = parts_for(max_seq_len, partition_size);
   if (P > 65535) return fail(PA_EINVAL, "pa_decode: too many partitions (%lld)", (long long)P);
   if (num_kv_heads > 65535 || B > 65535) return fail(PA_ENOTSUP, "pa_decode: grid too large");
-  const size_t need = pa_decode_workspace_bytes(B, num_q_heads, head_size, max_seq_len, partition_size);
+  if (P > 1 && int64_t(B) * num_kv_heads > kCounterCap)
+    return fail(PA_ENOTSUP, "pa_decode: split-K supports B * H_kv <= %lld",
+                (long long)kCounterCap);
+  const size_t need =
+      pa_decode_workspace_bytes(B, num_q_heads, num_kv_heads, head_size, max_seq_len, partition_size);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PA_EINVAL, "pa_decode: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if (need > 0 && (uintptr_t(workspace) & 255))
@@ -590,12 +683,12 @@ extern "C" int pa_decode(void* out, float* lse_out, const void* query, const voi
   a.part_blocks = P > 1 ? partition_size / kBlockSize : 0;
   a.max_parts = int(P);
   if (P > 1) {
-    const int64_t rows = int64_t(B) * num_q_heads * P;
-    const int64_t mbytes = (rows * 4 + 255) / 256 * 256;
-    uint8_t* w = static_cast<uint8_t*>(workspace);
-    a.ws_m = reinterpret_cast<float*>(w);
-    a.ws_l = reinterpret_cast<float*>(w + mbytes);
-    a.ws_o = reinterpret_cast<float*>(w + 2 * mbytes);
+    const WsLayout w = ws_layout(B, num_q_heads, num_kv_heads, head_size, P);
+    uint8_t* base = static_cast<uint8_t*>(workspace);
+    a.ws_count = reinterpret_cast<int*>(base + w.count_off);
+    a.ws_m = reinterpret_cast<float*>(base + w.m_off);
+    a.ws_l = reinterpret_cast<float*>(base + w.l_off);
+    a.ws_o = reinterpret_cast<float*>(base + w.o_off);
   }
   a.s = reinterpret_cast<hipStream_t>(stream);
 

@@ -41,7 +41,8 @@ SIGNATURES = {
     "pa_slot_mapping": (_c_int, [_vp, _c_i32, _vp, _vp, _c_i32, _c_i32, _vp, _vp]),
     "pa_reshape_and_cache": (_c_int, [_vp, _vp, _vp, _c_i32, _vp, _c_i32, _c_i32, _c_i32,
                                       _c_i32, _c_i32, _vp]),
-    "pa_decode_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "pa_decode_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "pa_decode_workspace_init": (_c_int, [_vp, _c_sz, _vp]),
     "pa_decode": (_c_int, [_vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _vp, _c_i32, _c_i32,
                            _c_i32, _c_i32, _c_i32, _c_i32, _f, _c_i32, _vp, _c_sz, _c_i32, _vp]),
     "pa_prefill_chunk": (_c_int, [_vp, _vp, _vp, _vp, _c_i32, _c_i32, _vp, _c_i32, _vp, _c_i32,
@@ -226,10 +227,27 @@ def reshape_and_cache(key, value, slot_mapping, kv_cache, stream=None) -> None:
                                       _stream(stream)))
 
 
-def decode_workspace_bytes(B: int, num_q_heads: int, head_size: int, max_seq_len: int,
-                           partition_size: int) -> int:
-    return int(lib().pa_decode_workspace_bytes(B, num_q_heads, head_size, max_seq_len,
-                                               partition_size))
+def decode_workspace_bytes(B: int, num_q_heads: int, num_kv_heads: int, head_size: int,
+                           max_seq_len: int, partition_size: int) -> int:
+    return int(lib().pa_decode_workspace_bytes(B, num_q_heads, num_kv_heads, head_size,
+                                               max_seq_len, partition_size))
+
+
+def decode_workspace_init(workspace, stream=None) -> None:
+    """Zero-fills a decode workspace (uint8 GPU tensor) on the stream."""
+    _need_gpu(workspace)
+    _check(lib().pa_decode_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                          _stream(stream)))
+
+
+def decode_workspace(B: int, num_q_heads: int, num_kv_heads: int, head_size: int,
+                     max_seq_len: int, partition_size: int, device="cuda", stream=None):
+    """A zeroed workspace for pa_decode (at least 256 bytes; torch allocates it)."""
+    torch = _torch()
+    n = decode_workspace_bytes(B, num_q_heads, num_kv_heads, head_size, max_seq_len, partition_size)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    decode_workspace_init(ws, stream)
+    return ws
 
 
 def decode(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int, scale: float,

@@ -93,8 +93,8 @@ class GpuSide:
         lse = torch.empty(q.shape[:2], dtype=torch.float32, device=self.device) if with_lse else None
         P = wl.partition_size if partition_size is None else partition_size
         msl = int(max(d.seq_lens)) if max_seq_len is None else max_seq_len
-        nbytes = ops.decode_workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.head_size, msl, P)
-        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.device)
+        ws = ops.decode_workspace(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_size, msl,
+                                  P, self.device)
         ops.decode(out, q, self.pool, self.bt_dev, self.seq_lens_dev, msl,
                    float(wl.scale if scale is None else scale), P, ws, lse)
         torch.cuda.synchronize()

@@ -159,3 +159,96 @@ def test_physical_permutation_is_bit_exact():
         o2, l2 = g2.decode(partition_size=P)
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
         assert torch.equal(l1, l2)
+
+
+def test_workspace_reused_across_calls_and_shapes():
+    """The split-K arrival counters reset themselves: one zeroed workspace
+    serves many calls, including calls with different batch shapes."""
+    from paged_attention_kv_block_amd import ops
+    from tests.gpu_setup import GpuSide
+    d1 = inputs.draw(1)
+    d2 = inputs.custom(kind="decode", seq_lens=(300, 17, 1000), num_q_heads=32, num_kv_heads=4,
+                       head_size=64)
+    g1, g2 = GpuSide(d1), GpuSide(d2)
+    o1 = OracleSide(d1).decode()[0]
+    o2 = OracleSide(d2).decode()[0]
+    nbytes = max(ops.decode_workspace_bytes(64, 32, 4, 64, int(d1.seq_lens.max()), 128),
+                 ops.decode_workspace_bytes(3, 32, 4, 64, int(d2.seq_lens.max()), 128))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ops.decode_workspace_init(ws)
+    from tests.gpu_setup import to_device
+    for rep in range(3):
+        for g, d, ref in ((g1, d1, o1), (g2, d2, o2)):
+            q = to_device(d.query(), d.wl)
+            out = torch.empty_like(q)
+            ops.decode(out, q, g.pool, g.bt_dev, g.seq_lens_dev, int(d.seq_lens.max()),
+                       float(d.wl.scale), 128, ws)
+            torch.cuda.synchronize()
+            err = np.max(np.abs(out_f64(out) - ref))
+            assert err <= 2e-2, (rep, err)
+
+
+def test_decode_step_in_a_hip_graph():
+    """The decode step (cache write + split-K decode) captured in a HIP graph
+    and replayed several times, with eager work between replays: every
+    replay matches the eager result bit for bit."""
+    from paged_attention_kv_block_amd import ops
+    from tests.gpu_setup import GpuSide, to_device
+    d = inputs.draw(1)
+    g = GpuSide(d)
+    wl = d.wl
+    L = d.seq_lens
+    msl = int(L.max())
+    q = to_device(d.query(), wl)
+    newk = torch.zeros((wl.num_seqs, wl.num_kv_heads, wl.head_size), dtype=torch.bfloat16, device="cuda")
+    newv = torch.ones_like(newk)
+    slots = torch.from_numpy(ops.slot_mapping(g.block_tables, L - 1, 1, 16)).cuda()
+    ws = ops.decode_workspace(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_size, msl, 256)
+    out = torch.empty_like(q)
+
+    def step():
+        ops.reshape_and_cache(newk, newv, slots, g.pool)
+        ops.decode(out, q, g.pool, g.bt_dev, g.seq_lens_dev, msl, float(wl.scale), 256, ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()                                   # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(4):
+        out.zero_()
+        _ = (q.float() * 2).sum()                # unrelated eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), rep
+
+
+def test_split_k_partials_never_stale():
+    """Two different inputs of the same shape alternate through one
+    workspace: the partials of call n+1 occupy the addresses call n used, so
+    a merge that read a stale partial would differ from the first result."""
+    from paged_attention_kv_block_amd import ops
+    from tests.gpu_setup import GpuSide, to_device
+    d = inputs.draw(1)
+    g = GpuSide(d)
+    wl = d.wl
+    msl = int(d.seq_lens.max())
+    qa = to_device(d.query(), wl)
+    qb = -qa
+    ws = ops.decode_workspace(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_size, msl, 128)
+    outs = {}
+    for it in range(12):
+        for name, q in (("a", qa), ("b", qb)):
+            out = torch.empty_like(q)
+            ops.decode(out, q, g.pool, g.bt_dev, g.seq_lens_dev, msl, float(wl.scale), 128, ws)
+            torch.cuda.synchronize()
+            if name not in outs:
+                outs[name] = out
+            else:
+                assert torch.equal(out.view(torch.int16), outs[name].view(torch.int16)), (it, name)
+    assert not torch.equal(outs["a"].view(torch.int16), outs["b"].view(torch.int16))

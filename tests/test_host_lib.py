@@ -250,11 +250,15 @@ def test_decode_validation(kw, status):
 
 
 def test_decode_workspace_size():
-    assert ops.decode_workspace_bytes(4, 8, 128, 64, 0) == 0
-    assert ops.decode_workspace_bytes(4, 8, 128, 64, 64) == 0       # one partition
-    n = ops.decode_workspace_bytes(4, 8, 128, 100, 32)              # 4 partitions
+    assert ops.decode_workspace_bytes(4, 8, 2, 128, 64, 0) == 0
+    assert ops.decode_workspace_bytes(4, 8, 2, 128, 64, 64) == 0       # one partition
+    n = ops.decode_workspace_bytes(4, 8, 2, 128, 100, 32)              # 4 partitions
     rows = 4 * 8 * 4
-    assert n >= rows * (128 + 2) * 4
+    assert n >= rows * (128 + 2) * 4 + 4 * 2 * 4
+    L = ops.lib()
+    assert L.pa_decode_workspace_init(None, 0, None) == ops.PA_OK
+    assert L.pa_decode_workspace_init(None, 256, None) == ops.PA_EINVAL
+    assert L.pa_decode_workspace_init(128, 256, None) == ops.PA_EINVAL   # misaligned
 
 
 def test_reshape_validation():
