@@ -182,6 +182,21 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads,
 int pa_decode_workspace_init(void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* Decode work plan (host).  The attention metadata of a step is prepared on
+ * the CPU and consumed by the kernels ("Inside vLLM", section "LLM Engine
+ * constructor"); this builds the decode kernel's work list from host-side
+ * sequence lengths: one entry per non-empty (sequence, partition) pair,
+ * encoded as (partition << 16) | sequence, longest partitions first.
+ *   seq_lens     [B] int32, host, each in [0, max_seq_len]
+ *   plan         [capacity] int32, host (nullable when capacity is 0)
+ *   num_entries  receives the number of entries (also when capacity is too
+ *                small, in which case PA_EINVAL is returned)
+ * At most B * ceil(max_seq_len / partition_size) entries (B when
+ * partition_size is 0).  B <= 65535 and <= 65535 partitions. */
+int pa_decode_plan(const int32_t* seq_lens, int32_t B, int32_t max_seq_len,
+                   int32_t partition_size, int32_t* plan, int32_t capacity,
+                   int32_t* num_entries);
+
 /* Decode attention: one query token per sequence, the last of its seq_len
  * cached tokens (already written), attends to all of them through its block
  * table; grouped-query heads share KV heads.  The attention itself is the
@@ -199,11 +214,17 @@ int pa_decode_workspace_init(void* workspace, size_t workspace_bytes,
  *                workgroup; the last workgroup of a (sequence, KV head) to
  *                finish combines the partials with a log-sum-exp weighted
  *                sum (split-K, one kernel launch).
+ *   plan, plan_entries  device copy of pa_decode_plan's output for these
+ *                seq_lens and partition_size, or NULL / 0: then every
+ *                (sequence, partition up to max_seq_len) pair is visited and
+ *                the empty ones are skipped on the device.
  *   workspace    device, >= pa_decode_workspace_bytes(...) bytes (nullable
  *                when that is 0), owned by the caller, zeroed once by
  *                pa_decode_workspace_init (or any zero fill) before first
  *                use.  Two pa_decode calls sharing a workspace must not run
  *                concurrently.
+ * The kernel is persistent: it launches at most as many workgroups as fit
+ * on the device and each walks the work items.
  * Supported: block_size 16; head_size 64 or 128; H_q % H_kv == 0 with
  * G = H_q/H_kv in {1, 2, 4, 8} (and 16 for head_size 64). */
 int pa_decode(void* out, float* lse_out, const void* query,
@@ -212,8 +233,8 @@ int pa_decode(void* out, float* lse_out, const void* query,
               const int32_t* seq_lens, int32_t B, int32_t max_seq_len,
               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
               int32_t block_size, float scale, int32_t partition_size,
-              void* workspace, size_t workspace_bytes, int32_t dtype,
-              void* stream);
+              const int32_t* plan, int32_t plan_entries, void* workspace,
+              size_t workspace_bytes, int32_t dtype, void* stream);
 
 /* Chunked prefill ("Im Inneren von vLLM", "Fortgeschrittene Funktionen":
  * long prompts are split into chunks; "Inside vLLM", "Generate function":

@@ -32,6 +32,11 @@
 //     global memory with each lane owning one column pair, and P.V is again
 //     v_dot2_f32_bf16 over token pairs after a byte permute;
 //   * the denominator sums the same bf16-rounded P that multiplies V.
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
 #include "pa.h"
 #include "pa_common.h"
 #include "pa_internal.h"
@@ -66,6 +71,8 @@ struct DecodeCfg {
   static constexpr int ROWS = 16 / HALVES;         // V rows per lane
   static constexpr int VW = BF16 ? 1 : DPL;        // V dwords per row per lane
   static constexpr int P_BYTES = BF16 ? G * 8 * 4 : G * 16 * 4;
+  // blocks in flight per wave (register ring); divides 64
+  static constexpr int PD = (LOADS * 4 + ROWS * VW) <= 16 ? 4 : 2;
   static_assert(CPR % DP == 0 && TPP >= 1 && 16 % TPP == 0, "bad decode lane split");
   static_assert(HG * DP * TPP == kWave, "lane split must cover the wave");
   static_assert(TILE_VEC % kWave == 0, "tile must be a whole number of wave loads");
@@ -294,25 +301,59 @@ __device__ __forceinline__ void process_block(BlockRegs<DecodeCfg<D, G, BF16>>& 
   }
 }
 
+// Arguments of one decode launch (passed by value as the kernel argument).
+struct DecodeParams {
+  void* out;
+  float* lse_out;
+  const void* query;
+  const uint8_t* cache;
+  const int* block_tables;
+  const int* seq_lens;
+  const int* plan;        // (part << 16 | b) entries, or nullptr: virtual grid
+  int* ws_count;
+  float* ws_m;
+  float* ws_l;
+  float* ws_o;
+  int num_blocks, max_blocks_per_seq, max_seq_len, num_kv_heads, B;
+  int part_blocks, max_parts, num_items;
+  float scale_log2;
+};
+
+// LDS of one workgroup: K tiles during the block loop (afterwards reused for
+// the per-wave outputs and the merge weights), P, and the merge state.
 template <int D, int G, bool BF16>
-__global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(
-    void* __restrict__ out, float* __restrict__ lse_out, const void* __restrict__ query,
-    const uint8_t* __restrict__ cache, int num_blocks, const int* __restrict__ block_tables,
-    int max_blocks_per_seq, const int* __restrict__ seq_lens, int max_seq_len, int num_kv_heads,
-    float scale_log2, int part_blocks, int max_parts, int* __restrict__ ws_count,
-    float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o) {
+struct DecodeSmem {
   using C = DecodeCfg<D, G, BF16>;
-  const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  static constexpr int kTiles = kDecodeWaves * C::LDS_TILE;
+  static constexpr int kOStage = kDecodeWaves * G * D * 4;
+  __attribute__((aligned(16))) uint8_t k[kTiles > kOStage ? kTiles : kOStage];
+  __attribute__((aligned(16))) uint32_t p[kDecodeWaves][C::P_BYTES / 4];
+  float alpha[kDecodeWaves][G];
+  float m[kDecodeWaves][G];
+  float l[kDecodeWaves][G];
+  float M[G], W[G];
+  int last;
+};
+
+// One work item: KV head g of sequence b, partition `part` (blocks
+// [part * pb, min((part + 1) * pb, nblk))).  Called by the whole workgroup.
+template <int D, int G, bool BF16>
+__device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D, G, BF16>& sm,
+                                            int b, int g, int part, int L, int nblk, int pb,
+                                            int nparts) {
+  using C = DecodeCfg<D, G, BF16>;
+  void* __restrict__ out = a.out;
+  float* __restrict__ lse_out = a.lse_out;
+  const uint8_t* __restrict__ cache = a.cache;
+  const int num_blocks = a.num_blocks, num_kv_heads = a.num_kv_heads, max_parts = a.max_parts;
+  const float scale_log2 = a.scale_log2;
+  int* __restrict__ ws_count = a.ws_count;
+  float* __restrict__ ws_m = a.ws_m;
+  float* __restrict__ ws_l = a.ws_l;
+  float* __restrict__ ws_o = a.ws_o;
   const int H_q = num_kv_heads * G;
-  int L = seq_lens[b];
-  L = L < 0 ? 0 : (L > max_seq_len ? max_seq_len : L);
-  const int nblk = (L + 15) >> 4;
-  const int pb = part_blocks > 0 ? part_blocks : (nblk > 0 ? nblk : 1);
-  const int nparts = (nblk + pb - 1) / pb;
-  if (part > 0 && part >= nparts) return;
   const int blk_lo = part * pb;
   const int blk_hi = min(blk_lo + pb, nblk);
-
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // QK lane roles
@@ -320,19 +361,10 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(
   const int tq = (lane / C::DP) % C::TPP;
   const int hg = lane / (C::DP * C::TPP);
 
-  // K tiles during the loop; afterwards the per-wave outputs [wave][G][D] fp32
-  constexpr int kTiles = kDecodeWaves * C::LDS_TILE;
-  constexpr int kOStage = kDecodeWaves * G * D * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t smem_k[kTiles > kOStage ? kTiles : kOStage];
-  __shared__ __attribute__((aligned(16))) uint32_t smem_p[kDecodeWaves][C::P_BYTES / 4];
-  __shared__ float smem_alpha[kDecodeWaves][G];
-  __shared__ float smem_m[kDecodeWaves][G];
-  __shared__ float smem_l[kDecodeWaves][G];
-
   // ---- query chunks for this lane: heads hg*HPL + hh, chunks dp*CPL + c
   u32x4 q[C::HPL][C::CPL];
   {
-    const u32x4* qb = reinterpret_cast<const u32x4*>(query) + int64_t(b) * H_q * C::CPR;
+    const u32x4* qb = reinterpret_cast<const u32x4*>(a.query) + int64_t(b) * H_q * C::CPR;
 #pragma unroll
     for (int hh = 0; hh < C::HPL; ++hh) {
       const int h = g * G + hg * C::HPL + hh;
@@ -343,7 +375,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(
 
   const int64_t tile_bytes = int64_t(16) * C::RB;
   const int64_t block_bytes = int64_t(2) * num_kv_heads * tile_bytes;
-  const int* bt_row = block_tables + int64_t(b) * max_blocks_per_seq;
+  const int* bt_row = a.block_tables + int64_t(b) * a.max_blocks_per_seq;
 
   DecodeState<C, G> st;
   st.init();
@@ -352,30 +384,41 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(
   const int half = C::HALVES == 2 ? (lane >> 5) : 0;
   const int col = C::HALVES == 2 ? (lane & 31) : lane;  // dword column within the row
 
-  uint8_t* kt_lds = smem_k + wave * C::LDS_TILE;
-  uint32_t* p_lds = smem_p[wave];
+  uint8_t* kt_lds = sm.k + wave * C::LDS_TILE;
+  uint32_t* p_lds = sm.p[wave];
 
   // Block ids of this wave's blocks (lane i holds the id of block
-  // blk_lo + wave + 4 * (chunk * 64 + i)), read per block with v_readlane.
+  // first + 4 * (chunk * 64 + i)), read per block with v_readlane.  Each wave
+  // keeps PD blocks in flight in a register ring: block k is computed while
+  // blocks k+1 .. k+PD are loading.  Loads past the wave's last block are
+  // clamped to that block (cache hits, never computed), so every iteration
+  // issues the same loads and the compiler's wait counts stay exact.
+  constexpr int PD = C::PD;
   const int first = blk_lo + wave;
   const int nmine = blk_hi > first ? (blk_hi - first + kDecodeWaves - 1) / kDecodeWaves : 0;
   if (nmine > 0) {
     int ids = load_ids(bt_row, first, nmine, 0, lane, num_blocks);
-    BlockRegs<C> nxt = load_block_regs<C>(cache, __builtin_amdgcn_readlane(ids, 0), block_bytes,
-                                          g, num_kv_heads, tile_bytes, lane, half, col);
-    for (int k = 0; k + 1 < nmine; ++k) {
-      if (((k + 1) & (kWave - 1)) == 0) ids = load_ids(bt_row, first, nmine, (k + 1) >> 6, lane, num_blocks);
-      const int id_next = __builtin_amdgcn_readlane(ids, (k + 1) & (kWave - 1));
-      BlockRegs<C> cur = nxt;
-      nxt = load_block_regs<C>(cache, id_next, block_bytes, g, num_kv_heads, tile_bytes, lane,
-                               half, col);
-      const int j = first + k * kDecodeWaves;
-      process_block<D, G, BF16>(cur, min(16, L - j * 16), q, st, kt_lds, p_lds, smem_alpha[wave],
-                                scale_log2, dp, tq, hg, half);
+    BlockRegs<C> buf[PD];
+#pragma unroll
+    for (int s = 0; s < PD; ++s)
+      buf[s] = load_block_regs<C>(cache, __builtin_amdgcn_readlane(ids, min(s, nmine - 1)),
+                                  block_bytes, g, num_kv_heads, tile_bytes, lane, half, col);
+    for (int k0 = 0; k0 < nmine; k0 += PD) {
+      const int kl = k0 + PD;  // first block loaded in this group
+      if (kl < nmine && (kl & (kWave - 1)) == 0) ids = load_ids(bt_row, first, nmine, kl >> 6, lane, num_blocks);
+#pragma unroll
+      for (int s = 0; s < PD; ++s) {
+        const int k = k0 + s;
+        if (k < nmine) {
+          const int j = first + k * kDecodeWaves;
+          process_block<D, G, BF16>(buf[s], min(16, L - j * 16), q, st, kt_lds, p_lds,
+                                    sm.alpha[wave], scale_log2, dp, tq, hg, half);
+        }
+        const int kn = min(kl + s, nmine - 1);
+        buf[s] = load_block_regs<C>(cache, __builtin_amdgcn_readlane(ids, kn & (kWave - 1)),
+                                    block_bytes, g, num_kv_heads, tile_bytes, lane, half, col);
+      }
     }
-    const int j = first + (nmine - 1) * kDecodeWaves;
-    process_block<D, G, BF16>(nxt, min(16, L - j * 16), q, st, kt_lds, p_lds, smem_alpha[wave],
-                              scale_log2, dp, tq, hg, half);
   }
 
   // ---- merge: this wave's denominator, then the 4 waves of the workgroup
@@ -387,8 +430,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(
     for (int bit = ilog2(C::DP); bit < ilog2(C::DP * C::TPP); ++bit)
       lsum += __shfl_xor(lsum, 1 << bit, kWave);
     if (tq == 0 && dp == 0) {
-      smem_m[wave][hg * C::HPL + hh] = st.m_run[hh];
-      smem_l[wave][hg * C::HPL + hh] = lsum;
+      sm.m[wave][hg * C::HPL + hh] = st.m_run[hh];
+      sm.l[wave][hg * C::HPL + hh] = lsum;
     }
   }
   if constexpr (C::HALVES == 2) {
@@ -398,7 +441,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(
       for (int jj = 0; jj < C::DPL; ++jj) st.o[h][jj] += __shfl_xor(st.o[h][jj], 32, kWave);
   }
   __syncthreads();  // all waves done with their tiles: reuse smem_k for o
-  float* o_lds = reinterpret_cast<float*>(smem_k);  // [wave][G][D]
+  float* o_lds = reinterpret_cast<float*>(sm.k);  // [wave][G][D]
   if (C::HALVES == 1 || half == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -414,13 +457,13 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(
     const int h = e / D, d = e % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, smem_m[w][h]);
+    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, sm.m[w][h]);
     float lsum = 0.f, acc = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kDecodeWaves; ++w) {
-        const float wt = exp2f(smem_m[w][h] - M);  // 0 for a wave with no tokens
-        lsum += wt * smem_l[w][h];
+        const float wt = exp2f(sm.m[w][h] - M);  // 0 for a wave with no tokens
+        lsum += wt * sm.l[w][h];
         acc += wt * o_lds[(w * G + h) * D + d];
       }
     }
@@ -445,22 +488,20 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(
   // are coherent across the XCDs' L2 caches (agent scope), and this
   // workgroup's writes have completed before its arrival is counted, so the
   // workgroup that counts last sees every partial.  No L2 flush is needed.
-  __shared__ int s_last;
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
   __syncthreads();
   if (tid == 0) {
     const int old = __hip_atomic_fetch_add(&ws_count[b * num_kv_heads + g], 1, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
-    s_last = old == nparts - 1;
+    sm.last = old == nparts - 1;
   }
   __syncthreads();
-  if (!s_last) return;
+  if (!sm.last) return;
   if (tid == 0)  // ready for the next call
     __hip_atomic_store(&ws_count[b * num_kv_heads + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // per head: M = max_p m_p and W = sum_p 2^(m_p - M) l_p (one wave per head)
-  __shared__ float s_M[G], s_W[G];
-  for (int h = wave; h < G; h += kDecodeWaves) {
+    for (int h = wave; h < G; h += kDecodeWaves) {
     const int64_t row = int64_t(b) * H_q + g * G + h;
     const float* m = ws_m + row * max_parts;
     const float* l = ws_l + row * max_parts;
@@ -471,13 +512,13 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(
     for (int p = lane; p < nparts; p += kWave)
       W += exp2f(coherent_load(m + p) - M) * coherent_load(l + p);
     W = allreduce_sum<0, 6>(W);
-    if (lane == 0) { s_M[h] = M; s_W[h] = W; }
+    if (lane == 0) { sm.M[h] = M; sm.W[h] = W; }
   }
   __syncthreads();
   // O = sum_p w_p o_p / W, the weights staged through LDS in chunks
   constexpr int EPT = (G * D + kDecodeWaves * kWave - 1) / (kDecodeWaves * kWave);
-  constexpr int WCAP = int(sizeof(smem_k) / sizeof(float)) / G;  // weights per head per chunk
-  float* wbuf = reinterpret_cast<float*>(smem_k);
+  constexpr int WCAP = int(sizeof(sm.k) / sizeof(float)) / G;  // weights per head per chunk
+  float* wbuf = reinterpret_cast<float*>(sm.k);
   float acc[EPT];
 #pragma unroll
   for (int k = 0; k < EPT; ++k) acc[k] = 0.f;
@@ -486,7 +527,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(
     for (int idx = tid; idx < G * pc; idx += kDecodeWaves * kWave) {
       const int h = idx / pc, pp = idx % pc;
       const int64_t prow = (int64_t(b) * H_q + g * G + h) * max_parts + p0 + pp;
-      wbuf[h * WCAP + pp] = exp2f(coherent_load(ws_m + prow) - s_M[h]) * coherent_load(ws_l + prow);
+      wbuf[h * WCAP + pp] = exp2f(coherent_load(ws_m + prow) - sm.M[h]) * coherent_load(ws_l + prow);
     }
     __syncthreads();
 #pragma unroll
@@ -509,9 +550,43 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_partition_kernel(
     if (e < G * D) {
       const int h = e / D, d = e % D;
       const int64_t row = int64_t(b) * H_q + g * G + h;
-      store_out<BF16>(out, row * D + d, acc[k] / s_W[h]);
-      if (lse_out && d == 0) lse_out[row] = s_M[h] * kLn2 + logf(s_W[h]);
+      store_out<BF16>(out, row * D + d, acc[k] / sm.W[h]);
+      if (lse_out && d == 0) lse_out[row] = sm.M[h] * kLn2 + logf(sm.W[h]);
     }
+  }
+}
+
+
+// Decode kernel: each workgroup walks work items t = blockIdx.x,
+// blockIdx.x + gridDim.x, ...  With a plan the items are its (b, part)
+// entries times the KV heads (one workgroup per item); without one they are
+// the virtual grid (part, b, g) walked by a grid of a few times the resident
+// workgroups, and items past a sequence's last partition are skipped in the
+// loop instead of being dispatched as empty workgroups.
+template <int D, int G, bool BF16>
+__global__ __launch_bounds__(kDecodeWaves * kWave) void decode_kernel(const DecodeParams a) {
+  __shared__ DecodeSmem<D, G, BF16> sm;
+  for (int t = blockIdx.x; t < a.num_items; t += gridDim.x) {
+    const int g = t % a.num_kv_heads;
+    int b, part;
+    if (a.plan) {
+      const int e = a.plan[t / a.num_kv_heads];
+      b = e & 0xFFFF;
+      part = (e >> 16) & 0xFFFF;
+      if (b >= a.B) continue;  // not an entry of this batch
+    } else {
+      const int r = t / a.num_kv_heads;
+      b = r % a.B;
+      part = r / a.B;
+    }
+    int L = a.seq_lens[b];
+    L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+    const int nblk = (L + 15) >> 4;
+    const int pb = a.part_blocks > 0 ? a.part_blocks : (nblk > 0 ? nblk : 1);
+    const int nparts = (nblk + pb - 1) / pb;
+    if (part > 0 && part >= nparts) continue;
+    decode_item<D, G, BF16>(a, sm, b, g, part, L, nblk, pb, nparts);
+    __syncthreads();  // LDS is reused by the next item
   }
 }
 
@@ -524,41 +599,47 @@ __global__ void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-struct DecodeArgs {
-  void* out;
-  float* lse;
-  const void* q;
-  const uint8_t* cache;
-  int num_blocks;
-  const int* bt;
-  int max_blocks;
-  const int* seq_lens;
-  int B, max_seq_len, H_kv;
-  float scale_log2;
-  int part_blocks, max_parts;
-  int* ws_count;
-  float *ws_m, *ws_l, *ws_o;
-  hipStream_t s;
-};
+// Workgroups that fit on the device at once for a kernel (cached per device
+// and kernel): the persistent grid never exceeds this.
+template <class K>
+static int resident_workgroups(K kernel) {
+  constexpr int kMaxDev = 64;
+  static int cached[kMaxDev] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) dev = 0;
+  if (cached[dev] > 0) return cached[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kDecodeWaves * kWave, 0) !=
+          hipSuccess || per_cu <= 0)
+    per_cu = 1;
+  cached[dev] = cus * per_cu;
+  if (std::getenv("PA_DEBUG"))
+    std::fprintf(stderr, "pa: device %d: %d CUs x %d resident workgroups\n", dev, cus, per_cu);
+  return cached[dev];
+}
 
 template <int D, int G, bool BF16>
-static void launch_decode(const DecodeArgs& a) {
-  dim3 grid(a.max_parts, a.H_kv, a.B);
-  hipLaunchKernelGGL((decode_partition_kernel<D, G, BF16>), grid, dim3(kDecodeWaves * kWave), 0,
-                     a.s, a.out, a.lse, a.q, a.cache, a.num_blocks, a.bt, a.max_blocks, a.seq_lens,
-                     a.max_seq_len, a.H_kv, a.scale_log2, a.part_blocks, a.max_parts, a.ws_count,
-                     a.ws_m, a.ws_l, a.ws_o);
+static void launch_decode(const DecodeParams& a, hipStream_t s) {
+  auto k = decode_kernel<D, G, BF16>;
+  // With a plan every item is real: one workgroup each, so the hardware
+  // dispatcher balances them and overlaps one item's merge with another's
+  // loads.  Without one, a persistent grid skips the empty virtual items.
+  const int grid = a.plan ? a.num_items
+                          : std::max(1, std::min(a.num_items, 4 * resident_workgroups(k)));
+  hipLaunchKernelGGL(k, dim3(grid), dim3(kDecodeWaves * kWave), 0, s, a);
 }
 
 template <int D, bool BF16>
-static bool dispatch_g(int G, const DecodeArgs& a) {
+static bool dispatch_g(int G, const DecodeParams& a, hipStream_t s) {
   switch (G) {
-    case 1: launch_decode<D, 1, BF16>(a); return true;
-    case 2: launch_decode<D, 2, BF16>(a); return true;
-    case 4: launch_decode<D, 4, BF16>(a); return true;
-    case 8: launch_decode<D, 8, BF16>(a); return true;
+    case 1: launch_decode<D, 1, BF16>(a, s); return true;
+    case 2: launch_decode<D, 2, BF16>(a, s); return true;
+    case 4: launch_decode<D, 4, BF16>(a, s); return true;
+    case 8: launch_decode<D, 8, BF16>(a, s); return true;
     case 16:
-      if constexpr (D == 64) { launch_decode<D, 16, BF16>(a); return true; }
+      if constexpr (D == 64) { launch_decode<D, 16, BF16>(a, s); return true; }
       return false;
     default: return false;
   }
@@ -623,14 +704,52 @@ extern "C" int pa_decode_workspace_init(void* workspace, size_t workspace_bytes,
   return PA_OK;
 }
 
+extern "C" int pa_decode_plan(const int32_t* seq_lens, int32_t B, int32_t max_seq_len,
+                              int32_t partition_size, int32_t* plan, int32_t capacity,
+                              int32_t* num_entries) {
+  if (B < 0 || max_seq_len < 0 || partition_size < 0 || partition_size % kBlockSize || capacity < 0)
+    return fail(PA_EINVAL, "pa_decode_plan: bad sizes");
+  if (B > 65535) return fail(PA_ENOTSUP, "pa_decode_plan: B %d > 65535", B);
+  if (B > 0 && !seq_lens) return fail(PA_EINVAL, "pa_decode_plan: NULL seq_lens");
+  const int64_t P = parts_for(max_seq_len, partition_size);
+  if (P > 65535) return fail(PA_ENOTSUP, "pa_decode_plan: too many partitions");
+  // (tokens, b, part) of every non-empty partition; a sequence of length 0
+  // still gets one item (its output row is zero)
+  struct Item { int32_t tokens, b, part; };
+  std::vector<Item> items;
+  items.reserve(size_t(B) * 2);
+  for (int32_t b = 0; b < B; ++b) {
+    int32_t L = seq_lens[b];
+    if (L < 0 || L > max_seq_len)
+      return fail(PA_EINVAL, "pa_decode_plan: seq_lens[%d] = %d outside [0, %d]", b, L, max_seq_len);
+    const int32_t ptok = P > 1 ? partition_size : std::max(L, 1);
+    const int32_t np = L == 0 ? 1 : (L + ptok - 1) / ptok;
+    for (int32_t p = 0; p < np; ++p) items.push_back({std::min(ptok, L - p * ptok), b, p});
+  }
+  // longest first; among equal sizes partition-major, so items running at
+  // the same time belong to different sequences (their split-K arrival
+  // counters differ).  Workgroups take items round robin.
+  std::stable_sort(items.begin(), items.end(), [](const Item& x, const Item& y) {
+    if (x.tokens != y.tokens) return x.tokens > y.tokens;
+    if (x.part != y.part) return x.part < y.part;
+    return x.b < y.b;
+  });
+  if (num_entries) *num_entries = int32_t(items.size());
+  if (int64_t(items.size()) > capacity)
+    return fail(PA_EINVAL, "pa_decode_plan: %zu entries, capacity %d", items.size(), capacity);
+  if (!items.empty() && !plan) return fail(PA_EINVAL, "pa_decode_plan: NULL plan");
+  for (size_t i = 0; i < items.size(); ++i) plan[i] = (items[i].part << 16) | items[i].b;
+  return PA_OK;
+}
+
 extern "C" int pa_decode(void* out, float* lse_out, const void* query, const void* kv_cache,
                          int32_t num_blocks, const int32_t* block_tables,
                          int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t B,
                          int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
                          int32_t head_size, int32_t block_size, float scale,
-                         int32_t partition_size, void* workspace, size_t workspace_bytes,
-                         int32_t dtype, void* stream) {
-  if (B < 0 || num_blocks < 0 || max_seq_len < 0 || max_blocks_per_seq < 0)
+                         int32_t partition_size, const int32_t* plan, int32_t plan_entries,
+                         void* workspace, size_t workspace_bytes, int32_t dtype, void* stream) {
+  if (B < 0 || num_blocks < 0 || max_seq_len < 0 || max_blocks_per_seq < 0 || plan_entries < 0)
     return fail(PA_EINVAL, "pa_decode: negative size");
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
     return fail(PA_EINVAL, "pa_decode: H_q %d not a multiple of H_kv %d", num_q_heads, num_kv_heads);
@@ -649,39 +768,43 @@ extern "C" int pa_decode(void* out, float* lse_out, const void* query, const voi
     return fail(PA_EINVAL, "pa_decode: NULL pointer");
   if ((uintptr_t(out) | uintptr_t(query) | uintptr_t(kv_cache)) & 15)
     return fail(PA_EINVAL, "pa_decode: out/query/cache must be 16-byte aligned");
-  if ((uintptr_t(block_tables) | uintptr_t(seq_lens) | uintptr_t(lse_out)) & 3)
+  if ((uintptr_t(block_tables) | uintptr_t(seq_lens) | uintptr_t(lse_out) | uintptr_t(plan)) & 3)
     return fail(PA_EINVAL, "pa_decode: int/float arrays must be 4-byte aligned");
   if (num_blocks == 0 && max_seq_len > 0)
     return fail(PA_EINVAL, "pa_decode: empty pool but max_seq_len %d", max_seq_len);
+  if (plan && (B > 65535 || plan_entries == 0))
+    return fail(PA_EINVAL, "pa_decode: a plan needs B <= 65535 and at least one entry");
   const int G = num_q_heads / num_kv_heads;
   const int64_t P = parts_for(max_seq_len, partition_size);
   if (P > 65535) return fail(PA_EINVAL, "pa_decode: too many partitions (%lld)", (long long)P);
-  if (num_kv_heads > 65535 || B > 65535) return fail(PA_ENOTSUP, "pa_decode: grid too large");
-  if (P > 1 && int64_t(B) * num_kv_heads > kCounterCap)
-    return fail(PA_ENOTSUP, "pa_decode: split-K supports B * H_kv <= %lld",
-                (long long)kCounterCap);
+  const int64_t items = (plan ? int64_t(plan_entries) : int64_t(B) * P) * num_kv_heads;
+  if (items > 0x7FFFFFFF) return fail(PA_ENOTSUP, "pa_decode: too many work items");
   const size_t need =
       pa_decode_workspace_bytes(B, num_q_heads, num_kv_heads, head_size, max_seq_len, partition_size);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PA_EINVAL, "pa_decode: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if (need > 0 && (uintptr_t(workspace) & 255))
     return fail(PA_EINVAL, "pa_decode: workspace must be 256-byte aligned");
+  if (P > 1 && int64_t(B) * num_kv_heads > kCounterCap)
+    return fail(PA_ENOTSUP, "pa_decode: split-K supports B * H_kv <= %lld", (long long)kCounterCap);
 
-  DecodeArgs a{};
+  DecodeParams a{};
   a.out = out;
-  a.lse = lse_out;
-  a.q = query;
+  a.lse_out = lse_out;
+  a.query = query;
   a.cache = static_cast<const uint8_t*>(kv_cache);
-  a.num_blocks = num_blocks;
-  a.bt = block_tables;
-  a.max_blocks = max_blocks_per_seq;
+  a.block_tables = block_tables;
   a.seq_lens = seq_lens;
-  a.B = B;
+  a.plan = plan;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_seq_len = max_seq_len;
-  a.H_kv = num_kv_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.B = B;
   a.scale_log2 = scale * kLog2e;
   a.part_blocks = P > 1 ? partition_size / kBlockSize : 0;
   a.max_parts = int(P);
+  a.num_items = int(items);
   if (P > 1) {
     const WsLayout w = ws_layout(B, num_q_heads, num_kv_heads, head_size, P);
     uint8_t* base = static_cast<uint8_t*>(workspace);
@@ -690,13 +813,12 @@ extern "C" int pa_decode(void* out, float* lse_out, const void* query, const voi
     a.ws_l = reinterpret_cast<float*>(base + w.l_off);
     a.ws_o = reinterpret_cast<float*>(base + w.o_off);
   }
-  a.s = reinterpret_cast<hipStream_t>(stream);
-
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   bool ok;
   if (dtype == PA_BF16)
-    ok = head_size == 64 ? dispatch_g<64, true>(G, a) : dispatch_g<128, true>(G, a);
+    ok = head_size == 64 ? dispatch_g<64, true>(G, a, st) : dispatch_g<128, true>(G, a, st);
   else
-    ok = head_size == 64 ? dispatch_g<64, false>(G, a) : dispatch_g<128, false>(G, a);
+    ok = head_size == 64 ? dispatch_g<64, false>(G, a, st) : dispatch_g<128, false>(G, a, st);
   if (!ok) return fail(PA_ENOTSUP, "pa_decode: group size %d with head_size %d", G, head_size);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_EHIP, "pa_decode: launch failed: %s", hipGetErrorString(e));

@@ -43,8 +43,10 @@ SIGNATURES = {
                                       _c_i32, _c_i32, _vp]),
     "pa_decode_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "pa_decode_workspace_init": (_c_int, [_vp, _c_sz, _vp]),
+    "pa_decode_plan": (_c_int, [_vp, _c_i32, _c_i32, _c_i32, _vp, _c_i32, _vp]),
     "pa_decode": (_c_int, [_vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _vp, _c_i32, _c_i32,
-                           _c_i32, _c_i32, _c_i32, _c_i32, _f, _c_i32, _vp, _c_sz, _c_i32, _vp]),
+                           _c_i32, _c_i32, _c_i32, _c_i32, _f, _c_i32, _vp, _c_i32, _vp, _c_sz,
+                           _c_i32, _vp]),
     "pa_prefill_chunk": (_c_int, [_vp, _vp, _vp, _vp, _c_i32, _c_i32, _vp, _c_i32, _vp, _c_i32,
                                   _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _f,
                                   _c_i32, _vp]),
@@ -250,12 +252,25 @@ def decode_workspace(B: int, num_q_heads: int, num_kv_heads: int, head_size: int
     return ws
 
 
+def decode_plan(seq_lens_host, max_seq_len: int, partition_size: int) -> np.ndarray:
+    """Host-built work list of pa_decode (int32 entries, longest first)."""
+    sl = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    n = ctypes.c_int32()
+    lib().pa_decode_plan(_np_ptr(sl), sl.size, int(max_seq_len), int(partition_size), None, 0,
+                         ctypes.byref(n))
+    out = np.empty(max(n.value, 1), dtype=np.int32)
+    _check(lib().pa_decode_plan(_np_ptr(sl), sl.size, int(max_seq_len), int(partition_size),
+                                _np_ptr(out), out.size, ctypes.byref(n)))
+    return out[:n.value]
+
+
 def decode(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int, scale: float,
-           partition_size: int = 0, workspace=None, lse=None, stream=None) -> None:
+           partition_size: int = 0, workspace=None, lse=None, plan=None, stream=None) -> None:
     """out/query [B, H_q, D]; kv_cache [N, 2, H_kv, 16, D]; block_tables int32
     [B, max_blocks]; seq_lens int32 [B]; lse fp32 [B, H_q] or None;
-    workspace a uint8 GPU tensor of decode_workspace_bytes(...) bytes."""
-    _need_gpu(out, query, kv_cache, block_tables, seq_lens, workspace, lse)
+    workspace a uint8 GPU tensor of decode_workspace_bytes(...) bytes; plan an
+    int32 GPU tensor holding decode_plan(...) for the same lengths, or None."""
+    _need_gpu(out, query, kv_cache, block_tables, seq_lens, workspace, lse, plan)
     torch = _torch()
     N, _, Hkv, bs, D = kv_cache.shape
     B, Hq, Dq = query.shape
@@ -271,10 +286,13 @@ def decode(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int, scale
         if t is not None and not t.is_contiguous():
             raise PAError(PA_EINVAL, "tensors must be contiguous")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if plan is not None and plan.dtype != torch.int32:
+        raise PAError(PA_EINVAL, "plan must be int32")
     _check(lib().pa_decode(_ptr(out), _ptr(lse), _ptr(query), _ptr(kv_cache), N,
                            _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), B,
                            int(max_seq_len), Hq, Hkv, D, bs, float(scale), int(partition_size),
-                           _ptr(workspace), ws_bytes, _dtype_code(kv_cache), _stream(stream)))
+                           _ptr(plan), 0 if plan is None else plan.numel(), _ptr(workspace),
+                           ws_bytes, _dtype_code(kv_cache), _stream(stream)))
 
 
 def prefill_chunk(out, query, query_start_loc, max_query_len: int, kv_cache, block_tables,

@@ -86,7 +86,8 @@ class GpuSide:
         ops.reshape_and_cache(key, val, sm, self.pool)
         return self.pool
 
-    def decode(self, partition_size=None, scale=None, with_lse=True, max_seq_len=None):
+    def decode(self, partition_size=None, scale=None, with_lse=True, max_seq_len=None,
+               use_plan=False):
         wl, d = self.wl, self.d
         q = to_device(d.query(), wl, self.device)
         out = torch.empty_like(q)
@@ -95,8 +96,11 @@ class GpuSide:
         msl = int(max(d.seq_lens)) if max_seq_len is None else max_seq_len
         ws = ops.decode_workspace(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_size, msl,
                                   P, self.device)
+        plan = None
+        if use_plan:
+            plan = torch.from_numpy(ops.decode_plan(d.seq_lens, msl, P)).to(self.device)
         ops.decode(out, q, self.pool, self.bt_dev, self.seq_lens_dev, msl,
-                   float(wl.scale if scale is None else scale), P, ws, lse)
+                   float(wl.scale if scale is None else scale), P, ws, lse, plan)
         torch.cuda.synchronize()
         return out, lse
 

@@ -47,14 +47,14 @@ def check_pool(o, g):
         np.testing.assert_array_equal(got, o.pool)
 
 
-def run_decode_case(d, partition_size=None, seqs=None, check_pool_bits=True):
+def run_decode_case(d, partition_size=None, seqs=None, check_pool_bits=True, use_plan=False):
     GpuSide, _ = _gpu()
     o = OracleSide(d, seqs=seqs)
     g = GpuSide(d)
     check_tables(o, g)
     if check_pool_bits and seqs is None:
         check_pool(o, g)
-    out, lse = g.decode(partition_size=partition_size)
+    out, lse = g.decode(partition_size=partition_size, use_plan=use_plan)
     ref, ref_lse = o.decode(seqs=seqs)
     rows = list(range(d.wl.num_seqs)) if seqs is None else list(seqs)
     got = out_f64(out)[rows]
@@ -103,13 +103,19 @@ def test_decode_edge_shapes(name, kw, P):
     run_decode_case(inputs.custom(kind="decode", **kw), partition_size=P)
 
 
+@pytest.mark.parametrize("name,kw", EDGE[:5], ids=[e[0] for e in EDGE[:5]])
+@pytest.mark.parametrize("P", [0, 32])
+def test_decode_edge_shapes_planned(name, kw, P):
+    run_decode_case(inputs.custom(kind="decode", **kw), partition_size=P, use_plan=True)
+
+
 def test_zero_length_row():
     GpuSide, _ = _gpu()
     d = inputs.custom(kind="decode", seq_lens=(0, 20, 0), num_q_heads=8, num_kv_heads=2,
                       head_size=64, num_blocks=4)
     g = GpuSide(d)
-    for P in (0, 16):
-        out, lse = g.decode(partition_size=P)
+    for P, up in ((0, False), (16, False), (0, True), (16, True)):
+        out, lse = g.decode(partition_size=P, use_plan=up)
         o = out_f64(out)
         assert np.all(o[0] == 0) and np.all(o[2] == 0)
         assert np.all(np.isneginf(lse[0].cpu().numpy())) and np.all(np.isneginf(lse[2].cpu().numpy()))
@@ -122,8 +128,9 @@ def test_tinyllama_workload_parity():
 
 
 @pytest.mark.parametrize("P", [256, 512])
-def test_tinyllama_workload_split(P):
-    run_decode_case(inputs.draw(1), partition_size=P)
+@pytest.mark.parametrize("use_plan", [False, True])
+def test_tinyllama_workload_split(P, use_plan):
+    run_decode_case(inputs.draw(1), partition_size=P, use_plan=use_plan)
 
 
 def test_llama3_workload_sampled():
@@ -132,7 +139,8 @@ def test_llama3_workload_sampled():
     d = inputs.draw(2)
     L = d.seq_lens
     seqs = sorted({int(np.argmax(L)), int(np.argmin(L)), 0, 1, 100, 255})
-    run_decode_case(d, partition_size=512, seqs=seqs)
+    run_decode_case(d, partition_size=512, seqs=seqs, use_plan=True)
+    run_decode_case(d, partition_size=512, seqs=seqs[:3], use_plan=False)
 
 
 def test_unit_values_give_unit_output():

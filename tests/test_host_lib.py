@@ -226,8 +226,8 @@ def _decode_status(**kw):
     L = ops.lib()
     st = L.pa_decode(args["out"], args["lse"], args["q"], args["cache"], args["nb"], args["bt"],
                      args["mbps"], args["sl"], args["B"], args["msl"], args["hq"], args["hkv"],
-                     args["d"], args["bs"], args["scale"], args["P"], args["ws"], args["wsb"],
-                     args["dtype"], None)
+                     args["d"], args["bs"], args["scale"], args["P"], args.get("plan"),
+                     args.get("plan_n", 0), args["ws"], args["wsb"], args["dtype"], None)
     return st, L.pa_last_error().decode()
 
 
@@ -242,6 +242,8 @@ def _decode_status(**kw):
     (dict(dtype=5), ops.PA_EINVAL),          # unknown dtype
     (dict(hq=48, hkv=2, d=128), ops.PA_ENOTSUP),  # group 24
     (dict(scale=float("nan")), ops.PA_EINVAL),
+    (dict(plan=16, plan_n=0), ops.PA_EINVAL),     # a plan without entries
+    (dict(plan=18, plan_n=2), ops.PA_EINVAL),     # misaligned plan
 ])
 def test_decode_validation(kw, status):
     st, msg = _decode_status(**kw)
@@ -284,3 +286,18 @@ def test_prefill_validation():
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         ops.lib(str(tmp_path / "libpa.so"))
+
+
+def test_decode_plan_lists_nonempty_partitions_longest_first():
+    sl = np.array([0, 100, 512, 513, 1100], np.int32)
+    plan = ops.decode_plan(sl, 1100, 512)
+    ent = [(int(e) & 0xFFFF, int(e) >> 16) for e in plan]
+    # (b, part): b0 -> 1 (empty row), b1 -> 1, b2 -> 1, b3 -> 2, b4 -> 3
+    assert sorted(ent) == [(0, 0), (1, 0), (2, 0), (3, 0), (3, 1), (4, 0), (4, 1), (4, 2)]
+    sizes = {(0, 0): 0, (1, 0): 100, (2, 0): 512, (3, 0): 512, (3, 1): 1, (4, 0): 512,
+             (4, 1): 512, (4, 2): 76}
+    got = [sizes[e] for e in ent]
+    assert got == sorted(got, reverse=True)
+    assert ops.decode_plan(sl, 1100, 0).size == 5               # one item per sequence
+    with pytest.raises(ops.PAError):
+        ops.decode_plan(np.array([5000], np.int32), 1100, 512)   # beyond max_seq_len
