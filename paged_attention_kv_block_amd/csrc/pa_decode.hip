@@ -43,9 +43,11 @@
 
 namespace pa {
 
-constexpr int kDecodeWaves = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// How far (in log2 units) a block's max may exceed the softmax reference
+// before the reference moves; P then stays <= 2^8.
+constexpr float kRescaleSlack = 8.f;
 
 template <int D, int G, bool BF16>
 struct DecodeCfg {
@@ -57,7 +59,7 @@ struct DecodeCfg {
   static constexpr int HG = G >= 4 ? 4 : G;        // head groups across lanes
   static constexpr int HPL = G / HG;               // heads per lane
   static constexpr int QCH_NEED = HPL * CPR;       // q chunks a lane would need with DP = 1
-  static constexpr int DP_Q = QCH_NEED <= 16 ? 1 : QCH_NEED / 16;  // keep q <= 16 chunks
+  static constexpr int DP_Q = QCH_NEED <= 8 ? 1 : QCH_NEED / 8;  // keep q <= 8 chunks (32 VGPRs)
   static constexpr int DP_MIN = 4 / HG;
   static constexpr int DP = DP_Q > DP_MIN ? DP_Q : DP_MIN;  // lanes sharing one token row
   static constexpr int TPP = kWave / (HG * DP);    // tokens per pass
@@ -72,7 +74,7 @@ struct DecodeCfg {
   static constexpr int VW = BF16 ? 1 : DPL;        // V dwords per row per lane
   static constexpr int P_BYTES = BF16 ? G * 8 * 4 : G * 16 * 4;
   // blocks in flight per wave (register ring); divides 64
-  static constexpr int PD = (LOADS * 4 + ROWS * VW) <= 16 ? 4 : 2;
+  static constexpr int PD = 2;
   static_assert(CPR % DP == 0 && TPP >= 1 && 16 % TPP == 0, "bad decode lane split");
   static_assert(HG * DP * TPP == kWave, "lane split must cover the wave");
   static_assert(TILE_VEC % kWave == 0, "tile must be a whole number of wave loads");
@@ -159,16 +161,6 @@ struct DecodeState {
   }
 };
 
-// Ids of up to 64 of a wave's blocks: lane i gets the id of logical block
-// first + 4 * (chunk * 64 + i) (clamped into the pool; lanes past the wave's
-// last block read nothing).
-__device__ __forceinline__ int load_ids(const int* __restrict__ bt_row, int first, int nmine,
-                                        int chunk, int lane, int num_blocks) {
-  const int k = chunk * kWave + lane;
-  int id = k < nmine ? bt_row[first + k * kDecodeWaves] : 0;
-  return (id < 0 || id >= num_blocks) ? 0 : id;  // out-of-range ids read block 0
-}
-
 // One 16-token block: K tile through LDS, scores, online softmax, P to LDS,
 // P.V into the lane's output columns.  `valid` tokens of the block are inside
 // the sequence (>= 1).
@@ -208,46 +200,73 @@ __device__ __forceinline__ void process_block(BlockRegs<DecodeCfg<D, G, BF16>>& 
     }
 #pragma unroll
     for (int hh = 0; hh < C::HPL; ++hh) {
-      float x = allreduce_sum<0, ilog2(C::DP)>(s[ps][hh]);
-      x *= scale_log2;
-      s[ps][hh] = (row < valid) ? x : -INFINITY;
+      float x = allreduce_sum<0, ilog2(C::DP)>(s[ps][hh]) * scale_log2;
+      if (valid < 16) x = (row < valid) ? x : -INFINITY;  // tail block only
+      s[ps][hh] = x;
     }
   }
 
-  // ---- online softmax per head (max over the block's 16 tokens)
+  // ---- online softmax per head with a lazily moved reference: the
+  // reference m_run moves only when the block's max exceeds it by more than
+  // kRescaleSlack (log2 units), so P = 2^(s - m_run) <= 2^kRescaleSlack and
+  // most blocks need no rescale of the accumulated output.
   float alpha[C::HPL];
+  bool moved = false;
 #pragma unroll
   for (int hh = 0; hh < C::HPL; ++hh) {
     float mb = s[0][hh];
 #pragma unroll
     for (int ps = 1; ps < C::NPASS; ++ps) mb = fmaxf(mb, s[ps][hh]);
     mb = allreduce_max<ilog2(C::DP), ilog2(C::DP * C::TPP)>(mb);
-    const float m_new = fmaxf(st.m_run[hh], mb);  // finite: token 0 of the block is valid
-    alpha[hh] = exp2f(st.m_run[hh] - m_new);
-    st.m_run[hh] = m_new;
+    // mb is finite: token 0 of the block is inside the sequence
+    const bool grow = mb > st.m_run[hh] + kRescaleSlack;
+    alpha[hh] = grow ? __builtin_amdgcn_exp2f(st.m_run[hh] - mb) : 1.f;
+    st.m_run[hh] = grow ? mb : st.m_run[hh];
     st.l_part[hh] *= alpha[hh];
+    moved |= grow;
   }
+  const bool any_moved = __builtin_amdgcn_ballot_w64(moved) != 0;  // wave-uniform
 
-  // ---- P to LDS
+  // ---- P to LDS (bf16 token pairs [head][pair], or fp32 [head][token])
 #pragma unroll
   for (int ps = 0; ps < C::NPASS; ++ps) {
     const int row = ps * C::TPP + tq;
+    float p[C::HPL];
 #pragma unroll
-    for (int hh = 0; hh < C::HPL; ++hh) {
-      const int h = hg * C::HPL + hh;
-      const float p = exp2f(s[ps][hh] - st.m_run[hh]);
-      if constexpr (BF16) {
-        const uint32_t pb16 = f32_to_bf16_rne(p);
-        st.l_part[hh] += (dp == 0) ? __uint_as_float(pb16 << 16) : 0.f;
-        const uint32_t nb = dpp_u<0x100 + C::DP>(pb16);  // row_shl: lane + DP = token + 1
-        if (dp == 0 && (row & 1) == 0) p_lds[h * 8 + (row >> 1)] = pb16 | (nb << 16);
+    for (int hh = 0; hh < C::HPL; ++hh) p[hh] = __builtin_amdgcn_exp2f(s[ps][hh] - st.m_run[hh]);
+    if constexpr (BF16) {
+      if constexpr (C::HPL % 2 == 0) {
+        // two heads per conversion: (head hh, head hh+1) of this token; the
+        // neighbour lane (token + 1) supplies the second token of each pair
+#pragma unroll
+        for (int hh = 0; hh < C::HPL; hh += 2) {
+          const uint32_t pk = pack_bf16x2(p[hh], p[hh + 1]);
+          if (dp == 0) {
+            st.l_part[hh] += bf16_lo(pk);
+            st.l_part[hh + 1] += bf16_hi(pk);
+          }
+          const uint32_t nb = dpp_u<0x100 + C::DP>(pk);  // row_shl: lane + DP = token + 1
+          if (dp == 0 && (row & 1) == 0) {
+            const int h = hg * C::HPL + hh;
+            p_lds[h * 8 + (row >> 1)] = __builtin_amdgcn_perm(nb, pk, 0x05040100u);
+            p_lds[(h + 1) * 8 + (row >> 1)] = __builtin_amdgcn_perm(nb, pk, 0x07060302u);
+          }
+        }
       } else {
-        st.l_part[hh] += (dp == 0) ? p : 0.f;
-        if (dp == 0) reinterpret_cast<float*>(p_lds)[h * 16 + row] = p;
+        const float pn = dpp_f<0x100 + C::DP>(p[0]);   // token + 1
+        const uint32_t pk = pack_bf16x2(p[0], pn);       // (token, token + 1)
+        if (dp == 0) st.l_part[0] += bf16_lo(pk);
+        if (dp == 0 && (row & 1) == 0) p_lds[hg * 8 + (row >> 1)] = pk;
+      }
+    } else {
+#pragma unroll
+      for (int hh = 0; hh < C::HPL; ++hh) {
+        st.l_part[hh] += (dp == 0) ? p[hh] : 0.f;
+        if (dp == 0) reinterpret_cast<float*>(p_lds)[(hg * C::HPL + hh) * 16 + row] = p[hh];
       }
     }
   }
-  if (tq == 0 && dp == 0) {
+  if (any_moved && tq == 0 && dp == 0) {
 #pragma unroll
     for (int hh = 0; hh < C::HPL; ++hh) alpha_lds[hg * C::HPL + hh] = alpha[hh];
   }
@@ -261,11 +280,13 @@ __device__ __forceinline__ void process_block(BlockRegs<DecodeCfg<D, G, BF16>>& 
       for (int w = 0; w < C::VW; ++w)
         cur.v[r][w] = (half * C::ROWS + r < valid) ? cur.v[r][w] : 0u;
   }
+  if (any_moved) {
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float a = alpha_lds[h];
+    for (int h = 0; h < G; ++h) {
+      const float a = alpha_lds[h];
 #pragma unroll
-    for (int jj = 0; jj < C::DPL; ++jj) st.o[h][jj] *= a;
+      for (int jj = 0; jj < C::DPL; ++jj) st.o[h][jj] *= a;
+    }
   }
   if constexpr (BF16) {
     // token pairs (2k, 2k+1) of this lane's rows
@@ -321,24 +342,24 @@ struct DecodeParams {
 
 // LDS of one workgroup: K tiles during the block loop (afterwards reused for
 // the per-wave outputs and the merge weights), P, and the merge state.
-template <int D, int G, bool BF16>
+template <int D, int G, bool BF16, int NW>
 struct DecodeSmem {
   using C = DecodeCfg<D, G, BF16>;
-  static constexpr int kTiles = kDecodeWaves * C::LDS_TILE;
-  static constexpr int kOStage = kDecodeWaves * G * D * 4;
+  static constexpr int kTiles = NW * C::LDS_TILE;
+  static constexpr int kOStage = NW * G * D * 4;
   __attribute__((aligned(16))) uint8_t k[kTiles > kOStage ? kTiles : kOStage];
-  __attribute__((aligned(16))) uint32_t p[kDecodeWaves][C::P_BYTES / 4];
-  float alpha[kDecodeWaves][G];
-  float m[kDecodeWaves][G];
-  float l[kDecodeWaves][G];
+  __attribute__((aligned(16))) uint32_t p[NW][C::P_BYTES / 4];
+  float alpha[NW][G];
+  float m[NW][G];
+  float l[NW][G];
   float M[G], W[G];
   int last;
 };
 
 // One work item: KV head g of sequence b, partition `part` (blocks
 // [part * pb, min((part + 1) * pb, nblk))).  Called by the whole workgroup.
-template <int D, int G, bool BF16>
-__device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D, G, BF16>& sm,
+template <int D, int G, bool BF16, int NW>
+__device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D, G, BF16, NW>& sm,
                                             int b, int g, int part, int L, int nblk, int pb,
                                             int nparts) {
   using C = DecodeCfg<D, G, BF16>;
@@ -387,37 +408,49 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
   uint8_t* kt_lds = sm.k + wave * C::LDS_TILE;
   uint32_t* p_lds = sm.p[wave];
 
-  // Block ids of this wave's blocks (lane i holds the id of block
-  // first + 4 * (chunk * 64 + i)), read per block with v_readlane.  Each wave
-  // keeps PD blocks in flight in a register ring: block k is computed while
-  // blocks k+1 .. k+PD are loading.  Loads past the wave's last block are
-  // clamped to that block (cache hits, never computed), so every iteration
-  // issues the same loads and the compiler's wait counts stay exact.
+  // Each wave keeps PD blocks in flight in a register ring: while block k is
+  // computed, blocks k+1 .. k+PD are loading.  Block ids come one group of
+  // PD ahead of the data (lane s of an id vector holds the id of the group's
+  // block s), loaded before the group's data so reading them never waits on
+  // data.  Loads past the wave's last block are clamped to that block (cache
+  // hits, never computed): every iteration issues the same loads, so the
+  // compiler's wait counts stay exact.
   constexpr int PD = C::PD;
+  // The query must have arrived before the block loop: waiting for it inside
+  // the loop would also wait for the prefetched blocks issued after it.
+#pragma unroll
+  for (int hh = 0; hh < C::HPL; ++hh)
+#pragma unroll
+    for (int c = 0; c < C::CPL; ++c) asm volatile("" ::"v"(q[hh][c]));
   const int first = blk_lo + wave;
-  const int nmine = blk_hi > first ? (blk_hi - first + kDecodeWaves - 1) / kDecodeWaves : 0;
+  const int nmine = blk_hi > first ? (blk_hi - first + NW - 1) / NW : 0;
   if (nmine > 0) {
-    int ids = load_ids(bt_row, first, nmine, 0, lane, num_blocks);
+    auto id_group = [&](int base) -> int {
+      const int k = min(base + (lane & (PD - 1)), nmine - 1);
+      int id = bt_row[first + k * NW];
+      return (id < 0 || id >= num_blocks) ? 0 : id;  // out-of-range ids read block 0
+    };
+    const int ids_cur = id_group(0);
+    int ids_next = id_group(PD);  // issued before the data, as in the loop
     BlockRegs<C> buf[PD];
 #pragma unroll
     for (int s = 0; s < PD; ++s)
-      buf[s] = load_block_regs<C>(cache, __builtin_amdgcn_readlane(ids, min(s, nmine - 1)),
-                                  block_bytes, g, num_kv_heads, tile_bytes, lane, half, col);
+      buf[s] = load_block_regs<C>(cache, __builtin_amdgcn_readlane(ids_cur, s), block_bytes, g,
+                                  num_kv_heads, tile_bytes, lane, half, col);
     for (int k0 = 0; k0 < nmine; k0 += PD) {
-      const int kl = k0 + PD;  // first block loaded in this group
-      if (kl < nmine && (kl & (kWave - 1)) == 0) ids = load_ids(bt_row, first, nmine, kl >> 6, lane, num_blocks);
+      const int ids_after = id_group(k0 + 2 * PD);
 #pragma unroll
       for (int s = 0; s < PD; ++s) {
         const int k = k0 + s;
         if (k < nmine) {
-          const int j = first + k * kDecodeWaves;
+          const int j = first + k * NW;
           process_block<D, G, BF16>(buf[s], min(16, L - j * 16), q, st, kt_lds, p_lds,
                                     sm.alpha[wave], scale_log2, dp, tq, hg, half);
         }
-        const int kn = min(kl + s, nmine - 1);
-        buf[s] = load_block_regs<C>(cache, __builtin_amdgcn_readlane(ids, kn & (kWave - 1)),
-                                    block_bytes, g, num_kv_heads, tile_bytes, lane, half, col);
+        buf[s] = load_block_regs<C>(cache, __builtin_amdgcn_readlane(ids_next, s), block_bytes, g,
+                                    num_kv_heads, tile_bytes, lane, half, col);
       }
+      ids_next = ids_after;
     }
   }
 
@@ -453,16 +486,16 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
 
   const bool single = nparts <= 1;
   const int tid = threadIdx.x;
-  for (int e = tid; e < G * D; e += kDecodeWaves * kWave) {
+  for (int e = tid; e < G * D; e += NW * kWave) {
     const int h = e / D, d = e % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, sm.m[w][h]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.m[w][h]);
     float lsum = 0.f, acc = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kDecodeWaves; ++w) {
-        const float wt = exp2f(sm.m[w][h] - M);  // 0 for a wave with no tokens
+      for (int w = 0; w < NW; ++w) {
+        const float wt = __builtin_amdgcn_exp2f(sm.m[w][h] - M);  // 0 for a wave with no tokens
         lsum += wt * sm.l[w][h];
         acc += wt * o_lds[(w * G + h) * D + d];
       }
@@ -501,7 +534,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
     __hip_atomic_store(&ws_count[b * num_kv_heads + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // per head: M = max_p m_p and W = sum_p 2^(m_p - M) l_p (one wave per head)
-    for (int h = wave; h < G; h += kDecodeWaves) {
+    for (int h = wave; h < G; h += NW) {
     const int64_t row = int64_t(b) * H_q + g * G + h;
     const float* m = ws_m + row * max_parts;
     const float* l = ws_l + row * max_parts;
@@ -516,7 +549,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
   }
   __syncthreads();
   // O = sum_p w_p o_p / W, the weights staged through LDS in chunks
-  constexpr int EPT = (G * D + kDecodeWaves * kWave - 1) / (kDecodeWaves * kWave);
+  constexpr int EPT = (G * D + NW * kWave - 1) / (NW * kWave);
   constexpr int WCAP = int(sizeof(sm.k) / sizeof(float)) / G;  // weights per head per chunk
   float* wbuf = reinterpret_cast<float*>(sm.k);
   float acc[EPT];
@@ -524,7 +557,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
   for (int k = 0; k < EPT; ++k) acc[k] = 0.f;
   for (int p0 = 0; p0 < nparts; p0 += WCAP) {
     const int pc = min(WCAP, nparts - p0);
-    for (int idx = tid; idx < G * pc; idx += kDecodeWaves * kWave) {
+    for (int idx = tid; idx < G * pc; idx += NW * kWave) {
       const int h = idx / pc, pp = idx % pc;
       const int64_t prow = (int64_t(b) * H_q + g * G + h) * max_parts + p0 + pp;
       wbuf[h * WCAP + pp] = exp2f(coherent_load(ws_m + prow) - sm.M[h]) * coherent_load(ws_l + prow);
@@ -532,7 +565,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {
-      const int e = tid + k * kDecodeWaves * kWave;
+      const int e = tid + k * NW * kWave;
       if (e < G * D) {
         const int h = e / D, d = e % D;
         const float* op = ws_o + ((int64_t(b) * H_q + g * G + h) * max_parts + p0) * D + d;
@@ -546,7 +579,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
   }
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
-    const int e = tid + k * kDecodeWaves * kWave;
+    const int e = tid + k * NW * kWave;
     if (e < G * D) {
       const int h = e / D, d = e % D;
       const int64_t row = int64_t(b) * H_q + g * G + h;
@@ -563,9 +596,9 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
 // the virtual grid (part, b, g) walked by a grid of a few times the resident
 // workgroups, and items past a sequence's last partition are skipped in the
 // loop instead of being dispatched as empty workgroups.
-template <int D, int G, bool BF16>
-__global__ __launch_bounds__(kDecodeWaves * kWave) void decode_kernel(const DecodeParams a) {
-  __shared__ DecodeSmem<D, G, BF16> sm;
+template <int D, int G, bool BF16, int NW>
+__global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams a) {
+  __shared__ DecodeSmem<D, G, BF16, NW> sm;
   for (int t = blockIdx.x; t < a.num_items; t += gridDim.x) {
     const int g = t % a.num_kv_heads;
     int b, part;
@@ -585,7 +618,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_kernel(const Deco
     const int pb = a.part_blocks > 0 ? a.part_blocks : (nblk > 0 ? nblk : 1);
     const int nparts = (nblk + pb - 1) / pb;
     if (part > 0 && part >= nparts) continue;
-    decode_item<D, G, BF16>(a, sm, b, g, part, L, nblk, pb, nparts);
+    decode_item<D, G, BF16, NW>(a, sm, b, g, part, L, nblk, pb, nparts);
     __syncthreads();  // LDS is reused by the next item
   }
 }
@@ -601,7 +634,7 @@ __global__ void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
 // ---------------------------------------------------------------------------
 // Workgroups that fit on the device at once for a kernel (cached per device
 // and kernel): the persistent grid never exceeds this.
-template <class K>
+template <int NW, class K>
 static int resident_workgroups(K kernel) {
   constexpr int kMaxDev = 64;
   static int cached[kMaxDev] = {0};
@@ -611,7 +644,7 @@ static int resident_workgroups(K kernel) {
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kDecodeWaves * kWave, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, NW * kWave, 0) !=
           hipSuccess || per_cu <= 0)
     per_cu = 1;
   cached[dev] = cus * per_cu;
@@ -620,15 +653,39 @@ static int resident_workgroups(K kernel) {
   return cached[dev];
 }
 
-template <int D, int G, bool BF16>
-static void launch_decode(const DecodeParams& a, hipStream_t s) {
-  auto k = decode_kernel<D, G, BF16>;
+template <int D, int G, bool BF16, int NW>
+static void launch_decode_nw(const DecodeParams& a, hipStream_t s) {
+  auto k = decode_kernel<D, G, BF16, NW>;
   // With a plan every item is real: one workgroup each, so the hardware
   // dispatcher balances them and overlaps one item's merge with another's
   // loads.  Without one, a persistent grid skips the empty virtual items.
   const int grid = a.plan ? a.num_items
-                          : std::max(1, std::min(a.num_items, 4 * resident_workgroups(k)));
-  hipLaunchKernelGGL(k, dim3(grid), dim3(kDecodeWaves * kWave), 0, s, a);
+                          : std::max(1, std::min(a.num_items, 4 * resident_workgroups<NW>(k)));
+  hipLaunchKernelGGL(k, dim3(grid), dim3(NW * kWave), 0, s, a);
+}
+
+// Fewer items than two per compute unit: 8 waves share each item, so the
+// blocks of one (sequence, head) spread over more SIMD slots.
+static int device_cus() {
+  constexpr int kMaxDev = 64;
+  static int cached[kMaxDev] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) dev = 0;
+  if (cached[dev] > 0) return cached[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  cached[dev] = cus;
+  return cus;
+}
+
+template <int D, int G, bool BF16>
+static void launch_decode(const DecodeParams& a, hipStream_t s) {
+  if (a.num_items < 2 * device_cus())
+    launch_decode_nw<D, G, BF16, 8>(a, s);
+  else
+    launch_decode_nw<D, G, BF16, 4>(a, s);
 }
 
 template <int D, bool BF16>
