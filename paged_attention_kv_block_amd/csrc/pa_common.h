@@ -66,6 +66,30 @@ __device__ __forceinline__ float partner(float x) {
   else return __shfl_xor(x, 1 << BIT, kWave);
 }
 
+// Value of lane (this lane xor 2^BIT), for any x.  Bits 2 and 3 compose two
+// DPP moves: half_mirror is xor 7 and mirror is xor 15 within their rows.
+constexpr int kQuadRev = 0x1B;        // quad_perm [3,2,1,0] = xor 3
+template <int BIT>
+__device__ __forceinline__ float xor_partner(float x) {
+  if constexpr (BIT == 0) return dpp_f<kQuadXor1>(x);
+  else if constexpr (BIT == 1) return dpp_f<kQuadXor2>(x);
+  else if constexpr (BIT == 2) return dpp_f<kQuadRev>(dpp_f<kRowHalfMirror>(x));
+  else if constexpr (BIT == 3) return dpp_f<kRowHalfMirror>(dpp_f<kRowMirror>(x));
+  else return __shfl_xor(x, 1 << BIT, kWave);
+}
+
+// Max over lane bits [LO, HI) for values that may differ across the bits
+// below LO.
+template <int LO, int HI>
+__device__ __forceinline__ float allreduce_max_xor(float x) {
+  if constexpr (LO < HI) {
+    x = fmaxf(x, xor_partner<LO>(x));
+    return allreduce_max_xor<LO + 1, HI>(x);
+  } else {
+    return x;
+  }
+}
+
 template <int LO, int HI>
 __device__ __forceinline__ float allreduce_max(float x) {
   if constexpr (LO < HI) {

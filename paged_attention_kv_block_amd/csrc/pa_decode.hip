@@ -72,9 +72,14 @@ struct DecodeCfg {
   static constexpr int HALVES = (BF16 && D == 64) ? 2 : 1;
   static constexpr int ROWS = 16 / HALVES;         // V rows per lane
   static constexpr int VW = BF16 ? 1 : DPL;        // V dwords per row per lane
+  static constexpr int PAIRS = ROWS / 2;           // bf16 token pairs per lane
+  static constexpr bool IN_LANE_PAIRS = NPASS >= 2;
+  static constexpr bool BF16_ = BF16;
   static constexpr int P_BYTES = BF16 ? G * 8 * 4 : G * 16 * 4;
   // blocks in flight per wave (register ring); divides 64
   static constexpr int PD = 2;
+  static_assert(DP >= HPL, "every head of a lane group needs a lane to follow it");
+  static_assert(!IN_LANE_PAIRS || TPP * NPASS == 16, "in-lane pairs are (k, k + 8)");
   static_assert(CPR % DP == 0 && TPP >= 1 && 16 % TPP == 0, "bad decode lane split");
   static_assert(HG * DP * TPP == kWave, "lane split must cover the wave");
   static_assert(TILE_VEC % kWave == 0, "tile must be a whole number of wave loads");
@@ -115,8 +120,24 @@ __device__ __forceinline__ float chunk_dot(const u32x4& q, const u32x4& k, float
   return acc;
 }
 
+// bf16 P.V pairs tokens for v_dot2: with two or more QK passes a lane owns
+// rows r and r + 8 (passes ps and ps + NPASS/2), so pair k is (k, k + 8)
+// and is packed without leaving the lane; with one pass pair k is
+// (2k, 2k + 1) and the second token comes from the neighbour lane.
+template <class C>
+__device__ __forceinline__ constexpr int pair_row(int k, int which) {
+  return C::IN_LANE_PAIRS ? k + 8 * which : 2 * k + which;
+}
+
+// Row of the V tile held in slot rr of a lane's V registers.
+template <class C>
+__device__ __forceinline__ int v_row(int rr, int half) {
+  if constexpr (C::BF16_) return pair_row<C>(half * C::PAIRS + rr / 2, rr % 2);
+  else return rr;
+}
+
 // Registers of one block: the K tile as coalesced 16-byte vectors (lane i
-// holds vectors i, i+64, ...) and this lane's V column(s) of each row.
+// holds vectors i, i+64, ...) and this lane's V column(s) of its rows.
 template <class C>
 struct BlockRegs {
   u32x4 k[C::LOADS];
@@ -137,23 +158,26 @@ __device__ __forceinline__ BlockRegs<C> load_block_regs(const uint8_t* __restric
   const uint32_t* vt = reinterpret_cast<const uint32_t*>(vbase);
 #pragma unroll
   for (int rr = 0; rr < C::ROWS; ++rr) {
-    const int row = half * C::ROWS + rr;
+    const int row = v_row<C>(rr, half);
 #pragma unroll
     for (int w = 0; w < C::VW; ++w) r.v[rr][w] = vt[row * (C::RB / 4) + col * C::VW + w];
   }
   return r;
 }
 
-// Online-softmax state of one wave: running max and denominator share per
-// lane head (log2 domain), and the unnormalised output columns of this lane.
+// Online-softmax state of one wave.  Each lane follows one query head of
+// its head group for the softmax (lanes dp and dp + HPL are replicas): the
+// running reference m_run and the threshold m_run + slack (log2 domain),
+// and its share of the denominator.  The unnormalised output columns cover
+// all G heads.
 template <class C, int G>
 struct DecodeState {
-  float m_run[C::HPL];
-  float l_part[C::HPL];
+  float m_run, m_thr, l;
   float o[G][C::DPL];
   __device__ __forceinline__ void init() {
-#pragma unroll
-    for (int hh = 0; hh < C::HPL; ++hh) { m_run[hh] = -INFINITY; l_part[hh] = 0.f; }
+    m_run = -INFINITY;
+    m_thr = -INFINITY;
+    l = 0.f;
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -161,16 +185,26 @@ struct DecodeState {
   }
 };
 
+// Lane roles inside a wave.
+struct LaneRoles {
+  int dp;    // d-part of the QK split
+  int tq;    // token within a QK pass
+  int hg;    // head group
+  int head;  // softmax head of this lane within the KV head's G query heads
+  int half;  // P.V: which half of the tile's rows (bf16 D = 64)
+  int col;   // P.V: dword column within a row
+};
+
 // One 16-token block: K tile through LDS, scores, online softmax, P to LDS,
-// P.V into the lane's output columns.  `valid` tokens of the block are inside
-// the sequence (>= 1).
-template <int D, int G, bool BF16>
+// P.V into the lane's output columns.  TAIL: only the first `valid` tokens of
+// the block are inside the sequence (1 <= valid < 16).
+template <int D, int G, bool BF16, bool TAIL>
 __device__ __forceinline__ void process_block(BlockRegs<DecodeCfg<D, G, BF16>>& cur, int valid,
                                             const u32x4 (&q)[DecodeCfg<D, G, BF16>::HPL]
                                                             [DecodeCfg<D, G, BF16>::CPL],
                                             DecodeState<DecodeCfg<D, G, BF16>, G>& st,
                                             uint8_t* kt_lds, uint32_t* p_lds, float* alpha_lds,
-                                            float scale_log2, int dp, int tq, int hg, int half) {
+                                            float scale_log2, const LaneRoles& r) {
   using C = DecodeCfg<D, G, BF16>;
   const int lane = threadIdx.x & (kWave - 1);
 
@@ -184,103 +218,96 @@ __device__ __forceinline__ void process_block(BlockRegs<DecodeCfg<D, G, BF16>>& 
   }
   wave_lds_sync();
 
-  // ---- scores for this lane's token(s) and heads
-  float s[C::NPASS][C::HPL];
+  // ---- scores (log2 domain) of this lane's head for its token of each pass
+  float x[C::NPASS];
 #pragma unroll
   for (int ps = 0; ps < C::NPASS; ++ps) {
-    const int row = ps * C::TPP + tq;
-    const u32x4* kr = reinterpret_cast<const u32x4*>(kt_lds + row * C::LDS_ROW) + dp * C::CPL;
+    const int row = ps * C::TPP + r.tq;
+    const u32x4* kr = reinterpret_cast<const u32x4*>(kt_lds + row * C::LDS_ROW) + r.dp * C::CPL;
+    float s[C::HPL];
 #pragma unroll
-    for (int hh = 0; hh < C::HPL; ++hh) s[ps][hh] = 0.f;
+    for (int hh = 0; hh < C::HPL; ++hh) s[hh] = 0.f;
 #pragma unroll
     for (int c = 0; c < C::CPL; ++c) {
       const u32x4 kv = kr[c];
 #pragma unroll
-      for (int hh = 0; hh < C::HPL; ++hh) s[ps][hh] = chunk_dot<BF16>(q[hh][c], kv, s[ps][hh]);
+      for (int hh = 0; hh < C::HPL; ++hh) s[hh] = chunk_dot<BF16>(q[hh][c], kv, s[hh]);
     }
+    float v = allreduce_sum<0, ilog2(C::DP)>(s[0]);
 #pragma unroll
-    for (int hh = 0; hh < C::HPL; ++hh) {
-      float x = allreduce_sum<0, ilog2(C::DP)>(s[ps][hh]) * scale_log2;
-      if (valid < 16) x = (row < valid) ? x : -INFINITY;  // tail block only
-      s[ps][hh] = x;
+    for (int hh = 1; hh < C::HPL; ++hh) {
+      const float w = allreduce_sum<0, ilog2(C::DP)>(s[hh]);
+      v = (r.dp % C::HPL) == hh ? w : v;
     }
+    v *= scale_log2;
+    if constexpr (TAIL) v = row < valid ? v : -INFINITY;
+    x[ps] = v;
   }
 
-  // ---- online softmax per head with a lazily moved reference: the
-  // reference m_run moves only when the block's max exceeds it by more than
-  // kRescaleSlack (log2 units), so P = 2^(s - m_run) <= 2^kRescaleSlack and
-  // most blocks need no rescale of the accumulated output.
-  float alpha[C::HPL];
-  bool moved = false;
+  // ---- online softmax with a lazily moved reference: m_run moves only
+  // when the block's max exceeds it by more than kRescaleSlack (log2 units),
+  // so P = 2^(s - m_run) <= 2^kRescaleSlack and most blocks neither reduce
+  // their max across lanes nor rescale the accumulated output.
+  float t = x[0];
 #pragma unroll
-  for (int hh = 0; hh < C::HPL; ++hh) {
-    float mb = s[0][hh];
-#pragma unroll
-    for (int ps = 1; ps < C::NPASS; ++ps) mb = fmaxf(mb, s[ps][hh]);
-    mb = allreduce_max<ilog2(C::DP), ilog2(C::DP * C::TPP)>(mb);
+  for (int ps = 1; ps < C::NPASS; ++ps) t = fmaxf(t, x[ps]);
+  const bool rescale = __builtin_amdgcn_ballot_w64(t > st.m_thr) != 0;  // wave-uniform
+  if (rescale) {
+    // lanes of other d-parts follow other heads: exact xor partners
+    const float mb = allreduce_max_xor<ilog2(C::DP), ilog2(C::DP * C::TPP)>(t);
     // mb is finite: token 0 of the block is inside the sequence
-    const bool grow = mb > st.m_run[hh] + kRescaleSlack;
-    alpha[hh] = grow ? __builtin_amdgcn_exp2f(st.m_run[hh] - mb) : 1.f;
-    st.m_run[hh] = grow ? mb : st.m_run[hh];
-    st.l_part[hh] *= alpha[hh];
-    moved |= grow;
+    const bool grow = mb > st.m_thr;
+    const float alpha = grow ? __builtin_amdgcn_exp2f(st.m_run - mb) : 1.f;
+    st.m_run = grow ? mb : st.m_run;
+    st.m_thr = st.m_run + kRescaleSlack;
+    st.l *= alpha;
+    if (r.tq == 0 && r.dp < C::HPL) alpha_lds[r.head] = alpha;
   }
-  const bool any_moved = __builtin_amdgcn_ballot_w64(moved) != 0;  // wave-uniform
 
-  // ---- P to LDS (bf16 token pairs [head][pair], or fp32 [head][token])
+  // ---- P to LDS: bf16 token pairs [head][pair], or fp32 [head][token].
+  // Replica lanes store the same value to the same word.
+  if constexpr (BF16) {
+    if constexpr (C::IN_LANE_PAIRS) {
 #pragma unroll
-  for (int ps = 0; ps < C::NPASS; ++ps) {
-    const int row = ps * C::TPP + tq;
-    float p[C::HPL];
-#pragma unroll
-    for (int hh = 0; hh < C::HPL; ++hh) p[hh] = __builtin_amdgcn_exp2f(s[ps][hh] - st.m_run[hh]);
-    if constexpr (BF16) {
-      if constexpr (C::HPL % 2 == 0) {
-        // two heads per conversion: (head hh, head hh+1) of this token; the
-        // neighbour lane (token + 1) supplies the second token of each pair
-#pragma unroll
-        for (int hh = 0; hh < C::HPL; hh += 2) {
-          const uint32_t pk = pack_bf16x2(p[hh], p[hh + 1]);
-          if (dp == 0) {
-            st.l_part[hh] += bf16_lo(pk);
-            st.l_part[hh + 1] += bf16_hi(pk);
-          }
-          const uint32_t nb = dpp_u<0x100 + C::DP>(pk);  // row_shl: lane + DP = token + 1
-          if (dp == 0 && (row & 1) == 0) {
-            const int h = hg * C::HPL + hh;
-            p_lds[h * 8 + (row >> 1)] = __builtin_amdgcn_perm(nb, pk, 0x05040100u);
-            p_lds[(h + 1) * 8 + (row >> 1)] = __builtin_amdgcn_perm(nb, pk, 0x07060302u);
-          }
-        }
-      } else {
-        const float pn = dpp_f<0x100 + C::DP>(p[0]);   // token + 1
-        const uint32_t pk = pack_bf16x2(p[0], pn);       // (token, token + 1)
-        if (dp == 0) st.l_part[0] += bf16_lo(pk);
-        if (dp == 0 && (row & 1) == 0) p_lds[hg * 8 + (row >> 1)] = pk;
+      for (int ps = 0; ps < C::NPASS / 2; ++ps) {
+        const float p0 = __builtin_amdgcn_exp2f(x[ps] - st.m_run);
+        const float p1 = __builtin_amdgcn_exp2f(x[ps + C::NPASS / 2] - st.m_run);
+        const uint32_t pk = pack_bf16x2(p0, p1);      // tokens (k, k + 8)
+        st.l = dot2_bf16(pk, 0x3F803F80u, st.l);      // + both rounded values
+        p_lds[r.head * 8 + ps * C::TPP + r.tq] = pk;  // pair k = row of pass ps
       }
     } else {
-#pragma unroll
-      for (int hh = 0; hh < C::HPL; ++hh) {
-        st.l_part[hh] += (dp == 0) ? p[hh] : 0.f;
-        if (dp == 0) reinterpret_cast<float*>(p_lds)[(hg * C::HPL + hh) * 16 + row] = p[hh];
-      }
+      const float p = __builtin_amdgcn_exp2f(x[0] - st.m_run);
+      const float pn = dpp_f<0x100 + C::DP>(p);  // row_shl: lane + DP = token + 1
+      const uint32_t pk = pack_bf16x2(p, pn);    // tokens (2k, 2k + 1) on even lanes
+      // (1.0, 0.0) as a bf16 pair, kept in a register: the assembler would
+      // encode the literal as the inline constant 1.0, which the hardware
+      // does not read as this pair
+      uint32_t lo_one = 0x00003F80u;
+      asm("" : "+v"(lo_one));
+      st.l = dot2_bf16(pk, lo_one, st.l);  // + this lane's rounded value
+      if ((r.tq & 1) == 0) p_lds[r.head * 8 + (r.tq >> 1)] = pk;
     }
-  }
-  if (any_moved && tq == 0 && dp == 0) {
+  } else {
+    float* pf = reinterpret_cast<float*>(p_lds);
 #pragma unroll
-    for (int hh = 0; hh < C::HPL; ++hh) alpha_lds[hg * C::HPL + hh] = alpha[hh];
+    for (int ps = 0; ps < C::NPASS; ++ps) {
+      const float p = __builtin_amdgcn_exp2f(x[ps] - st.m_run);
+      st.l += p;
+      pf[r.head * 16 + ps * C::TPP + r.tq] = p;
+    }
   }
   wave_lds_sync();
 
   // ---- rescale and accumulate P.V
-  if (valid < 16) {  // tail block: rows past the sequence may hold anything
+  if constexpr (TAIL) {  // rows past the sequence may hold anything
 #pragma unroll
-    for (int r = 0; r < C::ROWS; ++r)
+    for (int rr = 0; rr < C::ROWS; ++rr)
 #pragma unroll
       for (int w = 0; w < C::VW; ++w)
-        cur.v[r][w] = (half * C::ROWS + r < valid) ? cur.v[r][w] : 0u;
+        cur.v[rr][w] = v_row<C>(rr, r.half) < valid ? cur.v[rr][w] : 0u;
   }
-  if (any_moved) {
+  if (rescale) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float a = alpha_lds[h];
@@ -289,14 +316,13 @@ __device__ __forceinline__ void process_block(BlockRegs<DecodeCfg<D, G, BF16>>& 
     }
   }
   if constexpr (BF16) {
-    // token pairs (2k, 2k+1) of this lane's rows
-    constexpr int PAIRS = C::ROWS / 2;
+    constexpr int PAIRS = C::PAIRS;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       uint32_t pw[PAIRS];
 #pragma unroll
       for (int k4 = 0; k4 < PAIRS; k4 += 4) {
-        const u32x4 t4 = *reinterpret_cast<const u32x4*>(p_lds + h * 8 + half * PAIRS + k4);
+        const u32x4 t4 = *reinterpret_cast<const u32x4*>(p_lds + h * 8 + r.half * PAIRS + k4);
         pw[k4] = t4.x; pw[k4 + 1] = t4.y; pw[k4 + 2] = t4.z; pw[k4 + 3] = t4.w;
       }
 #pragma unroll
@@ -313,10 +339,10 @@ __device__ __forceinline__ void process_block(BlockRegs<DecodeCfg<D, G, BF16>>& 
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = pf[h * 16 + r];
+      for (int rr = 0; rr < 16; ++rr) {
+        const float p = pf[h * 16 + rr];
 #pragma unroll
-        for (int w = 0; w < C::VW; ++w) st.o[h][w] = fmaf(p, __uint_as_float(cur.v[r][w]), st.o[h][w]);
+        for (int w = 0; w < C::VW; ++w) st.o[h][w] = fmaf(p, __uint_as_float(cur.v[rr][w]), st.o[h][w]);
       }
     }
   }
@@ -377,10 +403,14 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
   const int blk_hi = min(blk_lo + pb, nblk);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // QK lane roles
-  const int dp = lane % C::DP;
-  const int tq = (lane / C::DP) % C::TPP;
-  const int hg = lane / (C::DP * C::TPP);
+  LaneRoles r;
+  r.dp = lane % C::DP;
+  r.tq = (lane / C::DP) % C::TPP;
+  r.hg = lane / (C::DP * C::TPP);
+  r.head = r.hg * C::HPL + r.dp % C::HPL;
+  r.half = C::HALVES == 2 ? (lane >> 5) : 0;
+  r.col = C::HALVES == 2 ? (lane & 31) : lane;  // dword column within the row
+  const int dp = r.dp, hg = r.hg, half = r.half, col = r.col;
 
   // ---- query chunks for this lane: heads hg*HPL + hh, chunks dp*CPL + c
   u32x4 q[C::HPL][C::CPL];
@@ -400,10 +430,6 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
 
   DecodeState<C, G> st;
   st.init();
-
-  // P.V lane roles
-  const int half = C::HALVES == 2 ? (lane >> 5) : 0;
-  const int col = C::HALVES == 2 ? (lane & 31) : lane;  // dword column within the row
 
   uint8_t* kt_lds = sm.k + wave * C::LDS_TILE;
   uint32_t* p_lds = sm.p[wave];
@@ -437,34 +463,39 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
     for (int s = 0; s < PD; ++s)
       buf[s] = load_block_regs<C>(cache, __builtin_amdgcn_readlane(ids_cur, s), block_bytes, g,
                                   num_kv_heads, tile_bytes, lane, half, col);
-    for (int k0 = 0; k0 < nmine; k0 += PD) {
+    // Only the sequence's last block can be partial; it is the last block of
+    // the wave that owns it and is processed after the loop, so the loop
+    // body needs no masking.
+    const int tail_valid = L - (first + (nmine - 1) * NW) * 16;
+    const int nfull = tail_valid < 16 ? nmine - 1 : nmine;
+    for (int k0 = 0; k0 < nfull; k0 += PD) {
       const int ids_after = id_group(k0 + 2 * PD);
 #pragma unroll
       for (int s = 0; s < PD; ++s) {
-        const int k = k0 + s;
-        if (k < nmine) {
-          const int j = first + k * NW;
-          process_block<D, G, BF16>(buf[s], min(16, L - j * 16), q, st, kt_lds, p_lds,
-                                    sm.alpha[wave], scale_log2, dp, tq, hg, half);
-        }
+        if (k0 + s < nfull)
+          process_block<D, G, BF16, false>(buf[s], 16, q, st, kt_lds, p_lds, sm.alpha[wave],
+                                           scale_log2, r);
         buf[s] = load_block_regs<C>(cache, __builtin_amdgcn_readlane(ids_next, s), block_bytes, g,
                                     num_kv_heads, tile_bytes, lane, half, col);
       }
       ids_next = ids_after;
     }
+    // Loads past the last block were clamped to it, so buf[0] now holds it.
+    if (nfull < nmine)
+      process_block<D, G, BF16, true>(buf[0], tail_valid, q, st, kt_lds, p_lds, sm.alpha[wave],
+                                      scale_log2, r);
   }
 
-  // ---- merge: this wave's denominator, then the 4 waves of the workgroup
-#pragma unroll
-  for (int hh = 0; hh < C::HPL; ++hh) {
-    // sum over token lanes of the row (d-part replicas contributed 0)
-    float lsum = st.l_part[hh];
+  // ---- merge: this wave's denominator, then the waves of the workgroup
+  {
+    // sum over the token lanes of this lane's head
+    float lsum = st.l;
 #pragma unroll
     for (int bit = ilog2(C::DP); bit < ilog2(C::DP * C::TPP); ++bit)
       lsum += __shfl_xor(lsum, 1 << bit, kWave);
-    if (tq == 0 && dp == 0) {
-      sm.m[wave][hg * C::HPL + hh] = st.m_run[hh];
-      sm.l[wave][hg * C::HPL + hh] = lsum;
+    if (r.tq == 0 && dp < C::HPL) {
+      sm.m[wave][r.head] = st.m_run;
+      sm.l[wave][r.head] = lsum;
     }
   }
   if constexpr (C::HALVES == 2) {
@@ -596,8 +627,16 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
 // the virtual grid (part, b, g) walked by a grid of a few times the resident
 // workgroups, and items past a sequence's last partition are skipped in the
 // loop instead of being dispatched as empty workgroups.
+// bf16 variants are held to 168 VGPRs (three waves per SIMD) so that
+// several workgroups share a compute unit when there are many items; the
+// register demand of fp32 and of bf16 G = 16 would spill there.
+template <int D, int G, bool BF16>
+constexpr int decode_min_waves() { return BF16 && !(D == 64 && G == 16) ? 3 : 1; }
+
 template <int D, int G, bool BF16, int NW>
-__global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams a) {
+__global__ __launch_bounds__(NW * kWave)
+__attribute__((amdgpu_waves_per_eu(decode_min_waves<D, G, BF16>())))
+void decode_kernel(const DecodeParams a) {
   __shared__ DecodeSmem<D, G, BF16, NW> sm;
   for (int t = blockIdx.x; t < a.num_items; t += gridDim.x) {
     const int g = t % a.num_kv_heads;
