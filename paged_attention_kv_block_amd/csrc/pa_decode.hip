@@ -76,9 +76,15 @@ struct DecodeCfg {
   static constexpr bool IN_LANE_PAIRS = NPASS >= 2;
   static constexpr bool BF16_ = BF16;
   static constexpr int P_BYTES = BF16 ? G * 8 * 4 : G * 16 * 4;
+  // LDS reads issued together: K chunks (16 bytes each) and heads of P words
+  static constexpr int KGRP_MAX = D == 64 ? 8 : (G >= 8 ? 2 : 4);
+  static constexpr int KGRP = NPASS * CPL < KGRP_MAX ? NPASS * CPL : KGRP_MAX;
+  static constexpr int PGRP_MAX = (D == 64 ? 32 : 16) / (PAIRS > 0 ? PAIRS : 1);
+  static constexpr int PGRP = G < PGRP_MAX ? G : PGRP_MAX;
   // blocks in flight per wave (register ring); divides 64
   static constexpr int PD = 2;
   static_assert(DP >= HPL, "every head of a lane group needs a lane to follow it");
+  static_assert((NPASS * CPL) % KGRP == 0 && G % PGRP == 0, "read groups must tile");
   static_assert(!IN_LANE_PAIRS || TPP * NPASS == 16, "in-lane pairs are (k, k + 8)");
   static_assert(CPR % DP == 0 && TPP >= 1 && 16 % TPP == 0, "bad decode lane split");
   static_assert(HG * DP * TPP == kWave, "lane split must cover the wave");
@@ -219,20 +225,34 @@ __device__ __forceinline__ void process_block(BlockRegs<DecodeCfg<D, G, BF16>>& 
   wave_lds_sync();
 
   // ---- scores (log2 domain) of this lane's head for its token of each pass
+  // K chunks are read from LDS in groups of KGRP (registers permitting) so
+  // that the reads of a group overlap one another
+  float sacc[C::NPASS][C::HPL];
+#pragma unroll
+  for (int ps = 0; ps < C::NPASS; ++ps)
+#pragma unroll
+    for (int hh = 0; hh < C::HPL; ++hh) sacc[ps][hh] = 0.f;
+  constexpr int NCH = C::NPASS * C::CPL;
+#pragma unroll
+  for (int base = 0; base < NCH; base += C::KGRP) {
+    u32x4 kv[C::KGRP];
+#pragma unroll
+    for (int i = 0; i < C::KGRP; ++i) {
+      const int ps = (base + i) / C::CPL, c = (base + i) % C::CPL;
+      kv[i] = reinterpret_cast<const u32x4*>(kt_lds + (ps * C::TPP + r.tq) * C::LDS_ROW)[r.dp * C::CPL + c];
+    }
+#pragma unroll
+    for (int i = 0; i < C::KGRP; ++i) {
+      const int ps = (base + i) / C::CPL, c = (base + i) % C::CPL;
+#pragma unroll
+      for (int hh = 0; hh < C::HPL; ++hh) sacc[ps][hh] = chunk_dot<BF16>(q[hh][c], kv[i], sacc[ps][hh]);
+    }
+  }
   float x[C::NPASS];
 #pragma unroll
   for (int ps = 0; ps < C::NPASS; ++ps) {
     const int row = ps * C::TPP + r.tq;
-    const u32x4* kr = reinterpret_cast<const u32x4*>(kt_lds + row * C::LDS_ROW) + r.dp * C::CPL;
-    float s[C::HPL];
-#pragma unroll
-    for (int hh = 0; hh < C::HPL; ++hh) s[hh] = 0.f;
-#pragma unroll
-    for (int c = 0; c < C::CPL; ++c) {
-      const u32x4 kv = kr[c];
-#pragma unroll
-      for (int hh = 0; hh < C::HPL; ++hh) s[hh] = chunk_dot<BF16>(q[hh][c], kv, s[hh]);
-    }
+    const float (&s)[C::HPL] = sacc[ps];
     float v = allreduce_sum<0, ilog2(C::DP)>(s[0]);
 #pragma unroll
     for (int hh = 1; hh < C::HPL; ++hh) {
@@ -317,21 +337,31 @@ __device__ __forceinline__ void process_block(BlockRegs<DecodeCfg<D, G, BF16>>& 
   }
   if constexpr (BF16) {
     constexpr int PAIRS = C::PAIRS;
+    // P words are read in groups of PGRP heads, each group's reads issued
+    // together
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      uint32_t pw[PAIRS];
+    for (int h0 = 0; h0 < G; h0 += C::PGRP) {
+      uint32_t pw[C::PGRP][PAIRS];
 #pragma unroll
-      for (int k4 = 0; k4 < PAIRS; k4 += 4) {
-        const u32x4 t4 = *reinterpret_cast<const u32x4*>(p_lds + h * 8 + r.half * PAIRS + k4);
-        pw[k4] = t4.x; pw[k4 + 1] = t4.y; pw[k4 + 2] = t4.z; pw[k4 + 3] = t4.w;
-      }
+      for (int hh = 0; hh < C::PGRP; ++hh)
 #pragma unroll
-      for (int k = 0; k < PAIRS; ++k) {
-        const uint32_t v0 = cur.v[2 * k][0], v1 = cur.v[2 * k + 1][0];
-        const uint32_t xlo = __builtin_amdgcn_perm(v1, v0, 0x05040100u);  // (v0.lo, v1.lo)
-        const uint32_t xhi = __builtin_amdgcn_perm(v1, v0, 0x07060302u);  // (v0.hi, v1.hi)
-        st.o[h][0] = dot2_bf16(xlo, pw[k], st.o[h][0]);
-        st.o[h][1] = dot2_bf16(xhi, pw[k], st.o[h][1]);
+        for (int k4 = 0; k4 < PAIRS; k4 += 4) {
+          const u32x4 t4 =
+              *reinterpret_cast<const u32x4*>(p_lds + (h0 + hh) * 8 + r.half * PAIRS + k4);
+          pw[hh][k4] = t4.x; pw[hh][k4 + 1] = t4.y;
+          pw[hh][k4 + 2] = t4.z; pw[hh][k4 + 3] = t4.w;
+        }
+#pragma unroll
+      for (int hh = 0; hh < C::PGRP; ++hh) {
+        const int h = h0 + hh;
+#pragma unroll
+        for (int k = 0; k < PAIRS; ++k) {
+          const uint32_t v0 = cur.v[2 * k][0], v1 = cur.v[2 * k + 1][0];
+          const uint32_t xlo = __builtin_amdgcn_perm(v1, v0, 0x05040100u);  // (v0.lo, v1.lo)
+          const uint32_t xhi = __builtin_amdgcn_perm(v1, v0, 0x07060302u);  // (v0.hi, v1.hi)
+          st.o[h][0] = dot2_bf16(xlo, pw[hh][k], st.o[h][0]);
+          st.o[h][1] = dot2_bf16(xhi, pw[hh][k], st.o[h][1]);
+        }
       }
     }
   } else {
@@ -627,15 +657,19 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
 // the virtual grid (part, b, g) walked by a grid of a few times the resident
 // workgroups, and items past a sequence's last partition are skipped in the
 // loop instead of being dispatched as empty workgroups.
-// bf16 variants are held to 168 VGPRs (three waves per SIMD) so that
-// several workgroups share a compute unit when there are many items; the
-// register demand of fp32 and of bf16 G = 16 would spill there.
-template <int D, int G, bool BF16>
-constexpr int decode_min_waves() { return BF16 && !(D == 64 && G == 16) ? 3 : 1; }
+// 4-wave bf16 variants are held to 168 VGPRs (three waves per SIMD, so
+// three workgroups share a compute unit when there are many items); the
+// register demand of fp32 and of bf16 G = 16 would spill there.  An 8-wave
+// workgroup holds a compute unit alone at two or three waves per SIMD, so
+// its registers are left free for loads in flight.
+template <int D, int G, bool BF16, int NW>
+constexpr int decode_min_waves() { return NW == 4 && BF16 && !(D == 64 && G == 16) ? 3 : 1; }
+template <int D, int G, bool BF16, int NW>
+constexpr int decode_max_waves() { return NW == 8 ? 2 : 8; }
 
 template <int D, int G, bool BF16, int NW>
 __global__ __launch_bounds__(NW * kWave)
-__attribute__((amdgpu_waves_per_eu(decode_min_waves<D, G, BF16>())))
+__attribute__((amdgpu_waves_per_eu(decode_min_waves<D, G, BF16, NW>(), decode_max_waves<D, G, BF16, NW>())))
 void decode_kernel(const DecodeParams a) {
   __shared__ DecodeSmem<D, G, BF16, NW> sm;
   for (int t = blockIdx.x; t < a.num_items; t += gridDim.x) {
