@@ -144,6 +144,8 @@ __device__ __forceinline__ int v_row(int rr, int half) {
 
 // Registers of one block: the K tile as coalesced 16-byte vectors (lane i
 // holds vectors i, i+64, ...) and this lane's V column(s) of its rows.
+// Each KV byte is read once per call, so the loads are non-temporal (they
+// stream past the caches instead of displacing other lines).
 template <class C>
 struct BlockRegs {
   u32x4 k[C::LOADS];
@@ -160,13 +162,14 @@ __device__ __forceinline__ BlockRegs<C> load_block_regs(const uint8_t* __restric
   BlockRegs<C> r;
   const u32x4* kt = reinterpret_cast<const u32x4*>(kbase);
 #pragma unroll
-  for (int i = 0; i < C::LOADS; ++i) r.k[i] = kt[i * kWave + lane];
+  for (int i = 0; i < C::LOADS; ++i) r.k[i] = __builtin_nontemporal_load(kt + i * kWave + lane);
   const uint32_t* vt = reinterpret_cast<const uint32_t*>(vbase);
 #pragma unroll
   for (int rr = 0; rr < C::ROWS; ++rr) {
     const int row = v_row<C>(rr, half);
 #pragma unroll
-    for (int w = 0; w < C::VW; ++w) r.v[rr][w] = vt[row * (C::RB / 4) + col * C::VW + w];
+    for (int w = 0; w < C::VW; ++w)
+      r.v[rr][w] = __builtin_nontemporal_load(vt + row * (C::RB / 4) + col * C::VW + w);
   }
   return r;
 }
