@@ -15,22 +15,27 @@
 // token positions.
 //
 // Design (gfx950, HBM-bound: 4-8 flop per byte of KV):
-//   * one workgroup of 4 waves per (partition, KV head, sequence); the G
-//     query heads of a KV head share every K/V byte loaded, so each byte of
-//     the cache is read from HBM once per step;
-//   * wave w of the workgroup takes logical blocks w, w+4, ... of its
-//     partition and keeps its own online-softmax state; the four states are
-//     merged through LDS at the end (split of the context inside the
-//     workgroup), and partitions are merged by the reduce kernel;
-//   * K tile (16 tokens x D): one coalesced global load per lane into
-//     registers, prefetched one block ahead, written to a padded LDS tile,
-//     read back as (token, head group, d-part) per lane, so q.k needs no
-//     cross-lane reduction beyond the d-parts; bf16 q.k uses v_dot2_f32_bf16;
-//   * softmax max over the 16 tokens of a block is a DPP butterfly in each
-//     16-lane row; scores are kept in the log2 domain (exp2);
-//   * P goes to LDS as packed bf16 token pairs; V is loaded straight from
-//     global memory with each lane owning one column pair, and P.V is again
-//     v_dot2_f32_bf16 over token pairs after a byte permute;
+//   * one workgroup of NW waves (8, 4 or 2, fewer when there are many work
+//     items) per work item = (partition, KV head, sequence), taken from a
+//     host-built plan; the G query heads of a KV head share every K/V byte
+//     loaded, so each byte of the cache is read from HBM once per call;
+//   * wave w of the workgroup takes logical blocks w, w+NW, ... of its
+//     partition and keeps its own online-softmax state; the states are
+//     merged through LDS at the end; with split-K the last workgroup of a
+//     (sequence, KV head) to finish merges the partitions' partials by
+//     log-sum-exp weights in the same launch;
+//   * each wave keeps two blocks in flight in registers (non-temporal
+//     loads: the cache is streamed once); the K tile (16 tokens x D) is
+//     loaded coalesced, written to a padded LDS tile and read back as
+//     (token, head group, d-part) per lane, so q.k needs a cross-lane sum
+//     over the d-parts only; bf16 q.k uses v_dot2_f32_bf16;
+//   * each lane then follows one query head for the softmax; scores are in
+//     the log2 domain and the softmax reference moves lazily (only when a
+//     block's max exceeds it by 2^8), so most blocks need no max reduction
+//     and no rescale of the accumulated output;
+//   * P goes to LDS as packed bf16 token pairs (k, k + 8) formed inside a
+//     lane; V is loaded straight from global memory with each lane owning
+//     one column pair, and P.V is again v_dot2_f32_bf16 over token pairs;
 //   * the denominator sums the same bf16-rounded P that multiplies V.
 #include <algorithm>
 #include <cstdio>
@@ -92,13 +97,25 @@ struct DecodeCfg {
   static_assert(!BF16 || D == 64 || D == 128, "bf16 head sizes 64/128");
 };
 
-// Agent-scope relaxed accesses: coherent across the L2 caches of all XCDs
-// (they bypass a possibly stale local L2 line), used for split-K partials.
+// Agent-scope relaxed stores: coherent across the L2 caches of all XCDs,
+// used for split-K partials.
 __device__ __forceinline__ void coherent_store(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float coherent_load(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over `bytes` bytes of a decode workspace (raw buffer,
+// 32-bit elements; reads past the end return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const float* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, bytes, 0x00020000);
+}
+constexpr int kSc1 = 16;  // cache policy bit sc1
+__device__ __forceinline__ float ws_load(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kSc1));
+}
+__device__ __forceinline__ f32x4 ws_load4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kSc1));
 }
 
 template <bool BF16>
@@ -597,58 +614,97 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
   if (tid == 0)  // ready for the next call
     __hip_atomic_store(&ws_count[b * num_kv_heads + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
+  // The partials of this KV head's G query-head rows, read through buffer
+  // resources with the sc1 cache policy: like agent-scope atomic loads they
+  // fetch past this XCD's L2 (which may hold stale lines from an earlier
+  // call), but as plain loads many of them can be in flight at once.
+  const int64_t row0 = int64_t(b) * H_q + int64_t(g) * G;
+  const __amdgpu_buffer_rsrc_t rm = ws_rsrc(ws_m + row0 * max_parts, G * max_parts * 4);
+  const __amdgpu_buffer_rsrc_t rl = ws_rsrc(ws_l + row0 * max_parts, G * max_parts * 4);
+  const __amdgpu_buffer_rsrc_t ro = ws_rsrc(ws_o + row0 * max_parts * D, G * max_parts * D * 4);
+
   // per head: M = max_p m_p and W = sum_p 2^(m_p - M) l_p (one wave per head)
-    for (int h = wave; h < G; h += NW) {
-    const int64_t row = int64_t(b) * H_q + g * G + h;
-    const float* m = ws_m + row * max_parts;
-    const float* l = ws_l + row * max_parts;
+  for (int h = wave; h < G; h += NW) {
     float M = -INFINITY;
-    for (int p = lane; p < nparts; p += kWave) M = fmaxf(M, coherent_load(m + p));
+    for (int p = lane; p < nparts; p += kWave) M = fmaxf(M, ws_load(rm, (h * max_parts + p) * 4));
     M = allreduce_max<0, 6>(M);
     float W = 0.f;
-    for (int p = lane; p < nparts; p += kWave)
-      W += exp2f(coherent_load(m + p) - M) * coherent_load(l + p);
+    for (int p = lane; p < nparts; p += kWave) {
+      const int off = (h * max_parts + p) * 4;
+      W += exp2f(ws_load(rm, off) - M) * ws_load(rl, off);
+    }
     W = allreduce_sum<0, 6>(W);
     if (lane == 0) { sm.M[h] = M; sm.W[h] = W; }
   }
   __syncthreads();
-  // O = sum_p w_p o_p / W, the weights staged through LDS in chunks
-  constexpr int EPT = (G * D + NW * kWave - 1) / (NW * kWave);
-  constexpr int WCAP = int(sizeof(sm.k) / sizeof(float)) / G;  // weights per head per chunk
+
+  // O = sum_p w_p o_p / W with w_p = 2^(m_p - M) l_p.  Each thread owns
+  // 16-byte quads of the output rows; when there are more threads than
+  // quads, S threads share a quad and take every S-th partition, and their
+  // sums meet in LDS.  Partials are loaded MB at a time; the weights are
+  // staged through LDS in chunks of WCAP partitions per head.
+  constexpr int NT = NW * kWave;
+  constexpr int Q = G * D / 4;
+  constexpr int S = NT > Q ? NT / Q : 1;
+  constexpr int QPT = Q > NT ? Q / NT : 1;
+  constexpr int MB = 8;
+  constexpr int WCAP = int(sizeof(sm.k) / sizeof(float)) / G;
+  static_assert(NT * 16 <= int(sizeof(sm.k)), "LDS too small for the subset sums");
   float* wbuf = reinterpret_cast<float*>(sm.k);
-  float acc[EPT];
+  const int sub = S > 1 ? tid / Q : 0;
+  f32x4 acc[QPT];
 #pragma unroll
-  for (int k = 0; k < EPT; ++k) acc[k] = 0.f;
+  for (int qi = 0; qi < QPT; ++qi) acc[qi] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int p0 = 0; p0 < nparts; p0 += WCAP) {
     const int pc = min(WCAP, nparts - p0);
-    for (int idx = tid; idx < G * pc; idx += NW * kWave) {
+    for (int idx = tid; idx < G * pc; idx += NT) {
       const int h = idx / pc, pp = idx % pc;
-      const int64_t prow = (int64_t(b) * H_q + g * G + h) * max_parts + p0 + pp;
-      wbuf[h * WCAP + pp] = exp2f(coherent_load(ws_m + prow) - sm.M[h]) * coherent_load(ws_l + prow);
+      const int off = (h * max_parts + p0 + pp) * 4;
+      wbuf[h * WCAP + pp] = exp2f(ws_load(rm, off) - sm.M[h]) * ws_load(rl, off);
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < EPT; ++k) {
-      const int e = tid + k * NW * kWave;
-      if (e < G * D) {
-        const int h = e / D, d = e % D;
-        const float* op = ws_o + ((int64_t(b) * H_q + g * G + h) * max_parts + p0) * D + d;
-        float a = acc[k];
-        for (int pp = 0; pp < pc; ++pp)
-          a = fmaf(wbuf[h * WCAP + pp], coherent_load(op + int64_t(pp) * D), a);
-        acc[k] = a;
+    for (int qi = 0; qi < QPT; ++qi) {
+      const int quad = (S > 1 ? tid % Q : tid) + qi * NT;
+      const int h = quad / (D / 4), d4 = quad % (D / 4);
+      const float* wh = wbuf + h * WCAP;
+      for (int pp = sub; pp < pc; pp += S * MB) {
+        f32x4 v[MB];
+        float w[MB];
+#pragma unroll
+        for (int j = 0; j < MB; ++j) {
+          const int p = pp + j * S;
+          const int pl = p < pc ? p : pc - 1;  // in range; weight 0 past the chunk
+          v[j] = ws_load4(ro, ((h * max_parts + p0 + pl) * D + d4 * 4) * 4);
+          w[j] = p < pc ? wh[pl] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < MB; ++j) acc[qi] += w[j] * v[j];
       }
     }
     __syncthreads();
   }
+  if constexpr (S > 1) {
+    f32x4* red = reinterpret_cast<f32x4*>(sm.k);  // [S][Q]
+    red[tid] = acc[0];
+    __syncthreads();
+    if (sub == 0) {
 #pragma unroll
-  for (int k = 0; k < EPT; ++k) {
-    const int e = tid + k * NW * kWave;
-    if (e < G * D) {
-      const int h = e / D, d = e % D;
-      const int64_t row = int64_t(b) * H_q + g * G + h;
-      store_out<BF16>(out, row * D + d, acc[k] / sm.W[h]);
-      if (lse_out && d == 0) lse_out[row] = sm.M[h] * kLn2 + logf(sm.W[h]);
+      for (int t = 1; t < S; ++t) acc[0] += red[t * Q + tid];
+    }
+  }
+  if (sub == 0) {
+#pragma unroll
+    for (int qi = 0; qi < QPT; ++qi) {
+      const int quad = tid + qi * NT;
+      const int h = quad / (D / 4), d4 = quad % (D / 4);
+      const int64_t row = row0 + h;
+      const float inv = 1.f / sm.W[h];
+      store_out<BF16>(out, row * D + d4 * 4 + 0, acc[qi].x * inv);
+      store_out<BF16>(out, row * D + d4 * 4 + 1, acc[qi].y * inv);
+      store_out<BF16>(out, row * D + d4 * 4 + 2, acc[qi].z * inv);
+      store_out<BF16>(out, row * D + d4 * 4 + 3, acc[qi].w * inv);
+      if (lse_out && d4 == 0) lse_out[row] = sm.M[h] * kLn2 + logf(sm.W[h]);
     }
   }
 }
@@ -740,8 +796,7 @@ static void launch_decode_nw(const DecodeParams& a, hipStream_t s) {
   hipLaunchKernelGGL(k, dim3(grid), dim3(NW * kWave), 0, s, a);
 }
 
-// Fewer items than two per compute unit: 8 waves share each item, so the
-// blocks of one (sequence, head) spread over more SIMD slots.
+// Compute units of the current device (cached per device).
 static int device_cus() {
   constexpr int kMaxDev = 64;
   static int cached[kMaxDev] = {0};
@@ -756,12 +811,19 @@ static int device_cus() {
   return cus;
 }
 
+// Waves per workgroup from the items per compute unit: few items get 8
+// waves each (a long item's blocks spread over more SIMD slots); many items
+// get small workgroups, so that several items share a compute unit and one
+// item's start and merge latency hides behind the others' loads.
 template <int D, int G, bool BF16>
 static void launch_decode(const DecodeParams& a, hipStream_t s) {
-  if (a.num_items < 2 * device_cus())
+  const int64_t cus = device_cus();
+  if (a.num_items < 2 * cus)
     launch_decode_nw<D, G, BF16, 8>(a, s);
-  else
+  else if (a.num_items < 8 * cus)
     launch_decode_nw<D, G, BF16, 4>(a, s);
+  else
+    launch_decode_nw<D, G, BF16, 2>(a, s);
 }
 
 template <int D, bool BF16>
