@@ -41,6 +41,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 METRIC = "paged-attn decode KV GB/s (% of HBM peak) + context-tokens/s, 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 DECODE_SOURCES = ["paged_attention_kv_block_amd/csrc/pa_decode.hip",
@@ -130,12 +131,197 @@ def cpu_baseline(d, min_seconds: float):
     return dt, reps
 
 
+def prefill_flops(seq_lens, chunk_lens, num_q_heads: int, head_size: int) -> int:
+    """Algorithmic flops of the causal chunks: query i of a chunk of C sits at
+    position L - C + i and sees L - C + i + 1 keys; 2 flops of q.k and 2 of
+    p.v per (query head, visible key, dim)."""
+    pairs = 0
+    for L, C in zip(seq_lens, chunk_lens):
+        L, C = int(L), int(C)
+        pairs += C * (L - C) + C * (C + 1) // 2
+    return 4 * head_size * num_q_heads * pairs
+
+
+def cpu_baseline_prefill(d, min_seconds: float):
+    """The fp64 oracle on this host: whole sequences of the chunked-prefill
+    step (write the chunk's keys/values, attend) until min_seconds; returns
+    (seconds, flops done, sequences done)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from tests.oracle_setup import OracleSide
+
+    wl = d.wl
+    side = OracleSide(d)
+    qsl = side.query_start_loc()
+    chunks = wl.chunk_lens()
+    done, flops, t0 = 0, 0, time.perf_counter()
+    with threadpool_limits(1):
+        while True:
+            b = done % wl.num_seqs
+            L, C = int(d.seq_lens[b]), int(chunks[b])
+            k, v = d.kv(b)
+            slots = oracle.slot_mapping(side.block_tables[b], L - C, C, wl.block_size)
+            oracle.reshape_and_cache(side.pool, k[L - C:], v[L - C:], slots)
+            oracle.prefill_chunk(d.query(), qsl, side.pool, side.block_tables, d.seq_lens,
+                                 wl.scale, seqs=[b])
+            flops += prefill_flops([L], [C], wl.num_q_heads, wl.head_size)
+            done += 1
+            if time.perf_counter() - t0 >= min_seconds:
+                break
+    return time.perf_counter() - t0, flops, done
+
+
+def bench_prefill(a, d, dev):
+    """Chunked prefill with a shared prefix: pa_reshape_and_cache of every
+    chunk token, then pa_prefill_chunk; MFMA roofline of the prefill kernel."""
+    import numpy as np
+    import torch
+    from paged_attention_kv_block_amd import host, ops
+
+    wl = d.wl
+    B, Hq, Hkv, D, bs = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_size, wl.block_size
+    seq_lens = d.seq_lens
+    chunks = np.asarray(wl.chunk_lens(), dtype=np.int64)
+    msl = int(seq_lens.max())
+
+    def dev_tensor(arr):
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    t0 = time.perf_counter()
+    alloc = ops.Allocator(d.num_blocks, d.pool_order)
+    own = int(seq_lens[0]) - wl.prefix_tokens
+    bt = host.prefill_block_tables(alloc, B, wl.prefix_tokens, own, bs, True)
+    chunk_slots = np.concatenate([ops.slot_mapping(bt[b], int(seq_lens[b]) - int(chunks[b]),
+                                                   int(chunks[b]), bs) for b in range(B)])
+    qsl = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    host_us = (time.perf_counter() - t0) * 1e6
+
+    # cache holds every token before the chunks (the shared prefix once)
+    pool0 = torch.zeros((d.num_blocks, 2, Hkv, bs, D), dtype=torch.bfloat16, device=dev)
+    ks, vs, sl, cks, cvs = [], [], [], [], []
+    for b in range(B):
+        L, C = int(seq_lens[b]), int(chunks[b])
+        k, v = d.kv(b)
+        lo = 0 if b == 0 else wl.prefix_tokens
+        ks.append(k[lo:L - C])
+        vs.append(v[lo:L - C])
+        sl.append(ops.slot_mapping(bt[b], lo, L - C - lo, bs))
+        cks.append(k[L - C:])
+        cvs.append(v[L - C:])
+    ops.reshape_and_cache(dev_tensor(np.concatenate(ks)), dev_tensor(np.concatenate(vs)),
+                          torch.from_numpy(np.concatenate(sl)).to(dev), pool0)
+    del ks, vs
+    pool_bytes = pool0.numel() * pool0.element_size()
+    R = max(1, -(-a.rotate_mb * (1 << 20) // pool_bytes))
+    pools = [pool0] + [pool0.clone() for _ in range(R - 1)]
+    ck, cv = dev_tensor(np.concatenate(cks)), dev_tensor(np.concatenate(cvs))
+    slots_dev = torch.from_numpy(chunk_slots).to(dev)
+    q = dev_tensor(d.query())
+    out = torch.empty_like(q)
+    qsl_dev = torch.from_numpy(qsl).to(dev)
+    bt_dev = torch.from_numpy(bt).to(dev)
+    sl_dev = torch.from_numpy(np.ascontiguousarray(seq_lens, dtype=np.int32)).to(dev)
+    max_q = int(chunks.max())
+    scale = float(wl.scale)
+    torch.cuda.synchronize()
+
+    def step(pool):
+        ops.reshape_and_cache(ck, cv, slots_dev, pool)
+        ops.prefill_chunk(out, q, qsl_dev, max_q, pool, bt_dev, sl_dev, msl, scale)
+
+    def prefill_only(pool):
+        ops.prefill_chunk(out, q, qsl_dev, max_q, pool, bt_dev, sl_dev, msl, scale)
+
+    def capture(fn, n):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(min(n, R)):
+                fn(pools[i % R])
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(pools[i % R])
+        return g
+
+    g_warm = capture(step, max(1, a.warmup))
+    g_step = capture(step, a.steps)
+    g_pf = capture(prefill_only, a.steps)
+    g_warm.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g_step.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / a.steps
+    g_pf.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    g_pf.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    pf_us = e0.elapsed_time(e1) * 1e3 / a.steps
+
+    flops = prefill_flops(seq_lens, chunks, Hq, D)
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (pf_us * 1e-6) / 1e12
+    res = {
+        "metric": "paged-attn prefill-chunk TFLOP/s (causal, algorithmic), 1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) keys/values/queries; no weights)",
+        "config": {
+            "workload": wl.name, "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
+            "head_size": D, "block_size": bs, "chunk_tokens": int(chunks.sum()),
+            "shared_prefix_tokens": wl.prefix_tokens, "max_seq_len": msl,
+            "pool_blocks": d.num_blocks, "pool_copies_rotated": R, "parallelism": "none (1 GPU)",
+        },
+        "host_metadata_us": round(host_us, 1),
+        "roofline": {
+            "kernel": "pa_prefill_chunk (prefill_chunk_kernel)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops,
+            "avg_launch_us": round(pf_us, 3),
+        },
+    }
+    if not a.no_cpu_baseline:
+        dt, cflops, nseq = cpu_baseline_prefill(d, a.cpu_seconds)
+        res["cpu_baseline"] = {
+            "value": round(cflops / dt / 1e12, 8),
+            "unit": "TFLOP/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"{nseq} of the {B} sequences of the {wl.name} step (write the chunk's "
+                      f"keys/values, attend), fp64 numpy, BLAS 1 thread; {dt:.1f} s",
+        }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=1, help="decode workload index (1, 2, 4; 0 = tiny)")
+    ap.add_argument("--workload", type=int, default=1,
+                    help="workload index: decode 1, 2, 4 (0 = tiny); 3 = chunked prefill")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="split-K partition in tokens (default: workload's, else 256/512)")
     ap.add_argument("--rotate-mb", type=int, default=768,
@@ -171,10 +357,9 @@ def main(argv=None):
         return 0
 
     wl = inputs.workload(a.workload)
-    if wl.kind != "decode":
-        print("bench.py: the benchmarked step is decode; pick a decode workload", file=sys.stderr)
-        return 2
     d = inputs.draw(a.workload)
+    if wl.kind == "prefill":
+        return bench_prefill(a, d, dev)
     B, Hq, Hkv, D, bs = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_size, wl.block_size
     P = default_partition(wl) if a.partition_size is None else a.partition_size
     seq_lens = d.seq_lens
@@ -302,7 +487,7 @@ def main(argv=None):
         "context_tokens_per_s": round(ctx / (ms_step * 1e-3), 1),
         "host_metadata_us": round(host_us, 1),
         "roofline": {
-            "kernel": "pa_decode (decode_partition_kernel)",
+            "kernel": "pa_decode (decode_kernel)",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,

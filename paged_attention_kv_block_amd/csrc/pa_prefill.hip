@@ -17,16 +17,20 @@
 //     of a tile are (token, head) pairs of the G query heads that share the
 //     KV head, token-major, 128 rows per workgroup and 32 per wave;
 //   * keys advance 32 at a time (two blocks).  K and V of the step are
-//     loaded by the whole workgroup (coalesced 16-byte vectors, gathered
-//     through the block table), double-buffered in padded LDS;
+//     loaded by the whole workgroup (16-byte vectors gathered through the
+//     block table) and double-buffered in LDS: K row-major, V transposed
+//     (one row per head dimension) with its keys permuted into the order in
+//     which P^T holds them, so every MFMA operand is one 16-byte LDS read;
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = Q^T
 //     held in registers for the whole loop).  The S^T output layout puts one
-//     query row per lane and 4 keys per lane group, which is exactly the
-//     B-operand layout of O^T = V^T P^T over those keys, so P never leaves
-//     registers; only V^T is gathered from LDS (8 keys of one column per lane);
-//   * online softmax in the log2 domain per row (row = lane % 16); the
-//     causal mask is applied only on steps that reach the diagonal; the
-//     denominator sums the same bf16-rounded P that multiplies V.
+//     query row per lane and 4 keys per lane group, which is the B-operand
+//     layout of O^T = V^T P^T over those keys, so P never leaves registers;
+//   * online softmax in the log2 domain per row (row = lane % 16), row
+//     maxima reduced across the four lane groups with lane-swap moves; the
+//     reference moves only when a row's max exceeds it by 2^8, so the
+//     accumulators are rarely rescaled; the causal mask is applied only on
+//     steps that reach the diagonal; the denominator sums the same
+//     bf16-rounded P that multiplies V.
 #include "pa.h"
 #include "pa_common.h"
 #include "pa_internal.h"
@@ -37,8 +41,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPrefillWaves = 4;
+constexpr int kPrefillThreads = kPrefillWaves * kWave;
 constexpr float kLog2eP = 1.4426950408889634f;
 constexpr float kLn2P = 0.6931471805599453f;
+constexpr float kPrefillSlack = 8.f;  // log2 units a row max may exceed the reference
 
 template <int D, int G>
 struct PrefillCfg {
@@ -49,20 +55,44 @@ struct PrefillCfg {
   static constexpr int KSTEP = 32;            // keys per step (two blocks)
   static constexpr int DS = D / 32;           // K-dim steps of S^T = K Q^T
   static constexpr int DT = D / 16;           // 16-column tiles of O^T
-  static constexpr int LROW = D + 8;          // padded LDS row in bf16 elements
+  static constexpr int LROW = D + 8;          // padded K row in LDS (bf16 elements)
+  static constexpr int VROW = KSTEP + 8;      // padded V^T row in LDS (bf16 elements)
   static constexpr int CH = D / 8;            // 16-byte chunks per K/V row
-  static constexpr int LOADS = KSTEP * CH / (kPrefillWaves * kWave);  // per thread, per K or V
-  static_assert(LOADS >= 1 && KSTEP * CH % (kPrefillWaves * kWave) == 0, "load split");
+  static constexpr int KLOADS = KSTEP * CH / kPrefillThreads;   // K chunks per thread
+  static constexpr int VPAIRS = KSTEP / 2 * CH;                 // V (key pair, chunk) items
+  static_assert(KLOADS >= 1 && KSTEP * CH % kPrefillThreads == 0, "K load split");
+  static_assert(VPAIRS <= kPrefillThreads, "V pair split");
   static_assert(RW % 16 == 0, "rows per wave");
 };
+
+// Position of key k (0..31 of a step) in a V^T row: P^T gives lane group lq
+// the keys 4*lq + i and 16 + 4*lq + i (i = 0..3) as its 8 B-operand slots.
+__device__ __forceinline__ constexpr int vt_pos(int k) {
+  return 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3);
+}
 
 __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// Max / sum of x over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane
+// groups), with the lane-swap moves of gfx950.
+__device__ __forceinline__ float group4_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group4_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int D, int G>
-__global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_chunk_kernel(
+__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_chunk_kernel(
     uint16_t* __restrict__ out, float* __restrict__ lse_out, const uint16_t* __restrict__ query,
     const int* __restrict__ qsl, const uint16_t* __restrict__ cache, int num_blocks,
     const int* __restrict__ block_tables, int max_blocks_per_seq, const int* __restrict__ seq_lens,
@@ -90,7 +120,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_chunk_kernel(
   const int lr = lane & 15;                     // row / column within a 16-tile
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C::KSTEP * C::LROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][C::KSTEP * C::LROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * C::VROW];
 
   const int64_t tile_elems = int64_t(16) * D;
   const int64_t block_elems = int64_t(2) * num_kv_heads * tile_elems;
@@ -114,36 +144,59 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_chunk_kernel(
     }
   }
 
-  // ---- staging of one step's K and V (registers -> LDS)
-  u32x4 kreg[C::LOADS], vreg[C::LOADS];
-  auto load_step = [&](int s, u32x4 (&kr)[C::LOADS], u32x4 (&vr)[C::LOADS]) {
+  // ---- staging of one step's K and V (registers -> LDS).  K: thread tid
+  // takes chunks tid, tid + 256, ... (row-major).  V: thread tid < VPAIRS
+  // takes chunk vch of the key pair (2 vkp, 2 vkp + 1), so that it can write
+  // the pair's values of each head dimension as one 32-bit word of V^T.
+  const int vkp = tid % (C::KSTEP / 2), vch = tid / (C::KSTEP / 2);
+  const bool vthread = tid < C::VPAIRS;
+  auto tile_of = [&](int kabs, int& off) -> const uint16_t* {
+    const int j = kabs >> 4;
+    int phys = j < nblk ? bt_row[j] : 0;
+    phys = (phys < 0 || phys >= num_blocks) ? 0 : phys;
+    off = (kabs & 15) * D;
+    return cache + int64_t(phys) * block_elems + int64_t(g) * tile_elems;
+  };
+  u32x4 kreg[C::KLOADS], vreg[2];
+  auto load_step = [&](int s) {
 #pragma unroll
-    for (int u = 0; u < C::LOADS; ++u) {
-      const int c = u * kPrefillWaves * kWave + tid;   // chunk index in the step
-      const int key = c / C::CH, ch = c % C::CH;
-      const int kabs = s * C::KSTEP + key;
-      const int j = kabs >> 4;
-      u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
+    for (int u = 0; u < C::KLOADS; ++u) {
+      const int c = u * kPrefillThreads + tid;
+      const int kabs = s * C::KSTEP + c / C::CH;
+      u32x4 kx = {0u, 0u, 0u, 0u};
       if (kabs < kend) {        // past kend: never needed (and may be unwritten)
-        int phys = j < nblk ? bt_row[j] : 0;
-        phys = (phys < 0 || phys >= num_blocks) ? 0 : phys;
-        const uint16_t* kt = cache + int64_t(phys) * block_elems + int64_t(g) * tile_elems;
-        const uint16_t* vt = kt + int64_t(num_kv_heads) * tile_elems;
-        const int off = (kabs & 15) * D + ch * 8;
-        kx = *reinterpret_cast<const u32x4*>(kt + off);
-        vx = *reinterpret_cast<const u32x4*>(vt + off);
+        int off;
+        const uint16_t* kt = tile_of(kabs, off);
+        kx = *reinterpret_cast<const u32x4*>(kt + off + (c % C::CH) * 8);
       }
-      kr[u] = kx;
-      vr[u] = vx;
+      kreg[u] = kx;
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int kabs = s * C::KSTEP + 2 * vkp + e;
+      u32x4 vx = {0u, 0u, 0u, 0u};
+      if (vthread && kabs < kend) {
+        int off;
+        const uint16_t* vt = tile_of(kabs, off) + int64_t(num_kv_heads) * tile_elems;
+        vx = *reinterpret_cast<const u32x4*>(vt + off + vch * 8);
+      }
+      vreg[e] = vx;
     }
   };
-  auto store_step = [&](int buf, const u32x4 (&kr)[C::LOADS], const u32x4 (&vr)[C::LOADS]) {
+  auto store_step = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < C::LOADS; ++u) {
-      const int c = u * kPrefillWaves * kWave + tid;
-      const int key = c / C::CH, ch = c % C::CH;
-      *reinterpret_cast<u32x4*>(&Ks[buf][key * C::LROW + ch * 8]) = kr[u];
-      *reinterpret_cast<u32x4*>(&Vs[buf][key * C::LROW + ch * 8]) = vr[u];
+    for (int u = 0; u < C::KLOADS; ++u) {
+      const int c = u * kPrefillThreads + tid;
+      *reinterpret_cast<u32x4*>(&Ks[buf][(c / C::CH) * C::LROW + (c % C::CH) * 8]) = kreg[u];
+    }
+    if (vthread) {
+      uint32_t* vt = reinterpret_cast<uint32_t*>(&Vt[buf][vch * 8 * C::VROW + vt_pos(2 * vkp)]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // head dims 8 vch + 2w (low halves) and 8 vch + 2w + 1 (high halves)
+        vt[(2 * w) * (C::VROW / 2)] = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u);
+        vt[(2 * w + 1) * (C::VROW / 2)] = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u);
+      }
     }
   };
 
@@ -152,21 +205,21 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_chunk_kernel(
   for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) acc[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[C::NT], l_part[C::NT];
+  float m_run[C::NT], m_thr[C::NT], l_part[C::NT];
 #pragma unroll
-  for (int nt = 0; nt < C::NT; ++nt) { m_run[nt] = -INFINITY; l_part[nt] = 0.f; }
+  for (int nt = 0; nt < C::NT; ++nt) { m_run[nt] = -INFINITY; m_thr[nt] = -INFINITY; l_part[nt] = 0.f; }
 
   // smallest query position of this wave's active rows (rows are token-major)
   const int wave_min_pos = ctx + t0 + (wave * C::RW) / G;
 
-  load_step(0, kreg, vreg);
-  store_step(0, kreg, vreg);
+  load_step(0);
+  store_step(0);
   __syncthreads();
 
   for (int s = 0; s < nsteps; ++s) {
     const int buf = s & 1;
     const bool more = s + 1 < nsteps;
-    if (more) load_step(s + 1, kreg, vreg);
+    if (more) load_step(s + 1);
 
     // ---- S^T = K Q^T for the step's two 16-key tiles
     f32x4 sacc[2][C::NT];
@@ -188,71 +241,70 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_chunk_kernel(
     // ---- online softmax; lane holds row lr of tile nt, keys kt*16 + 4*lq + i
     const int key0 = s * C::KSTEP;
     const bool need_mask = key0 + C::KSTEP - 1 > wave_min_pos;
-    u32x4 pb[C::NT];   // P^T as the B operand: 8 bf16 keys of this lane's row
+    float x[C::NT][8];
+    float mloc[C::NT];
+    bool grow = false;
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) {
-      float x[8];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float v = sacc[kt][nt][i] * scale_log2;
-          if (need_mask) {
-            const int key = key0 + kt * 16 + lq * 4 + i;
-            v = key <= row_pos[nt] ? v : -INFINITY;
-          }
-          x[kt * 4 + i] = v;
+          float v = sacc[kt][nt][i];
+          if (need_mask) v = key0 + kt * 16 + lq * 4 + i <= row_pos[nt] ? v : -INFINITY;
+          x[nt][kt * 4 + i] = v;
         }
-      float mloc = x[0];
+      float m = x[nt][0];
 #pragma unroll
-      for (int e = 1; e < 8; ++e) mloc = fmaxf(mloc, x[e]);
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-      const float m_new = fmaxf(m_run[nt], mloc);
-      const float mref = m_new == -INFINITY ? 0.f : m_new;   // rows with nothing visible yet
-      const float alpha = exp2f(m_run[nt] - mref);
-      m_run[nt] = m_new;
+      for (int e = 1; e < 8; ++e) m = fmaxf(m, x[nt][e]);
+      mloc[nt] = group4_max(m) * scale_log2;   // scale > 0 keeps the order
+      grow |= mloc[nt] > m_thr[nt];
+    }
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform, rare after the first step
+#pragma unroll
+      for (int nt = 0; nt < C::NT; ++nt) {
+        if (mloc[nt] > m_thr[nt]) {
+          const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - mloc[nt]);  // 0 on the first step
+          m_run[nt] = mloc[nt];
+          m_thr[nt] = mloc[nt] + kPrefillSlack;
+          l_part[nt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < C::DT; ++dt) acc[dt][nt] *= alpha;
+        }
+      }
+    }
+    u32x4 pb[C::NT];   // P^T as the B operand: 8 bf16 keys of this lane's row
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) {
+      const float mref = m_run[nt] == -INFINITY ? 0.f : m_run[nt];  // rows with nothing visible
       uint32_t pw[4];
-      float psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        const uint32_t lo = f32_to_bf16_rne(exp2f(x[e] - mref));
-        const uint32_t hi = f32_to_bf16_rne(exp2f(x[e + 1] - mref));
-        psum += __uint_as_float(lo << 16) + __uint_as_float(hi << 16);
-        pw[e / 2] = lo | (hi << 16);
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[nt][e], scale_log2, -mref));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[nt][e + 1], scale_log2, -mref));
+        pw[e / 2] = pack_bf16x2(p0, p1);
+        l_part[nt] = dot2_bf16(pw[e / 2], 0x3F803F80u, l_part[nt]);
       }
-      l_part[nt] = l_part[nt] * alpha + psum;
       pb[nt] = u32x4{pw[0], pw[1], pw[2], pw[3]};
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) acc[dt][nt] *= alpha;
     }
 
-    // ---- O^T += V^T P^T; lane (lq, lr) supplies V[key][dt*16 + lr] for the
-    // keys 4*lq + i and 16 + 4*lq + i (i = 0..3), matching P^T's key slots
+    // ---- O^T += V^T P^T: lane (lq, lr) reads head dim dt*16 + lr at the
+    // eight V^T positions of its P^T key slots
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
-      const uint16_t* vcol = &Vs[buf][dt * 16 + lr];
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const int k0 = (e < 4 ? 0 : 16) + lq * 4 + (e & 3);
-        w[e / 2] = uint32_t(vcol[k0 * C::LROW]) | (uint32_t(vcol[(k0 + 1) * C::LROW]) << 16);
-      }
-      const u32x4 a = u32x4{w[0], w[1], w[2], w[3]};
+      const u32x4 a = *reinterpret_cast<const u32x4*>(&Vt[buf][(dt * 16 + lr) * C::VROW + lq * 8]);
 #pragma unroll
       for (int nt = 0; nt < C::NT; ++nt) acc[dt][nt] = mfma16x16x32(a, pb[nt], acc[dt][nt]);
     }
 
-    if (more) store_step(buf ^ 1, kreg, vreg);
+    if (more) store_step(buf ^ 1);
     __syncthreads();
   }
 
   // ---- normalise and write: lane holds O^T[dt*16 + 4*lq + i][row lr of tile nt]
 #pragma unroll
   for (int nt = 0; nt < C::NT; ++nt) {
-    float l = l_part[nt];
-    l += __shfl_xor(l, 16, kWave);
-    l += __shfl_xor(l, 32, kWave);
+    const float l = group4_sum(l_part[nt]);
     if (row_pos[nt] < 0) continue;
     const int r = wave * C::RW + nt * 16 + lr;
     const int i = r / G, hh = r % G;
@@ -260,8 +312,8 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_chunk_kernel(
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
-      const uint32_t w0 = f32_to_bf16_rne(acc[dt][nt][0] * inv) | (f32_to_bf16_rne(acc[dt][nt][1] * inv) << 16);
-      const uint32_t w1 = f32_to_bf16_rne(acc[dt][nt][2] * inv) | (f32_to_bf16_rne(acc[dt][nt][3] * inv) << 16);
+      const uint32_t w0 = pack_bf16x2(acc[dt][nt][0] * inv, acc[dt][nt][1] * inv);
+      const uint32_t w1 = pack_bf16x2(acc[dt][nt][2] * inv, acc[dt][nt][3] * inv);
       *reinterpret_cast<uint2*>(out + orow * D + dt * 16 + lq * 4) = make_uint2(w0, w1);
     }
     if (lse_out && lq == 0) lse_out[orow] = l > 0.f ? m_run[nt] * kLn2P + logf(l) : -INFINITY;
@@ -275,7 +327,7 @@ static bool launch_prefill(int G, dim3 grid, hipStream_t s, uint16_t* out, float
 #define PA_PREFILL_CASE(GG)                                                                     \
   case GG:                                                                                      \
     grid.x = (grid.x + PrefillCfg<D, GG>::TQ - 1) / PrefillCfg<D, GG>::TQ;                      \
-    hipLaunchKernelGGL((prefill_chunk_kernel<D, GG>), grid, dim3(kPrefillWaves * kWave), 0, s,  \
+    hipLaunchKernelGGL((prefill_chunk_kernel<D, GG>), grid, dim3(kPrefillThreads), 0, s,        \
                        out, lse, q, qsl, cache, nb, bt, mbps, sl, msl, hkv, sc);                \
     return true;
   switch (G) {
