@@ -31,6 +31,8 @@
 //     accumulators are rarely rescaled; the causal mask is applied only on
 //     steps that reach the diagonal; the denominator sums the same
 //     bf16-rounded P that multiplies V.
+#include <type_traits>
+
 #include "pa.h"
 #include "pa_common.h"
 #include "pa_internal.h"
@@ -145,45 +147,49 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
   }
 
   // ---- staging of one step's K and V (registers -> LDS).  K: thread tid
-  // takes chunks tid, tid + 256, ... (row-major).  V: thread tid < VPAIRS
-  // takes chunk vch of the key pair (2 vkp, 2 vkp + 1), so that it can write
-  // the pair's values of each head dimension as one 32-bit word of V^T.
-  const int vkp = tid % (C::KSTEP / 2), vch = tid / (C::KSTEP / 2);
+  // takes chunks tid, tid + 256, ... (row-major).  V: thread t takes chunk
+  // vch of the key pair (2 vkp, 2 vkp + 1), so that it can write the pair's
+  // values of each head dimension as one 32-bit word of V^T (with fewer
+  // pairs than threads the others load a duplicate and store nothing).
+  // Every load is issued unconditionally (block indices clamped to the last
+  // block, V zeroed past the last visible key), so the loop's wait counts
+  // stay exact.
+  const int vsrc = tid % C::VPAIRS;
+  const int vkp = vsrc % (C::KSTEP / 2), vch = vsrc / (C::KSTEP / 2);
   const bool vthread = tid < C::VPAIRS;
-  auto tile_of = [&](int kabs, int& off) -> const uint16_t* {
-    const int j = kabs >> 4;
-    int phys = j < nblk ? bt_row[j] : 0;
-    phys = (phys < 0 || phys >= num_blocks) ? 0 : phys;
-    off = (kabs & 15) * D;
-    return cache + int64_t(phys) * block_elems + int64_t(g) * tile_elems;
+  auto step_ids = [&](int s) -> int2 {  // the step's two block ids (same in all lanes)
+    return make_int2(bt_row[min(2 * s, nblk - 1)], bt_row[min(2 * s + 1, nblk - 1)]);
   };
-  u32x4 kreg[C::KLOADS], vreg[2];
-  auto load_step = [&](int s) {
+  auto block_ptr = [&](int id) -> const uint16_t* {
+    id = __builtin_amdgcn_readfirstlane(id);
+    id = (id < 0 || id >= num_blocks) ? 0 : id;  // out-of-range ids read block 0
+    return cache + int64_t(id) * block_elems + int64_t(g) * tile_elems;
+  };
+  auto load_step = [&](int s, int2 ids, u32x4 (&kreg)[C::KLOADS], u32x4 (&vreg)[2])
+      __attribute__((always_inline)) {
+    const uint16_t* k0 = block_ptr(ids.x);
+    const uint16_t* k1 = block_ptr(ids.y);
 #pragma unroll
     for (int u = 0; u < C::KLOADS; ++u) {
       const int c = u * kPrefillThreads + tid;
-      const int kabs = s * C::KSTEP + c / C::CH;
-      u32x4 kx = {0u, 0u, 0u, 0u};
-      if (kabs < kend) {        // past kend: never needed (and may be unwritten)
-        int off;
-        const uint16_t* kt = tile_of(kabs, off);
-        kx = *reinterpret_cast<const u32x4*>(kt + off + (c % C::CH) * 8);
-      }
-      kreg[u] = kx;
+      const int key = c / C::CH;
+      const uint16_t* kt = key < 16 ? k0 : k1;
+      kreg[u] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(kt + (key & 15) * D + (c % C::CH) * 8));
     }
+    const int64_t vofs = int64_t(num_kv_heads) * tile_elems;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int kabs = s * C::KSTEP + 2 * vkp + e;
-      u32x4 vx = {0u, 0u, 0u, 0u};
-      if (vthread && kabs < kend) {
-        int off;
-        const uint16_t* vt = tile_of(kabs, off) + int64_t(num_kv_heads) * tile_elems;
-        vx = *reinterpret_cast<const u32x4*>(vt + off + vch * 8);
-      }
-      vreg[e] = vx;
+      const int key = 2 * vkp + e;
+      const uint16_t* vt = (key < 16 ? k0 : k1) + vofs;
+      const u32x4 vx = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(vt + (key & 15) * D + vch * 8));
+      const bool in = s * C::KSTEP + key < kend;  // past kend: may be unwritten
+      vreg[e] = u32x4{in ? vx.x : 0u, in ? vx.y : 0u, in ? vx.z : 0u, in ? vx.w : 0u};
     }
   };
-  auto store_step = [&](int buf) {
+  auto store_step = [&](int buf, const u32x4 (&kreg)[C::KLOADS], const u32x4 (&vreg)[2])
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < C::KLOADS; ++u) {
       const int c = u * kPrefillThreads + tid;
@@ -209,18 +215,14 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
   for (int nt = 0; nt < C::NT; ++nt) { m_run[nt] = -INFINITY; m_thr[nt] = -INFINITY; l_part[nt] = 0.f; }
 
-  // smallest query position of this wave's active rows (rows are token-major)
+  // smallest query position of this wave's active rows (rows are token-major);
+  // steps from s_diag on reach it and need the causal mask
   const int wave_min_pos = ctx + t0 + (wave * C::RW) / G;
+  const int s_diag = (wave_min_pos + 1) / C::KSTEP;
 
-  load_step(0);
-  store_step(0);
-  __syncthreads();
-
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    const bool more = s + 1 < nsteps;
-    if (more) load_step(s + 1);
-
+  // one step: S^T for 32 keys, online softmax, O^T += V^T P^T
+  auto compute = [&](int s, int buf, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     // ---- S^T = K Q^T for the step's two 16-key tiles
     f32x4 sacc[2][C::NT];
 #pragma unroll
@@ -240,7 +242,6 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
 
     // ---- online softmax; lane holds row lr of tile nt, keys kt*16 + 4*lq + i
     const int key0 = s * C::KSTEP;
-    const bool need_mask = key0 + C::KSTEP - 1 > wave_min_pos;
     float x[C::NT][8];
     float mloc[C::NT];
     bool grow = false;
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float v = sacc[kt][nt][i];
-          if (need_mask) v = key0 + kt * 16 + lq * 4 + i <= row_pos[nt] ? v : -INFINITY;
+          if constexpr (MASK) v = key0 + kt * 16 + lq * 4 + i <= row_pos[nt] ? v : -INFINITY;
           x[nt][kt * 4 + i] = v;
         }
       float m = x[nt][0];
@@ -296,10 +297,30 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
       for (int nt = 0; nt < C::NT; ++nt) acc[dt][nt] = mfma16x16x32(a, pb[nt], acc[dt][nt]);
     }
+  };
 
-    if (more) store_step(buf ^ 1);
+  // Pipeline: step s + 1's K/V are loaded while step s computes and stored
+  // to the other LDS buffer after it; the block ids of a step are loaded one
+  // step before its K/V, so no K/V load waits on a table read.  Steps before
+  // s_diag run without the causal mask, the rest with it (two loops: a
+  // branch between the variants inside one loop costs registers); each
+  // iteration has one barrier, so every wave meets the same barriers.
+  u32x4 kreg[C::KLOADS], vreg[2];
+  load_step(0, step_ids(0), kreg, vreg);
+  store_step(0, kreg, vreg);
+  int2 ids_next = step_ids(1);
+  __syncthreads();
+  auto iteration = [&](int s, auto mask_tag) __attribute__((always_inline)) {
+    const int2 ids = ids_next;
+    ids_next = step_ids(s + 2);
+    load_step(s + 1, ids, kreg, vreg);   // past the last step: clamped, never stored
+    compute(s, s & 1, mask_tag);
+    if (s + 1 < nsteps) store_step((s + 1) & 1, kreg, vreg);
     __syncthreads();
-  }
+  };
+  int s = 0;
+  for (const int sd = min(s_diag, nsteps); s < sd; ++s) iteration(s, std::false_type{});
+  for (; s < nsteps; ++s) iteration(s, std::true_type{});
 
   // ---- normalise and write: lane holds O^T[dt*16 + 4*lq + i][row lr of tile nt]
 #pragma unroll
