@@ -25,6 +25,11 @@ LIB = os.path.join(PKG, "libpa.so")
 HOST_LIB = os.path.join(PKG, "libpa_host.so")
 
 HIP_SOURCES = ["pa_host.cpp", "pa_cache.hip", "pa_decode.hip", "pa_prefill.hip"]
+# Per-source flags.  The prefill kernel never lets a NaN reach a max or an
+# exponent (scores of keys that may be unwritten are replaced by -inf with a
+# select first, and their V rows are zeroed), so it drops the NaN-quieting
+# of fmaxf.
+EXTRA_FLAGS = {"pa_prefill.hip": ["-fno-honor-nans"]}
 HOST_SOURCES = ["pa_host.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -53,7 +58,7 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
         if src.endswith(".hip"):
             cmd = [HIPCC, f"--offload-arch={ARCH}", "-x", "hip", "-c", path, "-o", obj,
                    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                   "-munsafe-fp-atomics"] + common
+                   "-munsafe-fp-atomics"] + common + EXTRA_FLAGS.get(src, [])
         else:
             cmd = [HIPCC, "-c", path, "-o", obj] + common
         cmds.append(cmd)

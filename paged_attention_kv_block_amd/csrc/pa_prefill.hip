@@ -44,6 +44,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillThreads = kPrefillWaves * kWave;
+constexpr int kPrefillBufs = 3;  // LDS ring of K/V steps
 constexpr float kLog2eP = 1.4426950408889634f;
 constexpr float kLn2P = 0.6931471805599453f;
 constexpr float kPrefillSlack = 8.f;  // log2 units a row max may exceed the reference
@@ -98,9 +99,23 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     uint16_t* __restrict__ out, float* __restrict__ lse_out, const uint16_t* __restrict__ query,
     const int* __restrict__ qsl, const uint16_t* __restrict__ cache, int num_blocks,
     const int* __restrict__ block_tables, int max_blocks_per_seq, const int* __restrict__ seq_lens,
-    int max_seq_len, int num_kv_heads, float scale_log2) {
+    int max_seq_len, int num_kv_heads, float scale_log2, int tiles, int num_groups) {
   using C = PrefillCfg<D, G>;
-  const int qtile = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // Workgroup -> (query tile, KV head g, sequence b).  The dispatcher hands
+  // consecutive workgroups to the 8 XCDs in turn; when the (sequence, KV
+  // head) groups split evenly over them, all query tiles of a group go to
+  // one XCD, so they share the KV blocks they stream through that XCD's L2.
+  const int wg = blockIdx.x;
+  int grp, qtile;
+  if ((num_groups & 7) == 0) {
+    const int r = wg >> 3;
+    grp = (r / tiles) * 8 + (wg & 7);
+    qtile = r % tiles;
+  } else {
+    grp = wg / tiles;
+    qtile = wg % tiles;
+  }
+  const int g = grp % num_kv_heads, b = grp / num_kv_heads;
   const int H_q = num_kv_heads * G;
   const int q0 = qsl[b];
   int L = seq_lens[b];
@@ -121,8 +136,8 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
   const int lq = lane >> 4;                     // lane group 0..3
   const int lr = lane & 15;                     // row / column within a 16-tile
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C::KSTEP * C::LROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * C::VROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kPrefillBufs][C::KSTEP * C::LROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[kPrefillBufs][D * C::VROW];
 
   const int64_t tile_elems = int64_t(16) * D;
   const int64_t block_elems = int64_t(2) * num_kv_heads * tile_elems;
@@ -157,8 +172,13 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
   const int vsrc = tid % C::VPAIRS;
   const int vkp = vsrc % (C::KSTEP / 2), vch = vsrc / (C::KSTEP / 2);
   const bool vthread = tid < C::VPAIRS;
-  auto step_ids = [&](int s) -> int2 {  // the step's two block ids (same in all lanes)
-    return make_int2(bt_row[min(2 * s, nblk - 1)], bt_row[min(2 * s + 1, nblk - 1)]);
+  // The step's two block ids (same in all lanes), read as vector buffer
+  // loads: a scalar load would share its wait counter with the LDS reads.
+  const __amdgpu_buffer_rsrc_t bt_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int*>(bt_row), 0, max_blocks_per_seq * 4, 0x00020000);
+  auto step_ids = [&](int s) -> int2 {
+    return make_int2(__builtin_amdgcn_raw_buffer_load_b32(bt_rsrc, min(2 * s, nblk - 1) * 4, 0, 0),
+                     __builtin_amdgcn_raw_buffer_load_b32(bt_rsrc, min(2 * s + 1, nblk - 1) * 4, 0, 0));
   };
   auto block_ptr = [&](int id) -> const uint16_t* {
     id = __builtin_amdgcn_readfirstlane(id);
@@ -220,27 +240,32 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
   const int wave_min_pos = ctx + t0 + (wave * C::RW) / G;
   const int s_diag = (wave_min_pos + 1) / C::KSTEP;
 
-  // one step: S^T for 32 keys, online softmax, O^T += V^T P^T
-  auto compute = [&](int s, int buf, auto mask_tag) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    // ---- S^T = K Q^T for the step's two 16-key tiles
-    f32x4 sacc[2][C::NT];
+  // S^T = K Q^T for a step's two 16-key tiles, K from LDS buffer buf
+  auto scores = [&](int buf, f32x4 (&sacc)[2][C::NT]) __attribute__((always_inline)) {
+    u32x4 ka[2][C::DS];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ds = 0; ds < C::DS; ++ds)
+        ka[kt][ds] =
+            *reinterpret_cast<const u32x4*>(&Ks[buf][(kt * 16 + lr) * C::LROW + ds * 32 + lq * 8]);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int nt = 0; nt < C::NT; ++nt) sacc[kt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int ds = 0; ds < C::DS; ++ds)
 #pragma unroll
-      for (int ds = 0; ds < C::DS; ++ds) {
-        const u32x4 a =
-            *reinterpret_cast<const u32x4*>(&Ks[buf][(kt * 16 + lr) * C::LROW + ds * 32 + lq * 8]);
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt) sacc[kt][nt] = mfma16x16x32(a, qt[nt][ds], sacc[kt][nt]);
-      }
-    }
+        for (int nt = 0; nt < C::NT; ++nt) sacc[kt][nt] = mfma16x16x32(ka[kt][ds], qt[nt][ds], sacc[kt][nt]);
+  };
 
-    // ---- online softmax; lane holds row lr of tile nt, keys kt*16 + 4*lq + i
+  // online softmax of step s and O^T += V^T P^T with V from LDS buffer buf
+  auto softmax_pv = [&](int s, const f32x4 (&sacc)[2][C::NT], int buf, auto mask_tag)
+      __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    // lane holds row lr of tile nt, keys kt*16 + 4*lq + i
     const int key0 = s * C::KSTEP;
     float x[C::NT][8];
     float mloc[C::NT];
@@ -255,9 +280,8 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
           if constexpr (MASK) v = key0 + kt * 16 + lq * 4 + i <= row_pos[nt] ? v : -INFINITY;
           x[nt][kt * 4 + i] = v;
         }
-      float m = x[nt][0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) m = fmaxf(m, x[nt][e]);
+      const float m = fmaxf(fmaxf(fmaxf(x[nt][0], x[nt][1]), fmaxf(x[nt][2], x[nt][3])),
+                            fmaxf(fmaxf(x[nt][4], x[nt][5]), fmaxf(x[nt][6], x[nt][7])));
       mloc[nt] = group4_max(m) * scale_log2;   // scale > 0 keeps the order
       grow |= mloc[nt] > m_thr[nt];
     }
@@ -288,34 +312,48 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
       }
       pb[nt] = u32x4{pw[0], pw[1], pw[2], pw[3]};
     }
-
-    // ---- O^T += V^T P^T: lane (lq, lr) reads head dim dt*16 + lr at the
-    // eight V^T positions of its P^T key slots
+    // lane (lq, lr) reads head dim dt*16 + lr at the eight V^T positions of
+    // its P^T key slots
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(&Vt[buf][(dt * 16 + lr) * C::VROW + lq * 8]);
+      const u32x4 va = *reinterpret_cast<const u32x4*>(&Vt[buf][(dt * 16 + lr) * C::VROW + lq * 8]);
 #pragma unroll
-      for (int nt = 0; nt < C::NT; ++nt) acc[dt][nt] = mfma16x16x32(a, pb[nt], acc[dt][nt]);
+      for (int nt = 0; nt < C::NT; ++nt) acc[dt][nt] = mfma16x16x32(va, pb[nt], acc[dt][nt]);
     }
   };
 
-  // Pipeline: step s + 1's K/V are loaded while step s computes and stored
-  // to the other LDS buffer after it; the block ids of a step are loaded one
-  // step before its K/V, so no K/V load waits on a table read.  Steps before
-  // s_diag run without the causal mask, the rest with it (two loops: a
-  // branch between the variants inside one loop costs registers); each
-  // iteration has one barrier, so every wave meets the same barriers.
+  // Pipeline over a ring of three LDS buffers: while the VALU runs step s's
+  // softmax, the MFMA pipe already computes step s + 1's scores; step s + 2's
+  // K/V are loaded meanwhile and stored to the third buffer after it.  The
+  // block ids of a step are loaded one step before its K/V, so no K/V load
+  // waits on a table read.  Steps before s_diag run without the causal
+  // mask, the rest with it (two loops: a branch between the variants inside
+  // one loop costs registers); each iteration has one barrier, so every
+  // wave meets the same barriers.
   u32x4 kreg[C::KLOADS], vreg[2];
   load_step(0, step_ids(0), kreg, vreg);
   store_step(0, kreg, vreg);
-  int2 ids_next = step_ids(1);
+  load_step(1, step_ids(1), kreg, vreg);
+  store_step(1, kreg, vreg);
+  int2 ids_next = step_ids(2);
   __syncthreads();
+  f32x4 s_cur[2][C::NT], s_next[2][C::NT];
+  scores(0, s_cur);
+  int b_cur = 0;  // LDS buffer of step s
   auto iteration = [&](int s, auto mask_tag) __attribute__((always_inline)) {
+    const int b_next = b_cur == kPrefillBufs - 1 ? 0 : b_cur + 1;
+    const int b_load = b_next == kPrefillBufs - 1 ? 0 : b_next + 1;
     const int2 ids = ids_next;
-    ids_next = step_ids(s + 2);
-    load_step(s + 1, ids, kreg, vreg);   // past the last step: clamped, never stored
-    compute(s, s & 1, mask_tag);
-    if (s + 1 < nsteps) store_step((s + 1) & 1, kreg, vreg);
+    ids_next = step_ids(s + 3);
+    load_step(s + 2, ids, kreg, vreg);   // past the last step: clamped, never stored
+    scores(b_next, s_next);              // past the last step: stale buffer, never used
+    softmax_pv(s, s_cur, b_cur, mask_tag);
+    if (s + 2 < nsteps) store_step(b_load, kreg, vreg);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int nt = 0; nt < C::NT; ++nt) s_cur[kt][nt] = s_next[kt][nt];
+    b_cur = b_next;
     __syncthreads();
   };
   int s = 0;
@@ -342,15 +380,19 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
 }
 
 template <int D>
-static bool launch_prefill(int G, dim3 grid, hipStream_t s, uint16_t* out, float* lse,
-                           const uint16_t* q, const int* qsl, const uint16_t* cache, int nb,
-                           const int* bt, int mbps, const int* sl, int msl, int hkv, float sc) {
+static bool launch_prefill(int G, int max_query_len, int B, hipStream_t s, uint16_t* out,
+                           float* lse, const uint16_t* q, const int* qsl, const uint16_t* cache,
+                           int nb, const int* bt, int mbps, const int* sl, int msl, int hkv,
+                           float sc) {
 #define PA_PREFILL_CASE(GG)                                                                     \
-  case GG:                                                                                      \
-    grid.x = (grid.x + PrefillCfg<D, GG>::TQ - 1) / PrefillCfg<D, GG>::TQ;                      \
-    hipLaunchKernelGGL((prefill_chunk_kernel<D, GG>), grid, dim3(kPrefillThreads), 0, s,        \
-                       out, lse, q, qsl, cache, nb, bt, mbps, sl, msl, hkv, sc);                \
-    return true;
+  case GG: {                                                                                    \
+    const int tiles = (max_query_len + PrefillCfg<D, GG>::TQ - 1) / PrefillCfg<D, GG>::TQ;      \
+    const int groups = B * hkv;                                                                 \
+    hipLaunchKernelGGL((prefill_chunk_kernel<D, GG>), dim3(tiles * groups),                     \
+                       dim3(kPrefillThreads), 0, s, out, lse, q, qsl, cache, nb, bt, mbps, sl,  \
+                       msl, hkv, sc, tiles, groups);                                            \
+    return true;                                                                                \
+  }
   switch (G) {
     PA_PREFILL_CASE(1)
     PA_PREFILL_CASE(2)
@@ -406,17 +448,20 @@ extern "C" int pa_prefill_chunk(void* out, float* lse_out, const void* query,
     return fail(PA_EINVAL, "pa_prefill_chunk: int/float arrays must be 4-byte aligned");
   if (num_blocks == 0) return fail(PA_EINVAL, "pa_prefill_chunk: empty pool");
   if (num_kv_heads > 65535 || B > 65535) return fail(PA_ENOTSUP, "pa_prefill_chunk: grid too large");
-  dim3 grid(max_query_len, num_kv_heads, B);  // x is divided by the tile size at launch
+  if (max_blocks_per_seq > (1 << 28))
+    return fail(PA_ENOTSUP, "pa_prefill_chunk: max_blocks_per_seq %d too large", max_blocks_per_seq);
+  if (int64_t(max_query_len) * num_kv_heads * B > 0x7FFFFFFF)
+    return fail(PA_ENOTSUP, "pa_prefill_chunk: grid too large");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   auto o = static_cast<uint16_t*>(out);
   auto q = static_cast<const uint16_t*>(query);
   auto c = static_cast<const uint16_t*>(kv_cache);
   const float sl2 = scale * kLog2eP;
   bool ok = head_size == 64
-                ? launch_prefill<64>(G, grid, s, o, lse_out, q, query_start_loc, c, num_blocks,
+                ? launch_prefill<64>(G, max_query_len, B, s, o, lse_out, q, query_start_loc, c, num_blocks,
                                      block_tables, max_blocks_per_seq, seq_lens, max_seq_len,
                                      num_kv_heads, sl2)
-                : launch_prefill<128>(G, grid, s, o, lse_out, q, query_start_loc, c, num_blocks,
+                : launch_prefill<128>(G, max_query_len, B, s, o, lse_out, q, query_start_loc, c, num_blocks,
                                       block_tables, max_blocks_per_seq, seq_lens, max_seq_len,
                                       num_kv_heads, sl2);
   if (!ok) return fail(PA_ENOTSUP, "pa_prefill_chunk: group size %d", G);
