@@ -109,6 +109,27 @@ def test_decode_edge_shapes_planned(name, kw, P):
     run_decode_case(inputs.custom(kind="decode", **kw), partition_size=P, use_plan=True)
 
 
+# Many short ragged sequences: enough (sequence, KV head[, partition]) items
+# that the launch uses small workgroups (4 waves from 2 items per compute
+# unit, 2 waves from 8), with tails and one-token sequences among them.
+MANY = [
+    ("many-g8-d64-b300", 300, 32, 4, 64),     # 1 200 items: 4-wave workgroups
+    ("many-g8-d64-b600", 600, 32, 4, 64),     # 2 400 items: 2-wave workgroups
+    ("many-g4-d128-b600", 600, 32, 8, 128),   # 4 800 items
+]
+
+
+@pytest.mark.parametrize("name,B,hq,hkv,D", MANY, ids=[m[0] for m in MANY])
+@pytest.mark.parametrize("P,use_plan", [(0, True), (0, False), (32, True)])
+def test_decode_many_items(name, B, hq, hkv, D, P, use_plan):
+    rng = np.random.default_rng(B + D)
+    lens = rng.integers(1, 97, B)
+    lens[:3] = (1, 16, 17)
+    d = inputs.custom(kind="decode", seq_lens=tuple(int(x) for x in lens), num_q_heads=hq,
+                      num_kv_heads=hkv, head_size=D, seed=B)
+    run_decode_case(d, partition_size=P, use_plan=use_plan)
+
+
 def test_zero_length_row():
     GpuSide, _ = _gpu()
     d = inputs.custom(kind="decode", seq_lens=(0, 20, 0), num_q_heads=8, num_kv_heads=2,
