@@ -164,6 +164,29 @@ def test_llama3_workload_sampled():
     run_decode_case(d, partition_size=512, seqs=seqs[:3], use_plan=False)
 
 
+def test_long_context_workload_sampled():
+    """Full-size long-context workload (16 sequences of 32K-131K tokens, a
+    5.4 GB pool), split-K 1024 with the plan, in the launch bench.py times.
+    Both pools hold the sampled sequences (the longest and the shortest); the
+    GPU's other rows read NaN poison and are not compared."""
+    GpuSide, _ = _gpu()
+    d = inputs.draw(4)
+    L = d.seq_lens
+    seqs = sorted({int(np.argmax(L)), int(np.argmin(L))})
+    o = OracleSide(d, seqs=seqs)
+    g = GpuSide(d, fill=False)
+    g.fill(seqs)
+    check_tables(o, g)
+    out, lse = g.decode(partition_size=1024, use_plan=True)
+    ref, ref_lse = o.decode(seqs=seqs)
+    got = out_f64(out)[seqs]
+    assert np.all(np.isfinite(got))
+    err = np.max(np.abs(got - ref[seqs]))
+    lerr = np.max(np.abs(lse.cpu().numpy().astype(np.float64)[seqs] - ref_lse[seqs]))
+    print("long-context max err", err, "lse", lerr)
+    assert err <= TOL["bf16"] and lerr <= TOL["bf16"]
+
+
 def test_unit_values_give_unit_output():
     """V == 1 everywhere: softmax rows sum to one, so every output is 1."""
     GpuSide, _ = _gpu()
