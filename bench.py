@@ -4,16 +4,18 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1]
 
 One step is the device half of a decode step of the engine for a batch of
-sequences: pa_reshape_and_cache writes the new token's key/value of every
-sequence into its cache slot, then pa_decode attends from that token over the
-whole cached context (one launch; with split-K the partials are merged inside
-the same launch).  Host metadata (block tables from the free_block_queue
-allocator, slot mapping, the decode work plan) is built once before timing,
-as the engine's CPU side does ahead of the step, and its cost is reported
-separately.  The steps are replayed from a captured HIP graph, as the pages'
-engine replays pre-recorded graphs to cut launch overhead; the decode
-kernel's own duration is timed the same way from a graph of decode launches
-alone (HIP events around the replays, on the stream the kernels run on).
+sequences: the new token's key/value of every sequence is written into its
+cache slot, and attention runs from that token over the whole cached
+context.  By default both happen in one launch (pa_decode_append; with
+split-K the partials are merged inside the same launch); --unfused runs
+pa_reshape_and_cache and pa_decode as two launches.  Host metadata (block
+tables from the free_block_queue allocator, slot mapping, the decode work
+plan) is built once before timing, as the engine's CPU side does ahead of
+the step, and its cost is reported separately.  The steps are replayed from
+a captured HIP graph, as the pages' engine replays pre-recorded graphs to cut
+launch overhead; the decode kernel's own duration is timed the same way from
+a graph of its launches alone (HIP events around the replays, on the stream
+the kernels run on).
 
 Inputs are seeded synthetic draws (paged_attention_kv_block_amd.inputs) that
 are resident in HBM before timing.  The default workload is the
@@ -43,7 +45,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 METRIC = "paged-attn decode KV GB/s (% of HBM peak) + context-tokens/s, 1 GPU"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+TRAFFIC_FILES = {False: os.path.join(ROOT, "profiles", "decode_append_traffic.json"),
+                 True: os.path.join(ROOT, "profiles", "decode_traffic.json")}
 DECODE_SOURCES = ["paged_attention_kv_block_amd/csrc/pa_decode.hip",
                   "paged_attention_kv_block_amd/csrc/pa_common.h"]
 
@@ -80,17 +83,18 @@ def decode_bytes(wl, seq_lens) -> int:
 
 
 def cache_write_bytes(wl) -> int:
-    """pa_reshape_and_cache of one new token per sequence: read K and V rows,
-    write them, read the slot."""
+    """Writing one new token per sequence into the cache: read its K and V
+    rows, write them."""
     row = wl.num_kv_heads * wl.head_size * wl.dtype_bytes
-    return wl.num_seqs * (4 * row + 8)
+    return wl.num_seqs * 4 * row
 
 
-def load_traffic(kernel_hash: str, launches_per_step: int):
-    """HBM bytes per decode launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source."""
+def load_traffic(kernel_hash: str, unfused: bool):
+    """HBM bytes per launch of the timed decode kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source
+    and workload."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILES[unfused]) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -328,6 +332,9 @@ def main(argv=None):
                     help="total size of rotated pool copies (defeats the 256 MB Infinity Cache)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="decode step as two launches (pa_reshape_and_cache, pa_decode) "
+                         "instead of pa_decode_append")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     a = ap.parse_args(argv)
@@ -409,12 +416,23 @@ def main(argv=None):
     scale = float(wl.scale)
     torch.cuda.synchronize()
 
+    nk3 = nk.view(B, Hkv, D)
+    nv3 = nv.view(B, Hkv, D)
+
     def step(pool):
-        ops.reshape_and_cache(nk, nv, slots_dev, pool)
-        ops.decode(out, q, pool, bt_dev, sl_dev, msl, scale, P, ws, plan=plan_dev)
+        if a.unfused:
+            ops.reshape_and_cache(nk, nv, slots_dev, pool)
+            ops.decode(out, q, pool, bt_dev, sl_dev, msl, scale, P, ws, plan=plan_dev)
+        else:   # pa_decode_append: cache write + decode in one launch
+            ops.decode(out, q, pool, bt_dev, sl_dev, msl, scale, P, ws, plan=plan_dev,
+                       new_key=nk3, new_value=nv3)
 
     def decode_only(pool):
-        ops.decode(out, q, pool, bt_dev, sl_dev, msl, scale, P, ws, plan=plan_dev)
+        if a.unfused:
+            ops.decode(out, q, pool, bt_dev, sl_dev, msl, scale, P, ws, plan=plan_dev)
+        else:
+            ops.decode(out, q, pool, bt_dev, sl_dev, msl, scale, P, ws, plan=plan_dev,
+                       new_key=nk3, new_value=nv3)
 
     def capture(fn, n):
         """One HIP graph of n calls of fn, call i on pool copy i % R (the pages'
@@ -459,10 +477,11 @@ def main(argv=None):
     ctx = int(seq_lens.sum())
     dbytes = decode_bytes(wl, seq_lens)
     step_bytes = dbytes + cache_write_bytes(wl)
+    kbytes = dbytes if a.unfused else step_bytes   # the timed kernel's own bytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    achieved = dbytes / (dec_us * 1e-6) / 1e9
+    achieved = kbytes / (dec_us * 1e-6) / 1e9
     khash = source_hash(DECODE_SOURCES)
-    traffic = load_traffic(khash, 1)
+    traffic = load_traffic(khash, a.unfused) if a.workload == 1 and P == 0 else None
 
     res = {
         "metric": METRIC,
@@ -487,14 +506,15 @@ def main(argv=None):
         "context_tokens_per_s": round(ctx / (ms_step * 1e-3), 1),
         "host_metadata_us": round(host_us, 1),
         "roofline": {
-            "kernel": "pa_decode (decode_kernel)",
+            "kernel": ("pa_decode (decode_kernel)" if a.unfused else
+                       "pa_decode_append (decode_kernel, cache write fused)"),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": dbytes,
+            "algorithmic_bytes_per_launch": kbytes,
             "avg_launch_us": round(dec_us, 3),
             "kernel_source_hash": khash,
         },

@@ -223,8 +223,8 @@ int pa_decode_plan(const int32_t* seq_lens, int32_t B, int32_t max_seq_len,
  *                pa_decode_workspace_init (or any zero fill) before first
  *                use.  Two pa_decode calls sharing a workspace must not run
  *                concurrently.
- * The kernel is persistent: it launches at most as many workgroups as fit
- * on the device and each walks the work items.
+ * With a plan the launch has one workgroup per work item; without one, a
+ * grid of a few times the resident workgroups walks the items.
  * Supported: block_size 16; head_size 64 or 128; H_q % H_kv == 0 with
  * G = H_q/H_kv in {1, 2, 4, 8} (and 16 for head_size 64). */
 int pa_decode(void* out, float* lse_out, const void* query,
@@ -235,6 +235,29 @@ int pa_decode(void* out, float* lse_out, const void* query,
               int32_t block_size, float scale, int32_t partition_size,
               const int32_t* plan, int32_t plan_entries, void* workspace,
               size_t workspace_bytes, int32_t dtype, void* stream);
+
+/* The device half of a decode step in one launch: the new token of every
+ * sequence is written into the cache and attended to with the others.  The
+ * result, the cache and the errors equal pa_reshape_and_cache of the new
+ * tokens (each at its position seq_len - 1, in the slot the block table
+ * gives: block_tables[b][(seq_len - 1) / 16] * 16 + (seq_len - 1) % 16)
+ * followed by pa_decode with the same arguments ("Inside vLLM", "LLM
+ * Engine constructor": the new K/V are bound into the paged cache before
+ * attention reads it).
+ *   new_key, new_value  [B][H_kv][D] dtype, device, 16-byte aligned: the K
+ *                and V of token seq_len[b] - 1 of each sequence (unused
+ *                for seq_len 0).
+ *   kv_cache     written at those slots only; a block id out of range is
+ *                read as block 0 (as in pa_decode) and not written.
+ * All other arguments as pa_decode. */
+int pa_decode_append(void* out, float* lse_out, const void* query,
+                     const void* new_key, const void* new_value, void* kv_cache,
+                     int32_t num_blocks, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t B,
+                     int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_size, int32_t block_size, float scale,
+                     int32_t partition_size, const int32_t* plan, int32_t plan_entries,
+                     void* workspace, size_t workspace_bytes, int32_t dtype, void* stream);
 
 /* Chunked prefill ("Im Inneren von vLLM", "Fortgeschrittene Funktionen":
  * long prompts are split into chunks; "Inside vLLM", "Generate function":

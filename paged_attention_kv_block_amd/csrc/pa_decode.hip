@@ -411,10 +411,50 @@ struct DecodeParams {
   float* ws_m;
   float* ws_l;
   float* ws_o;
+  const void* new_k;      // append mode: the new token's K/V per sequence, [B][H_kv][D];
+  const void* new_v;      // nullptr: the cache already holds token L - 1
   int num_blocks, max_blocks_per_seq, max_seq_len, num_kv_heads, B;
   int part_blocks, max_parts, num_items;
   float scale_log2;
 };
+
+// Append mode: the new token (position L - 1 of sequence b, KV head g)
+// replaces its row of the block held in registers and is stored to the
+// cache at the same place, so the call equals pa_reshape_and_cache of the
+// token followed by pa_decode.  A block id out of range is read as block 0
+// and not written.
+template <class C>
+__device__ __forceinline__ void append_new_token(BlockRegs<C>& rg, const DecodeParams& a, int b,
+                                                 int g, int row, int phys, int64_t block_bytes,
+                                                 int64_t tile_bytes, int lane, int half, int col) {
+  const int64_t src = (int64_t(b) * a.num_kv_heads + g) * C::RB;
+  const bool store = phys >= 0 && phys < a.num_blocks;
+  uint8_t* kbase = const_cast<uint8_t*>(a.cache) + int64_t(store ? phys : 0) * block_bytes +
+                   int64_t(g) * tile_bytes;
+  uint8_t* vbase = kbase + int64_t(a.num_kv_heads) * tile_bytes;
+  const u32x4* nk = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.new_k) + src);
+  const uint32_t* nv = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.new_v) + src);
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int v = i * kWave + lane;
+    if (v / C::CPR == row) {
+      const u32x4 x = nk[v % C::CPR];
+      rg.k[i] = x;
+      if (store) reinterpret_cast<u32x4*>(kbase)[v] = x;
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < C::ROWS; ++rr) {
+    if (v_row<C>(rr, half) == row) {
+#pragma unroll
+      for (int w = 0; w < C::VW; ++w) {
+        const uint32_t x = nv[col * C::VW + w];
+        rg.v[rr][w] = x;
+        if (store) reinterpret_cast<uint32_t*>(vbase)[row * (C::RB / 4) + col * C::VW + w] = x;
+      }
+    }
+  }
+}
 
 // LDS of one workgroup: K tiles during the block loop (afterwards reused for
 // the per-wave outputs and the merge weights), P, and the merge state.
@@ -434,7 +474,7 @@ struct DecodeSmem {
 
 // One work item: KV head g of sequence b, partition `part` (blocks
 // [part * pb, min((part + 1) * pb, nblk))).  Called by the whole workgroup.
-template <int D, int G, bool BF16, int NW>
+template <int D, int G, bool BF16, int NW, bool APPEND>
 __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D, G, BF16, NW>& sm,
                                             int b, int g, int part, int L, int nblk, int pb,
                                             int nparts) {
@@ -515,9 +555,12 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
                                   num_kv_heads, tile_bytes, lane, half, col);
     // Only the sequence's last block can be partial; it is the last block of
     // the wave that owns it and is processed after the loop, so the loop
-    // body needs no masking.
-    const int tail_valid = L - (first + (nmine - 1) * NW) * 16;
-    const int nfull = tail_valid < 16 ? nmine - 1 : nmine;
+    // body needs no masking.  In append mode that block (partial or not)
+    // also takes the new token there.
+    const int j_last = first + (nmine - 1) * NW;
+    const int tail_valid = L - j_last * 16;
+    const bool seq_last = APPEND && j_last == nblk - 1;
+    const int nfull = (tail_valid < 16 || seq_last) ? nmine - 1 : nmine;
     for (int k0 = 0; k0 < nfull; k0 += PD) {
       const int ids_after = id_group(k0 + 2 * PD);
 #pragma unroll
@@ -531,9 +574,15 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
       ids_next = ids_after;
     }
     // Loads past the last block were clamped to it, so buf[0] now holds it.
-    if (nfull < nmine)
-      process_block<D, G, BF16, true>(buf[0], tail_valid, q, st, kt_lds, p_lds, sm.alpha[wave],
-                                      scale_log2, r);
+    if (nfull < nmine) {
+      if constexpr (APPEND) {
+        if (seq_last)
+          append_new_token<C>(buf[0], a, b, g, (L - 1) & 15, bt_row[nblk - 1], block_bytes,
+                              tile_bytes, lane, half, col);
+      }
+      process_block<D, G, BF16, true>(buf[0], min(tail_valid, 16), q, st, kt_lds, p_lds,
+                                      sm.alpha[wave], scale_log2, r);
+    }
   }
 
   // ---- merge: this wave's denominator, then the waves of the workgroup
@@ -726,7 +775,7 @@ constexpr int decode_min_waves() { return NW == 4 && BF16 && !(D == 64 && G == 1
 template <int D, int G, bool BF16, int NW>
 constexpr int decode_max_waves() { return NW == 8 ? 2 : 8; }
 
-template <int D, int G, bool BF16, int NW>
+template <int D, int G, bool BF16, int NW, bool APPEND>
 __global__ __launch_bounds__(NW * kWave)
 __attribute__((amdgpu_waves_per_eu(decode_min_waves<D, G, BF16, NW>(), decode_max_waves<D, G, BF16, NW>())))
 void decode_kernel(const DecodeParams a) {
@@ -750,7 +799,7 @@ void decode_kernel(const DecodeParams a) {
     const int pb = a.part_blocks > 0 ? a.part_blocks : (nblk > 0 ? nblk : 1);
     const int nparts = (nblk + pb - 1) / pb;
     if (part > 0 && part >= nparts) continue;
-    decode_item<D, G, BF16, NW>(a, sm, b, g, part, L, nblk, pb, nparts);
+    decode_item<D, G, BF16, NW, APPEND>(a, sm, b, g, part, L, nblk, pb, nparts);
     __syncthreads();  // LDS is reused by the next item
   }
 }
@@ -764,10 +813,10 @@ __global__ void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-// Workgroups that fit on the device at once for a kernel (cached per device
-// and kernel): the persistent grid never exceeds this.
-template <int NW, class K>
-static int resident_workgroups(K kernel) {
+// Workgroups of one decode kernel variant that fit on the device at once
+// (cached per device and variant): the persistent grid never exceeds this.
+template <int D, int G, bool BF16, int NW, bool APPEND>
+static int resident_workgroups() {
   constexpr int kMaxDev = 64;
   static int cached[kMaxDev] = {0};
   int dev = 0;
@@ -776,8 +825,9 @@ static int resident_workgroups(K kernel) {
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, NW * kWave, 0) !=
-          hipSuccess || per_cu <= 0)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<D, G, BF16, NW, APPEND>,
+                                                   NW * kWave, 0) != hipSuccess ||
+      per_cu <= 0)
     per_cu = 1;
   cached[dev] = cus * per_cu;
   if (std::getenv("PA_DEBUG"))
@@ -785,15 +835,24 @@ static int resident_workgroups(K kernel) {
   return cached[dev];
 }
 
-template <int D, int G, bool BF16, int NW>
-static void launch_decode_nw(const DecodeParams& a, hipStream_t s) {
-  auto k = decode_kernel<D, G, BF16, NW>;
+template <int D, int G, bool BF16, int NW, bool APPEND>
+static void launch_decode_variant(const DecodeParams& a, hipStream_t s) {
+  auto k = decode_kernel<D, G, BF16, NW, APPEND>;
   // With a plan every item is real: one workgroup each, so the hardware
   // dispatcher balances them and overlaps one item's merge with another's
   // loads.  Without one, a persistent grid skips the empty virtual items.
   const int grid = a.plan ? a.num_items
-                          : std::max(1, std::min(a.num_items, 4 * resident_workgroups<NW>(k)));
+                          : std::max(1, std::min(a.num_items,
+                                                 4 * resident_workgroups<D, G, BF16, NW, APPEND>()));
   hipLaunchKernelGGL(k, dim3(grid), dim3(NW * kWave), 0, s, a);
+}
+
+template <int D, int G, bool BF16, int NW>
+static void launch_decode_nw(const DecodeParams& a, hipStream_t s) {
+  if (a.new_k)
+    launch_decode_variant<D, G, BF16, NW, true>(a, s);
+  else
+    launch_decode_variant<D, G, BF16, NW, false>(a, s);
 }
 
 // Compute units of the current device (cached per device).
@@ -937,51 +996,56 @@ extern "C" int pa_decode_plan(const int32_t* seq_lens, int32_t B, int32_t max_se
   return PA_OK;
 }
 
-extern "C" int pa_decode(void* out, float* lse_out, const void* query, const void* kv_cache,
-                         int32_t num_blocks, const int32_t* block_tables,
-                         int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t B,
-                         int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
-                         int32_t head_size, int32_t block_size, float scale,
-                         int32_t partition_size, const int32_t* plan, int32_t plan_entries,
-                         void* workspace, size_t workspace_bytes, int32_t dtype, void* stream) {
+static int decode_call(const char* fn, void* out, float* lse_out, const void* query,
+                       const void* new_key, const void* new_value, const void* kv_cache,
+                       int32_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* seq_lens, int32_t B, int32_t max_seq_len,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
+                       int32_t block_size, float scale, int32_t partition_size,
+                       const int32_t* plan, int32_t plan_entries, void* workspace,
+                       size_t workspace_bytes, int32_t dtype, void* stream) {
   if (B < 0 || num_blocks < 0 || max_seq_len < 0 || max_blocks_per_seq < 0 || plan_entries < 0)
-    return fail(PA_EINVAL, "pa_decode: negative size");
+    return fail(PA_EINVAL, "%s: negative size", fn);
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
-    return fail(PA_EINVAL, "pa_decode: H_q %d not a multiple of H_kv %d", num_q_heads, num_kv_heads);
-  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_EINVAL, "pa_decode: unknown dtype %d", dtype);
-  if (block_size != kBlockSize) return fail(PA_ENOTSUP, "pa_decode: block_size %d (only 16)", block_size);
+    return fail(PA_EINVAL, "%s: H_q %d not a multiple of H_kv %d", fn, num_q_heads, num_kv_heads);
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_EINVAL, "%s: unknown dtype %d", fn, dtype);
+  if (block_size != kBlockSize) return fail(PA_ENOTSUP, "%s: block_size %d (only 16)", fn, block_size);
   if (head_size != 64 && head_size != 128)
-    return fail(PA_ENOTSUP, "pa_decode: head_size %d (64 or 128)", head_size);
+    return fail(PA_ENOTSUP, "%s: head_size %d (64 or 128)", fn, head_size);
   if (partition_size < 0 || partition_size % kBlockSize)
-    return fail(PA_EINVAL, "pa_decode: partition_size %d must be a multiple of 16", partition_size);
+    return fail(PA_EINVAL, "%s: partition_size %d must be a multiple of 16", fn, partition_size);
   if (int64_t(max_blocks_per_seq) * kBlockSize < max_seq_len)
-    return fail(PA_EINVAL, "pa_decode: max_seq_len %d exceeds the table (%d blocks)", max_seq_len,
+    return fail(PA_EINVAL, "%s: max_seq_len %d exceeds the table (%d blocks)", fn, max_seq_len,
                 max_blocks_per_seq);
-  if (!(scale == scale)) return fail(PA_EINVAL, "pa_decode: scale is NaN");
+  if (!(scale == scale)) return fail(PA_EINVAL, "%s: scale is NaN", fn);
   if (B == 0) return PA_OK;
   if (!out || !query || !block_tables || !seq_lens || (!kv_cache && num_blocks > 0))
-    return fail(PA_EINVAL, "pa_decode: NULL pointer");
+    return fail(PA_EINVAL, "%s: NULL pointer", fn);
   if ((uintptr_t(out) | uintptr_t(query) | uintptr_t(kv_cache)) & 15)
-    return fail(PA_EINVAL, "pa_decode: out/query/cache must be 16-byte aligned");
+    return fail(PA_EINVAL, "%s: out/query/cache must be 16-byte aligned", fn);
   if ((uintptr_t(block_tables) | uintptr_t(seq_lens) | uintptr_t(lse_out) | uintptr_t(plan)) & 3)
-    return fail(PA_EINVAL, "pa_decode: int/float arrays must be 4-byte aligned");
+    return fail(PA_EINVAL, "%s: int/float arrays must be 4-byte aligned", fn);
+  if ((new_key == nullptr) != (new_value == nullptr))
+    return fail(PA_EINVAL, "%s: new_key and new_value go together", fn);
+  if ((uintptr_t(new_key) | uintptr_t(new_value)) & 15)
+    return fail(PA_EINVAL, "%s: new_key/new_value must be 16-byte aligned", fn);
   if (num_blocks == 0 && max_seq_len > 0)
-    return fail(PA_EINVAL, "pa_decode: empty pool but max_seq_len %d", max_seq_len);
+    return fail(PA_EINVAL, "%s: empty pool but max_seq_len %d", fn, max_seq_len);
   if (plan && (B > 65535 || plan_entries == 0))
-    return fail(PA_EINVAL, "pa_decode: a plan needs B <= 65535 and at least one entry");
+    return fail(PA_EINVAL, "%s: a plan needs B <= 65535 and at least one entry", fn);
   const int G = num_q_heads / num_kv_heads;
   const int64_t P = parts_for(max_seq_len, partition_size);
-  if (P > 65535) return fail(PA_EINVAL, "pa_decode: too many partitions (%lld)", (long long)P);
+  if (P > 65535) return fail(PA_EINVAL, "%s: too many partitions (%lld)", fn, (long long)P);
   const int64_t items = (plan ? int64_t(plan_entries) : int64_t(B) * P) * num_kv_heads;
-  if (items > 0x7FFFFFFF) return fail(PA_ENOTSUP, "pa_decode: too many work items");
+  if (items > 0x7FFFFFFF) return fail(PA_ENOTSUP, "%s: too many work items", fn);
   const size_t need =
       pa_decode_workspace_bytes(B, num_q_heads, num_kv_heads, head_size, max_seq_len, partition_size);
   if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(PA_EINVAL, "pa_decode: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    return fail(PA_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes);
   if (need > 0 && (uintptr_t(workspace) & 255))
-    return fail(PA_EINVAL, "pa_decode: workspace must be 256-byte aligned");
+    return fail(PA_EINVAL, "%s: workspace must be 256-byte aligned", fn);
   if (P > 1 && int64_t(B) * num_kv_heads > kCounterCap)
-    return fail(PA_ENOTSUP, "pa_decode: split-K supports B * H_kv <= %lld", (long long)kCounterCap);
+    return fail(PA_ENOTSUP, "%s: split-K supports B * H_kv <= %lld", fn, (long long)kCounterCap);
 
   DecodeParams a{};
   a.out = out;
@@ -997,6 +1061,8 @@ extern "C" int pa_decode(void* out, float* lse_out, const void* query, const voi
   a.num_kv_heads = num_kv_heads;
   a.B = B;
   a.scale_log2 = scale * kLog2e;
+  a.new_k = new_key;
+  a.new_v = new_value;
   a.part_blocks = P > 1 ? partition_size / kBlockSize : 0;
   a.max_parts = int(P);
   a.num_items = int(items);
@@ -1014,8 +1080,38 @@ extern "C" int pa_decode(void* out, float* lse_out, const void* query, const voi
     ok = head_size == 64 ? dispatch_g<64, true>(G, a, st) : dispatch_g<128, true>(G, a, st);
   else
     ok = head_size == 64 ? dispatch_g<64, false>(G, a, st) : dispatch_g<128, false>(G, a, st);
-  if (!ok) return fail(PA_ENOTSUP, "pa_decode: group size %d with head_size %d", G, head_size);
+  if (!ok) return fail(PA_ENOTSUP, "%s: group size %d with head_size %d", fn, G, head_size);
   const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(PA_EHIP, "pa_decode: launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(PA_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return PA_OK;
+}
+
+extern "C" int pa_decode(void* out, float* lse_out, const void* query, const void* kv_cache,
+                         int32_t num_blocks, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t B,
+                         int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_size, int32_t block_size, float scale,
+                         int32_t partition_size, const int32_t* plan, int32_t plan_entries,
+                         void* workspace, size_t workspace_bytes, int32_t dtype, void* stream) {
+  return decode_call("pa_decode", out, lse_out, query, nullptr, nullptr, kv_cache, num_blocks,
+                     block_tables, max_blocks_per_seq, seq_lens, B, max_seq_len, num_q_heads,
+                     num_kv_heads, head_size, block_size, scale, partition_size, plan,
+                     plan_entries, workspace, workspace_bytes, dtype, stream);
+}
+
+extern "C" int pa_decode_append(void* out, float* lse_out, const void* query,
+                                const void* new_key, const void* new_value, void* kv_cache,
+                                int32_t num_blocks, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t B,
+                                int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_size, int32_t block_size, float scale,
+                                int32_t partition_size, const int32_t* plan,
+                                int32_t plan_entries, void* workspace, size_t workspace_bytes,
+                                int32_t dtype, void* stream) {
+  if (B > 0 && (!new_key || !new_value))
+    return fail(PA_EINVAL, "pa_decode_append: NULL new_key/new_value");
+  return decode_call("pa_decode_append", out, lse_out, query, new_key, new_value, kv_cache,
+                     num_blocks, block_tables, max_blocks_per_seq, seq_lens, B, max_seq_len,
+                     num_q_heads, num_kv_heads, head_size, block_size, scale, partition_size,
+                     plan, plan_entries, workspace, workspace_bytes, dtype, stream);
 }

@@ -47,6 +47,9 @@ SIGNATURES = {
     "pa_decode": (_c_int, [_vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _vp, _c_i32, _c_i32,
                            _c_i32, _c_i32, _c_i32, _c_i32, _f, _c_i32, _vp, _c_i32, _vp, _c_sz,
                            _c_i32, _vp]),
+    "pa_decode_append": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _vp,
+                                  _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _f, _c_i32,
+                                  _vp, _c_i32, _vp, _c_sz, _c_i32, _vp]),
     "pa_prefill_chunk": (_c_int, [_vp, _vp, _vp, _vp, _c_i32, _c_i32, _vp, _c_i32, _vp, _c_i32,
                                   _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _f,
                                   _c_i32, _vp]),
@@ -265,12 +268,16 @@ def decode_plan(seq_lens_host, max_seq_len: int, partition_size: int) -> np.ndar
 
 
 def decode(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int, scale: float,
-           partition_size: int = 0, workspace=None, lse=None, plan=None, stream=None) -> None:
+           partition_size: int = 0, workspace=None, lse=None, plan=None, stream=None,
+           new_key=None, new_value=None) -> None:
     """out/query [B, H_q, D]; kv_cache [N, 2, H_kv, 16, D]; block_tables int32
     [B, max_blocks]; seq_lens int32 [B]; lse fp32 [B, H_q] or None;
     workspace a uint8 GPU tensor of decode_workspace_bytes(...) bytes; plan an
-    int32 GPU tensor holding decode_plan(...) for the same lengths, or None."""
-    _need_gpu(out, query, kv_cache, block_tables, seq_lens, workspace, lse, plan)
+    int32 GPU tensor holding decode_plan(...) for the same lengths, or None.
+    With new_key/new_value ([B, H_kv, D]) the call is pa_decode_append: the
+    new token of each sequence is written into the cache in the same launch."""
+    _need_gpu(out, query, kv_cache, block_tables, seq_lens, workspace, lse, plan, new_key,
+              new_value)
     torch = _torch()
     N, _, Hkv, bs, D = kv_cache.shape
     B, Hq, Dq = query.shape
@@ -288,11 +295,20 @@ def decode(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int, scale
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if plan is not None and plan.dtype != torch.int32:
         raise PAError(PA_EINVAL, "plan must be int32")
-    _check(lib().pa_decode(_ptr(out), _ptr(lse), _ptr(query), _ptr(kv_cache), N,
-                           _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), B,
-                           int(max_seq_len), Hq, Hkv, D, bs, float(scale), int(partition_size),
-                           _ptr(plan), 0 if plan is None else plan.numel(), _ptr(workspace),
-                           ws_bytes, _dtype_code(kv_cache), _stream(stream)))
+    tail = (N, _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), B, int(max_seq_len),
+            Hq, Hkv, D, bs, float(scale), int(partition_size), _ptr(plan),
+            0 if plan is None else plan.numel(), _ptr(workspace), ws_bytes,
+            _dtype_code(kv_cache), _stream(stream))
+    if new_key is None and new_value is None:
+        _check(lib().pa_decode(_ptr(out), _ptr(lse), _ptr(query), _ptr(kv_cache), *tail))
+        return
+    for t in (new_key, new_value):
+        if t is None or tuple(t.shape) != (B, Hkv, D) or t.dtype != kv_cache.dtype \
+                or not t.is_contiguous():
+            raise PAError(PA_EINVAL, "new_key/new_value must be contiguous [B, H_kv, D] "
+                                     "in the cache dtype")
+    _check(lib().pa_decode_append(_ptr(out), _ptr(lse), _ptr(query), _ptr(new_key),
+                                  _ptr(new_value), _ptr(kv_cache), *tail))
 
 
 def prefill_chunk(out, query, query_start_loc, max_query_len: int, kv_cache, block_tables,

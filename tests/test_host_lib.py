@@ -251,6 +251,38 @@ def test_decode_validation(kw, status):
     assert msg
 
 
+def _append_status(nk=16, nv=16, **kw):
+    args = dict(out=16, lse=None, q=16, cache=16, nb=4, bt=16, mbps=4, sl=16, B=1, msl=64,
+                hq=8, hkv=2, d=128, bs=16, scale=0.1, P=0, ws=None, wsb=0, dtype=ops.PA_BF16)
+    args.update(kw)
+    L = ops.lib()
+    st = L.pa_decode_append(args["out"], args["lse"], args["q"], nk, nv, args["cache"],
+                            args["nb"], args["bt"], args["mbps"], args["sl"], args["B"],
+                            args["msl"], args["hq"], args["hkv"], args["d"], args["bs"],
+                            args["scale"], args["P"], None, 0, args["ws"], args["wsb"],
+                            args["dtype"], None)
+    return st, L.pa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nk=None), ops.PA_EINVAL),          # new key missing
+    (dict(nv=None), ops.PA_EINVAL),          # new value missing
+    (dict(nk=24), ops.PA_EINVAL),            # misaligned new key
+    (dict(hq=7), ops.PA_EINVAL),             # the decode checks apply too
+    (dict(d=96), ops.PA_ENOTSUP),
+    (dict(P=16), ops.PA_EINVAL),             # workspace missing
+])
+def test_decode_append_validation(kw, status):
+    st, msg = _append_status(**kw)
+    assert st == status, msg
+    assert "pa_decode_append" in msg
+
+
+def test_decode_append_empty_batch_is_a_no_op():
+    st, _ = _append_status(nk=None, nv=None, B=0)
+    assert st == ops.PA_OK
+
+
 def test_decode_workspace_size():
     assert ops.decode_workspace_bytes(4, 8, 2, 128, 64, 0) == 0
     assert ops.decode_workspace_bytes(4, 8, 2, 128, 64, 64) == 0       # one partition
