@@ -221,16 +221,23 @@ struct LaneRoles {
   int col;   // P.V: dword column within a row
 };
 
-// One 16-token block: K tile through LDS, scores, online softmax, P to LDS,
-// P.V into the lane's output columns.  TAIL: only the first `valid` tokens of
-// the block are inside the sequence (1 <= valid < 16).
+// The stages of one 16-token block (they run in this order for a block; the
+// 8-wave loop overlaps block k's P.V with block k + 1's scores):
+//   block_scores   K tile through LDS, q.k of this lane's head and token(s);
+//   block_softmax  lazily moved softmax reference, P to LDS;
+//   pv_rescale     o *= alpha when the block moved the reference;
+//   pv_read        P words of this lane's rows for all heads, from LDS;
+//   pv_accumulate  P.V into the lane's output columns.
+// TAIL: only the first `valid` tokens of the block are inside the sequence
+// (1 <= valid <= 16).
+
+// Scores (log2 domain) of this lane's head for its token of each pass.
 template <int D, int G, bool BF16, bool TAIL>
-__device__ __forceinline__ void process_block(BlockRegs<DecodeCfg<D, G, BF16>>& cur, int valid,
-                                            const u32x4 (&q)[DecodeCfg<D, G, BF16>::HPL]
-                                                            [DecodeCfg<D, G, BF16>::CPL],
-                                            DecodeState<DecodeCfg<D, G, BF16>, G>& st,
-                                            uint8_t* kt_lds, uint32_t* p_lds, float* alpha_lds,
-                                            float scale_log2, const LaneRoles& r) {
+__device__ __forceinline__ void block_scores(const BlockRegs<DecodeCfg<D, G, BF16>>& cur, int valid,
+                                             const u32x4 (&q)[DecodeCfg<D, G, BF16>::HPL]
+                                                             [DecodeCfg<D, G, BF16>::CPL],
+                                             uint8_t* kt_lds, float scale_log2, const LaneRoles& r,
+                                             float (&x)[DecodeCfg<D, G, BF16>::NPASS]) {
   using C = DecodeCfg<D, G, BF16>;
   const int lane = threadIdx.x & (kWave - 1);
 
@@ -244,7 +251,6 @@ __device__ __forceinline__ void process_block(BlockRegs<DecodeCfg<D, G, BF16>>& 
   }
   wave_lds_sync();
 
-  // ---- scores (log2 domain) of this lane's head for its token of each pass
   // K chunks are read from LDS in groups of KGRP (registers permitting) so
   // that the reads of a group overlap one another
   float sacc[C::NPASS][C::HPL];
@@ -268,7 +274,6 @@ __device__ __forceinline__ void process_block(BlockRegs<DecodeCfg<D, G, BF16>>& 
       for (int hh = 0; hh < C::HPL; ++hh) sacc[ps][hh] = chunk_dot<BF16>(q[hh][c], kv[i], sacc[ps][hh]);
     }
   }
-  float x[C::NPASS];
 #pragma unroll
   for (int ps = 0; ps < C::NPASS; ++ps) {
     const int row = ps * C::TPP + r.tq;
@@ -283,11 +288,21 @@ __device__ __forceinline__ void process_block(BlockRegs<DecodeCfg<D, G, BF16>>& 
     if constexpr (TAIL) v = row < valid ? v : -INFINITY;
     x[ps] = v;
   }
+}
 
-  // ---- online softmax with a lazily moved reference: m_run moves only
-  // when the block's max exceeds it by more than kRescaleSlack (log2 units),
-  // so P = 2^(s - m_run) <= 2^kRescaleSlack and most blocks neither reduce
-  // their max across lanes nor rescale the accumulated output.
+// Online softmax with a lazily moved reference: m_run moves only when the
+// block's max exceeds it by more than kRescaleSlack (log2 units), so
+// P = 2^(s - m_run) <= 2^kRescaleSlack and most blocks neither reduce their
+// max across lanes nor rescale the accumulated output.  Writes P to LDS
+// (bf16 token pairs [head][pair], or fp32 [head][token]; replica lanes store
+// the same value to the same word) and, when the reference moved, each
+// head's alpha; returns whether it moved (wave-uniform).  The caller orders
+// the P stores after any earlier reads of P (wave_lds_sync).
+template <int D, int G, bool BF16>
+__device__ __forceinline__ bool block_softmax(const float (&x)[DecodeCfg<D, G, BF16>::NPASS],
+                                              DecodeState<DecodeCfg<D, G, BF16>, G>& st,
+                                              uint32_t* p_lds, float* alpha_lds, const LaneRoles& r) {
+  using C = DecodeCfg<D, G, BF16>;
   float t = x[0];
 #pragma unroll
   for (int ps = 1; ps < C::NPASS; ++ps) t = fmaxf(t, x[ps]);
@@ -303,9 +318,6 @@ __device__ __forceinline__ void process_block(BlockRegs<DecodeCfg<D, G, BF16>>& 
     st.l *= alpha;
     if (r.tq == 0 && r.dp < C::HPL) alpha_lds[r.head] = alpha;
   }
-
-  // ---- P to LDS: bf16 token pairs [head][pair], or fp32 [head][token].
-  // Replica lanes store the same value to the same word.
   if constexpr (BF16) {
     if constexpr (C::IN_LANE_PAIRS) {
 #pragma unroll
@@ -337,16 +349,13 @@ __device__ __forceinline__ void process_block(BlockRegs<DecodeCfg<D, G, BF16>>& 
       pf[r.head * 16 + ps * C::TPP + r.tq] = p;
     }
   }
-  wave_lds_sync();
+  return rescale;
+}
 
-  // ---- rescale and accumulate P.V
-  if constexpr (TAIL) {  // rows past the sequence may hold anything
-#pragma unroll
-    for (int rr = 0; rr < C::ROWS; ++rr)
-#pragma unroll
-      for (int w = 0; w < C::VW; ++w)
-        cur.v[rr][w] = v_row<C>(rr, r.half) < valid ? cur.v[rr][w] : 0u;
-  }
+template <int D, int G, bool BF16>
+__device__ __forceinline__ void pv_rescale(bool rescale, DecodeState<DecodeCfg<D, G, BF16>, G>& st,
+                                           const float* alpha_lds) {
+  using C = DecodeCfg<D, G, BF16>;
   if (rescale) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -355,47 +364,107 @@ __device__ __forceinline__ void process_block(BlockRegs<DecodeCfg<D, G, BF16>>& 
       for (int jj = 0; jj < C::DPL; ++jj) st.o[h][jj] *= a;
     }
   }
+}
+
+// P words of this lane's rows for HN heads starting at H0 (bf16: token
+// pairs of its half; fp32: all 16 tokens), read as 16-byte vectors.
+template <class C, int HN>
+struct PWords {
+  static constexpr int N = C::BF16_ ? C::PAIRS : 16;
+  uint32_t w[HN][N];
+};
+
+template <int D, int G, bool BF16, int H0, int HN>
+__device__ __forceinline__ void pv_read(const uint32_t* p_lds, const LaneRoles& r,
+                                        PWords<DecodeCfg<D, G, BF16>, HN>& pw) {
+  using C = DecodeCfg<D, G, BF16>;
+  constexpr int N = PWords<C, HN>::N;
+  const int off = BF16 ? r.half * C::PAIRS : 0;
+  constexpr int STRIDE = BF16 ? 8 : 16;
+#pragma unroll
+  for (int h = 0; h < HN; ++h)
+#pragma unroll
+    for (int k4 = 0; k4 < N; k4 += 4) {
+      const u32x4 t4 = *reinterpret_cast<const u32x4*>(p_lds + (H0 + h) * STRIDE + off + k4);
+      pw.w[h][k4] = t4.x; pw.w[h][k4 + 1] = t4.y; pw.w[h][k4 + 2] = t4.z; pw.w[h][k4 + 3] = t4.w;
+    }
+}
+
+// Rows past the sequence may hold anything: zero them in a tail block.
+template <int D, int G, bool BF16>
+__device__ __forceinline__ void mask_tail_rows(BlockRegs<DecodeCfg<D, G, BF16>>& cur, int valid,
+                                               const LaneRoles& r) {
+  using C = DecodeCfg<D, G, BF16>;
+#pragma unroll
+  for (int rr = 0; rr < C::ROWS; ++rr)
+#pragma unroll
+    for (int w = 0; w < C::VW; ++w)
+      cur.v[rr][w] = v_row<C>(rr, r.half) < valid ? cur.v[rr][w] : 0u;
+}
+
+template <int D, int G, bool BF16, int H0, int HN>
+__device__ __forceinline__ void pv_accumulate(const BlockRegs<DecodeCfg<D, G, BF16>>& cur,
+                                              const PWords<DecodeCfg<D, G, BF16>, HN>& pw,
+                                              DecodeState<DecodeCfg<D, G, BF16>, G>& st) {
+  using C = DecodeCfg<D, G, BF16>;
   if constexpr (BF16) {
-    constexpr int PAIRS = C::PAIRS;
-    // P words are read in groups of PGRP heads, each group's reads issued
-    // together
 #pragma unroll
-    for (int h0 = 0; h0 < G; h0 += C::PGRP) {
-      uint32_t pw[C::PGRP][PAIRS];
+    for (int h = 0; h < HN; ++h) {
 #pragma unroll
-      for (int hh = 0; hh < C::PGRP; ++hh)
-#pragma unroll
-        for (int k4 = 0; k4 < PAIRS; k4 += 4) {
-          const u32x4 t4 =
-              *reinterpret_cast<const u32x4*>(p_lds + (h0 + hh) * 8 + r.half * PAIRS + k4);
-          pw[hh][k4] = t4.x; pw[hh][k4 + 1] = t4.y;
-          pw[hh][k4 + 2] = t4.z; pw[hh][k4 + 3] = t4.w;
-        }
-#pragma unroll
-      for (int hh = 0; hh < C::PGRP; ++hh) {
-        const int h = h0 + hh;
-#pragma unroll
-        for (int k = 0; k < PAIRS; ++k) {
-          const uint32_t v0 = cur.v[2 * k][0], v1 = cur.v[2 * k + 1][0];
-          const uint32_t xlo = __builtin_amdgcn_perm(v1, v0, 0x05040100u);  // (v0.lo, v1.lo)
-          const uint32_t xhi = __builtin_amdgcn_perm(v1, v0, 0x07060302u);  // (v0.hi, v1.hi)
-          st.o[h][0] = dot2_bf16(xlo, pw[hh][k], st.o[h][0]);
-          st.o[h][1] = dot2_bf16(xhi, pw[hh][k], st.o[h][1]);
-        }
+      for (int k = 0; k < C::PAIRS; ++k) {
+        const uint32_t v0 = cur.v[2 * k][0], v1 = cur.v[2 * k + 1][0];
+        const uint32_t xlo = __builtin_amdgcn_perm(v1, v0, 0x05040100u);  // (v0.lo, v1.lo)
+        const uint32_t xhi = __builtin_amdgcn_perm(v1, v0, 0x07060302u);  // (v0.hi, v1.hi)
+        st.o[H0 + h][0] = dot2_bf16(xlo, pw.w[h][k], st.o[H0 + h][0]);
+        st.o[H0 + h][1] = dot2_bf16(xhi, pw.w[h][k], st.o[H0 + h][1]);
       }
     }
   } else {
-    const float* pf = reinterpret_cast<const float*>(p_lds);
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int h = 0; h < HN; ++h) {
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
-        const float p = pf[h * 16 + rr];
+        const float p = __uint_as_float(pw.w[h][rr]);
 #pragma unroll
-        for (int w = 0; w < C::VW; ++w) st.o[h][w] = fmaf(p, __uint_as_float(cur.v[rr][w]), st.o[h][w]);
+        for (int w = 0; w < C::VW; ++w)
+          st.o[H0 + h][w] = fmaf(p, __uint_as_float(cur.v[rr][w]), st.o[H0 + h][w]);
       }
     }
   }
+}
+
+// P.V over all heads, the P words read in groups of PGRP heads (each
+// group's reads issued together).
+template <int D, int G, bool BF16, int H0 = 0>
+__device__ __forceinline__ void pv_grouped(const BlockRegs<DecodeCfg<D, G, BF16>>& cur,
+                                           const uint32_t* p_lds, const LaneRoles& r,
+                                           DecodeState<DecodeCfg<D, G, BF16>, G>& st) {
+  using C = DecodeCfg<D, G, BF16>;
+  constexpr int HN = BF16 ? C::PGRP : 1;
+  if constexpr (H0 < G) {
+    PWords<C, HN> pw;
+    pv_read<D, G, BF16, H0, HN>(p_lds, r, pw);
+    pv_accumulate<D, G, BF16, H0, HN>(cur, pw, st);
+    pv_grouped<D, G, BF16, H0 + HN>(cur, p_lds, r, st);
+  }
+}
+
+// One block, stage after stage (the 4- and 2-wave loop and every tail block).
+template <int D, int G, bool BF16, bool TAIL>
+__device__ __forceinline__ void process_block(BlockRegs<DecodeCfg<D, G, BF16>>& cur, int valid,
+                                            const u32x4 (&q)[DecodeCfg<D, G, BF16>::HPL]
+                                                            [DecodeCfg<D, G, BF16>::CPL],
+                                            DecodeState<DecodeCfg<D, G, BF16>, G>& st,
+                                            uint8_t* kt_lds, uint32_t* p_lds, float* alpha_lds,
+                                            float scale_log2, const LaneRoles& r) {
+  using C = DecodeCfg<D, G, BF16>;
+  float x[C::NPASS];
+  block_scores<D, G, BF16, TAIL>(cur, valid, q, kt_lds, scale_log2, r, x);
+  const bool rescale = block_softmax<D, G, BF16>(x, st, p_lds, alpha_lds, r);
+  wave_lds_sync();
+  if constexpr (TAIL) mask_tail_rows<D, G, BF16>(cur, valid, r);
+  pv_rescale<D, G, BF16>(rescale, st, alpha_lds);
+  pv_grouped<D, G, BF16>(cur, p_lds, r, st);
 }
 
 // Arguments of one decode launch (passed by value as the kernel argument).
@@ -456,15 +525,32 @@ __device__ __forceinline__ void append_new_token(BlockRegs<C>& rg, const DecodeP
   }
 }
 
-// LDS of one workgroup: K tiles during the block loop (afterwards reused for
-// the per-wave outputs and the merge weights), P, and the merge state.
+// Shapes of the bf16 (matrix-core) block loop; see mfma_blocks.
+template <int D>
+struct MfmaCfg {
+  static_assert(D == 64 || D == 128, "head size");
+  static constexpr int KS = D / 32;   // S^T products per block
+  static constexpr int VWD = D / 32;  // dwords of a V row per lane
+  static constexpr int NPV = D / 16;  // P V products per block (16 columns each)
+  static constexpr int RB = 2 * D;    // bytes of a cache row
+  static constexpr int CPR = D / 8;   // 16-byte chunks per row
+  static constexpr int LROW = RB + 16;  // padded LDS row: conflict-free operand reads
+  static constexpr int TILE = 16 * LROW;
+  static constexpr int PD = 2;        // blocks in flight per wave
+};
+
+// LDS of one workgroup: K tiles during the block loop, then the per-wave
+// outputs, the merge weights and the split-K subset sums; fp32 P (the bf16
+// loop keeps P in registers); and the merge state.
 template <int D, int G, bool BF16, int NW>
 struct DecodeSmem {
   using C = DecodeCfg<D, G, BF16>;
-  static constexpr int kTiles = NW * C::LDS_TILE;
+  static constexpr int kTiles = NW * (BF16 ? MfmaCfg<D>::TILE : C::LDS_TILE);
   static constexpr int kOStage = NW * G * D * 4;
-  __attribute__((aligned(16))) uint8_t k[kTiles > kOStage ? kTiles : kOStage];
-  __attribute__((aligned(16))) uint32_t p[NW][C::P_BYTES / 4];
+  static constexpr int kSubsets = NW * kWave * 16;
+  static constexpr int kBytes = std::max(kTiles, std::max(kOStage, kSubsets));
+  __attribute__((aligned(16))) uint8_t k[kBytes];
+  __attribute__((aligned(16))) uint32_t p[BF16 ? 1 : NW][BF16 ? 1 : C::P_BYTES / 4];
   float alpha[NW][G];
   float m[NW][G];
   float l[NW][G];
@@ -472,25 +558,321 @@ struct DecodeSmem {
   int last;
 };
 
-// One work item: KV head g of sequence b, partition `part` (blocks
-// [part * pb, min((part + 1) * pb, nblk))).  Called by the whole workgroup.
-template <int D, int G, bool BF16, int NW, bool APPEND>
-__device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D, G, BF16, NW>& sm,
-                                            int b, int g, int part, int L, int nblk, int pb,
-                                            int nparts) {
-  using C = DecodeCfg<D, G, BF16>;
-  void* __restrict__ out = a.out;
-  float* __restrict__ lse_out = a.lse_out;
+// ---------------------------------------------------------------------------
+// bf16 blocks on the matrix cores.  Per 16-token block of one KV head, a
+// wave forms S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (rows: the block's
+// tokens; columns: the G query heads, padded to 16 with zero queries;
+// contraction over D, 32 at a time) and accumulates O += P V with
+// v_mfma_f32_16x16x16_bf16 (rows: heads; columns: 16 output columns;
+// contraction over the block's 16 tokens).  With lane = 16 * grp + n:
+//   * K operand: token n, 16-byte d-chunk 4 * s + grp of product s.  The K
+//     tile is loaded coalesced (each load instruction covers whole rows: a
+//     compute unit streams at a rate set by the cache lines it requests, and
+//     the operand layout would split every line between two requests),
+//     written to a padded per-wave LDS tile and read back in operand layout;
+//     the Q^T operand holds the same chunk of query head n;
+//   * the S^T result gives the lane tokens 4 * grp + i (i < 4) of head n,
+//     which is exactly where P V wants P (row n, contraction slots i), so
+//     the softmax runs in place and P never leaves the registers;
+//   * V operand: the same four tokens at output column 2 * (VWD * n + w) + hb,
+//     built with v_perm from the lane's dwords of those rows (16 lanes read a
+//     whole row as one coalesced segment);
+//   * the O result holds heads 4 * grp + i at columns (D / 16) * n + p.
+// P and V never touch LDS; the softmax reference moves lazily as in the
+// fp32 path, now one head per lane column n.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+
+// K: lane holds 16-byte vectors lane + 64 j of the tile (D / 32 of them);
+// V: operand layout (rows 4 grp + i, dwords VWD n ..).
+template <int D>
+struct MfmaBlock {
+  u32x4 k[MfmaCfg<D>::KS];
+  uint32_t v[4][MfmaCfg<D>::VWD];
+};
+
+template <int D>
+struct MfmaState {
+  float m_run, m_thr, l;  // head n's reference, threshold; this lane's share of l
+  f32x4 o[MfmaCfg<D>::NPV];
+};
+
+__device__ __forceinline__ f32x4 mfma_k32(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_k16(const u32x2& a, const u32x2& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// Non-temporal loads of one block's K and V operands (the cache is streamed
+// once per call).
+template <int D>
+__device__ __forceinline__ MfmaBlock<D> load_mfma_block(const uint8_t* __restrict__ cache, int phys,
+                                                        int64_t block_bytes, int g,
+                                                        int num_kv_heads, int64_t tile_bytes,
+                                                        int lane) {
+  using M = MfmaCfg<D>;
+  const uint8_t* kbase = cache + int64_t(phys) * block_bytes + int64_t(g) * tile_bytes;
+  const uint8_t* vbase = kbase + int64_t(num_kv_heads) * tile_bytes;
+  const int n = lane & 15, grp = lane >> 4;
+  MfmaBlock<D> r;
+  const u32x4* kt = reinterpret_cast<const u32x4*>(kbase);
+#pragma unroll
+  for (int j = 0; j < M::KS; ++j) r.k[j] = __builtin_nontemporal_load(kt + j * kWave + lane);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint8_t* vp = vbase + (4 * grp + i) * M::RB + n * (M::VWD * 4);
+    if constexpr (M::VWD == 2) {
+      const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vp));
+      r.v[i][0] = x.x;
+      r.v[i][1] = x.y;
+    } else {
+      const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp));
+      r.v[i][0] = x.x;
+      r.v[i][1] = x.y;
+      r.v[i][2] = x.z;
+      r.v[i][3] = x.w;
+    }
+  }
+  return r;
+}
+
+// Token `row` of the registers of the sequence's last block becomes the new
+// key/value (new_k / new_v row (b, g)), which is also stored to the cache
+// (skipped when the block id is out of range).
+template <int D>
+__device__ __forceinline__ void append_new_token_mfma(MfmaBlock<D>& rg, const DecodeParams& a,
+                                                      int b, int g, int row, int phys,
+                                                      int64_t block_bytes, int64_t tile_bytes,
+                                                      int lane) {
+  using M = MfmaCfg<D>;
+  const int64_t src = (int64_t(b) * a.num_kv_heads + g) * M::RB;
+  const bool store = phys >= 0 && phys < a.num_blocks;
+  uint8_t* kbase = const_cast<uint8_t*>(a.cache) + int64_t(store ? phys : 0) * block_bytes +
+                   int64_t(g) * tile_bytes;
+  uint8_t* vbase = kbase + int64_t(a.num_kv_heads) * tile_bytes;
+  const uint8_t* nk = static_cast<const uint8_t*>(a.new_k) + src;
+  const uint8_t* nv = static_cast<const uint8_t*>(a.new_v) + src;
+  const int n = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < M::KS; ++j) {
+    const int v = j * kWave + lane;
+    if (v / M::CPR == row) {
+      const u32x4 x = reinterpret_cast<const u32x4*>(nk)[v % M::CPR];
+      rg.k[j] = x;
+      if (store) reinterpret_cast<u32x4*>(kbase)[v] = x;
+    }
+  }
+  const int off = n * (M::VWD * 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (4 * grp + i == row) {
+#pragma unroll
+      for (int w = 0; w < M::VWD; ++w) {
+        const uint32_t x = reinterpret_cast<const uint32_t*>(nv + off)[w];
+        rg.v[i][w] = x;
+        if (store) reinterpret_cast<uint32_t*>(vbase + row * M::RB + off)[w] = x;
+      }
+    }
+  }
+}
+
+// One block.  TAIL: only the first `valid` tokens (1 <= valid <= 16) are in
+// the sequence; the others get score -inf and their V rows are zeroed (they
+// may hold anything).
+template <int D, bool TAIL>
+__device__ __forceinline__ void mfma_block(MfmaBlock<D>& cur, int valid,
+                                           const u32x4 (&qb)[MfmaCfg<D>::KS], MfmaState<D>& st,
+                                           uint8_t* kt_lds, float scale_log2, int lane) {
+  using M = MfmaCfg<D>;
+  const int n = lane & 15, grp = lane >> 4;
+  // K tile -> LDS -> operand layout
+  wave_lds_sync();  // the previous block's operand reads are done
+#pragma unroll
+  for (int j = 0; j < M::KS; ++j) {
+    const int v = j * kWave + lane;
+    *reinterpret_cast<u32x4*>(kt_lds + (v / M::CPR) * M::LROW + (v % M::CPR) * 16) = cur.k[j];
+  }
+  wave_lds_sync();
+  u32x4 ka[M::KS];
+#pragma unroll
+  for (int s = 0; s < M::KS; ++s)
+    ka[s] = *reinterpret_cast<const u32x4*>(kt_lds + n * M::LROW + (4 * s + grp) * 16);
+  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < M::KS; ++s) sc = mfma_k32(ka[s], qb[s], sc);
+  float x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v = sc[i] * scale_log2;
+    if constexpr (TAIL) v = 4 * grp + i < valid ? v : -INFINITY;
+    x[i] = v;
+  }
+  const float t = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  if (__builtin_amdgcn_ballot_w64(t > st.m_thr) != 0) {  // wave-uniform
+    // max over the head's 16 tokens (lanes n, n + 16, n + 32, n + 48); it
+    // is finite: token 0 of the block is in the sequence
+    const float mb = allreduce_max_xor<4, 6>(t);
+    const bool grow = mb > st.m_thr;
+    const float alpha = grow ? __builtin_amdgcn_exp2f(st.m_run - mb) : 1.f;
+    st.m_run = grow ? mb : st.m_run;
+    st.m_thr = st.m_run + kRescaleSlack;
+    st.l *= alpha;
+    // output rows are heads 4 * grp + i; lane 4 * grp + i holds their alpha
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ai = __shfl(alpha, 4 * grp + i, kWave);
+#pragma unroll
+      for (int p = 0; p < M::NPV; ++p) st.o[p][i] *= ai;
+    }
+  }
+  u32x2 pa;
+  pa.x = pack_bf16x2(__builtin_amdgcn_exp2f(x[0] - st.m_run), __builtin_amdgcn_exp2f(x[1] - st.m_run));
+  pa.y = pack_bf16x2(__builtin_amdgcn_exp2f(x[2] - st.m_run), __builtin_amdgcn_exp2f(x[3] - st.m_run));
+  st.l = dot2_bf16(pa.x, 0x3F803F80u, st.l);  // the rounded values that multiply V
+  st.l = dot2_bf16(pa.y, 0x3F803F80u, st.l);
+  if constexpr (TAIL) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int w = 0; w < M::VWD; ++w) cur.v[i][w] = 4 * grp + i < valid ? cur.v[i][w] : 0u;
+  }
+#pragma unroll
+  for (int w = 0; w < M::VWD; ++w) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const uint32_t sel = hb ? 0x07060302u : 0x05040100u;  // high or low bf16 of each dword
+      u32x2 vb;
+      vb.x = __builtin_amdgcn_perm(cur.v[1][w], cur.v[0][w], sel);  // tokens 4 grp + 0, + 1
+      vb.y = __builtin_amdgcn_perm(cur.v[3][w], cur.v[2][w], sel);  // tokens 4 grp + 2, + 3
+      st.o[2 * w + hb] = mfma_k16(pa, vb, st.o[2 * w + hb]);
+    }
+  }
+}
+
+// The bf16 block loop of one wave, then its (m, l) into sm.m / sm.l and its
+// unnormalised output rows into the LDS output stage; synchronises the
+// workgroup.
+template <int D, int G, int NW, bool APPEND>
+__device__ __forceinline__ void mfma_blocks(const DecodeParams& a, DecodeSmem<D, G, true, NW>& sm,
+                                            int b, int g, int L, int nblk, int blk_lo,
+                                            int blk_hi) {
+  using M = MfmaCfg<D>;
+  static_assert(G <= 16, "query heads per KV head");
   const uint8_t* __restrict__ cache = a.cache;
-  const int num_blocks = a.num_blocks, num_kv_heads = a.num_kv_heads, max_parts = a.max_parts;
+  const int num_blocks = a.num_blocks, num_kv_heads = a.num_kv_heads;
   const float scale_log2 = a.scale_log2;
-  int* __restrict__ ws_count = a.ws_count;
-  float* __restrict__ ws_m = a.ws_m;
-  float* __restrict__ ws_l = a.ws_l;
-  float* __restrict__ ws_o = a.ws_o;
   const int H_q = num_kv_heads * G;
-  const int blk_lo = part * pb;
-  const int blk_hi = min(blk_lo + pb, nblk);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, grp = lane >> 4;
+
+  // Q^T operand: head n of this KV head (zero past G), d-chunks 4 s + grp
+  u32x4 qb[M::KS];
+  {
+    const u32x4* qrow = reinterpret_cast<const u32x4*>(a.query) +
+                        (int64_t(b) * H_q + g * G + (n < G ? n : 0)) * (D / 8);
+#pragma unroll
+    for (int s = 0; s < M::KS; ++s) {
+      const u32x4 v = qrow[4 * s + grp];
+      qb[s] = n < G ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  const int64_t tile_bytes = int64_t(16) * M::RB;
+  const int64_t block_bytes = int64_t(2) * num_kv_heads * tile_bytes;
+  const int* bt_row = a.block_tables + int64_t(b) * a.max_blocks_per_seq;
+
+  uint8_t* kt_lds = sm.k + wave * M::TILE;
+  MfmaState<D> st;
+  st.m_run = -INFINITY;
+  st.m_thr = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int p = 0; p < M::NPV; ++p) st.o[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Register ring of PD blocks in flight, block ids one group ahead; the
+  // same scheme as the fp32 loop (see there).
+  constexpr int PD = M::PD;
+#pragma unroll
+  for (int s = 0; s < M::KS; ++s) asm volatile("" ::"v"(qb[s]));
+  const int first = blk_lo + wave;
+  const int nmine = blk_hi > first ? (blk_hi - first + NW - 1) / NW : 0;
+  if (nmine > 0) {
+    auto id_group = [&](int base) -> int {
+      const int k = min(base + (lane & (PD - 1)), nmine - 1);
+      int id = bt_row[first + k * NW];
+      return (id < 0 || id >= num_blocks) ? 0 : id;  // out-of-range ids read block 0
+    };
+    const int ids_cur = id_group(0);
+    int ids_next = id_group(PD);
+    MfmaBlock<D> buf[PD];
+#pragma unroll
+    for (int s = 0; s < PD; ++s)
+      buf[s] = load_mfma_block<D>(cache, __builtin_amdgcn_readlane(ids_cur, s), block_bytes, g,
+                                  num_kv_heads, tile_bytes, lane);
+    const int j_last = first + (nmine - 1) * NW;
+    const int tail_valid = L - j_last * 16;
+    const bool seq_last = APPEND && j_last == nblk - 1;
+    const int nfull = (tail_valid < 16 || seq_last) ? nmine - 1 : nmine;
+    for (int k0 = 0; k0 < nfull; k0 += PD) {
+      const int ids_after = id_group(k0 + 2 * PD);
+#pragma unroll
+      for (int s = 0; s < PD; ++s) {
+        if (k0 + s < nfull) mfma_block<D, false>(buf[s], 16, qb, st, kt_lds, scale_log2, lane);
+        buf[s] = load_mfma_block<D>(cache, __builtin_amdgcn_readlane(ids_next, s), block_bytes, g,
+                                    num_kv_heads, tile_bytes, lane);
+      }
+      ids_next = ids_after;
+    }
+    if (nfull < nmine) {  // buf[0] holds the last block (later loads were clamped to it)
+      if constexpr (APPEND) {
+        if (seq_last)
+          append_new_token_mfma<D>(buf[0], a, b, g, (L - 1) & 15, bt_row[nblk - 1], block_bytes,
+                                   tile_bytes, lane);
+      }
+      mfma_block<D, true>(buf[0], min(tail_valid, 16), qb, st, kt_lds, scale_log2, lane);
+    }
+  }
+
+  const float lsum = allreduce_sum<4, 6>(st.l);  // over the head's four lanes
+  if (lane < G) {
+    sm.m[wave][lane] = st.m_run;
+    sm.l[wave][lane] = lsum;
+  }
+  __syncthreads();  // every wave is done with its K tile: reuse the LDS for o
+  float* o_lds = reinterpret_cast<float*>(sm.k);  // [wave][G][D]
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int head = 4 * grp + i;
+    if (head < G) {
+      float* dst = o_lds + (wave * G + head) * D + M::NPV * n;
+#pragma unroll
+      for (int p = 0; p < M::NPV; p += 4)
+        *reinterpret_cast<f32x4*>(dst + p) =
+            f32x4{st.o[p][i], st.o[p + 1][i], st.o[p + 2][i], st.o[p + 3][i]};
+    }
+  }
+  __syncthreads();
+}
+
+// fp32 blocks on the vector ALUs: q.k through the LDS K tile, P through
+// LDS.  Leaves this wave's (m, l) in sm.m / sm.l and its unnormalised output
+// rows in the LDS output stage, then synchronises the workgroup.
+template <int D, int G, bool BF16, int NW, bool APPEND>
+__device__ __forceinline__ void valu_blocks(const DecodeParams& a, DecodeSmem<D, G, BF16, NW>& sm,
+                                            int b, int g, int L, int nblk, int blk_lo,
+                                            int blk_hi) {
+  using C = DecodeCfg<D, G, BF16>;
+  const uint8_t* __restrict__ cache = a.cache;
+  const int num_blocks = a.num_blocks, num_kv_heads = a.num_kv_heads;
+  const float scale_log2 = a.scale_log2;
+  const int H_q = num_kv_heads * G;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   LaneRoles r;
@@ -613,6 +995,31 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
         o_lds[(wave * G + h) * D + col * C::DPL + jj] = st.o[h][jj];
   }
   __syncthreads();
+}
+
+// One work item: KV head g of sequence b, partition `part` (blocks
+// [part * pb, min((part + 1) * pb, nblk))).  Called by the whole workgroup.
+template <int D, int G, bool BF16, int NW, bool APPEND>
+__device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D, G, BF16, NW>& sm,
+                                            int b, int g, int part, int L, int nblk, int pb,
+                                            int nparts) {
+  void* __restrict__ out = a.out;
+  float* __restrict__ lse_out = a.lse_out;
+  const int num_kv_heads = a.num_kv_heads, max_parts = a.max_parts;
+  int* __restrict__ ws_count = a.ws_count;
+  float* __restrict__ ws_m = a.ws_m;
+  float* __restrict__ ws_l = a.ws_l;
+  float* __restrict__ ws_o = a.ws_o;
+  const int H_q = num_kv_heads * G;
+  const int blk_lo = part * pb;
+  const int blk_hi = min(blk_lo + pb, nblk);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if constexpr (BF16)
+    mfma_blocks<D, G, NW, APPEND>(a, sm, b, g, L, nblk, blk_lo, blk_hi);
+  else
+    valu_blocks<D, G, BF16, NW, APPEND>(a, sm, b, g, L, nblk, blk_lo, blk_hi);
+  float* o_lds = reinterpret_cast<float*>(sm.k);  // [wave][G][D]
 
   const bool single = nparts <= 1;
   const int tid = threadIdx.x;
@@ -765,13 +1172,13 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
 // the virtual grid (part, b, g) walked by a grid of a few times the resident
 // workgroups, and items past a sequence's last partition are skipped in the
 // loop instead of being dispatched as empty workgroups.
-// 4-wave bf16 variants are held to 168 VGPRs (three waves per SIMD, so
-// three workgroups share a compute unit when there are many items); the
-// register demand of fp32 and of bf16 G = 16 would spill there.  An 8-wave
+// 4-wave bf16 variants of head size 64 are held to 168 VGPRs (three waves
+// per SIMD, so three workgroups share a compute unit when there are many
+// items); head size 128 and fp32 need more registers than that.  An 8-wave
 // workgroup holds a compute unit alone at two or three waves per SIMD, so
 // its registers are left free for loads in flight.
 template <int D, int G, bool BF16, int NW>
-constexpr int decode_min_waves() { return NW == 4 && BF16 && !(D == 64 && G == 16) ? 3 : 1; }
+constexpr int decode_min_waves() { return NW == 4 && BF16 && D == 64 ? 3 : 1; }
 template <int D, int G, bool BF16, int NW>
 constexpr int decode_max_waves() { return NW == 8 ? 2 : 8; }
 
