@@ -25,18 +25,18 @@
 //     (sequence, KV head) to finish merges the partitions' partials by
 //     log-sum-exp weights in the same launch;
 //   * each wave keeps two blocks in flight in registers (non-temporal
-//     loads: the cache is streamed once); the K tile (16 tokens x D) is
-//     loaded coalesced, written to a padded LDS tile and read back as
-//     (token, head group, d-part) per lane, so q.k needs a cross-lane sum
-//     over the d-parts only; bf16 q.k uses v_dot2_f32_bf16;
-//   * each lane then follows one query head for the softmax; scores are in
-//     the log2 domain and the softmax reference moves lazily (only when a
-//     block's max exceeds it by 2^8), so most blocks need no max reduction
-//     and no rescale of the accumulated output;
-//   * P goes to LDS as packed bf16 token pairs (k, k + 8) formed inside a
-//     lane; V is loaded straight from global memory with each lane owning
-//     one column pair, and P.V is again v_dot2_f32_bf16 over token pairs;
-//   * the denominator sums the same bf16-rounded P that multiplies V.
+//     loads: the cache is streamed once); every load instruction covers
+//     whole cache rows, because a compute unit streams at a rate set by the
+//     cache lines it requests;
+//   * scores are in the log2 domain and the softmax reference moves lazily
+//     (only when a block's max exceeds it by 2^8), so most blocks need no
+//     max reduction and no rescale of the accumulated output;
+//   * bf16 (mfma_blocks): S^T = K Q^T and O += P V on the matrix cores;
+//     K goes through a small LDS tile into operand order, the S^T result is
+//     already the P operand, V is loaded in operand order; P is rounded to
+//     bf16 for the product and the denominator sums the same rounded values;
+//   * fp32 (valu_blocks): q.k with v_fma through the LDS K tile and a
+//     cross-lane sum over d-parts, P through LDS, P.V with v_fma.
 #include <algorithm>
 #include <cstdio>
 #include <cstdlib>
@@ -54,10 +54,13 @@ constexpr float kLn2 = 0.6931471805599453f;
 // before the reference moves; P then stays <= 2^8.
 constexpr float kRescaleSlack = 8.f;
 
-template <int D, int G, bool BF16>
-struct DecodeCfg {
-  static constexpr int ES = BF16 ? 2 : 4;          // element bytes
-  static constexpr int RB = D * ES;                // bytes per K/V row
+// Shapes of the fp32 block loop on the vector ALUs.  The K tile goes
+// through LDS and is read back as (token, head group, d-part) per lane, so
+// q.k needs a cross-lane sum over the d-parts only; for P.V each lane owns
+// D / 64 output columns of every head.
+template <int D, int G>
+struct F32Cfg {
+  static constexpr int RB = D * 4;                 // bytes per K/V row
   static constexpr int CPR = RB / 16;              // 16-byte chunks per row
   static constexpr int TILE_VEC = 16 * CPR;        // 16-byte vectors per tile
   static constexpr int LOADS = TILE_VEC / kWave;   // vector loads per lane per tile
@@ -72,29 +75,17 @@ struct DecodeCfg {
   static constexpr int CPL = CPR / DP;             // chunks per lane per row
   static constexpr int LDS_ROW = RB + 16;          // padded row (bank spread)
   static constexpr int LDS_TILE = 16 * LDS_ROW;
-  // P.V layout: lanes own columns; bf16 D=64 splits the 16 rows over 2 halves
-  static constexpr int DPL = BF16 ? 2 : D / kWave;  // output columns per lane
-  static constexpr int HALVES = (BF16 && D == 64) ? 2 : 1;
-  static constexpr int ROWS = 16 / HALVES;         // V rows per lane
-  static constexpr int VW = BF16 ? 1 : DPL;        // V dwords per row per lane
-  static constexpr int PAIRS = ROWS / 2;           // bf16 token pairs per lane
-  static constexpr bool IN_LANE_PAIRS = NPASS >= 2;
-  static constexpr bool BF16_ = BF16;
-  static constexpr int P_BYTES = BF16 ? G * 8 * 4 : G * 16 * 4;
-  // LDS reads issued together: K chunks (16 bytes each) and heads of P words
+  static constexpr int DPL = D / kWave;            // output columns (= V dwords) per lane
+  static constexpr int P_BYTES = G * 16 * 4;
+  // K chunks (16 bytes each) read from LDS together
   static constexpr int KGRP_MAX = D == 64 ? 8 : (G >= 8 ? 2 : 4);
   static constexpr int KGRP = NPASS * CPL < KGRP_MAX ? NPASS * CPL : KGRP_MAX;
-  static constexpr int PGRP_MAX = (D == 64 ? 32 : 16) / (PAIRS > 0 ? PAIRS : 1);
-  static constexpr int PGRP = G < PGRP_MAX ? G : PGRP_MAX;
-  // blocks in flight per wave (register ring); divides 64
-  static constexpr int PD = 2;
+  static constexpr int PD = 2;                     // blocks in flight per wave (register ring)
   static_assert(DP >= HPL, "every head of a lane group needs a lane to follow it");
-  static_assert((NPASS * CPL) % KGRP == 0 && G % PGRP == 0, "read groups must tile");
-  static_assert(!IN_LANE_PAIRS || TPP * NPASS == 16, "in-lane pairs are (k, k + 8)");
+  static_assert((NPASS * CPL) % KGRP == 0, "read groups must tile");
   static_assert(CPR % DP == 0 && TPP >= 1 && 16 % TPP == 0, "bad decode lane split");
   static_assert(HG * DP * TPP == kWave, "lane split must cover the wave");
   static_assert(TILE_VEC % kWave == 0, "tile must be a whole number of wave loads");
-  static_assert(!BF16 || D == 64 || D == 128, "bf16 head sizes 64/128");
 };
 
 // Agent-scope relaxed stores: coherent across the L2 caches of all XCDs,
@@ -126,54 +117,30 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
     reinterpret_cast<float*>(out)[idx] = v;
 }
 
-// q.k partial over one 16-byte chunk
-template <bool BF16>
+// q.k partial over one 16-byte chunk (four fp32 values)
 __device__ __forceinline__ float chunk_dot(const u32x4& q, const u32x4& k, float acc) {
-  if constexpr (BF16) {
-    acc = dot2_bf16(q.x, k.x, acc);
-    acc = dot2_bf16(q.y, k.y, acc);
-    acc = dot2_bf16(q.z, k.z, acc);
-    acc = dot2_bf16(q.w, k.w, acc);
-  } else {
-    acc = fmaf(__uint_as_float(q.x), __uint_as_float(k.x), acc);
-    acc = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
-    acc = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
-    acc = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
-  }
+  acc = fmaf(__uint_as_float(q.x), __uint_as_float(k.x), acc);
+  acc = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
+  acc = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
+  acc = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
   return acc;
 }
 
-// bf16 P.V pairs tokens for v_dot2: with two or more QK passes a lane owns
-// rows r and r + 8 (passes ps and ps + NPASS/2), so pair k is (k, k + 8)
-// and is packed without leaving the lane; with one pass pair k is
-// (2k, 2k + 1) and the second token comes from the neighbour lane.
-template <class C>
-__device__ __forceinline__ constexpr int pair_row(int k, int which) {
-  return C::IN_LANE_PAIRS ? k + 8 * which : 2 * k + which;
-}
-
-// Row of the V tile held in slot rr of a lane's V registers.
-template <class C>
-__device__ __forceinline__ int v_row(int rr, int half) {
-  if constexpr (C::BF16_) return pair_row<C>(half * C::PAIRS + rr / 2, rr % 2);
-  else return rr;
-}
-
 // Registers of one block: the K tile as coalesced 16-byte vectors (lane i
-// holds vectors i, i+64, ...) and this lane's V column(s) of its rows.
+// holds vectors i, i+64, ...) and this lane's V columns of all 16 rows.
 // Each KV byte is read once per call, so the loads are non-temporal (they
 // stream past the caches instead of displacing other lines).
 template <class C>
 struct BlockRegs {
   u32x4 k[C::LOADS];
-  uint32_t v[C::ROWS][C::VW];
+  uint32_t v[16][C::DPL];
 };
 
 template <class C>
 __device__ __forceinline__ BlockRegs<C> load_block_regs(const uint8_t* __restrict__ cache, int phys,
                                                         int64_t block_bytes, int g,
                                                         int num_kv_heads, int64_t tile_bytes,
-                                                        int lane, int half, int col) {
+                                                        int lane) {
   const uint8_t* kbase = cache + int64_t(phys) * block_bytes + int64_t(g) * tile_bytes;
   const uint8_t* vbase = kbase + int64_t(num_kv_heads) * tile_bytes;
   BlockRegs<C> r;
@@ -182,12 +149,10 @@ __device__ __forceinline__ BlockRegs<C> load_block_regs(const uint8_t* __restric
   for (int i = 0; i < C::LOADS; ++i) r.k[i] = __builtin_nontemporal_load(kt + i * kWave + lane);
   const uint32_t* vt = reinterpret_cast<const uint32_t*>(vbase);
 #pragma unroll
-  for (int rr = 0; rr < C::ROWS; ++rr) {
-    const int row = v_row<C>(rr, half);
+  for (int row = 0; row < 16; ++row)
 #pragma unroll
-    for (int w = 0; w < C::VW; ++w)
-      r.v[rr][w] = __builtin_nontemporal_load(vt + row * (C::RB / 4) + col * C::VW + w);
-  }
+    for (int w = 0; w < C::DPL; ++w)
+      r.v[row][w] = __builtin_nontemporal_load(vt + row * (C::RB / 4) + lane * C::DPL + w);
   return r;
 }
 
@@ -217,28 +182,24 @@ struct LaneRoles {
   int tq;    // token within a QK pass
   int hg;    // head group
   int head;  // softmax head of this lane within the KV head's G query heads
-  int half;  // P.V: which half of the tile's rows (bf16 D = 64)
-  int col;   // P.V: dword column within a row
 };
 
-// The stages of one 16-token block (they run in this order for a block; the
-// 8-wave loop overlaps block k's P.V with block k + 1's scores):
+// The stages of one 16-token block, in order:
 //   block_scores   K tile through LDS, q.k of this lane's head and token(s);
 //   block_softmax  lazily moved softmax reference, P to LDS;
 //   pv_rescale     o *= alpha when the block moved the reference;
-//   pv_read        P words of this lane's rows for all heads, from LDS;
-//   pv_accumulate  P.V into the lane's output columns.
+//   pv_accumulate  P of each head from LDS, P.V into the lane's columns.
 // TAIL: only the first `valid` tokens of the block are inside the sequence
 // (1 <= valid <= 16).
 
 // Scores (log2 domain) of this lane's head for its token of each pass.
-template <int D, int G, bool BF16, bool TAIL>
-__device__ __forceinline__ void block_scores(const BlockRegs<DecodeCfg<D, G, BF16>>& cur, int valid,
-                                             const u32x4 (&q)[DecodeCfg<D, G, BF16>::HPL]
-                                                             [DecodeCfg<D, G, BF16>::CPL],
+template <int D, int G, bool TAIL>
+__device__ __forceinline__ void block_scores(const BlockRegs<F32Cfg<D, G>>& cur, int valid,
+                                             const u32x4 (&q)[F32Cfg<D, G>::HPL]
+                                                             [F32Cfg<D, G>::CPL],
                                              uint8_t* kt_lds, float scale_log2, const LaneRoles& r,
-                                             float (&x)[DecodeCfg<D, G, BF16>::NPASS]) {
-  using C = DecodeCfg<D, G, BF16>;
+                                             float (&x)[F32Cfg<D, G>::NPASS]) {
+  using C = F32Cfg<D, G>;
   const int lane = threadIdx.x & (kWave - 1);
 
   // K tile -> LDS (padded rows)
@@ -271,7 +232,7 @@ __device__ __forceinline__ void block_scores(const BlockRegs<DecodeCfg<D, G, BF1
     for (int i = 0; i < C::KGRP; ++i) {
       const int ps = (base + i) / C::CPL, c = (base + i) % C::CPL;
 #pragma unroll
-      for (int hh = 0; hh < C::HPL; ++hh) sacc[ps][hh] = chunk_dot<BF16>(q[hh][c], kv[i], sacc[ps][hh]);
+      for (int hh = 0; hh < C::HPL; ++hh) sacc[ps][hh] = chunk_dot(q[hh][c], kv[i], sacc[ps][hh]);
     }
   }
 #pragma unroll
@@ -294,15 +255,15 @@ __device__ __forceinline__ void block_scores(const BlockRegs<DecodeCfg<D, G, BF1
 // block's max exceeds it by more than kRescaleSlack (log2 units), so
 // P = 2^(s - m_run) <= 2^kRescaleSlack and most blocks neither reduce their
 // max across lanes nor rescale the accumulated output.  Writes P to LDS
-// (bf16 token pairs [head][pair], or fp32 [head][token]; replica lanes store
-// the same value to the same word) and, when the reference moved, each
+// ([head][token]; replica lanes store the same value to the same word) and,
+// when the reference moved, each
 // head's alpha; returns whether it moved (wave-uniform).  The caller orders
 // the P stores after any earlier reads of P (wave_lds_sync).
-template <int D, int G, bool BF16>
-__device__ __forceinline__ bool block_softmax(const float (&x)[DecodeCfg<D, G, BF16>::NPASS],
-                                              DecodeState<DecodeCfg<D, G, BF16>, G>& st,
+template <int D, int G>
+__device__ __forceinline__ bool block_softmax(const float (&x)[F32Cfg<D, G>::NPASS],
+                                              DecodeState<F32Cfg<D, G>, G>& st,
                                               uint32_t* p_lds, float* alpha_lds, const LaneRoles& r) {
-  using C = DecodeCfg<D, G, BF16>;
+  using C = F32Cfg<D, G>;
   float t = x[0];
 #pragma unroll
   for (int ps = 1; ps < C::NPASS; ++ps) t = fmaxf(t, x[ps]);
@@ -318,44 +279,20 @@ __device__ __forceinline__ bool block_softmax(const float (&x)[DecodeCfg<D, G, B
     st.l *= alpha;
     if (r.tq == 0 && r.dp < C::HPL) alpha_lds[r.head] = alpha;
   }
-  if constexpr (BF16) {
-    if constexpr (C::IN_LANE_PAIRS) {
+  float* pf = reinterpret_cast<float*>(p_lds);
 #pragma unroll
-      for (int ps = 0; ps < C::NPASS / 2; ++ps) {
-        const float p0 = __builtin_amdgcn_exp2f(x[ps] - st.m_run);
-        const float p1 = __builtin_amdgcn_exp2f(x[ps + C::NPASS / 2] - st.m_run);
-        const uint32_t pk = pack_bf16x2(p0, p1);      // tokens (k, k + 8)
-        st.l = dot2_bf16(pk, 0x3F803F80u, st.l);      // + both rounded values
-        p_lds[r.head * 8 + ps * C::TPP + r.tq] = pk;  // pair k = row of pass ps
-      }
-    } else {
-      const float p = __builtin_amdgcn_exp2f(x[0] - st.m_run);
-      const float pn = dpp_f<0x100 + C::DP>(p);  // row_shl: lane + DP = token + 1
-      const uint32_t pk = pack_bf16x2(p, pn);    // tokens (2k, 2k + 1) on even lanes
-      // (1.0, 0.0) as a bf16 pair, kept in a register: the assembler would
-      // encode the literal as the inline constant 1.0, which the hardware
-      // does not read as this pair
-      uint32_t lo_one = 0x00003F80u;
-      asm("" : "+v"(lo_one));
-      st.l = dot2_bf16(pk, lo_one, st.l);  // + this lane's rounded value
-      if ((r.tq & 1) == 0) p_lds[r.head * 8 + (r.tq >> 1)] = pk;
-    }
-  } else {
-    float* pf = reinterpret_cast<float*>(p_lds);
-#pragma unroll
-    for (int ps = 0; ps < C::NPASS; ++ps) {
-      const float p = __builtin_amdgcn_exp2f(x[ps] - st.m_run);
-      st.l += p;
-      pf[r.head * 16 + ps * C::TPP + r.tq] = p;
-    }
+  for (int ps = 0; ps < C::NPASS; ++ps) {
+    const float p = __builtin_amdgcn_exp2f(x[ps] - st.m_run);
+    st.l += p;
+    pf[r.head * 16 + ps * C::TPP + r.tq] = p;
   }
   return rescale;
 }
 
-template <int D, int G, bool BF16>
-__device__ __forceinline__ void pv_rescale(bool rescale, DecodeState<DecodeCfg<D, G, BF16>, G>& st,
+template <int D, int G>
+__device__ __forceinline__ void pv_rescale(bool rescale, DecodeState<F32Cfg<D, G>, G>& st,
                                            const float* alpha_lds) {
-  using C = DecodeCfg<D, G, BF16>;
+  using C = F32Cfg<D, G>;
   if (rescale) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -366,105 +303,57 @@ __device__ __forceinline__ void pv_rescale(bool rescale, DecodeState<DecodeCfg<D
   }
 }
 
-// P words of this lane's rows for HN heads starting at H0 (bf16: token
-// pairs of its half; fp32: all 16 tokens), read as 16-byte vectors.
-template <class C, int HN>
-struct PWords {
-  static constexpr int N = C::BF16_ ? C::PAIRS : 16;
-  uint32_t w[HN][N];
-};
-
-template <int D, int G, bool BF16, int H0, int HN>
-__device__ __forceinline__ void pv_read(const uint32_t* p_lds, const LaneRoles& r,
-                                        PWords<DecodeCfg<D, G, BF16>, HN>& pw) {
-  using C = DecodeCfg<D, G, BF16>;
-  constexpr int N = PWords<C, HN>::N;
-  const int off = BF16 ? r.half * C::PAIRS : 0;
-  constexpr int STRIDE = BF16 ? 8 : 16;
-#pragma unroll
-  for (int h = 0; h < HN; ++h)
-#pragma unroll
-    for (int k4 = 0; k4 < N; k4 += 4) {
-      const u32x4 t4 = *reinterpret_cast<const u32x4*>(p_lds + (H0 + h) * STRIDE + off + k4);
-      pw.w[h][k4] = t4.x; pw.w[h][k4 + 1] = t4.y; pw.w[h][k4 + 2] = t4.z; pw.w[h][k4 + 3] = t4.w;
-    }
-}
-
 // Rows past the sequence may hold anything: zero them in a tail block.
-template <int D, int G, bool BF16>
-__device__ __forceinline__ void mask_tail_rows(BlockRegs<DecodeCfg<D, G, BF16>>& cur, int valid,
-                                               const LaneRoles& r) {
-  using C = DecodeCfg<D, G, BF16>;
+template <int D, int G>
+__device__ __forceinline__ void mask_tail_rows(BlockRegs<F32Cfg<D, G>>& cur, int valid) {
+  using C = F32Cfg<D, G>;
 #pragma unroll
-  for (int rr = 0; rr < C::ROWS; ++rr)
+  for (int row = 0; row < 16; ++row)
 #pragma unroll
-    for (int w = 0; w < C::VW; ++w)
-      cur.v[rr][w] = v_row<C>(rr, r.half) < valid ? cur.v[rr][w] : 0u;
+    for (int w = 0; w < C::DPL; ++w) cur.v[row][w] = row < valid ? cur.v[row][w] : 0u;
 }
 
-template <int D, int G, bool BF16, int H0, int HN>
-__device__ __forceinline__ void pv_accumulate(const BlockRegs<DecodeCfg<D, G, BF16>>& cur,
-                                              const PWords<DecodeCfg<D, G, BF16>, HN>& pw,
-                                              DecodeState<DecodeCfg<D, G, BF16>, G>& st) {
-  using C = DecodeCfg<D, G, BF16>;
-  if constexpr (BF16) {
+// P.V: each head's 16 P values are read from LDS (four 16-byte reads, the
+// same words for every lane) and multiply the lane's V columns.
+template <int D, int G>
+__device__ __forceinline__ void pv_accumulate(const BlockRegs<F32Cfg<D, G>>& cur,
+                                              const uint32_t* p_lds,
+                                              DecodeState<F32Cfg<D, G>, G>& st) {
+  using C = F32Cfg<D, G>;
 #pragma unroll
-    for (int h = 0; h < HN; ++h) {
+  for (int h = 0; h < G; ++h) {
+    float p[16];
 #pragma unroll
-      for (int k = 0; k < C::PAIRS; ++k) {
-        const uint32_t v0 = cur.v[2 * k][0], v1 = cur.v[2 * k + 1][0];
-        const uint32_t xlo = __builtin_amdgcn_perm(v1, v0, 0x05040100u);  // (v0.lo, v1.lo)
-        const uint32_t xhi = __builtin_amdgcn_perm(v1, v0, 0x07060302u);  // (v0.hi, v1.hi)
-        st.o[H0 + h][0] = dot2_bf16(xlo, pw.w[h][k], st.o[H0 + h][0]);
-        st.o[H0 + h][1] = dot2_bf16(xhi, pw.w[h][k], st.o[H0 + h][1]);
-      }
+    for (int k4 = 0; k4 < 16; k4 += 4) {
+      const u32x4 t4 = *reinterpret_cast<const u32x4*>(p_lds + h * 16 + k4);
+      p[k4] = __uint_as_float(t4.x);
+      p[k4 + 1] = __uint_as_float(t4.y);
+      p[k4 + 2] = __uint_as_float(t4.z);
+      p[k4 + 3] = __uint_as_float(t4.w);
     }
-  } else {
 #pragma unroll
-    for (int h = 0; h < HN; ++h) {
+    for (int row = 0; row < 16; ++row)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const float p = __uint_as_float(pw.w[h][rr]);
-#pragma unroll
-        for (int w = 0; w < C::VW; ++w)
-          st.o[H0 + h][w] = fmaf(p, __uint_as_float(cur.v[rr][w]), st.o[H0 + h][w]);
-      }
-    }
+      for (int w = 0; w < C::DPL; ++w) st.o[h][w] = fmaf(p[row], __uint_as_float(cur.v[row][w]), st.o[h][w]);
   }
 }
 
-// P.V over all heads, the P words read in groups of PGRP heads (each
-// group's reads issued together).
-template <int D, int G, bool BF16, int H0 = 0>
-__device__ __forceinline__ void pv_grouped(const BlockRegs<DecodeCfg<D, G, BF16>>& cur,
-                                           const uint32_t* p_lds, const LaneRoles& r,
-                                           DecodeState<DecodeCfg<D, G, BF16>, G>& st) {
-  using C = DecodeCfg<D, G, BF16>;
-  constexpr int HN = BF16 ? C::PGRP : 1;
-  if constexpr (H0 < G) {
-    PWords<C, HN> pw;
-    pv_read<D, G, BF16, H0, HN>(p_lds, r, pw);
-    pv_accumulate<D, G, BF16, H0, HN>(cur, pw, st);
-    pv_grouped<D, G, BF16, H0 + HN>(cur, p_lds, r, st);
-  }
-}
-
-// One block, stage after stage (the 4- and 2-wave loop and every tail block).
-template <int D, int G, bool BF16, bool TAIL>
-__device__ __forceinline__ void process_block(BlockRegs<DecodeCfg<D, G, BF16>>& cur, int valid,
-                                            const u32x4 (&q)[DecodeCfg<D, G, BF16>::HPL]
-                                                            [DecodeCfg<D, G, BF16>::CPL],
-                                            DecodeState<DecodeCfg<D, G, BF16>, G>& st,
+// One block, stage after stage.
+template <int D, int G, bool TAIL>
+__device__ __forceinline__ void process_block(BlockRegs<F32Cfg<D, G>>& cur, int valid,
+                                            const u32x4 (&q)[F32Cfg<D, G>::HPL]
+                                                            [F32Cfg<D, G>::CPL],
+                                            DecodeState<F32Cfg<D, G>, G>& st,
                                             uint8_t* kt_lds, uint32_t* p_lds, float* alpha_lds,
                                             float scale_log2, const LaneRoles& r) {
-  using C = DecodeCfg<D, G, BF16>;
+  using C = F32Cfg<D, G>;
   float x[C::NPASS];
-  block_scores<D, G, BF16, TAIL>(cur, valid, q, kt_lds, scale_log2, r, x);
-  const bool rescale = block_softmax<D, G, BF16>(x, st, p_lds, alpha_lds, r);
+  block_scores<D, G, TAIL>(cur, valid, q, kt_lds, scale_log2, r, x);
+  const bool rescale = block_softmax<D, G>(x, st, p_lds, alpha_lds, r);
   wave_lds_sync();
-  if constexpr (TAIL) mask_tail_rows<D, G, BF16>(cur, valid, r);
-  pv_rescale<D, G, BF16>(rescale, st, alpha_lds);
-  pv_grouped<D, G, BF16>(cur, p_lds, r, st);
+  if constexpr (TAIL) mask_tail_rows<D, G>(cur, valid);
+  pv_rescale<D, G>(rescale, st, alpha_lds);
+  pv_accumulate<D, G>(cur, p_lds, st);
 }
 
 // Arguments of one decode launch (passed by value as the kernel argument).
@@ -495,7 +384,7 @@ struct DecodeParams {
 template <class C>
 __device__ __forceinline__ void append_new_token(BlockRegs<C>& rg, const DecodeParams& a, int b,
                                                  int g, int row, int phys, int64_t block_bytes,
-                                                 int64_t tile_bytes, int lane, int half, int col) {
+                                                 int64_t tile_bytes, int lane) {
   const int64_t src = (int64_t(b) * a.num_kv_heads + g) * C::RB;
   const bool store = phys >= 0 && phys < a.num_blocks;
   uint8_t* kbase = const_cast<uint8_t*>(a.cache) + int64_t(store ? phys : 0) * block_bytes +
@@ -513,13 +402,13 @@ __device__ __forceinline__ void append_new_token(BlockRegs<C>& rg, const DecodeP
     }
   }
 #pragma unroll
-  for (int rr = 0; rr < C::ROWS; ++rr) {
-    if (v_row<C>(rr, half) == row) {
+  for (int rr = 0; rr < 16; ++rr) {
+    if (rr == row) {
 #pragma unroll
-      for (int w = 0; w < C::VW; ++w) {
-        const uint32_t x = nv[col * C::VW + w];
+      for (int w = 0; w < C::DPL; ++w) {
+        const uint32_t x = nv[lane * C::DPL + w];
         rg.v[rr][w] = x;
-        if (store) reinterpret_cast<uint32_t*>(vbase)[row * (C::RB / 4) + col * C::VW + w] = x;
+        if (store) reinterpret_cast<uint32_t*>(vbase)[row * (C::RB / 4) + lane * C::DPL + w] = x;
       }
     }
   }
@@ -544,7 +433,7 @@ struct MfmaCfg {
 // loop keeps P in registers); and the merge state.
 template <int D, int G, bool BF16, int NW>
 struct DecodeSmem {
-  using C = DecodeCfg<D, G, BF16>;
+  using C = F32Cfg<D, G>;
   static constexpr int kTiles = NW * (BF16 ? MfmaCfg<D>::TILE : C::LDS_TILE);
   static constexpr int kOStage = NW * G * D * 4;
   static constexpr int kSubsets = NW * kWave * 16;
@@ -864,11 +753,11 @@ __device__ __forceinline__ void mfma_blocks(const DecodeParams& a, DecodeSmem<D,
 // fp32 blocks on the vector ALUs: q.k through the LDS K tile, P through
 // LDS.  Leaves this wave's (m, l) in sm.m / sm.l and its unnormalised output
 // rows in the LDS output stage, then synchronises the workgroup.
-template <int D, int G, bool BF16, int NW, bool APPEND>
-__device__ __forceinline__ void valu_blocks(const DecodeParams& a, DecodeSmem<D, G, BF16, NW>& sm,
+template <int D, int G, int NW, bool APPEND>
+__device__ __forceinline__ void valu_blocks(const DecodeParams& a, DecodeSmem<D, G, false, NW>& sm,
                                             int b, int g, int L, int nblk, int blk_lo,
                                             int blk_hi) {
-  using C = DecodeCfg<D, G, BF16>;
+  using C = F32Cfg<D, G>;
   const uint8_t* __restrict__ cache = a.cache;
   const int num_blocks = a.num_blocks, num_kv_heads = a.num_kv_heads;
   const float scale_log2 = a.scale_log2;
@@ -880,9 +769,7 @@ __device__ __forceinline__ void valu_blocks(const DecodeParams& a, DecodeSmem<D,
   r.tq = (lane / C::DP) % C::TPP;
   r.hg = lane / (C::DP * C::TPP);
   r.head = r.hg * C::HPL + r.dp % C::HPL;
-  r.half = C::HALVES == 2 ? (lane >> 5) : 0;
-  r.col = C::HALVES == 2 ? (lane & 31) : lane;  // dword column within the row
-  const int dp = r.dp, hg = r.hg, half = r.half, col = r.col;
+  const int dp = r.dp, hg = r.hg;
 
   // ---- query chunks for this lane: heads hg*HPL + hh, chunks dp*CPL + c
   u32x4 q[C::HPL][C::CPL];
@@ -934,7 +821,7 @@ __device__ __forceinline__ void valu_blocks(const DecodeParams& a, DecodeSmem<D,
 #pragma unroll
     for (int s = 0; s < PD; ++s)
       buf[s] = load_block_regs<C>(cache, __builtin_amdgcn_readlane(ids_cur, s), block_bytes, g,
-                                  num_kv_heads, tile_bytes, lane, half, col);
+                                  num_kv_heads, tile_bytes, lane);
     // Only the sequence's last block can be partial; it is the last block of
     // the wave that owns it and is processed after the loop, so the loop
     // body needs no masking.  In append mode that block (partial or not)
@@ -948,10 +835,10 @@ __device__ __forceinline__ void valu_blocks(const DecodeParams& a, DecodeSmem<D,
 #pragma unroll
       for (int s = 0; s < PD; ++s) {
         if (k0 + s < nfull)
-          process_block<D, G, BF16, false>(buf[s], 16, q, st, kt_lds, p_lds, sm.alpha[wave],
+          process_block<D, G, false>(buf[s], 16, q, st, kt_lds, p_lds, sm.alpha[wave],
                                            scale_log2, r);
         buf[s] = load_block_regs<C>(cache, __builtin_amdgcn_readlane(ids_next, s), block_bytes, g,
-                                    num_kv_heads, tile_bytes, lane, half, col);
+                                    num_kv_heads, tile_bytes, lane);
       }
       ids_next = ids_after;
     }
@@ -960,9 +847,9 @@ __device__ __forceinline__ void valu_blocks(const DecodeParams& a, DecodeSmem<D,
       if constexpr (APPEND) {
         if (seq_last)
           append_new_token<C>(buf[0], a, b, g, (L - 1) & 15, bt_row[nblk - 1], block_bytes,
-                              tile_bytes, lane, half, col);
+                              tile_bytes, lane);
       }
-      process_block<D, G, BF16, true>(buf[0], min(tail_valid, 16), q, st, kt_lds, p_lds,
+      process_block<D, G, true>(buf[0], min(tail_valid, 16), q, st, kt_lds, p_lds,
                                       sm.alpha[wave], scale_log2, r);
     }
   }
@@ -979,21 +866,12 @@ __device__ __forceinline__ void valu_blocks(const DecodeParams& a, DecodeSmem<D,
       sm.l[wave][r.head] = lsum;
     }
   }
-  if constexpr (C::HALVES == 2) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int jj = 0; jj < C::DPL; ++jj) st.o[h][jj] += __shfl_xor(st.o[h][jj], 32, kWave);
-  }
   __syncthreads();  // all waves done with their tiles: reuse smem_k for o
   float* o_lds = reinterpret_cast<float*>(sm.k);  // [wave][G][D]
-  if (C::HALVES == 1 || half == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int jj = 0; jj < C::DPL; ++jj)
-        o_lds[(wave * G + h) * D + col * C::DPL + jj] = st.o[h][jj];
-  }
+    for (int jj = 0; jj < C::DPL; ++jj) o_lds[(wave * G + h) * D + lane * C::DPL + jj] = st.o[h][jj];
   __syncthreads();
 }
 
@@ -1018,7 +896,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
   if constexpr (BF16)
     mfma_blocks<D, G, NW, APPEND>(a, sm, b, g, L, nblk, blk_lo, blk_hi);
   else
-    valu_blocks<D, G, BF16, NW, APPEND>(a, sm, b, g, L, nblk, blk_lo, blk_hi);
+    valu_blocks<D, G, NW, APPEND>(a, sm, b, g, L, nblk, blk_lo, blk_hi);
   float* o_lds = reinterpret_cast<float*>(sm.k);  // [wave][G][D]
 
   const bool single = nparts <= 1;
