@@ -166,8 +166,9 @@ int pa_reshape_and_cache(const void* key, const void* value,
 
 /* Device workspace pa_decode needs for split-K, in bytes: a fixed region of
  * 65536 arrival counters (one per (sequence, KV head), so B * H_kv <= 65536
- * with split-K) followed by the per-partition partials (max, denominator,
- * normalised output; fp32).  0 when partition_size == 0 or one partition
+ * with split-K) followed by one fp32 record per (sequence, KV head,
+ * partition): the G heads' normalised outputs, maxima and denominators,
+ * padded to 128-byte lines.  0 when partition_size == 0 or one partition
  * covers max_seq_len.  A workspace sized for the largest shape serves calls
  * of any smaller shape. */
 size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads,

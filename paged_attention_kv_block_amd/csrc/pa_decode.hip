@@ -54,6 +54,14 @@ constexpr float kLn2 = 0.6931471805599453f;
 // before the reference moves; P then stays <= 2^8.
 constexpr float kRescaleSlack = 8.f;
 
+// Split-K partial of one (sequence, KV head, partition): the G heads'
+// normalised outputs [G][D] in the cache's precision (bf16 or fp32), then
+// their maxima [G] and denominators [G] in fp32 in a 128-byte line of their
+// own.  One work item writes one contiguous record; writes into a
+// read-saturated HBM cost far more than their bytes, so bf16 outputs are
+// not widened.  Records are sized for fp32 outputs.
+constexpr int64_t ws_record_bytes(int64_t G, int64_t D) { return G * D * 4 + 128; }
+
 // Shapes of the fp32 block loop on the vector ALUs.  The K tile goes
 // through LDS and is read back as (token, head group, d-part) per lane, so
 // q.k needs a cross-lane sum over the d-parts only; for P.V each lane owns
@@ -93,6 +101,9 @@ struct F32Cfg {
 __device__ __forceinline__ void coherent_store(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void coherent_store_u32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -107,6 +118,12 @@ __device__ __forceinline__ float ws_load(__amdgpu_buffer_rsrc_t r, int byte_off)
 }
 __device__ __forceinline__ f32x4 ws_load4(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kSc1));
+}
+// Four bf16 values (8 bytes) widened to fp32.
+__device__ __forceinline__ f32x4 ws_load_bf16x4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t w = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, kSc1));
+  return f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
 }
 
 template <bool BF16>
@@ -366,9 +383,7 @@ struct DecodeParams {
   const int* seq_lens;
   const int* plan;        // (part << 16 | b) entries, or nullptr: virtual grid
   int* ws_count;
-  float* ws_m;
-  float* ws_l;
-  float* ws_o;
+  uint8_t* ws_rec;        // split-K records, [b * H_kv + g][max_parts]
   const void* new_k;      // append mode: the new token's K/V per sequence, [B][H_kv][D];
   const void* new_v;      // nullptr: the cache already holds token L - 1
   int num_blocks, max_blocks_per_seq, max_seq_len, num_kv_heads, B;
@@ -885,9 +900,9 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
   float* __restrict__ lse_out = a.lse_out;
   const int num_kv_heads = a.num_kv_heads, max_parts = a.max_parts;
   int* __restrict__ ws_count = a.ws_count;
-  float* __restrict__ ws_m = a.ws_m;
-  float* __restrict__ ws_l = a.ws_l;
-  float* __restrict__ ws_o = a.ws_o;
+  constexpr int REC = int(ws_record_bytes(G, D));
+  constexpr int ML = G * D * (BF16 ? 2 : 4);  // offset of the maxima within a record
+  uint8_t* __restrict__ recs = a.ws_rec + int64_t(b * num_kv_heads + g) * max_parts * REC;
   const int H_q = num_kv_heads * G;
   const int blk_lo = part * pb;
   const int blk_hi = min(blk_lo + pb, nblk);
@@ -901,35 +916,58 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
 
   const bool single = nparts <= 1;
   const int tid = threadIdx.x;
-  for (int e = tid; e < G * D; e += NW * kWave) {
-    const int h = e / D, d = e % D;
-    float M = -INFINITY;
+  // head h's (M, sum l, sum o[d]) over the waves, each wave weighted by
+  // 2^(m_w - M) (0 for a wave with no tokens)
+  auto wave_merge = [&](int h, int d, float& M, float& lsum, float& acc) {
+    M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.m[w][h]);
-    float lsum = 0.f, acc = 0.f;
+    lsum = 0.f;
+    acc = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const float wt = __builtin_amdgcn_exp2f(sm.m[w][h] - M);  // 0 for a wave with no tokens
+        const float wt = __builtin_amdgcn_exp2f(sm.m[w][h] - M);
         lsum += wt * sm.l[w][h];
         acc += wt * o_lds[(w * G + h) * D + d];
       }
     }
-    const int64_t row = int64_t(b) * H_q + g * G + h;
-    if (single) {
-      const float val = lsum > 0.f ? acc / lsum : 0.f;
-      store_out<BF16>(out, row * D + d, val);
+  };
+  if (single) {
+    for (int e = tid; e < G * D; e += NW * kWave) {
+      const int h = e / D, d = e % D;
+      float M, lsum, acc;
+      wave_merge(h, d, M, lsum, acc);
+      const int64_t row = int64_t(b) * H_q + g * G + h;
+      store_out<BF16>(out, row * D + d, lsum > 0.f ? acc / lsum : 0.f);
       if (lse_out && d == 0) lse_out[row] = lsum > 0.f ? M * kLn2 + logf(lsum) : -INFINITY;
+    }
+    return;
+  }
+  // this partition's record: the outputs, then the maxima and sums
+  uint8_t* rec = recs + int64_t(part) * REC;
+  constexpr int PER = BF16 ? 2 : 1;  // outputs per 4-byte store
+  for (int e = tid; e < G * D / PER; e += NW * kWave) {
+    const int h = e / (D / PER), d = PER * (e % (D / PER));
+    float M, lsum, a0;
+    wave_merge(h, d, M, lsum, a0);
+    if constexpr (BF16) {
+      float a1;
+      wave_merge(h, d + 1, M, lsum, a1);
+      const float o0 = lsum > 0.f ? a0 / lsum : 0.f, o1 = lsum > 0.f ? a1 / lsum : 0.f;
+      coherent_store_u32(reinterpret_cast<uint32_t*>(rec + (h * D + d) * 2),
+                         (f32_to_bf16_rne(o0) & 0xFFFFu) | (f32_to_bf16_rne(o1) << 16));
     } else {
-      const int64_t prow = row * max_parts + part;
-      coherent_store(ws_o + prow * D + d, lsum > 0.f ? acc / lsum : 0.f);
-      if (d == 0) {
-        coherent_store(ws_m + prow, M);
-        coherent_store(ws_l + prow, lsum);
-      }
+      coherent_store(reinterpret_cast<float*>(rec) + h * D + d, lsum > 0.f ? a0 / lsum : 0.f);
+    }
+    if (d == 0) {
+      sm.M[h] = M;
+      sm.W[h] = lsum;
     }
   }
-  if (single) return;
+  __syncthreads();
+  if (tid < 2 * G)  // the maxima and sums in one store
+    coherent_store(reinterpret_cast<float*>(rec + ML) + tid, tid < G ? sm.M[tid] : sm.W[tid - G]);
 
   // ---- split-K: the last workgroup of this (sequence, KV head) to finish
   // merges all partitions.  Partials are written and read with accesses that
@@ -953,20 +991,18 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
   // fetch past this XCD's L2 (which may hold stale lines from an earlier
   // call), but as plain loads many of them can be in flight at once.
   const int64_t row0 = int64_t(b) * H_q + int64_t(g) * G;
-  const __amdgpu_buffer_rsrc_t rm = ws_rsrc(ws_m + row0 * max_parts, G * max_parts * 4);
-  const __amdgpu_buffer_rsrc_t rl = ws_rsrc(ws_l + row0 * max_parts, G * max_parts * 4);
-  const __amdgpu_buffer_rsrc_t ro = ws_rsrc(ws_o + row0 * max_parts * D, G * max_parts * D * 4);
+  const __amdgpu_buffer_rsrc_t rr = ws_rsrc(reinterpret_cast<const float*>(recs), max_parts * REC);
+  auto m_off = [&](int h, int p) { return p * REC + ML + h * 4; };
+  auto l_off = [&](int h, int p) { return p * REC + ML + (G + h) * 4; };
 
   // per head: M = max_p m_p and W = sum_p 2^(m_p - M) l_p (one wave per head)
   for (int h = wave; h < G; h += NW) {
     float M = -INFINITY;
-    for (int p = lane; p < nparts; p += kWave) M = fmaxf(M, ws_load(rm, (h * max_parts + p) * 4));
+    for (int p = lane; p < nparts; p += kWave) M = fmaxf(M, ws_load(rr, m_off(h, p)));
     M = allreduce_max<0, 6>(M);
     float W = 0.f;
-    for (int p = lane; p < nparts; p += kWave) {
-      const int off = (h * max_parts + p) * 4;
-      W += exp2f(ws_load(rm, off) - M) * ws_load(rl, off);
-    }
+    for (int p = lane; p < nparts; p += kWave)
+      W += exp2f(ws_load(rr, m_off(h, p)) - M) * ws_load(rr, l_off(h, p));
     W = allreduce_sum<0, 6>(W);
     if (lane == 0) { sm.M[h] = M; sm.W[h] = W; }
   }
@@ -993,8 +1029,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
     const int pc = min(WCAP, nparts - p0);
     for (int idx = tid; idx < G * pc; idx += NT) {
       const int h = idx / pc, pp = idx % pc;
-      const int off = (h * max_parts + p0 + pp) * 4;
-      wbuf[h * WCAP + pp] = exp2f(ws_load(rm, off) - sm.M[h]) * ws_load(rl, off);
+      wbuf[h * WCAP + pp] = exp2f(ws_load(rr, m_off(h, p0 + pp)) - sm.M[h]) * ws_load(rr, l_off(h, p0 + pp));
     }
     __syncthreads();
 #pragma unroll
@@ -1009,7 +1044,10 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
         for (int j = 0; j < MB; ++j) {
           const int p = pp + j * S;
           const int pl = p < pc ? p : pc - 1;  // in range; weight 0 past the chunk
-          v[j] = ws_load4(ro, ((h * max_parts + p0 + pl) * D + d4 * 4) * 4);
+          if constexpr (BF16)
+            v[j] = ws_load_bf16x4(rr, (p0 + pl) * REC + (h * D + d4 * 4) * 2);
+          else
+            v[j] = ws_load4(rr, (p0 + pl) * REC + (h * D + d4 * 4) * 4);
           w[j] = p < pc ? wh[pl] : 0.f;
         }
 #pragma unroll
@@ -1189,27 +1227,24 @@ static int64_t parts_for(int max_seq_len, int partition_size) {
   return (int64_t(max_seq_len) + partition_size - 1) / partition_size;
 }
 
-// Workspace layout (all offsets 256-byte aligned):
-//   [arrival counters: kCounterCap int32][m: rows][l: rows][o: rows * D]
-// with rows = B * H_q * partitions.  Counter (b, g) sits at index
+// Workspace layout:
+//   [arrival counters: kCounterCap int32][records: B * H_kv * partitions]
+// with one split-K record per (sequence, KV head, partition) (see
+// ws_record_floats).  Counter (b, g) sits at index
 // b * H_kv + g of a region of fixed size, so calls of any shape can share
 // one workspace without their partials overlapping another shape's
 // counters.  Only the counters need a defined initial value (zero); every
 // completed call leaves them at zero.
 constexpr int64_t kCounterCap = 65536;
 struct WsLayout {
-  int64_t count_off, m_off, l_off, o_off, total;
+  int64_t count_off, rec_off, total;
 };
 static inline int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
 static WsLayout ws_layout(int64_t B, int64_t H_q, int64_t H_kv, int64_t D, int64_t P) {
   WsLayout w{};
-  const int64_t rows = B * H_q * P;
-  (void)H_kv;
   w.count_off = 0;
-  w.m_off = kCounterCap * 4;
-  w.l_off = w.m_off + round256(rows * 4);
-  w.o_off = w.l_off + round256(rows * 4);
-  w.total = w.o_off + rows * D * 4;
+  w.rec_off = round256(kCounterCap * 4);
+  w.total = w.rec_off + B * H_kv * P * ws_record_bytes(H_q / H_kv, D);
   return w;
 }
 
@@ -1355,9 +1390,7 @@ static int decode_call(const char* fn, void* out, float* lse_out, const void* qu
     const WsLayout w = ws_layout(B, num_q_heads, num_kv_heads, head_size, P);
     uint8_t* base = static_cast<uint8_t*>(workspace);
     a.ws_count = reinterpret_cast<int*>(base + w.count_off);
-    a.ws_m = reinterpret_cast<float*>(base + w.m_off);
-    a.ws_l = reinterpret_cast<float*>(base + w.l_off);
-    a.ws_o = reinterpret_cast<float*>(base + w.o_off);
+    a.ws_rec = base + w.rec_off;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   bool ok;
