@@ -17,6 +17,7 @@ and obvious code:
   gather_kv                               pool + block table -> logical K/V
   attention                               softmax(scale * q K^T) V, and lse
   decode, prefill_chunk                   the two attention entry points
+  fp8: e4m3_encode/decode, quantize      the FP8 (E4M3) KV-cache codec
 
 Pins (tests/test_oracle_*.py) tie each function to something other than
 itself: hand-worked fixtures under tests/golden/, closed forms, torch's
@@ -34,6 +35,14 @@ from .paged_attention import (  # noqa: F401
     prefill_chunk,
     to_f64,
     empty_pool,
+)
+from .fp8 import (  # noqa: F401
+    E4M3_MAX,
+    e4m3_decode,
+    e4m3_encode,
+    e4m3_decode_array,
+    e4m3_encode_array,
+    quantize,
 )
 from .allocator import (  # noqa: F401
     OracleAllocator,

@@ -36,6 +36,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from .fp8 import e4m3_decode_array
+
 
 # ---------------------------------------------------------------------------
 # closed forms
@@ -62,8 +64,11 @@ def num_blocks_for_budget(budget_bytes: int, block_bytes: int, num_layers: int) 
 # ---------------------------------------------------------------------------
 def to_f64(x: np.ndarray) -> np.ndarray:
     """Exact float64 value of stored elements: float32 arrays are widened;
-    uint16 arrays are bf16 bit patterns (the top half of a float32)."""
+    uint16 arrays are bf16 bit patterns (the top half of a float32); uint8
+    arrays are FP8 E4M3 codes (oracle/fp8.py), before any scale."""
     x = np.asarray(x)
+    if x.dtype == np.uint8:
+        return e4m3_decode_array(x)
     if x.dtype == np.uint16:
         wide = x.astype(np.uint32) * np.uint32(65536)
         return wide.view(np.float32).astype(np.float64)
@@ -160,14 +165,16 @@ def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
 
 
 def decode(query: np.ndarray, pool: np.ndarray, block_tables: np.ndarray,
-           seq_lens, scale: float, seqs=None):
+           seq_lens, scale: float, seqs=None, k_scale: float = 1.0,
+           v_scale: float = 1.0):
     """One query token per sequence (the sequence's last token, already in the
     cache) attending to all seq_len[b] cached tokens through its block table.
 
     query [B, H_q, D] (stored dtype), pool [N][2][H_kv][bs][D],
     block_tables int32 [B, max_blocks] (padding entries are never read).
     Returns (out [B, H_q, D] float64, lse [B, H_q] float64); ``seqs`` limits
-    the work to a subset of sequences (other rows stay NaN)."""
+    the work to a subset of sequences (other rows stay NaN).  An FP8 pool
+    holds codes: keys and values are their values times k_scale / v_scale."""
     B, Hq, D = query.shape
     Hkv = pool.shape[2]
     assert Hq % Hkv == 0
@@ -177,6 +184,7 @@ def decode(query: np.ndarray, pool: np.ndarray, block_tables: np.ndarray,
     for b in (range(B) if seqs is None else seqs):
         L = int(seq_lens[b])
         K, V = gather_kv(pool, block_tables[b], L)
+        K, V = K * float(k_scale), V * float(v_scale)
         qb = to_f64(query[b])
         for g in range(Hkv):
             heads = slice(g * G, (g + 1) * G)          # query heads of KV head g
