@@ -61,7 +61,10 @@ typedef enum {
   PA_EHIP = 4        /* the HIP runtime reported an error at launch */
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+/* PA_FP8: an FP8 (OCP E4M3) KV cache with per-tensor key/value scales; the
+ * queries and outputs around it are bf16 (pa_reshape_and_cache_fp8,
+ * pa_decode_fp8). */
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8 = 2 } pa_dtype;
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* pa_last_error(void);
@@ -164,6 +167,27 @@ int pa_reshape_and_cache(const void* key, const void* value,
                          int32_t block_size, int32_t num_kv_heads,
                          int32_t head_size, int32_t dtype, void* stream);
 
+/* FP8 cache write: keys/values arrive in bf16 and are stored as FP8 (OCP
+ * E4M3) codes, one byte per element, in the same pool layout ("Inside
+ * vLLM", "LLM Engine constructor", for the cache; the FP8 format and the
+ * scales are this library's reading, as the pages fix none).  Element x of
+ * the keys becomes the E4M3 code of x / k_scale, computed in fp32 with IEEE
+ * division, saturated at +-448 and rounded to nearest even, sign kept; the
+ * values likewise with v_scale.  The cache then represents code * scale.
+ *   key, value   [num_tokens][num_kv_heads][head_size] bf16, device,
+ *                16-byte aligned
+ *   slot_mapping as pa_reshape_and_cache
+ *   kv_cache     [num_blocks][2][num_kv_heads][16][head_size] uint8, device,
+ *                16-byte aligned
+ *   k_scale, v_scale  positive and finite (PA_EINVAL otherwise)
+ * block_size 16, head_size 64 or 128. */
+int pa_reshape_and_cache_fp8(const void* key, const void* value,
+                             const int64_t* slot_mapping, int32_t num_tokens,
+                             void* kv_cache, int32_t num_blocks,
+                             int32_t block_size, int32_t num_kv_heads,
+                             int32_t head_size, float k_scale, float v_scale,
+                             void* stream);
+
 /* Device workspace pa_decode needs for split-K, in bytes: a fixed region of
  * 65536 arrival counters (one per (sequence, KV head), so B * H_kv <= 65536
  * with split-K) followed by one fp32 record per (sequence, KV head,
@@ -259,6 +283,23 @@ int pa_decode_append(void* out, float* lse_out, const void* query,
                      int32_t head_size, int32_t block_size, float scale,
                      int32_t partition_size, const int32_t* plan, int32_t plan_entries,
                      void* workspace, size_t workspace_bytes, int32_t dtype, void* stream);
+
+/* pa_decode over an FP8 cache written by pa_reshape_and_cache_fp8: keys and
+ * values are their codes times k_scale / v_scale, and the result is
+ * pa_decode's on those values (scores scale * q . (code * k_scale)).
+ * query and out are bf16; lse_out, the workspace, plan and every other
+ * argument as pa_decode.  E4M3 codes are exact in bf16, so the products run
+ * on the same bf16 matrix-core path; k_scale folds into the score scale and
+ * v_scale into the outputs.  Same shapes as pa_decode's bf16 path. */
+int pa_decode_fp8(void* out, float* lse_out, const void* query,
+                  const void* kv_cache, int32_t num_blocks,
+                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* seq_lens, int32_t B, int32_t max_seq_len,
+                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
+                  int32_t block_size, float scale, float k_scale, float v_scale,
+                  int32_t partition_size, const int32_t* plan,
+                  int32_t plan_entries, void* workspace, size_t workspace_bytes,
+                  void* stream);
 
 /* Chunked prefill ("Im Inneren von vLLM", "Fortgeschrittene Funktionen":
  * long prompts are split into chunks; "Inside vLLM", "Generate function":

@@ -40,9 +40,104 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   cache[vbase] = vx;
 }
 
+// FP8 cache write: each thread quantises one 16-byte vector of 8 bf16 inputs
+// into 8 bytes of the pool [num_blocks][2][H_kv][16][D] (one byte per
+// element).  An element x becomes the OCP E4M3 code of x / scale computed in
+// fp32 (IEEE division), saturated at +-448 and rounded to nearest even by the
+// hardware conversion, with its sign.  The pages name an FP8 KV cache but no
+// format or scale; this is the reading the reference side implements too.
+__device__ __forceinline__ uint32_t bf16x2_lo(uint32_t w) { return w << 16; }
+__device__ __forceinline__ uint32_t bf16x2_hi(uint32_t w) { return w & 0xFFFF0000u; }
+
+__device__ __forceinline__ float e4m3_input(uint32_t bits, float scale) {
+  const float q = __uint_as_float(bits) / scale;
+  return fminf(fmaxf(q, -448.f), 448.f);
+}
+
+__device__ __forceinline__ uint2 quantize8(const uint4& x, float scale) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t out[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t a = w[2 * h], b = w[2 * h + 1];
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_input(bf16x2_lo(a), scale),
+                                           e4m3_input(bf16x2_hi(a), scale), 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_input(bf16x2_lo(b), scale),
+                                       e4m3_input(bf16x2_hi(b), scale), r, true);
+    out[h] = uint32_t(r);
+  }
+  return make_uint2(out[0], out[1]);
+}
+
+template <int VPR>  // 16-byte input vectors per head row (D / 8)
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
+    const uint4* __restrict__ key, const uint4* __restrict__ value,
+    const int64_t* __restrict__ slot_mapping, int num_tokens, uint2* __restrict__ cache,
+    int64_t num_slots, int num_kv_heads, float k_scale, float v_scale) {
+  const int64_t per_token = int64_t(num_kv_heads) * VPR;
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= per_token * num_tokens) return;
+  const int64_t t = idx / per_token;
+  const int rem = int(idx - t * per_token);
+  const int h = rem / VPR, v = rem % VPR;
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / kBlockSize;
+  const int off = int(slot % kBlockSize);
+  // 8-byte units: a cache row of D bytes is VPR units, as the input row is
+  // VPR 16-byte vectors
+  const int64_t kbase = ((blk * 2) * num_kv_heads + h) * (kBlockSize * VPR) + off * VPR + v;
+  const int64_t vbase = kbase + int64_t(num_kv_heads) * kBlockSize * VPR;
+  cache[kbase] = quantize8(key[idx], k_scale);
+  cache[vbase] = quantize8(value[idx], v_scale);
+}
+
 }  // namespace pa
 
 using namespace pa;
+
+extern "C" int pa_reshape_and_cache_fp8(const void* key, const void* value,
+                                        const int64_t* slot_mapping, int32_t num_tokens,
+                                        void* kv_cache, int32_t num_blocks, int32_t block_size,
+                                        int32_t num_kv_heads, int32_t head_size, float k_scale,
+                                        float v_scale, void* stream) {
+  if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0)
+    return fail(PA_EINVAL,
+                "pa_reshape_and_cache_fp8: bad sizes (tokens %d, blocks %d, kv heads %d)",
+                num_tokens, num_blocks, num_kv_heads);
+  if (block_size != kBlockSize)
+    return fail(PA_ENOTSUP, "pa_reshape_and_cache_fp8: block_size %d (only 16)", block_size);
+  if (head_size != 64 && head_size != 128)
+    return fail(PA_ENOTSUP, "pa_reshape_and_cache_fp8: head_size %d (64 or 128)", head_size);
+  if (!(k_scale > 0.f && k_scale < INFINITY && v_scale > 0.f && v_scale < INFINITY))
+    return fail(PA_EINVAL, "pa_reshape_and_cache_fp8: scales must be positive and finite");
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !slot_mapping || !kv_cache)
+    return fail(PA_EINVAL, "pa_reshape_and_cache_fp8: NULL pointer");
+  if ((uintptr_t(key) | uintptr_t(value) | uintptr_t(kv_cache)) & 15)
+    return fail(PA_EINVAL, "pa_reshape_and_cache_fp8: key/value/cache must be 16-byte aligned");
+  if (uintptr_t(slot_mapping) & 7)
+    return fail(PA_EINVAL, "pa_reshape_and_cache_fp8: slot_mapping must be 8-byte aligned");
+  const int vpr = head_size / 8;
+  const int64_t total = int64_t(num_tokens) * num_kv_heads * vpr;
+  const int64_t grid = (total + 255) / 256;
+  if (grid > 0x7FFFFFFF) return fail(PA_EINVAL, "pa_reshape_and_cache_fp8: too many tokens");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t num_slots = int64_t(num_blocks) * kBlockSize;
+  auto k = static_cast<const uint4*>(key);
+  auto v = static_cast<const uint4*>(value);
+  auto c = static_cast<uint2*>(kv_cache);
+  if (vpr == 8)
+    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<8>, dim3(grid), dim3(256), 0, s, k, v,
+                       slot_mapping, num_tokens, c, num_slots, num_kv_heads, k_scale, v_scale);
+  else
+    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<16>, dim3(grid), dim3(256), 0, s, k, v,
+                       slot_mapping, num_tokens, c, num_slots, num_kv_heads, k_scale, v_scale);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(PA_EHIP, "pa_reshape_and_cache_fp8: launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
 
 extern "C" int pa_reshape_and_cache(const void* key, const void* value,
                                     const int64_t* slot_mapping, int32_t num_tokens,

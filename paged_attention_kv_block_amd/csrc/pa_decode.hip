@@ -388,7 +388,8 @@ struct DecodeParams {
   const void* new_v;      // nullptr: the cache already holds token L - 1
   int num_blocks, max_blocks_per_seq, max_seq_len, num_kv_heads, B;
   int part_blocks, max_parts, num_items;
-  float scale_log2;
+  float scale_log2;       // scale * log2(e), times the key scale for an FP8 cache
+  float v_scale;          // FP8 cache: value scale (applied to the outputs)
 };
 
 // Append mode: the new token (position L - 1 of sequence b, KV head g)
@@ -430,14 +431,17 @@ __device__ __forceinline__ void append_new_token(BlockRegs<C>& rg, const DecodeP
 }
 
 // Shapes of the bf16 (matrix-core) block loop; see mfma_blocks.
-template <int D>
+// KV8: the cache holds FP8 E4M3 codes (converted to bf16 operands, exactly).
+template <int D, bool KV8 = false>
 struct MfmaCfg {
   static_assert(D == 64 || D == 128, "head size");
+  static constexpr int EB = KV8 ? 1 : 2;  // bytes of a cache element
   static constexpr int KS = D / 32;   // S^T products per block
-  static constexpr int VWD = D / 32;  // dwords of a V row per lane
   static constexpr int NPV = D / 16;  // P V products per block (16 columns each)
-  static constexpr int RB = 2 * D;    // bytes of a cache row
-  static constexpr int CPR = D / 8;   // 16-byte chunks per row
+  static constexpr int RB = EB * D;   // bytes of a cache row
+  static constexpr int CPR = RB / 16;  // 16-byte chunks per row
+  static constexpr int KLD = RB / 64;  // 16-byte vectors of the K tile per lane
+  static constexpr int VWD = RB / 64;  // dwords of a V row per lane (16 lanes per row)
   static constexpr int LROW = RB + 16;  // padded LDS row: conflict-free operand reads
   static constexpr int TILE = 16 * LROW;
   static constexpr int PD = 2;        // blocks in flight per wave
@@ -446,10 +450,10 @@ struct MfmaCfg {
 // LDS of one workgroup: K tiles during the block loop, then the per-wave
 // outputs, the merge weights and the split-K subset sums; fp32 P (the bf16
 // loop keeps P in registers); and the merge state.
-template <int D, int G, bool BF16, int NW>
+template <int D, int G, bool BF16, int NW, bool KV8 = false>
 struct DecodeSmem {
   using C = F32Cfg<D, G>;
-  static constexpr int kTiles = NW * (BF16 ? MfmaCfg<D>::TILE : C::LDS_TILE);
+  static constexpr int kTiles = NW * (BF16 ? MfmaCfg<D, KV8>::TILE : C::LDS_TILE);
   static constexpr int kOStage = NW * G * D * 4;
   static constexpr int kSubsets = NW * kWave * 16;
   static constexpr int kBytes = std::max(kTiles, std::max(kOStage, kSubsets));
@@ -492,10 +496,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // K: lane holds 16-byte vectors lane + 64 j of the tile (D / 32 of them);
 // V: operand layout (rows 4 grp + i, dwords VWD n ..).
-template <int D>
+template <int D, bool KV8 = false>
 struct MfmaBlock {
-  u32x4 k[MfmaCfg<D>::KS];
-  uint32_t v[4][MfmaCfg<D>::VWD];
+  u32x4 k[MfmaCfg<D, KV8>::KLD];
+  uint32_t v[4][MfmaCfg<D, KV8>::VWD];
 };
 
 template <int D>
@@ -514,25 +518,35 @@ __device__ __forceinline__ f32x4 mfma_k16(const u32x2& a, const u32x2& b, const 
                                                    __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
+// Two FP8 E4M3 codes (bytes 0-1, or 2-3 when `hi`) as a bf16 pair, element
+// 0 in the low half.  E4M3 values are exact in bf16 (3 mantissa bits,
+// exponents 2^-9 .. 2^8), and the scale here is 1.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
 // Non-temporal loads of one block's K and V operands (the cache is streamed
 // once per call).
-template <int D>
-__device__ __forceinline__ MfmaBlock<D> load_mfma_block(const uint8_t* __restrict__ cache, int phys,
-                                                        int64_t block_bytes, int g,
-                                                        int num_kv_heads, int64_t tile_bytes,
-                                                        int lane) {
-  using M = MfmaCfg<D>;
+template <int D, bool KV8 = false>
+__device__ __forceinline__ MfmaBlock<D, KV8> load_mfma_block(const uint8_t* __restrict__ cache,
+                                                             int phys, int64_t block_bytes, int g,
+                                                             int num_kv_heads, int64_t tile_bytes,
+                                                             int lane) {
+  using M = MfmaCfg<D, KV8>;
   const uint8_t* kbase = cache + int64_t(phys) * block_bytes + int64_t(g) * tile_bytes;
   const uint8_t* vbase = kbase + int64_t(num_kv_heads) * tile_bytes;
   const int n = lane & 15, grp = lane >> 4;
-  MfmaBlock<D> r;
+  MfmaBlock<D, KV8> r;
   const u32x4* kt = reinterpret_cast<const u32x4*>(kbase);
 #pragma unroll
-  for (int j = 0; j < M::KS; ++j) r.k[j] = __builtin_nontemporal_load(kt + j * kWave + lane);
+  for (int j = 0; j < M::KLD; ++j) r.k[j] = __builtin_nontemporal_load(kt + j * kWave + lane);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint8_t* vp = vbase + (4 * grp + i) * M::RB + n * (M::VWD * 4);
-    if constexpr (M::VWD == 2) {
+    if constexpr (M::VWD == 1) {
+      r.v[i][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vp));
+    } else if constexpr (M::VWD == 2) {
       const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vp));
       r.v[i][0] = x.x;
       r.v[i][1] = x.y;
@@ -590,24 +604,33 @@ __device__ __forceinline__ void append_new_token_mfma(MfmaBlock<D>& rg, const De
 // One block.  TAIL: only the first `valid` tokens (1 <= valid <= 16) are in
 // the sequence; the others get score -inf and their V rows are zeroed (they
 // may hold anything).
-template <int D, bool TAIL>
-__device__ __forceinline__ void mfma_block(MfmaBlock<D>& cur, int valid,
+template <int D, bool TAIL, bool KV8 = false>
+__device__ __forceinline__ void mfma_block(MfmaBlock<D, KV8>& cur, int valid,
                                            const u32x4 (&qb)[MfmaCfg<D>::KS], MfmaState<D>& st,
                                            uint8_t* kt_lds, float scale_log2, int lane) {
-  using M = MfmaCfg<D>;
+  using M = MfmaCfg<D, KV8>;
   const int n = lane & 15, grp = lane >> 4;
   // K tile -> LDS -> operand layout
   wave_lds_sync();  // the previous block's operand reads are done
 #pragma unroll
-  for (int j = 0; j < M::KS; ++j) {
+  for (int j = 0; j < M::KLD; ++j) {
     const int v = j * kWave + lane;
     *reinterpret_cast<u32x4*>(kt_lds + (v / M::CPR) * M::LROW + (v % M::CPR) * 16) = cur.k[j];
   }
   wave_lds_sync();
   u32x4 ka[M::KS];
 #pragma unroll
-  for (int s = 0; s < M::KS; ++s)
-    ka[s] = *reinterpret_cast<const u32x4*>(kt_lds + n * M::LROW + (4 * s + grp) * 16);
+  for (int s = 0; s < M::KS; ++s) {
+    // 8 elements of token n, d-chunk 4 s + grp
+    const uint8_t* src = kt_lds + n * M::LROW + (4 * s + grp) * 8 * M::EB;
+    if constexpr (KV8) {
+      const u32x2 c = *reinterpret_cast<const u32x2*>(src);
+      ka[s] = u32x4{fp8x2_to_bf16x2<false>(c.x), fp8x2_to_bf16x2<true>(c.x),
+                    fp8x2_to_bf16x2<false>(c.y), fp8x2_to_bf16x2<true>(c.y)};
+    } else {
+      ka[s] = *reinterpret_cast<const u32x4*>(src);
+    }
+  }
   f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < M::KS; ++s) sc = mfma_k32(ka[s], qb[s], sc);
@@ -647,15 +670,34 @@ __device__ __forceinline__ void mfma_block(MfmaBlock<D>& cur, int valid,
 #pragma unroll
       for (int w = 0; w < M::VWD; ++w) cur.v[i][w] = 4 * grp + i < valid ? cur.v[i][w] : 0u;
   }
+  if constexpr (KV8) {
+    // dword w of a row holds output columns 4 (VWD n + w) + c, c < 4: bytes
+    // c of the four rows pair up with v_perm and widen to bf16 pairs
 #pragma unroll
-  for (int w = 0; w < M::VWD; ++w) {
+    for (int w = 0; w < M::VWD; ++w) {
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const uint32_t sel = hb ? 0x07060302u : 0x05040100u;  // high or low bf16 of each dword
-      u32x2 vb;
-      vb.x = __builtin_amdgcn_perm(cur.v[1][w], cur.v[0][w], sel);  // tokens 4 grp + 0, + 1
-      vb.y = __builtin_amdgcn_perm(cur.v[3][w], cur.v[2][w], sel);  // tokens 4 grp + 2, + 3
-      st.o[2 * w + hb] = mfma_k16(pa, vb, st.o[2 * w + hb]);
+      for (int c2 = 0; c2 < 2; ++c2) {  // columns (2 c2, 2 c2 + 1)
+        const uint32_t sel = c2 ? 0x07030602u : 0x05010400u;
+        const uint32_t t01 = __builtin_amdgcn_perm(cur.v[1][w], cur.v[0][w], sel);
+        const uint32_t t23 = __builtin_amdgcn_perm(cur.v[3][w], cur.v[2][w], sel);
+        const int p = 4 * w + 2 * c2;
+        const u32x2 vlo = {fp8x2_to_bf16x2<false>(t01), fp8x2_to_bf16x2<false>(t23)};
+        const u32x2 vhi = {fp8x2_to_bf16x2<true>(t01), fp8x2_to_bf16x2<true>(t23)};
+        st.o[p] = mfma_k16(pa, vlo, st.o[p]);
+        st.o[p + 1] = mfma_k16(pa, vhi, st.o[p + 1]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < M::VWD; ++w) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const uint32_t sel = hb ? 0x07060302u : 0x05040100u;  // high or low bf16 of each dword
+        u32x2 vb;
+        vb.x = __builtin_amdgcn_perm(cur.v[1][w], cur.v[0][w], sel);  // tokens 4 grp + 0, + 1
+        vb.y = __builtin_amdgcn_perm(cur.v[3][w], cur.v[2][w], sel);  // tokens 4 grp + 2, + 3
+        st.o[2 * w + hb] = mfma_k16(pa, vb, st.o[2 * w + hb]);
+      }
     }
   }
 }
@@ -663,11 +705,12 @@ __device__ __forceinline__ void mfma_block(MfmaBlock<D>& cur, int valid,
 // The bf16 block loop of one wave, then its (m, l) into sm.m / sm.l and its
 // unnormalised output rows into the LDS output stage; synchronises the
 // workgroup.
-template <int D, int G, int NW, bool APPEND>
-__device__ __forceinline__ void mfma_blocks(const DecodeParams& a, DecodeSmem<D, G, true, NW>& sm,
-                                            int b, int g, int L, int nblk, int blk_lo,
-                                            int blk_hi) {
-  using M = MfmaCfg<D>;
+template <int D, int G, int NW, bool APPEND, bool KV8 = false>
+__device__ __forceinline__ void mfma_blocks(const DecodeParams& a,
+                                            DecodeSmem<D, G, true, NW, KV8>& sm, int b, int g,
+                                            int L, int nblk, int blk_lo, int blk_hi) {
+  static_assert(!(APPEND && KV8), "the FP8 cache has no fused append");
+  using M = MfmaCfg<D, KV8>;
   static_assert(G <= 16, "query heads per KV head");
   const uint8_t* __restrict__ cache = a.cache;
   const int num_blocks = a.num_blocks, num_kv_heads = a.num_kv_heads;
@@ -715,11 +758,11 @@ __device__ __forceinline__ void mfma_blocks(const DecodeParams& a, DecodeSmem<D,
     };
     const int ids_cur = id_group(0);
     int ids_next = id_group(PD);
-    MfmaBlock<D> buf[PD];
+    MfmaBlock<D, KV8> buf[PD];
 #pragma unroll
     for (int s = 0; s < PD; ++s)
-      buf[s] = load_mfma_block<D>(cache, __builtin_amdgcn_readlane(ids_cur, s), block_bytes, g,
-                                  num_kv_heads, tile_bytes, lane);
+      buf[s] = load_mfma_block<D, KV8>(cache, __builtin_amdgcn_readlane(ids_cur, s), block_bytes,
+                                       g, num_kv_heads, tile_bytes, lane);
     const int j_last = first + (nmine - 1) * NW;
     const int tail_valid = L - j_last * 16;
     const bool seq_last = APPEND && j_last == nblk - 1;
@@ -728,9 +771,10 @@ __device__ __forceinline__ void mfma_blocks(const DecodeParams& a, DecodeSmem<D,
       const int ids_after = id_group(k0 + 2 * PD);
 #pragma unroll
       for (int s = 0; s < PD; ++s) {
-        if (k0 + s < nfull) mfma_block<D, false>(buf[s], 16, qb, st, kt_lds, scale_log2, lane);
-        buf[s] = load_mfma_block<D>(cache, __builtin_amdgcn_readlane(ids_next, s), block_bytes, g,
-                                    num_kv_heads, tile_bytes, lane);
+        if (k0 + s < nfull)
+          mfma_block<D, false, KV8>(buf[s], 16, qb, st, kt_lds, scale_log2, lane);
+        buf[s] = load_mfma_block<D, KV8>(cache, __builtin_amdgcn_readlane(ids_next, s),
+                                         block_bytes, g, num_kv_heads, tile_bytes, lane);
       }
       ids_next = ids_after;
     }
@@ -740,10 +784,14 @@ __device__ __forceinline__ void mfma_blocks(const DecodeParams& a, DecodeSmem<D,
           append_new_token_mfma<D>(buf[0], a, b, g, (L - 1) & 15, bt_row[nblk - 1], block_bytes,
                                    tile_bytes, lane);
       }
-      mfma_block<D, true>(buf[0], min(tail_valid, 16), qb, st, kt_lds, scale_log2, lane);
+      mfma_block<D, true, KV8>(buf[0], min(tail_valid, 16), qb, st, kt_lds, scale_log2, lane);
     }
   }
 
+  if constexpr (KV8) {  // values are codes times v_scale
+#pragma unroll
+    for (int p = 0; p < M::NPV; ++p) st.o[p] *= a.v_scale;
+  }
   const float lsum = allreduce_sum<4, 6>(st.l);  // over the head's four lanes
   if (lane < G) {
     sm.m[wave][lane] = st.m_run;
@@ -892,8 +940,9 @@ __device__ __forceinline__ void valu_blocks(const DecodeParams& a, DecodeSmem<D,
 
 // One work item: KV head g of sequence b, partition `part` (blocks
 // [part * pb, min((part + 1) * pb, nblk))).  Called by the whole workgroup.
-template <int D, int G, bool BF16, int NW, bool APPEND>
-__device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D, G, BF16, NW>& sm,
+template <int D, int G, bool BF16, int NW, bool APPEND, bool KV8 = false>
+__device__ __forceinline__ void decode_item(const DecodeParams& a,
+                                            DecodeSmem<D, G, BF16, NW, KV8>& sm,
                                             int b, int g, int part, int L, int nblk, int pb,
                                             int nparts) {
   void* __restrict__ out = a.out;
@@ -909,7 +958,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, DecodeSmem<D,
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if constexpr (BF16)
-    mfma_blocks<D, G, NW, APPEND>(a, sm, b, g, L, nblk, blk_lo, blk_hi);
+    mfma_blocks<D, G, NW, APPEND, KV8>(a, sm, b, g, L, nblk, blk_lo, blk_hi);
   else
     valu_blocks<D, G, NW, APPEND>(a, sm, b, g, L, nblk, blk_lo, blk_hi);
   float* o_lds = reinterpret_cast<float*>(sm.k);  // [wave][G][D]
@@ -1098,11 +1147,11 @@ constexpr int decode_min_waves() { return NW == 4 && BF16 && D == 64 ? 3 : 1; }
 template <int D, int G, bool BF16, int NW>
 constexpr int decode_max_waves() { return NW == 8 ? 2 : 8; }
 
-template <int D, int G, bool BF16, int NW, bool APPEND>
+template <int D, int G, bool BF16, int NW, bool APPEND, bool KV8 = false>
 __global__ __launch_bounds__(NW * kWave)
 __attribute__((amdgpu_waves_per_eu(decode_min_waves<D, G, BF16, NW>(), decode_max_waves<D, G, BF16, NW>())))
 void decode_kernel(const DecodeParams a) {
-  __shared__ DecodeSmem<D, G, BF16, NW> sm;
+  __shared__ DecodeSmem<D, G, BF16, NW, KV8> sm;
   for (int t = blockIdx.x; t < a.num_items; t += gridDim.x) {
     const int g = t % a.num_kv_heads;
     int b, part;
@@ -1122,7 +1171,7 @@ void decode_kernel(const DecodeParams a) {
     const int pb = a.part_blocks > 0 ? a.part_blocks : (nblk > 0 ? nblk : 1);
     const int nparts = (nblk + pb - 1) / pb;
     if (part > 0 && part >= nparts) continue;
-    decode_item<D, G, BF16, NW, APPEND>(a, sm, b, g, part, L, nblk, pb, nparts);
+    decode_item<D, G, BF16, NW, APPEND, KV8>(a, sm, b, g, part, L, nblk, pb, nparts);
     __syncthreads();  // LDS is reused by the next item
   }
 }
@@ -1138,7 +1187,7 @@ __global__ void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
 // ---------------------------------------------------------------------------
 // Workgroups of one decode kernel variant that fit on the device at once
 // (cached per device and variant): the persistent grid never exceeds this.
-template <int D, int G, bool BF16, int NW, bool APPEND>
+template <int D, int G, bool BF16, int NW, bool APPEND, bool KV8>
 static int resident_workgroups() {
   constexpr int kMaxDev = 64;
   static int cached[kMaxDev] = {0};
@@ -1148,7 +1197,7 @@ static int resident_workgroups() {
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<D, G, BF16, NW, APPEND>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<D, G, BF16, NW, APPEND, KV8>,
                                                    NW * kWave, 0) != hipSuccess ||
       per_cu <= 0)
     per_cu = 1;
@@ -1158,24 +1207,26 @@ static int resident_workgroups() {
   return cached[dev];
 }
 
-template <int D, int G, bool BF16, int NW, bool APPEND>
+template <int D, int G, bool BF16, int NW, bool APPEND, bool KV8>
 static void launch_decode_variant(const DecodeParams& a, hipStream_t s) {
-  auto k = decode_kernel<D, G, BF16, NW, APPEND>;
+  auto k = decode_kernel<D, G, BF16, NW, APPEND, KV8>;
   // With a plan every item is real: one workgroup each, so the hardware
   // dispatcher balances them and overlaps one item's merge with another's
   // loads.  Without one, a persistent grid skips the empty virtual items.
   const int grid = a.plan ? a.num_items
                           : std::max(1, std::min(a.num_items,
-                                                 4 * resident_workgroups<D, G, BF16, NW, APPEND>()));
+                                                 4 * resident_workgroups<D, G, BF16, NW, APPEND, KV8>()));
   hipLaunchKernelGGL(k, dim3(grid), dim3(NW * kWave), 0, s, a);
 }
 
-template <int D, int G, bool BF16, int NW>
+template <int D, int G, bool BF16, int NW, bool KV8>
 static void launch_decode_nw(const DecodeParams& a, hipStream_t s) {
-  if (a.new_k)
-    launch_decode_variant<D, G, BF16, NW, true>(a, s);
+  if constexpr (KV8)
+    launch_decode_variant<D, G, BF16, NW, false, true>(a, s);
+  else if (a.new_k)
+    launch_decode_variant<D, G, BF16, NW, true, false>(a, s);
   else
-    launch_decode_variant<D, G, BF16, NW, false>(a, s);
+    launch_decode_variant<D, G, BF16, NW, false, false>(a, s);
 }
 
 // Compute units of the current device (cached per device).
@@ -1197,26 +1248,26 @@ static int device_cus() {
 // waves each (a long item's blocks spread over more SIMD slots); many items
 // get small workgroups, so that several items share a compute unit and one
 // item's start and merge latency hides behind the others' loads.
-template <int D, int G, bool BF16>
+template <int D, int G, bool BF16, bool KV8>
 static void launch_decode(const DecodeParams& a, hipStream_t s) {
   const int64_t cus = device_cus();
   if (a.num_items < 2 * cus)
-    launch_decode_nw<D, G, BF16, 8>(a, s);
+    launch_decode_nw<D, G, BF16, 8, KV8>(a, s);
   else if (a.num_items < 8 * cus)
-    launch_decode_nw<D, G, BF16, 4>(a, s);
+    launch_decode_nw<D, G, BF16, 4, KV8>(a, s);
   else
-    launch_decode_nw<D, G, BF16, 2>(a, s);
+    launch_decode_nw<D, G, BF16, 2, KV8>(a, s);
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool KV8 = false>
 static bool dispatch_g(int G, const DecodeParams& a, hipStream_t s) {
   switch (G) {
-    case 1: launch_decode<D, 1, BF16>(a, s); return true;
-    case 2: launch_decode<D, 2, BF16>(a, s); return true;
-    case 4: launch_decode<D, 4, BF16>(a, s); return true;
-    case 8: launch_decode<D, 8, BF16>(a, s); return true;
+    case 1: launch_decode<D, 1, BF16, KV8>(a, s); return true;
+    case 2: launch_decode<D, 2, BF16, KV8>(a, s); return true;
+    case 4: launch_decode<D, 4, BF16, KV8>(a, s); return true;
+    case 8: launch_decode<D, 8, BF16, KV8>(a, s); return true;
     case 16:
-      if constexpr (D == 64) { launch_decode<D, 16, BF16>(a, s); return true; }
+      if constexpr (D == 64) { launch_decode<D, 16, BF16, KV8>(a, s); return true; }
       return false;
     default: return false;
   }
@@ -1230,7 +1281,7 @@ static int64_t parts_for(int max_seq_len, int partition_size) {
 // Workspace layout:
 //   [arrival counters: kCounterCap int32][records: B * H_kv * partitions]
 // with one split-K record per (sequence, KV head, partition) (see
-// ws_record_floats).  Counter (b, g) sits at index
+// ws_record_bytes).  Counter (b, g) sits at index
 // b * H_kv + g of a region of fixed size, so calls of any shape can share
 // one workspace without their partials overlapping another shape's
 // counters.  Only the counters need a defined initial value (zero); every
@@ -1321,14 +1372,19 @@ static int decode_call(const char* fn, void* out, float* lse_out, const void* qu
                        int32_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
                        const int32_t* seq_lens, int32_t B, int32_t max_seq_len,
                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
-                       int32_t block_size, float scale, int32_t partition_size,
-                       const int32_t* plan, int32_t plan_entries, void* workspace,
-                       size_t workspace_bytes, int32_t dtype, void* stream) {
+                       int32_t block_size, float scale, float k_scale, float v_scale,
+                       int32_t partition_size, const int32_t* plan, int32_t plan_entries,
+                       void* workspace, size_t workspace_bytes, int32_t dtype, void* stream) {
   if (B < 0 || num_blocks < 0 || max_seq_len < 0 || max_blocks_per_seq < 0 || plan_entries < 0)
     return fail(PA_EINVAL, "%s: negative size", fn);
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
     return fail(PA_EINVAL, "%s: H_q %d not a multiple of H_kv %d", fn, num_q_heads, num_kv_heads);
-  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_EINVAL, "%s: unknown dtype %d", fn, dtype);
+  if (dtype != PA_F32 && dtype != PA_BF16 && dtype != PA_FP8)
+    return fail(PA_EINVAL, "%s: unknown dtype %d", fn, dtype);
+  if (dtype == PA_FP8 && new_key)
+    return fail(PA_ENOTSUP, "%s: no fused cache write for an FP8 cache", fn);
+  if (!(k_scale > 0.f && k_scale < INFINITY && v_scale > 0.f && v_scale < INFINITY))
+    return fail(PA_EINVAL, "%s: cache scales must be positive and finite", fn);
   if (block_size != kBlockSize) return fail(PA_ENOTSUP, "%s: block_size %d (only 16)", fn, block_size);
   if (head_size != 64 && head_size != 128)
     return fail(PA_ENOTSUP, "%s: head_size %d (64 or 128)", fn, head_size);
@@ -1380,7 +1436,8 @@ static int decode_call(const char* fn, void* out, float* lse_out, const void* qu
   a.max_seq_len = max_seq_len;
   a.num_kv_heads = num_kv_heads;
   a.B = B;
-  a.scale_log2 = scale * kLog2e;
+  a.scale_log2 = scale * k_scale * kLog2e;
+  a.v_scale = v_scale;
   a.new_k = new_key;
   a.new_v = new_value;
   a.part_blocks = P > 1 ? partition_size / kBlockSize : 0;
@@ -1394,7 +1451,10 @@ static int decode_call(const char* fn, void* out, float* lse_out, const void* qu
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   bool ok;
-  if (dtype == PA_BF16)
+  if (dtype == PA_FP8)
+    ok = head_size == 64 ? dispatch_g<64, true, true>(G, a, st)
+                         : dispatch_g<128, true, true>(G, a, st);
+  else if (dtype == PA_BF16)
     ok = head_size == 64 ? dispatch_g<64, true>(G, a, st) : dispatch_g<128, true>(G, a, st);
   else
     ok = head_size == 64 ? dispatch_g<64, false>(G, a, st) : dispatch_g<128, false>(G, a, st);
@@ -1411,10 +1471,27 @@ extern "C" int pa_decode(void* out, float* lse_out, const void* query, const voi
                          int32_t head_size, int32_t block_size, float scale,
                          int32_t partition_size, const int32_t* plan, int32_t plan_entries,
                          void* workspace, size_t workspace_bytes, int32_t dtype, void* stream) {
+  if (dtype == PA_FP8)
+    return fail(PA_EINVAL, "pa_decode: an FP8 cache needs pa_decode_fp8 (its scales)");
   return decode_call("pa_decode", out, lse_out, query, nullptr, nullptr, kv_cache, num_blocks,
                      block_tables, max_blocks_per_seq, seq_lens, B, max_seq_len, num_q_heads,
-                     num_kv_heads, head_size, block_size, scale, partition_size, plan,
+                     num_kv_heads, head_size, block_size, scale, 1.f, 1.f, partition_size, plan,
                      plan_entries, workspace, workspace_bytes, dtype, stream);
+}
+
+extern "C" int pa_decode_fp8(void* out, float* lse_out, const void* query, const void* kv_cache,
+                             int32_t num_blocks, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t B,
+                             int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_size, int32_t block_size, float scale, float k_scale,
+                             float v_scale, int32_t partition_size, const int32_t* plan,
+                             int32_t plan_entries, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return decode_call("pa_decode_fp8", out, lse_out, query, nullptr, nullptr, kv_cache, num_blocks,
+                     block_tables, max_blocks_per_seq, seq_lens, B, max_seq_len, num_q_heads,
+                     num_kv_heads, head_size, block_size, scale, k_scale, v_scale,
+                     partition_size, plan, plan_entries, workspace, workspace_bytes, PA_FP8,
+                     stream);
 }
 
 extern "C" int pa_decode_append(void* out, float* lse_out, const void* query,
@@ -1430,6 +1507,7 @@ extern "C" int pa_decode_append(void* out, float* lse_out, const void* query,
     return fail(PA_EINVAL, "pa_decode_append: NULL new_key/new_value");
   return decode_call("pa_decode_append", out, lse_out, query, new_key, new_value, kv_cache,
                      num_blocks, block_tables, max_blocks_per_seq, seq_lens, B, max_seq_len,
-                     num_q_heads, num_kv_heads, head_size, block_size, scale, partition_size,
-                     plan, plan_entries, workspace, workspace_bytes, dtype, stream);
+                     num_q_heads, num_kv_heads, head_size, block_size, scale, 1.f, 1.f,
+                     partition_size, plan, plan_entries, workspace, workspace_bytes, dtype,
+                     stream);
 }

@@ -18,7 +18,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpa.so")
 
 PA_OK, PA_EINVAL, PA_ENOBLOCKS, PA_ENOTSUP, PA_EHIP = 0, 1, 2, 3, 4
-PA_F32, PA_BF16 = 0, 1
+PA_F32, PA_BF16, PA_FP8 = 0, 1, 2
 _STATUS = {PA_EINVAL: "EINVAL", PA_ENOBLOCKS: "ENOBLOCKS", PA_ENOTSUP: "ENOTSUP", PA_EHIP: "EHIP"}
 
 # name -> (restype, argtypes); mirrors include/pa.h
@@ -41,6 +41,8 @@ SIGNATURES = {
     "pa_slot_mapping": (_c_int, [_vp, _c_i32, _vp, _vp, _c_i32, _c_i32, _vp, _vp]),
     "pa_reshape_and_cache": (_c_int, [_vp, _vp, _vp, _c_i32, _vp, _c_i32, _c_i32, _c_i32,
                                       _c_i32, _c_i32, _vp]),
+    "pa_reshape_and_cache_fp8": (_c_int, [_vp, _vp, _vp, _c_i32, _vp, _c_i32, _c_i32, _c_i32,
+                                          _c_i32, _f, _f, _vp]),
     "pa_decode_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "pa_decode_workspace_init": (_c_int, [_vp, _c_sz, _vp]),
     "pa_decode_plan": (_c_int, [_vp, _c_i32, _c_i32, _c_i32, _vp, _c_i32, _vp]),
@@ -50,6 +52,9 @@ SIGNATURES = {
     "pa_decode_append": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _vp,
                                   _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _f, _c_i32,
                                   _vp, _c_i32, _vp, _c_sz, _c_i32, _vp]),
+    "pa_decode_fp8": (_c_int, [_vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _vp, _c_i32, _c_i32,
+                               _c_i32, _c_i32, _c_i32, _c_i32, _f, _f, _f, _c_i32, _vp, _c_i32,
+                               _vp, _c_sz, _vp]),
     "pa_prefill_chunk": (_c_int, [_vp, _vp, _vp, _vp, _c_i32, _c_i32, _vp, _c_i32, _vp, _c_i32,
                                   _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _f,
                                   _c_i32, _vp]),
@@ -232,6 +237,27 @@ def reshape_and_cache(key, value, slot_mapping, kv_cache, stream=None) -> None:
                                       _stream(stream)))
 
 
+def reshape_and_cache_fp8(key, value, slot_mapping, kv_cache, k_scale: float, v_scale: float,
+                          stream=None) -> None:
+    """key/value bf16 [T, H_kv, D]; slot_mapping int64 [T]; kv_cache uint8
+    [N, 2, H_kv, 16, D] holding FP8 E4M3 codes (code * scale = value)."""
+    torch = _torch()
+    _need_gpu(key, value, slot_mapping, kv_cache)
+    for t in (key, value, slot_mapping, kv_cache):
+        if not t.is_contiguous():
+            raise PAError(PA_EINVAL, "tensors must be contiguous")
+    N, two, Hkv, bs, D = kv_cache.shape
+    if two != 2 or key.shape != value.shape or tuple(key.shape[1:]) != (Hkv, D) \
+            or key.dtype != torch.bfloat16 or value.dtype != torch.bfloat16 \
+            or kv_cache.dtype != torch.uint8:
+        raise PAError(PA_EINVAL, "key/value must be bf16 [T, H_kv, D], kv_cache uint8")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != key.shape[0]:
+        raise PAError(PA_EINVAL, "slot_mapping must be int64 [T]")
+    _check(lib().pa_reshape_and_cache_fp8(_ptr(key), _ptr(value), _ptr(slot_mapping), key.shape[0],
+                                          _ptr(kv_cache), N, bs, Hkv, D, float(k_scale),
+                                          float(v_scale), _stream(stream)))
+
+
 def decode_workspace_bytes(B: int, num_q_heads: int, num_kv_heads: int, head_size: int,
                            max_seq_len: int, partition_size: int) -> int:
     return int(lib().pa_decode_workspace_bytes(B, num_q_heads, num_kv_heads, head_size,
@@ -309,6 +335,37 @@ def decode(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int, scale
                                      "in the cache dtype")
     _check(lib().pa_decode_append(_ptr(out), _ptr(lse), _ptr(query), _ptr(new_key),
                                   _ptr(new_value), _ptr(kv_cache), *tail))
+
+
+def decode_fp8(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int, scale: float,
+               k_scale: float, v_scale: float, partition_size: int = 0, workspace=None,
+               lse=None, plan=None, stream=None) -> None:
+    """pa_decode over an FP8 cache (uint8 [N, 2, H_kv, 16, D] of E4M3 codes):
+    out/query bf16 [B, H_q, D]; the other arguments as decode()."""
+    _need_gpu(out, query, kv_cache, block_tables, seq_lens, workspace, lse, plan)
+    torch = _torch()
+    N, _, Hkv, bs, D = kv_cache.shape
+    B, Hq, Dq = query.shape
+    if Dq != D or tuple(out.shape) != (B, Hq, D) or out.dtype != torch.bfloat16 \
+            or query.dtype != torch.bfloat16 or kv_cache.dtype != torch.uint8:
+        raise PAError(PA_EINVAL, "out/query must be bf16 [B, H_q, D] and kv_cache uint8")
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32 \
+            or block_tables.shape[0] != B or seq_lens.numel() != B:
+        raise PAError(PA_EINVAL, "block_tables/seq_lens must be int32 with B rows")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq)):
+        raise PAError(PA_EINVAL, "lse must be fp32 [B, H_q]")
+    for t in (out, query, kv_cache, block_tables, seq_lens, workspace, lse):
+        if t is not None and not t.is_contiguous():
+            raise PAError(PA_EINVAL, "tensors must be contiguous")
+    if plan is not None and plan.dtype != torch.int32:
+        raise PAError(PA_EINVAL, "plan must be int32")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode_fp8(_ptr(out), _ptr(lse), _ptr(query), _ptr(kv_cache), N,
+                               _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), B,
+                               int(max_seq_len), Hq, Hkv, D, bs, float(scale), float(k_scale),
+                               float(v_scale), int(partition_size), _ptr(plan),
+                               0 if plan is None else plan.numel(), _ptr(workspace), ws_bytes,
+                               _stream(stream)))
 
 
 def prefill_chunk(out, query, query_start_loc, max_query_len: int, kv_cache, block_tables,
