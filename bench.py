@@ -72,21 +72,25 @@ def default_partition(wl) -> int:
     return 0
 
 
-def decode_bytes(wl, seq_lens) -> int:
+def decode_bytes(wl, seq_lens, kv_bytes=None) -> int:
     """Algorithmic bytes of one decode launch: valid K/V of every context
-    token, query in, output out, the used block-table entries, seq_lens."""
+    token, query in, output out, the used block-table entries, seq_lens.
+    kv_bytes: bytes of a cached element when the cache is narrower than the
+    queries (1 for FP8)."""
     db = wl.dtype_bytes
-    kv = int(sum(int(L) for L in seq_lens)) * 2 * wl.num_kv_heads * wl.head_size * db
+    kb = db if kv_bytes is None else kv_bytes
+    kv = int(sum(int(L) for L in seq_lens)) * 2 * wl.num_kv_heads * wl.head_size * kb
     qo = 2 * wl.num_seqs * wl.num_q_heads * wl.head_size * db
     bt = sum((int(L) + wl.block_size - 1) // wl.block_size for L in seq_lens) * 4
     return kv + qo + bt + 4 * wl.num_seqs
 
 
-def cache_write_bytes(wl) -> int:
+def cache_write_bytes(wl, kv_bytes=None) -> int:
     """Writing one new token per sequence into the cache: read its K and V
-    rows, write them."""
+    rows, write them (as kv_bytes-wide elements for an FP8 cache)."""
     row = wl.num_kv_heads * wl.head_size * wl.dtype_bytes
-    return wl.num_seqs * 4 * row
+    out_row = row if kv_bytes is None else wl.num_kv_heads * wl.head_size * kv_bytes
+    return wl.num_seqs * 2 * (row + out_row)
 
 
 def load_traffic(kernel_hash: str, unfused: bool):
@@ -103,10 +107,11 @@ def load_traffic(kernel_hash: str, unfused: bool):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(d, min_seconds: float):
+def cpu_baseline(d, min_seconds: float, fp8_scales=None):
     """The fp64 oracle (as it stands) on this host: the same step (write the
     new tokens, decode) repeated until min_seconds of CPU time; BLAS limited
-    to one thread so `cores` is what it used."""
+    to one thread so `cores` is what it used.  fp8_scales = (k, v): the FP8
+    cache step (quantise the new tokens, decode the codes)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     import oracle
@@ -114,6 +119,9 @@ def cpu_baseline(d, min_seconds: float):
 
     wl = d.wl
     side = OracleSide(d)   # allocator, tables and the full cache (setup, untimed)
+    if fp8_scales is not None:
+        side.pool = np.stack([oracle.quantize(side.pool[:, 0], fp8_scales[0]),
+                              oracle.quantize(side.pool[:, 1], fp8_scales[1])], axis=1)
     q = d.query()
     new_k, new_v, slots = [], [], []
     for b in range(wl.num_seqs):
@@ -126,8 +134,15 @@ def cpu_baseline(d, min_seconds: float):
     reps, t0 = 0, time.perf_counter()
     with threadpool_limits(1):
         while True:
-            oracle.reshape_and_cache(side.pool, new_k, new_v, slots)
-            oracle.decode(q, side.pool, side.block_tables, d.seq_lens, wl.scale)
+            if fp8_scales is None:
+                oracle.reshape_and_cache(side.pool, new_k, new_v, slots)
+                oracle.decode(q, side.pool, side.block_tables, d.seq_lens, wl.scale)
+            else:
+                ks, vs = fp8_scales
+                oracle.reshape_and_cache(side.pool, oracle.quantize(new_k, ks),
+                                         oracle.quantize(new_v, vs), slots)
+                oracle.decode(q, side.pool, side.block_tables, d.seq_lens, wl.scale,
+                              k_scale=ks, v_scale=vs)
             reps += 1
             if time.perf_counter() - t0 >= min_seconds:
                 break
@@ -335,6 +350,10 @@ def main(argv=None):
     ap.add_argument("--unfused", action="store_true",
                     help="decode step as two launches (pa_reshape_and_cache, pa_decode) "
                          "instead of pa_decode_append")
+    ap.add_argument("--kv-cache", choices=["native", "fp8"], default="native",
+                    help="decode workloads: keep the cache in the workload dtype (default) "
+                         "or in FP8 E4M3 with per-tensor scales (pa_reshape_and_cache_fp8 + "
+                         "pa_decode_fp8, two launches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     a = ap.parse_args(argv)
@@ -367,6 +386,10 @@ def main(argv=None):
     d = inputs.draw(a.workload)
     if wl.kind == "prefill":
         return bench_prefill(a, d, dev)
+    fp8 = a.kv_cache == "fp8"
+    if fp8 and wl.dtype != "bf16":
+        print("bench.py: the FP8 cache is for bf16 workloads", file=sys.stderr)
+        return 2
     B, Hq, Hkv, D, bs = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_size, wl.block_size
     P = default_partition(wl) if a.partition_size is None else a.partition_size
     seq_lens = d.seq_lens
@@ -388,7 +411,7 @@ def main(argv=None):
 
     # ---- device inputs: cache holds tokens 0..L-2; the step writes token L-1
     pool_shape = (d.num_blocks, 2, Hkv, bs, D)
-    pool0 = torch.zeros(pool_shape, dtype=tdt, device=dev)
+    pool0 = torch.zeros(pool_shape, dtype=torch.uint8 if fp8 else tdt, device=dev)
     ks, vs, sl = [], [], []
     new_k, new_v = [], []
     for b in range(B):
@@ -399,8 +422,19 @@ def main(argv=None):
         sl.append(ops.slot_mapping(bt[b], 0, L - 1, bs))
         new_k.append(k[L - 1])
         new_v.append(v[L - 1])
-    ops.reshape_and_cache(dev_tensor(np.concatenate(ks)), dev_tensor(np.concatenate(vs)),
-                          torch.from_numpy(np.concatenate(sl)).to(dev), pool0)
+    k_scale = v_scale = 1.0
+    if fp8:   # per-tensor scales mapping the largest |key| / |value| to 448
+        def absmax(rows):
+            return max(float(np.max(np.abs((np.asarray(x).astype(np.uint32) << 16)
+                                            .view(np.float32)))) for x in rows if np.size(x))
+        k_scale = absmax(ks + new_k) / 448.0
+        v_scale = absmax(vs + new_v) / 448.0
+        ops.reshape_and_cache_fp8(dev_tensor(np.concatenate(ks)), dev_tensor(np.concatenate(vs)),
+                                  torch.from_numpy(np.concatenate(sl)).to(dev), pool0,
+                                  k_scale, v_scale)
+    else:
+        ops.reshape_and_cache(dev_tensor(np.concatenate(ks)), dev_tensor(np.concatenate(vs)),
+                              torch.from_numpy(np.concatenate(sl)).to(dev), pool0)
     del ks, vs
     pool_bytes = pool0.numel() * pool0.element_size()
     R = max(1, -(-a.rotate_mb * (1 << 20) // pool_bytes))
@@ -419,8 +453,15 @@ def main(argv=None):
     nk3 = nk.view(B, Hkv, D)
     nv3 = nv.view(B, Hkv, D)
 
+    if fp8:
+        a.unfused = True   # the FP8 cache has no fused append
+
     def step(pool):
-        if a.unfused:
+        if fp8:
+            ops.reshape_and_cache_fp8(nk, nv, slots_dev, pool, k_scale, v_scale)
+            ops.decode_fp8(out, q, pool, bt_dev, sl_dev, msl, scale, k_scale, v_scale, P, ws,
+                           plan=plan_dev)
+        elif a.unfused:
             ops.reshape_and_cache(nk, nv, slots_dev, pool)
             ops.decode(out, q, pool, bt_dev, sl_dev, msl, scale, P, ws, plan=plan_dev)
         else:   # pa_decode_append: cache write + decode in one launch
@@ -428,7 +469,10 @@ def main(argv=None):
                        new_key=nk3, new_value=nv3)
 
     def decode_only(pool):
-        if a.unfused:
+        if fp8:
+            ops.decode_fp8(out, q, pool, bt_dev, sl_dev, msl, scale, k_scale, v_scale, P, ws,
+                           plan=plan_dev)
+        elif a.unfused:
             ops.decode(out, q, pool, bt_dev, sl_dev, msl, scale, P, ws, plan=plan_dev)
         else:
             ops.decode(out, q, pool, bt_dev, sl_dev, msl, scale, P, ws, plan=plan_dev,
@@ -475,13 +519,14 @@ def main(argv=None):
     dec_us = d0.elapsed_time(d1) * 1e3 / a.steps
 
     ctx = int(seq_lens.sum())
-    dbytes = decode_bytes(wl, seq_lens)
-    step_bytes = dbytes + cache_write_bytes(wl)
+    kvb = 1 if fp8 else None
+    dbytes = decode_bytes(wl, seq_lens, kvb)
+    step_bytes = dbytes + cache_write_bytes(wl, kvb)
     kbytes = dbytes if a.unfused else step_bytes   # the timed kernel's own bytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = kbytes / (dec_us * 1e-6) / 1e9
     khash = source_hash(DECODE_SOURCES)
-    traffic = load_traffic(khash, a.unfused) if a.workload == 1 and P == 0 else None
+    traffic = load_traffic(khash, a.unfused) if a.workload == 1 and P == 0 and not fp8 else None
 
     res = {
         "metric": METRIC,
@@ -500,13 +545,16 @@ def main(argv=None):
             "workload": wl.name, "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
             "head_size": D, "block_size": bs, "context_tokens": ctx, "max_seq_len": msl,
             "partition_size": P, "pool_blocks": d.num_blocks, "pool_copies_rotated": R,
+            "kv_cache": ("fp8-e4m3, per-tensor scales k %.6g v %.6g" % (k_scale, v_scale)
+                         if fp8 else wl.dtype),
             "parallelism": "none (1 GPU)",
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "context_tokens_per_s": round(ctx / (ms_step * 1e-3), 1),
         "host_metadata_us": round(host_us, 1),
         "roofline": {
-            "kernel": ("pa_decode (decode_kernel)" if a.unfused else
+            "kernel": ("pa_decode_fp8 (decode_kernel, FP8 cache)" if fp8 else
+                       "pa_decode (decode_kernel)" if a.unfused else
                        "pa_decode_append (decode_kernel, cache write fused)"),
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -520,7 +568,7 @@ def main(argv=None):
         },
     }
     if not a.no_cpu_baseline:
-        dt, reps = cpu_baseline(d, a.cpu_seconds)
+        dt, reps = cpu_baseline(d, a.cpu_seconds, (k_scale, v_scale) if fp8 else None)
         res["cpu_baseline"] = {
             "value": round(step_bytes / dt / 1e9, 4),
             "unit": "GB/s",

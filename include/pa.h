@@ -169,8 +169,10 @@ int pa_reshape_and_cache(const void* key, const void* value,
 
 /* FP8 cache write: keys/values arrive in bf16 and are stored as FP8 (OCP
  * E4M3) codes, one byte per element, in the same pool layout ("Inside
- * vLLM", "LLM Engine constructor", for the cache; the FP8 format and the
- * scales are this library's reading, as the pages fix none).  Element x of
+ * vLLM", "LLM Engine constructor", for the cache; "vLLM: Ein tiefer
+ * Einblick ...", "Tiefenanalyse", lists FP8 among the engine's quantisation
+ * formats but fixes no format or scale: E4M3 and per-tensor scales are this
+ * library's reading).  Element x of
  * the keys becomes the E4M3 code of x / k_scale, computed in fp32 with IEEE
  * division, saturated at +-448 and rounded to nearest even, sign kept; the
  * values likewise with v_scale.  The cache then represents code * scale.

@@ -44,8 +44,9 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
 // into 8 bytes of the pool [num_blocks][2][H_kv][16][D] (one byte per
 // element).  An element x becomes the OCP E4M3 code of x / scale computed in
 // fp32 (IEEE division), saturated at +-448 and rounded to nearest even by the
-// hardware conversion, with its sign.  The pages name an FP8 KV cache but no
-// format or scale; this is the reading the reference side implements too.
+// hardware conversion, with its sign.  "vLLM: Ein tiefer Einblick ...",
+// section "Tiefenanalyse", lists FP8 among the engine's quantisation formats
+// without a format or scale; E4M3 with per-tensor scales is the reading.
 __device__ __forceinline__ uint32_t bf16x2_lo(uint32_t w) { return w << 16; }
 __device__ __forceinline__ uint32_t bf16x2_hi(uint32_t w) { return w & 0xFFFF0000u; }
 
