@@ -352,8 +352,8 @@ def main(argv=None):
                          "instead of pa_decode_append")
     ap.add_argument("--kv-cache", choices=["native", "fp8"], default="native",
                     help="decode workloads: keep the cache in the workload dtype (default) "
-                         "or in FP8 E4M3 with per-tensor scales (pa_reshape_and_cache_fp8 + "
-                         "pa_decode_fp8, two launches)")
+                         "or in FP8 E4M3 with per-tensor scales (pa_decode_append_fp8; with "
+                         "--unfused pa_reshape_and_cache_fp8 + pa_decode_fp8)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     a = ap.parse_args(argv)
@@ -453,14 +453,14 @@ def main(argv=None):
     nk3 = nk.view(B, Hkv, D)
     nv3 = nv.view(B, Hkv, D)
 
-    if fp8:
-        a.unfused = True   # the FP8 cache has no fused append
-
     def step(pool):
-        if fp8:
+        if fp8 and a.unfused:
             ops.reshape_and_cache_fp8(nk, nv, slots_dev, pool, k_scale, v_scale)
             ops.decode_fp8(out, q, pool, bt_dev, sl_dev, msl, scale, k_scale, v_scale, P, ws,
                            plan=plan_dev)
+        elif fp8:   # pa_decode_append_fp8: quantised cache write + decode in one launch
+            ops.decode_fp8(out, q, pool, bt_dev, sl_dev, msl, scale, k_scale, v_scale, P, ws,
+                           plan=plan_dev, new_key=nk3, new_value=nv3)
         elif a.unfused:
             ops.reshape_and_cache(nk, nv, slots_dev, pool)
             ops.decode(out, q, pool, bt_dev, sl_dev, msl, scale, P, ws, plan=plan_dev)
@@ -469,9 +469,12 @@ def main(argv=None):
                        new_key=nk3, new_value=nv3)
 
     def decode_only(pool):
-        if fp8:
+        if fp8 and a.unfused:
             ops.decode_fp8(out, q, pool, bt_dev, sl_dev, msl, scale, k_scale, v_scale, P, ws,
                            plan=plan_dev)
+        elif fp8:
+            ops.decode_fp8(out, q, pool, bt_dev, sl_dev, msl, scale, k_scale, v_scale, P, ws,
+                           plan=plan_dev, new_key=nk3, new_value=nv3)
         elif a.unfused:
             ops.decode(out, q, pool, bt_dev, sl_dev, msl, scale, P, ws, plan=plan_dev)
         else:
@@ -553,7 +556,9 @@ def main(argv=None):
         "context_tokens_per_s": round(ctx / (ms_step * 1e-3), 1),
         "host_metadata_us": round(host_us, 1),
         "roofline": {
-            "kernel": ("pa_decode_fp8 (decode_kernel, FP8 cache)" if fp8 else
+            "kernel": ("pa_decode_fp8 (decode_kernel, FP8 cache)" if fp8 and a.unfused else
+                       "pa_decode_append_fp8 (decode_kernel, FP8 cache, quantised cache write "
+                       "fused)" if fp8 else
                        "pa_decode (decode_kernel)" if a.unfused else
                        "pa_decode_append (decode_kernel, cache write fused)"),
             "bound": "hbm",

@@ -303,6 +303,22 @@ int pa_decode_fp8(void* out, float* lse_out, const void* query,
                   int32_t plan_entries, void* workspace, size_t workspace_bytes,
                   void* stream);
 
+/* pa_decode_append for an FP8 cache: the new token of every sequence is
+ * quantised exactly as pa_reshape_and_cache_fp8 does (new_key/new_value
+ * bf16 [B][H_kv][D], 16-byte aligned; k_scale/v_scale), written to its slot
+ * and attended to, in one launch.  Equals pa_reshape_and_cache_fp8 of the
+ * new tokens followed by pa_decode_fp8 (pool bit for bit, outputs as
+ * pa_decode_fp8).  Other arguments as pa_decode_fp8. */
+int pa_decode_append_fp8(void* out, float* lse_out, const void* query,
+                         const void* new_key, const void* new_value, void* kv_cache,
+                         int32_t num_blocks, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t B,
+                         int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_size, int32_t block_size, float scale,
+                         float k_scale, float v_scale, int32_t partition_size,
+                         const int32_t* plan, int32_t plan_entries, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* Chunked prefill ("Im Inneren von vLLM", "Fortgeschrittene Funktionen":
  * long prompts are split into chunks; "Inside vLLM", "Generate function":
  * the batch is flattened into one sequence of tokens).  Sequence b owns the

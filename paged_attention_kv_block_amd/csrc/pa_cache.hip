@@ -42,32 +42,9 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
 
 // FP8 cache write: each thread quantises one 16-byte vector of 8 bf16 inputs
 // into 8 bytes of the pool [num_blocks][2][H_kv][16][D] (one byte per
-// element).  An element x becomes the OCP E4M3 code of x / scale computed in
-// fp32 (IEEE division), saturated at +-448 and rounded to nearest even by the
-// hardware conversion, with its sign.  "vLLM: Ein tiefer Einblick ...",
-// section "Tiefenanalyse", lists FP8 among the engine's quantisation formats
-// without a format or scale; E4M3 with per-tensor scales is the reading.
-__device__ __forceinline__ uint32_t bf16x2_lo(uint32_t w) { return w << 16; }
-__device__ __forceinline__ uint32_t bf16x2_hi(uint32_t w) { return w & 0xFFFF0000u; }
-
-__device__ __forceinline__ float e4m3_input(uint32_t bits, float scale) {
-  const float q = __uint_as_float(bits) / scale;
-  return fminf(fmaxf(q, -448.f), 448.f);
-}
-
+// element) with quantize4_e4m3 (the E4M3 reading is stated there).
 __device__ __forceinline__ uint2 quantize8(const uint4& x, float scale) {
-  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-  uint32_t out[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t a = w[2 * h], b = w[2 * h + 1];
-    int r = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_input(bf16x2_lo(a), scale),
-                                           e4m3_input(bf16x2_hi(a), scale), 0, false);
-    r = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_input(bf16x2_lo(b), scale),
-                                       e4m3_input(bf16x2_hi(b), scale), r, true);
-    out[h] = uint32_t(r);
-  }
-  return make_uint2(out[0], out[1]);
+  return make_uint2(quantize4_e4m3(x.x, x.y, scale), quantize4_e4m3(x.z, x.w, scale));
 }
 
 template <int VPR>  // 16-byte input vectors per head row (D / 8)

@@ -120,4 +120,23 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 
+// FP8 (OCP E4M3) codes of four bf16 cache inputs (elements w0.lo, w0.hi,
+// w1.lo, w1.hi -> bytes 0..3) under a per-tensor scale: each input divided by
+// the scale in fp32 (IEEE division), saturated at +-448 and rounded to
+// nearest even by the hardware conversion, sign kept.  "vLLM: Ein tiefer
+// Einblick ...", section "Tiefenanalyse", lists FP8 among the engine's
+// quantisation formats without a format or scale: E4M3 with per-tensor
+// scales is the reading.
+__device__ __forceinline__ float e4m3_input(uint32_t f32_bits, float scale) {
+  const float q = __uint_as_float(f32_bits) / scale;
+  return fminf(fmaxf(q, -448.f), 448.f);
+}
+__device__ __forceinline__ uint32_t quantize4_e4m3(uint32_t w0, uint32_t w1, float scale) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_input(w0 << 16, scale),
+                                         e4m3_input(w0 & 0xFFFF0000u, scale), 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_input(w1 << 16, scale),
+                                     e4m3_input(w1 & 0xFFFF0000u, scale), r, true);
+  return uint32_t(r);
+}
+
 }  // namespace pa

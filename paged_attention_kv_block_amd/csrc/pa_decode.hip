@@ -389,7 +389,7 @@ struct DecodeParams {
   int num_blocks, max_blocks_per_seq, max_seq_len, num_kv_heads, B;
   int part_blocks, max_parts, num_items;
   float scale_log2;       // scale * log2(e), times the key scale for an FP8 cache
-  float v_scale;          // FP8 cache: value scale (applied to the outputs)
+  float k_scale, v_scale;  // FP8 cache: key / value scales
 };
 
 // Append mode: the new token (position L - 1 of sequence b, KV head g)
@@ -601,6 +601,50 @@ __device__ __forceinline__ void append_new_token_mfma(MfmaBlock<D>& rg, const De
   }
 }
 
+// The same for an FP8 cache: the new bf16 key/value row is quantised with
+// the key/value scale (quantize4_e4m3, as pa_reshape_and_cache_fp8 does)
+// into the registers and the cache.
+template <int D>
+__device__ __forceinline__ void append_new_token_fp8(MfmaBlock<D, true>& rg,
+                                                     const DecodeParams& a, int b, int g, int row,
+                                                     int phys, int64_t block_bytes,
+                                                     int64_t tile_bytes, int lane) {
+  using M = MfmaCfg<D, true>;
+  const int64_t src = (int64_t(b) * a.num_kv_heads + g) * (2 * D);  // bf16 input rows
+  const bool store = phys >= 0 && phys < a.num_blocks;
+  uint8_t* kbase = const_cast<uint8_t*>(a.cache) + int64_t(store ? phys : 0) * block_bytes +
+                   int64_t(g) * tile_bytes;
+  uint8_t* vbase = kbase + int64_t(a.num_kv_heads) * tile_bytes;
+  const uint8_t* nk = static_cast<const uint8_t*>(a.new_k) + src;
+  const uint8_t* nv = static_cast<const uint8_t*>(a.new_v) + src;
+  const int n = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < M::KLD; ++j) {
+    const int v = j * kWave + lane;  // 16 codes: elements 16 c .. 16 c + 15 of row v / CPR
+    if (v / M::CPR == row) {
+      const u32x4* in = reinterpret_cast<const u32x4*>(nk) + 2 * (v % M::CPR);
+      const u32x4 x0 = in[0], x1 = in[1];
+      const u32x4 c = {quantize4_e4m3(x0.x, x0.y, a.k_scale), quantize4_e4m3(x0.z, x0.w, a.k_scale),
+                       quantize4_e4m3(x1.x, x1.y, a.k_scale), quantize4_e4m3(x1.z, x1.w, a.k_scale)};
+      rg.k[j] = c;
+      if (store) reinterpret_cast<u32x4*>(kbase)[v] = c;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (4 * grp + i == row) {
+#pragma unroll
+      for (int w = 0; w < M::VWD; ++w) {
+        const int dw = M::VWD * n + w;  // dword of the row: elements 4 dw .. 4 dw + 3
+        const u32x2 x = reinterpret_cast<const u32x2*>(nv)[dw];
+        const uint32_t c = quantize4_e4m3(x.x, x.y, a.v_scale);
+        rg.v[i][w] = c;
+        if (store) reinterpret_cast<uint32_t*>(vbase + row * M::RB)[dw] = c;
+      }
+    }
+  }
+}
+
 // One block.  TAIL: only the first `valid` tokens (1 <= valid <= 16) are in
 // the sequence; the others get score -inf and their V rows are zeroed (they
 // may hold anything).
@@ -709,7 +753,6 @@ template <int D, int G, int NW, bool APPEND, bool KV8 = false>
 __device__ __forceinline__ void mfma_blocks(const DecodeParams& a,
                                             DecodeSmem<D, G, true, NW, KV8>& sm, int b, int g,
                                             int L, int nblk, int blk_lo, int blk_hi) {
-  static_assert(!(APPEND && KV8), "the FP8 cache has no fused append");
   using M = MfmaCfg<D, KV8>;
   static_assert(G <= 16, "query heads per KV head");
   const uint8_t* __restrict__ cache = a.cache;
@@ -780,9 +823,14 @@ __device__ __forceinline__ void mfma_blocks(const DecodeParams& a,
     }
     if (nfull < nmine) {  // buf[0] holds the last block (later loads were clamped to it)
       if constexpr (APPEND) {
-        if (seq_last)
-          append_new_token_mfma<D>(buf[0], a, b, g, (L - 1) & 15, bt_row[nblk - 1], block_bytes,
-                                   tile_bytes, lane);
+        if (seq_last) {
+          if constexpr (KV8)
+            append_new_token_fp8<D>(buf[0], a, b, g, (L - 1) & 15, bt_row[nblk - 1],
+                                    block_bytes, tile_bytes, lane);
+          else
+            append_new_token_mfma<D>(buf[0], a, b, g, (L - 1) & 15, bt_row[nblk - 1],
+                                     block_bytes, tile_bytes, lane);
+        }
       }
       mfma_block<D, true, KV8>(buf[0], min(tail_valid, 16), qb, st, kt_lds, scale_log2, lane);
     }
@@ -1221,12 +1269,10 @@ static void launch_decode_variant(const DecodeParams& a, hipStream_t s) {
 
 template <int D, int G, bool BF16, int NW, bool KV8>
 static void launch_decode_nw(const DecodeParams& a, hipStream_t s) {
-  if constexpr (KV8)
-    launch_decode_variant<D, G, BF16, NW, false, true>(a, s);
-  else if (a.new_k)
-    launch_decode_variant<D, G, BF16, NW, true, false>(a, s);
+  if (a.new_k)
+    launch_decode_variant<D, G, BF16, NW, true, KV8>(a, s);
   else
-    launch_decode_variant<D, G, BF16, NW, false, false>(a, s);
+    launch_decode_variant<D, G, BF16, NW, false, KV8>(a, s);
 }
 
 // Compute units of the current device (cached per device).
@@ -1381,8 +1427,6 @@ static int decode_call(const char* fn, void* out, float* lse_out, const void* qu
     return fail(PA_EINVAL, "%s: H_q %d not a multiple of H_kv %d", fn, num_q_heads, num_kv_heads);
   if (dtype != PA_F32 && dtype != PA_BF16 && dtype != PA_FP8)
     return fail(PA_EINVAL, "%s: unknown dtype %d", fn, dtype);
-  if (dtype == PA_FP8 && new_key)
-    return fail(PA_ENOTSUP, "%s: no fused cache write for an FP8 cache", fn);
   if (!(k_scale > 0.f && k_scale < INFINITY && v_scale > 0.f && v_scale < INFINITY))
     return fail(PA_EINVAL, "%s: cache scales must be positive and finite", fn);
   if (block_size != kBlockSize) return fail(PA_ENOTSUP, "%s: block_size %d (only 16)", fn, block_size);
@@ -1437,6 +1481,7 @@ static int decode_call(const char* fn, void* out, float* lse_out, const void* qu
   a.num_kv_heads = num_kv_heads;
   a.B = B;
   a.scale_log2 = scale * k_scale * kLog2e;
+  a.k_scale = k_scale;
   a.v_scale = v_scale;
   a.new_k = new_key;
   a.new_v = new_value;
@@ -1494,6 +1539,25 @@ extern "C" int pa_decode_fp8(void* out, float* lse_out, const void* query, const
                      stream);
 }
 
+extern "C" int pa_decode_append_fp8(void* out, float* lse_out, const void* query,
+                                    const void* new_key, const void* new_value, void* kv_cache,
+                                    int32_t num_blocks, const int32_t* block_tables,
+                                    int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                    int32_t B, int32_t max_seq_len, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                    float scale, float k_scale, float v_scale,
+                                    int32_t partition_size, const int32_t* plan,
+                                    int32_t plan_entries, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (B > 0 && (!new_key || !new_value))
+    return fail(PA_EINVAL, "pa_decode_append_fp8: NULL new_key/new_value");
+  return decode_call("pa_decode_append_fp8", out, lse_out, query, new_key, new_value, kv_cache,
+                     num_blocks, block_tables, max_blocks_per_seq, seq_lens, B, max_seq_len,
+                     num_q_heads, num_kv_heads, head_size, block_size, scale, k_scale, v_scale,
+                     partition_size, plan, plan_entries, workspace, workspace_bytes, PA_FP8,
+                     stream);
+}
+
 extern "C" int pa_decode_append(void* out, float* lse_out, const void* query,
                                 const void* new_key, const void* new_value, void* kv_cache,
                                 int32_t num_blocks, const int32_t* block_tables,
@@ -1503,6 +1567,8 @@ extern "C" int pa_decode_append(void* out, float* lse_out, const void* query,
                                 int32_t partition_size, const int32_t* plan,
                                 int32_t plan_entries, void* workspace, size_t workspace_bytes,
                                 int32_t dtype, void* stream) {
+  if (dtype == PA_FP8)
+    return fail(PA_EINVAL, "pa_decode_append: an FP8 cache needs pa_decode_append_fp8");
   if (B > 0 && (!new_key || !new_value))
     return fail(PA_EINVAL, "pa_decode_append: NULL new_key/new_value");
   return decode_call("pa_decode_append", out, lse_out, query, new_key, new_value, kv_cache,

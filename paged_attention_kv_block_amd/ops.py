@@ -55,6 +55,9 @@ SIGNATURES = {
     "pa_decode_fp8": (_c_int, [_vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _vp, _c_i32, _c_i32,
                                _c_i32, _c_i32, _c_i32, _c_i32, _f, _f, _f, _c_i32, _vp, _c_i32,
                                _vp, _c_sz, _vp]),
+    "pa_decode_append_fp8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _vp,
+                                      _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _f, _f, _f,
+                                      _c_i32, _vp, _c_i32, _vp, _c_sz, _vp]),
     "pa_prefill_chunk": (_c_int, [_vp, _vp, _vp, _vp, _c_i32, _c_i32, _vp, _c_i32, _vp, _c_i32,
                                   _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _f,
                                   _c_i32, _vp]),
@@ -339,10 +342,13 @@ def decode(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int, scale
 
 def decode_fp8(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int, scale: float,
                k_scale: float, v_scale: float, partition_size: int = 0, workspace=None,
-               lse=None, plan=None, stream=None) -> None:
+               lse=None, plan=None, stream=None, new_key=None, new_value=None) -> None:
     """pa_decode over an FP8 cache (uint8 [N, 2, H_kv, 16, D] of E4M3 codes):
-    out/query bf16 [B, H_q, D]; the other arguments as decode()."""
-    _need_gpu(out, query, kv_cache, block_tables, seq_lens, workspace, lse, plan)
+    out/query bf16 [B, H_q, D]; the other arguments as decode().  With
+    new_key/new_value (bf16 [B, H_kv, D]) the call is pa_decode_append_fp8:
+    the new tokens are quantised into the cache in the same launch."""
+    _need_gpu(out, query, kv_cache, block_tables, seq_lens, workspace, lse, plan, new_key,
+              new_value)
     torch = _torch()
     N, _, Hkv, bs, D = kv_cache.shape
     B, Hq, Dq = query.shape
@@ -360,12 +366,19 @@ def decode_fp8(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int, s
     if plan is not None and plan.dtype != torch.int32:
         raise PAError(PA_EINVAL, "plan must be int32")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().pa_decode_fp8(_ptr(out), _ptr(lse), _ptr(query), _ptr(kv_cache), N,
-                               _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), B,
-                               int(max_seq_len), Hq, Hkv, D, bs, float(scale), float(k_scale),
-                               float(v_scale), int(partition_size), _ptr(plan),
-                               0 if plan is None else plan.numel(), _ptr(workspace), ws_bytes,
-                               _stream(stream)))
+    tail = (N, _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), B, int(max_seq_len),
+            Hq, Hkv, D, bs, float(scale), float(k_scale), float(v_scale), int(partition_size),
+            _ptr(plan), 0 if plan is None else plan.numel(), _ptr(workspace), ws_bytes,
+            _stream(stream))
+    if new_key is None and new_value is None:
+        _check(lib().pa_decode_fp8(_ptr(out), _ptr(lse), _ptr(query), _ptr(kv_cache), *tail))
+        return
+    for t in (new_key, new_value):
+        if t is None or tuple(t.shape) != (B, Hkv, D) or t.dtype != torch.bfloat16 \
+                or not t.is_contiguous():
+            raise PAError(PA_EINVAL, "new_key/new_value must be contiguous bf16 [B, H_kv, D]")
+    _check(lib().pa_decode_append_fp8(_ptr(out), _ptr(lse), _ptr(query), _ptr(new_key),
+                                      _ptr(new_value), _ptr(kv_cache), *tail))
 
 
 def prefill_chunk(out, query, query_start_loc, max_query_len: int, kv_cache, block_tables,

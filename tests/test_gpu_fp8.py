@@ -188,3 +188,90 @@ def test_decode_fp8_needs_its_entry_point():
     st = L.pa_decode(16, None, 16, 16, 1, 16, 1, 16, 1, 16, 8, 2, 64, 16, 0.125, 0, None, 0,
                      None, 0, ops.PA_FP8, None)
     assert st == ops.PA_EINVAL
+
+
+# ---------------------------------------------------------------------------
+# decode with the new token's cache write fused (pa_decode_append_fp8)
+# ---------------------------------------------------------------------------
+def _append_case(d, P=0, use_plan=False, rounds=1):
+    """GPU pool: every token but each sequence's last through
+    pa_reshape_and_cache_fp8, the last written by pa_decode_append_fp8.
+    Oracle pool: every token through the oracle quantiser."""
+    from tests.gpu_setup import GpuSide, from_device, to_device
+    from tests.oracle_setup import OracleSide
+    wl = d.wl
+    ks, vs = _data_scales(d)
+    o = OracleSide(d, fill_pool=False)
+    g = GpuSide(d, fill=False)
+    np.testing.assert_array_equal(g.block_tables, o.block_tables)
+    opool = oracle.empty_pool(d.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_size,
+                              np.uint8, fill=np.uint8(POISON))
+    keys, vals, sl, nk, nv = [], [], [], [], []
+    for b in range(wl.num_seqs):
+        L = int(d.seq_lens[b])
+        k, v = d.kv(b)
+        if L > 0:
+            oracle.reshape_and_cache(opool, oracle.quantize(k, ks), oracle.quantize(v, vs),
+                                     o.slots_for(b, 0, L))
+        if L > 1:
+            keys.append(k[:L - 1])
+            vals.append(v[:L - 1])
+            sl.append(ops.slot_mapping(g.block_tables[b], 0, L - 1, wl.block_size))
+        z = np.zeros((wl.num_kv_heads, wl.head_size), dtype=np.uint16)
+        nk.append(k[L - 1] if L > 0 else z)
+        nv.append(v[L - 1] if L > 0 else z)
+    gpool = torch.full(_pool_shape(d), POISON, dtype=torch.uint8, device="cuda")
+    if keys:
+        ops.reshape_and_cache_fp8(to_device(np.concatenate(keys), wl),
+                                  to_device(np.concatenate(vals), wl),
+                                  torch.from_numpy(np.concatenate(sl).astype(np.int64)).cuda(),
+                                  gpool, ks, vs)
+    new_k, new_v = to_device(np.stack(nk), wl), to_device(np.stack(nv), wl)
+    q = to_device(d.query(), wl)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    msl = int(max(d.seq_lens)) if wl.num_seqs else 0
+    ws = ops.decode_workspace(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_size, msl, P,
+                              "cuda")
+    plan = torch.from_numpy(ops.decode_plan(d.seq_lens, msl, P)).cuda() if use_plan else None
+    for _ in range(rounds):   # a repeated call rewrites the same codes
+        ops.decode_fp8(out, q, gpool, g.bt_dev, g.seq_lens_dev, msl, float(wl.scale), ks, vs, P,
+                       ws, lse, plan, new_key=new_k, new_value=new_v)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gpool.cpu().numpy(), opool)
+    ref, ref_lse = oracle.decode(d.query(), opool, o.block_tables, d.seq_lens, wl.scale,
+                                 k_scale=ks, v_scale=vs)
+    got = oracle.to_f64(from_device(out))
+    assert np.all(np.isfinite(got))
+    err = np.max(np.abs(got - ref))
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    both_empty = np.isneginf(got_lse) & np.isneginf(ref_lse)
+    lerr = np.max(np.abs(np.where(both_empty, 0.0, got_lse - np.where(both_empty, 0.0, ref_lse))))
+    assert err <= TOL, f"max abs error {err} > {TOL}"
+    assert lerr <= TOL, f"lse max abs error {lerr} > {TOL}"
+    return err
+
+
+@pytest.mark.parametrize("name,kw", CASES[:4], ids=[c[0] for c in CASES[:4]])
+@pytest.mark.parametrize("P,use_plan", [(0, False), (0, True), (32, True)])
+def test_decode_append_fp8(name, kw, P, use_plan):
+    _append_case(inputs.custom(kind="decode", **kw), P=P, use_plan=use_plan)
+
+
+def test_decode_append_fp8_zero_length_rows_and_repeats():
+    _append_case(inputs.custom(kind="decode", seq_lens=(0, 20, 0, 16), num_q_heads=8,
+                               num_kv_heads=2, head_size=64, num_blocks=6), use_plan=True,
+                 rounds=3)
+
+
+def test_decode_append_fp8_tinyllama_workload():
+    err = _append_case(inputs.draw(1), use_plan=True)
+    print("tinyllama fp8 append max err", err)
+
+
+def test_decode_append_refuses_fp8_dtype():
+    """pa_decode_append with an FP8 dtype would lose the scales."""
+    L = ops.lib()
+    st = L.pa_decode_append(16, None, 16, 16, 16, 16, 1, 16, 1, 16, 1, 16, 8, 2, 64, 16, 0.125, 0,
+                            None, 0, None, 0, ops.PA_FP8, None)
+    assert st == ops.PA_EINVAL
