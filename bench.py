@@ -48,6 +48,7 @@ METRIC = "paged-attn decode KV GB/s (% of HBM peak) + context-tokens/s, 1 GPU"
 TRAFFIC_FILES = {False: os.path.join(ROOT, "profiles", "decode_append_traffic.json"),
                  True: os.path.join(ROOT, "profiles", "decode_traffic.json")}
 DECODE_SOURCES = ["paged_attention_kv_block_amd/csrc/pa_decode.hip",
+                  "paged_attention_kv_block_amd/csrc/pa_decode_dev.h",
                   "paged_attention_kv_block_amd/csrc/pa_common.h"]
 
 

@@ -344,6 +344,60 @@ int pa_prefill_chunk(void* out, float* lse_out, const void* query,
                      int32_t block_size, float scale, int32_t dtype,
                      void* stream);
 
+/* Work plan of a flattened batch (host).  A step's query rows come from
+ * every scheduled sequence at once: one row for a sequence in decode, a
+ * chunk of its prompt for one in prefill ("Inside vLLM", "Generate
+ * function" and "LLM Engine & Engine Core": continuous batching over a
+ * batch flattened into one sequence).  Sequences with C_b = 1 query row
+ * become decode items (split into partitions of partition_size tokens
+ * when that is non-zero and max_seq_len needs more than one), sequences
+ * with C_b >= 2 rows become query tiles of 128 / G rows, C_b = 0 nothing.
+ * Entries are (x << 16) | b, the query tiles first (x = tile), then the
+ * decode items (x = partition), each kind longest first.
+ *   query_start_loc [B+1] int32, host, [0] = 0, non-decreasing
+ *   seq_lens        [B] int32, host, C_b <= seq_lens[b] <= max_seq_len
+ *   plan            [capacity] int32, host (nullable when capacity is 0)
+ *   num_entries, num_prefill_entries  receive the entry counts (also when
+ *                   capacity is too small: then PA_EINVAL)
+ * G = num_q_heads / num_kv_heads in {1, 2, 4, 8}; B <= 65535. */
+int pa_varlen_plan(const int32_t* query_start_loc, const int32_t* seq_lens,
+                   int32_t B, int32_t max_seq_len, int32_t num_q_heads,
+                   int32_t num_kv_heads, int32_t partition_size, int32_t* plan,
+                   int32_t capacity, int32_t* num_entries,
+                   int32_t* num_prefill_entries);
+
+/* Attention over a flattened batch in one launch: decode rows and prefill
+ * chunks together.  Every query row computes what pa_prefill_chunk defines
+ * for it (query i of sequence b, at position seq_lens[b] - C_b + i, attends
+ * causally to tokens 0..position through the block table; keys/values
+ * already written); a sequence with one row gets exactly pa_decode's
+ * result for it.  Chunks run on the prefill path (matrix-core tiles),
+ * single rows on the decode path (optionally split-K), in one grid.
+ *   out, query      [total_query_tokens][H_q][D] bf16, device
+ *   lse_out         [total_query_tokens][H_q] fp32, device, nullable
+ *   query_start_loc [B+1] int32, device: the same values the plan was
+ *                   built from (the kernel reads rows from it)
+ *   seq_lens        [B] int32, device, likewise
+ *   partition_size  as given to pa_varlen_plan
+ *   plan, plan_entries, prefill_entries  device copy of pa_varlen_plan's
+ *                   output and its two counts
+ *   workspace       as pa_decode's, sized by pa_decode_workspace_bytes(B,
+ *                   H_q, H_kv, D, max_seq_len, partition_size); calls
+ *                   sharing a workspace must not run concurrently
+ * Rows of sequences with C_b = 0 are not touched.  Supported: bf16;
+ * block_size 16; head_size 64 or 128; G in {1, 2, 4, 8}. */
+int pa_attention_varlen(void* out, float* lse_out, const void* query,
+                        const int32_t* query_start_loc,
+                        int32_t total_query_tokens, const void* kv_cache,
+                        int32_t num_blocks, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                        int32_t B, int32_t max_seq_len, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_size,
+                        int32_t block_size, float scale, int32_t partition_size,
+                        const int32_t* plan, int32_t plan_entries,
+                        int32_t prefill_entries, void* workspace,
+                        size_t workspace_bytes, int32_t dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,12 +24,16 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 HOST_LIB = os.path.join(PKG, "libpa_host.so")
 
-HIP_SOURCES = ["pa_host.cpp", "pa_cache.hip", "pa_decode.hip", "pa_prefill.hip"]
+HIP_SOURCES = ["pa_host.cpp", "pa_cache.hip", "pa_decode.hip", "pa_prefill.hip",
+               "pa_varlen.hip"]
 # Per-source flags.  The prefill kernel never lets a NaN reach a max or an
 # exponent (scores of keys that may be unwritten are replaced by -inf with a
 # select first, and their V rows are zeroed), so it drops the NaN-quieting
-# of fmaxf.
-EXTRA_FLAGS = {"pa_prefill.hip": ["-fno-honor-nans"]}
+# of fmaxf; the varlen kernel holds the same prefill code and a decode path
+# that masks the same way.  Device code only: the host-side argument checks
+# keep their NaN tests.
+NO_NANS = ["-Xarch_device", "-fno-honor-nans"]
+EXTRA_FLAGS = {"pa_prefill.hip": NO_NANS, "pa_varlen.hip": NO_NANS}
 HOST_SOURCES = ["pa_host.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -61,6 +61,11 @@ SIGNATURES = {
     "pa_prefill_chunk": (_c_int, [_vp, _vp, _vp, _vp, _c_i32, _c_i32, _vp, _c_i32, _vp, _c_i32,
                                   _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _f,
                                   _c_i32, _vp]),
+    "pa_varlen_plan": (_c_int, [_vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _c_i32,
+                                _vp, _vp]),
+    "pa_attention_varlen": (_c_int, [_vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _vp, _c_i32, _vp,
+                                     _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _f, _c_i32,
+                                     _vp, _c_i32, _c_i32, _vp, _c_sz, _c_i32, _vp]),
 }
 
 _lib = None
@@ -403,3 +408,57 @@ def prefill_chunk(out, query, query_start_loc, max_query_len: int, kv_cache, blo
                                   block_tables.shape[1], _ptr(seq_lens), B, int(max_seq_len), Hq,
                                   Hkv, D, bs, float(scale), _dtype_code(kv_cache),
                                   _stream(stream)))
+
+
+def varlen_plan(query_start_loc_host, seq_lens_host, max_seq_len: int, num_q_heads: int,
+                num_kv_heads: int, partition_size: int = 0):
+    """Host-built work list of pa_attention_varlen: (int32 entries, number of
+    prefill-tile entries at its front)."""
+    qsl = np.ascontiguousarray(query_start_loc_host, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    if qsl.size != sl.size + 1:
+        raise PAError(PA_EINVAL, "query_start_loc must have B+1 entries")
+    n, npre = ctypes.c_int32(), ctypes.c_int32()
+    lib().pa_varlen_plan(_np_ptr(qsl), _np_ptr(sl), sl.size, int(max_seq_len), int(num_q_heads),
+                         int(num_kv_heads), int(partition_size), None, 0, ctypes.byref(n),
+                         ctypes.byref(npre))
+    out = np.empty(max(n.value, 1), dtype=np.int32)
+    _check(lib().pa_varlen_plan(_np_ptr(qsl), _np_ptr(sl), sl.size, int(max_seq_len),
+                                int(num_q_heads), int(num_kv_heads), int(partition_size),
+                                _np_ptr(out), out.size, ctypes.byref(n), ctypes.byref(npre)))
+    return out[:n.value], int(npre.value)
+
+
+def attention_varlen(out, query, query_start_loc, kv_cache, block_tables, seq_lens,
+                     max_seq_len: int, scale: float, plan, prefill_entries: int,
+                     partition_size: int = 0, workspace=None, lse=None, stream=None) -> None:
+    """One launch over a flattened batch of decode rows and prefill chunks:
+    out/query packed bf16 [T, H_q, D]; query_start_loc int32 [B+1]; plan an
+    int32 GPU tensor holding varlen_plan(...)[0] and prefill_entries its
+    second value, built from the same lengths and partition_size."""
+    _need_gpu(out, query, query_start_loc, kv_cache, block_tables, seq_lens, plan, workspace, lse)
+    torch = _torch()
+    N, _, Hkv, bs, D = kv_cache.shape
+    T, Hq, Dq = query.shape
+    B = seq_lens.numel()
+    if Dq != D or tuple(out.shape) != (T, Hq, D) or out.dtype != kv_cache.dtype \
+            or query.dtype != kv_cache.dtype:
+        raise PAError(PA_EINVAL, "shape/dtype mismatch between out/query and kv_cache")
+    if query_start_loc.dtype != torch.int32 or query_start_loc.numel() != B + 1:
+        raise PAError(PA_EINVAL, "query_start_loc must be int32 [B+1]")
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32 or block_tables.shape[0] != B:
+        raise PAError(PA_EINVAL, "block_tables/seq_lens must be int32 with B rows")
+    if plan.dtype != torch.int32:
+        raise PAError(PA_EINVAL, "plan must be int32")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (T, Hq)):
+        raise PAError(PA_EINVAL, "lse must be fp32 [T, H_q]")
+    for t in (out, query, query_start_loc, kv_cache, block_tables, seq_lens, plan, workspace, lse):
+        if t is not None and not t.is_contiguous():
+            raise PAError(PA_EINVAL, "tensors must be contiguous")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_attention_varlen(_ptr(out), _ptr(lse), _ptr(query), _ptr(query_start_loc), T,
+                                     _ptr(kv_cache), N, _ptr(block_tables), block_tables.shape[1],
+                                     _ptr(seq_lens), B, int(max_seq_len), Hq, Hkv, D, bs,
+                                     float(scale), int(partition_size), _ptr(plan), plan.numel(),
+                                     int(prefill_entries), _ptr(workspace), ws_bytes,
+                                     _dtype_code(kv_cache), _stream(stream)))

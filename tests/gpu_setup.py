@@ -118,3 +118,26 @@ class GpuSide:
                           float(wl.scale if scale is None else scale), lse)
         torch.cuda.synchronize()
         return out, lse
+
+    def varlen(self, partition_size=0, scale=None, with_lse=True, max_seq_len=None, out=None,
+               workspace=None):
+        """pa_attention_varlen over the packed rows (chunk lengths of the
+        workload; a length of 1 makes a decode row)."""
+        wl, d = self.wl, self.d
+        q = to_device(d.query(), wl, self.device)
+        if out is None:
+            out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=self.device) if with_lse else None
+        qsl = self.query_start_loc()
+        msl = int(max(d.seq_lens)) if max_seq_len is None else max_seq_len
+        plan, npre = ops.varlen_plan(qsl, d.seq_lens, msl, wl.num_q_heads, wl.num_kv_heads,
+                                     partition_size)
+        ws = workspace
+        if ws is None:
+            ws = ops.decode_workspace(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_size,
+                                      msl, partition_size, self.device)
+        ops.attention_varlen(out, q, torch.from_numpy(qsl).to(self.device), self.pool, self.bt_dev,
+                             self.seq_lens_dev, msl, float(wl.scale if scale is None else scale),
+                             torch.from_numpy(plan).to(self.device), npre, partition_size, ws, lse)
+        torch.cuda.synchronize()
+        return out, lse

@@ -1,0 +1,169 @@
+"""GPU parity of pa_attention_varlen: decode rows and prefill chunks of one
+flattened batch in one launch, against the fp64 oracle's chunked prefill,
+which defines every row (a sequence with one query row is a decode step).
+
+Bars: max |error| <= 2e-2 on bf16 outputs and on lse; the chunk rows are
+bit-identical to pa_prefill_chunk's (the same tile code runs them)."""
+import numpy as np
+import pytest
+import torch
+
+from paged_attention_kv_block_amd import inputs
+from tests.conftest import gpu_available
+from tests.oracle_setup import OracleSide
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+TOL = 2e-2
+
+
+def _f64(t):
+    import oracle
+    from tests.gpu_setup import from_device
+    return oracle.to_f64(from_device(t))
+
+
+def _rows(qsl, seqs):
+    return np.concatenate([np.arange(qsl[b], qsl[b + 1]) for b in seqs] +
+                          [np.zeros(0, dtype=np.int64)]).astype(int)
+
+
+def check_varlen(d, partition_size=0, seqs=None, g=None):
+    from tests.gpu_setup import GpuSide
+    print(f"varlen case {d.wl.name} B={d.wl.num_seqs} P={partition_size}", flush=True)
+    o = OracleSide(d, seqs=seqs)
+    g = g or GpuSide(d)
+    out, lse = g.varlen(partition_size)
+    ref, ref_lse = o.prefill(seqs=seqs)
+    qsl = o.query_start_loc()
+    rows = _rows(qsl, range(d.wl.num_seqs) if seqs is None else seqs)
+    got = _f64(out)[rows]
+    assert np.all(np.isfinite(got))
+    err = np.max(np.abs(got - ref[rows])) if rows.size else 0.0
+    lerr = np.max(np.abs(lse.cpu().numpy().astype(np.float64)[rows] - ref_lse[rows])) \
+        if rows.size else 0.0
+    assert err <= TOL, f"max abs error {err}"
+    assert lerr <= TOL, f"lse max abs error {lerr}"
+    return out, lse, g
+
+
+CASES = [
+    ("g4-d128-mixed", dict(seq_lens=(20, 37, 100, 64, 300, 1), chunk_lens=(1, 17, 1, 33, 1, 1),
+                           num_q_heads=8, num_kv_heads=2, head_size=128)),
+    ("g8-d128-decode-rows-only", dict(seq_lens=(300, 45, 17), chunk_lens=(1, 1, 1),
+                                      num_q_heads=16, num_kv_heads=2, head_size=128)),
+    ("g1-d128-long-chunk", dict(seq_lens=(260, 700, 16), chunk_lens=(200, 1, 1), num_q_heads=2,
+                                num_kv_heads=2, head_size=128)),
+    ("g2-d64-mixed", dict(seq_lens=(50, 90, 1, 513), chunk_lens=(50, 1, 1, 1), num_q_heads=4,
+                          num_kv_heads=2, head_size=64)),
+    ("g8-d64-empty-chunk", dict(seq_lens=(40, 70, 33), chunk_lens=(0, 70, 1), num_q_heads=8,
+                                num_kv_heads=1, head_size=64)),
+    ("g4-d64-chunks-only", dict(seq_lens=(33, 64, 17), chunk_lens=(2, 64, 17), num_q_heads=16,
+                                num_kv_heads=4, head_size=64)),
+]
+
+
+@pytest.mark.parametrize("P", [0, 64])
+@pytest.mark.parametrize("name,kw", CASES, ids=[c[0] for c in CASES])
+def test_varlen_shapes(name, kw, P):
+    check_varlen(inputs.custom(kind="prefill", **kw), P)
+
+
+def _ragged_mix(seed, n=40, G=4, D=64):
+    rng = np.random.default_rng(seed)
+    lens, chunks = [], []
+    for _ in range(n):
+        L = int(rng.integers(1, 400))
+        r = rng.random()
+        if r < 0.45:
+            C = 1                                   # decode row
+        elif r < 0.55:
+            C = 0                                   # nothing scheduled this step
+        else:
+            C = int(rng.integers(1, min(L, 160) + 1))   # prefill chunk (1 row at times)
+        lens.append(L)
+        chunks.append(C)
+    return inputs.custom(kind="prefill", seq_lens=lens, chunk_lens=chunks, num_q_heads=2 * G,
+                         num_kv_heads=2, head_size=D, seed=seed)
+
+
+@pytest.mark.parametrize("seed,G,D,P", [(1, 4, 64, 0), (2, 8, 128, 48), (3, 2, 128, 0),
+                                        (4, 1, 64, 32)])
+def test_varlen_random_mix(seed, G, D, P):
+    check_varlen(_ragged_mix(seed, G=G, D=D), P)
+
+
+def test_chunk_rows_equal_prefill_chunk_bit_exact():
+    from tests.gpu_setup import GpuSide
+    d = inputs.custom(kind="prefill", seq_lens=(20, 37, 100, 64, 300, 1, 260),
+                      chunk_lens=(1, 17, 1, 33, 1, 1, 200), num_q_heads=8, num_kv_heads=2,
+                      head_size=128)
+    g = GpuSide(d)
+    o1, l1 = g.prefill()
+    o2, l2 = g.varlen(64)
+    qsl = g.query_start_loc()
+    chunks = [b for b in range(d.wl.num_seqs) if qsl[b + 1] - qsl[b] > 1]
+    rows = torch.from_numpy(_rows(qsl, chunks)).cuda()
+    assert torch.equal(o1[rows].view(torch.int16), o2[rows].view(torch.int16))
+    assert torch.equal(l1[rows], l2[rows])
+
+
+def test_decode_rows_match_pa_decode():
+    """A batch of one-row sequences gives pa_decode's outputs within
+    rounding.  The two launches split a row's blocks over a different number
+    of waves, and each wave rounds its probabilities to bf16 relative to its
+    own running maximum, so the sums differ by a few 1e-4 relative: 2e-3 on
+    lse, 1e-2 on the bf16 outputs."""
+    from paged_attention_kv_block_amd import ops
+    from tests.gpu_setup import GpuSide, to_device
+    lens = (300, 45, 17, 1000, 64)
+    d = inputs.custom(kind="prefill", seq_lens=lens, chunk_lens=(1,) * 5, num_q_heads=16,
+                      num_kv_heads=2, head_size=128)
+    g = GpuSide(d)
+    out, lse = g.varlen(0)
+    q = to_device(d.query(), d.wl)
+    ref = torch.empty_like(q)
+    ref_lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    ws = ops.decode_workspace(5, 16, 2, 128, 1000, 0)
+    ops.decode(ref, q, g.pool, g.bt_dev, g.seq_lens_dev, 1000, float(d.wl.scale), 0, ws, ref_lse)
+    torch.cuda.synchronize()
+    assert (out.float() - ref.float()).abs().max().item() <= 1e-2
+    assert (lse - ref_lse).abs().max().item() <= 2e-3
+
+
+def test_every_row_written_and_repeatable():
+    """All packed rows are written (the output starts as NaN), and a second
+    call with the same workspace gives the same bits (split-K counters were
+    left at zero)."""
+    from paged_attention_kv_block_amd import ops
+    from tests.gpu_setup import GpuSide
+    d = _ragged_mix(7, G=4, D=128)
+    g = GpuSide(d)
+    wl = d.wl
+    T = int(sum(wl.chunk_lens()))
+    out = torch.full((T, wl.num_q_heads, wl.head_size), float("nan"), dtype=torch.bfloat16,
+                     device="cuda")
+    msl = int(max(d.seq_lens))
+    ws = ops.decode_workspace(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_size, msl, 32)
+    assert ws.numel() > 256                          # split-K is in use
+    o1, l1 = g.varlen(32, out=out, workspace=ws)
+    assert torch.isfinite(o1.float()).all()
+    o2, l2 = g.varlen(32, workspace=ws)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_mixed_step_sampled():
+    """The full mixed step (16 chunks of 256 rows after 2560 cached tokens,
+    240 decode rows of log-normal length): the oracle checks two chunk
+    sequences and the longest, shortest and a middle decode row, without and
+    with 512-token split-K partitions for the decode rows."""
+    from tests.gpu_setup import GpuSide
+    d = inputs.mixed_step()
+    dec = np.arange(16, d.wl.num_seqs)
+    by_len = dec[np.argsort(d.seq_lens[dec], kind="stable")]
+    seqs = [0, 15, int(by_len[0]), int(by_len[len(by_len) // 2]), int(by_len[-1])]
+    g = GpuSide(d)
+    for P in (0, 512):
+        check_varlen(d, P, seqs=seqs, g=g)

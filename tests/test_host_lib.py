@@ -313,6 +313,10 @@ def test_prefill_validation():
     st = L.pa_prefill_chunk(16, None, 16, 16, 4, 4, 16, 4, 16, 4, 16, 1, 64, 7, 2, 128, 16, 0.1,
                             ops.PA_BF16, None)
     assert st == ops.PA_EINVAL
+    # a NaN scale is refused (the check survives the kernel's no-NaN build flags)
+    st = L.pa_prefill_chunk(16, None, 16, 16, 4, 4, 16, 4, 16, 4, 16, 1, 64, 8, 2, 128, 16,
+                            float("nan"), ops.PA_BF16, None)
+    assert st == ops.PA_EINVAL, L.pa_last_error().decode()
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
@@ -333,3 +337,98 @@ def test_decode_plan_lists_nonempty_partitions_longest_first():
     assert ops.decode_plan(sl, 1100, 0).size == 5               # one item per sequence
     with pytest.raises(ops.PAError):
         ops.decode_plan(np.array([5000], np.int32), 1100, 512)   # beyond max_seq_len
+
+
+def _varlen_items(qsl, sl, msl, G, P):
+    """Expected (kind, b, x, work) of a flattened batch, written out from the
+    plan's definition: chunks of C_b >= 2 rows in tiles of 128 / G rows, one
+    decode item per non-empty partition of a sequence with one row."""
+    TQ = 128 // G
+    parts = 1 if P == 0 or msl <= P else -(-msl // P)
+    pre, dec = [], []
+    for b in range(len(sl)):
+        C, L = qsl[b + 1] - qsl[b], int(sl[b])
+        if C == 1:
+            ptok = P if parts > 1 else L
+            for p in range(-(-L // ptok)):
+                dec.append((b, p, min(ptok, L - p * ptok)))
+        elif C > 1:
+            for t in range(-(-C // TQ)):
+                rows = min(TQ, C - t * TQ)
+                pre.append((b, t, rows * (L - C + t * TQ + rows)))
+    return pre, dec
+
+
+def test_varlen_plan_orders_tiles_then_decode_items():
+    qsl = np.array([0, 1, 40, 40, 41, 341, 342], np.int32)   # C = 1, 39, 0, 1, 300, 1
+    sl = np.array([700, 39, 5, 1, 900, 1300], np.int32)
+    for G, P in [(4, 0), (8, 512), (1, 256), (2, 0)]:
+        plan, npre = ops.varlen_plan(qsl, sl, 1300, 8 * G, 8, P)
+        pre, dec = _varlen_items(qsl, sl, 1300, G, P)
+        assert npre == len(pre) and plan.size == len(pre) + len(dec)
+        got = [(int(e) & 0xFFFF, int(e) >> 16) for e in plan]
+        assert sorted(got[:npre]) == sorted((b, x) for b, x, _ in pre)
+        assert sorted(got[npre:]) == sorted((b, x) for b, x, _ in dec)
+        wp = {(b, x): w for b, x, w in pre}
+        wd = {(b, x): w for b, x, w in dec}
+        assert [wp[e] for e in got[:npre]] == sorted(wp.values(), reverse=True)
+        assert [wd[e] for e in got[npre:]] == sorted(wd.values(), reverse=True)
+
+
+def test_varlen_plan_rejects_bad_metadata():
+    sl = np.array([10, 10], np.int32)
+    with pytest.raises(ops.PAError):            # more rows than tokens
+        ops.varlen_plan(np.array([0, 11, 12], np.int32), sl, 16, 8, 2)
+    with pytest.raises(ops.PAError):            # decreasing start locations
+        ops.varlen_plan(np.array([0, 5, 3], np.int32), sl, 16, 8, 2)
+    with pytest.raises(ops.PAError):            # first start location not 0
+        ops.varlen_plan(np.array([1, 5, 6], np.int32), sl, 16, 8, 2)
+    with pytest.raises(ops.PAError):            # group size 3
+        ops.varlen_plan(np.array([0, 5, 6], np.int32), sl, 16, 6, 2)
+    with pytest.raises(ops.PAError):            # beyond max_seq_len
+        ops.varlen_plan(np.array([0, 5, 6], np.int32), sl, 8, 8, 2)
+    plan, npre = ops.varlen_plan(np.array([0, 0, 0], np.int32), sl, 16, 8, 2)
+    assert plan.size == 0 and npre == 0
+
+
+def _varlen_status(**kw):
+    args = dict(out=16, lse=None, q=16, qsl=16, T=4, cache=16, nb=4, bt=16, mbps=4, sl=16, B=1,
+                msl=64, hq=8, hkv=2, d=128, bs=16, scale=0.1, P=0, plan=16, plan_n=1, npre=0,
+                ws=None, wsb=0, dtype=ops.PA_BF16)
+    args.update(kw)
+    L = ops.lib()
+    st = L.pa_attention_varlen(args["out"], args["lse"], args["q"], args["qsl"], args["T"],
+                               args["cache"], args["nb"], args["bt"], args["mbps"], args["sl"],
+                               args["B"], args["msl"], args["hq"], args["hkv"], args["d"],
+                               args["bs"], args["scale"], args["P"], args["plan"],
+                               args["plan_n"], args["npre"], args["ws"], args["wsb"],
+                               args["dtype"], None)
+    return st, L.pa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hq=7), ops.PA_EINVAL),             # H_q not a multiple of H_kv
+    (dict(hq=32, hkv=2), ops.PA_ENOTSUP),    # group 16: no prefill tile for it
+    (dict(d=96), ops.PA_ENOTSUP),
+    (dict(bs=32), ops.PA_ENOTSUP),
+    (dict(dtype=ops.PA_F32), ops.PA_ENOTSUP),
+    (dict(dtype=ops.PA_FP8), ops.PA_EINVAL),
+    (dict(P=24), ops.PA_EINVAL),
+    (dict(P=16), ops.PA_EINVAL),             # workspace missing
+    (dict(npre=2), ops.PA_EINVAL),           # more prefill entries than entries
+    (dict(plan=None), ops.PA_EINVAL),
+    (dict(plan=18), ops.PA_EINVAL),          # misaligned plan
+    (dict(qsl=None), ops.PA_EINVAL),
+    (dict(out=8), ops.PA_EINVAL),
+    (dict(msl=65), ops.PA_EINVAL),           # beyond the table
+    (dict(scale=float("nan")), ops.PA_EINVAL),
+])
+def test_varlen_validation(kw, status):
+    st, msg = _varlen_status(**kw)
+    assert st == status, msg
+    assert "pa_attention_varlen" in msg
+
+
+def test_varlen_empty_batch_is_a_no_op():
+    assert _varlen_status(B=0)[0] == ops.PA_OK
+    assert _varlen_status(plan=None, plan_n=0)[0] == ops.PA_OK
