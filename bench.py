@@ -47,6 +47,11 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 METRIC = "paged-attn decode KV GB/s (% of HBM peak) + context-tokens/s, 1 GPU"
 TRAFFIC_FILES = {False: os.path.join(ROOT, "profiles", "decode_append_traffic.json"),
                  True: os.path.join(ROOT, "profiles", "decode_traffic.json")}
+VARLEN_TRAFFIC = os.path.join(ROOT, "profiles", "varlen_traffic.json")
+VARLEN_SOURCES = ["paged_attention_kv_block_amd/csrc/pa_varlen.hip",
+                  "paged_attention_kv_block_amd/csrc/pa_decode_dev.h",
+                  "paged_attention_kv_block_amd/csrc/pa_prefill_dev.h",
+                  "paged_attention_kv_block_amd/csrc/pa_common.h"]
 DECODE_SOURCES = ["paged_attention_kv_block_amd/csrc/pa_decode.hip",
                   "paged_attention_kv_block_amd/csrc/pa_decode_dev.h",
                   "paged_attention_kv_block_amd/csrc/pa_common.h"]
@@ -94,12 +99,12 @@ def cache_write_bytes(wl, kv_bytes=None) -> int:
     return wl.num_seqs * 2 * (row + out_row)
 
 
-def load_traffic(kernel_hash: str, unfused: bool):
+def load_traffic(kernel_hash: str, unfused: bool, path=None):
     """HBM bytes per launch of the timed decode kernel from the committed
     rocprofv3 counter summary, if it was taken on the current kernel source
     and workload."""
     try:
-        with open(TRAFFIC_FILES[unfused]) as f:
+        with open(path or TRAFFIC_FILES[unfused]) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -335,6 +340,232 @@ def bench_prefill(a, d, dev):
     return 0
 
 
+def varlen_bytes(wl, seq_lens, chunk_lens) -> int:
+    """Algorithmic bytes of one pa_attention_varlen launch: every context
+    token's K/V once, query rows in, output rows out, the used block-table
+    entries, seq_lens and query_start_loc."""
+    db = wl.dtype_bytes
+    kv = int(sum(int(L) for L in seq_lens)) * 2 * wl.num_kv_heads * wl.head_size * db
+    rows = int(sum(int(C) for C in chunk_lens))
+    qo = 2 * rows * wl.num_q_heads * wl.head_size * db
+    bt = sum((int(L) + wl.block_size - 1) // wl.block_size for L in seq_lens) * 4
+    return kv + qo + bt + 4 * (2 * len(seq_lens) + 1)
+
+
+def cpu_baseline_mixed(d, min_seconds: float):
+    """The fp64 oracle on this host over a bounded sample of the mixed step:
+    sequences in turn (write the step's new keys/values, attend with the
+    chunked-prefill definition, which covers the one-row decode sequences),
+    until min_seconds; returns (seconds, algorithmic bytes, sequences)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from tests.oracle_setup import OracleSide
+
+    wl = d.wl
+    chunks = wl.chunk_lens()
+    npre = sum(1 for c in chunks if c > 1)
+    # alternate chunk sequences and decode rows so the sample has both kinds
+    order = []
+    for i in range(wl.num_seqs):
+        order.append(i % npre if i % 2 == 0 else npre + (i // 2) % (wl.num_seqs - npre))
+    order = order[:16]
+    side = OracleSide(d, seqs=sorted(set(order)))
+    qsl = side.query_start_loc()
+    q = d.query()
+    done, nbytes, t0 = 0, 0, time.perf_counter()
+    with threadpool_limits(1):
+        while True:
+            b = order[done % len(order)]
+            L, C = int(d.seq_lens[b]), int(chunks[b])
+            k, v = d.kv(b)
+            slots = oracle.slot_mapping(side.block_tables[b], L - C, C, wl.block_size)
+            oracle.reshape_and_cache(side.pool, k[L - C:], v[L - C:], slots)
+            oracle.prefill_chunk(q, qsl, side.pool, side.block_tables, d.seq_lens, wl.scale,
+                                 seqs=[b])
+            nbytes += varlen_bytes(wl, [L], [C])
+            done += 1
+            if time.perf_counter() - t0 >= min_seconds:
+                break
+    return time.perf_counter() - t0, nbytes, done
+
+
+def bench_mixed(a, dev):
+    """One continuous-batching step over a flattened batch: 16 prefill chunks
+    of 256 rows after 2560 cached tokens and 240 decode rows of log-normal
+    length (Llama-3-8B-shaped heads).  The step writes the new tokens'
+    keys/values (pa_reshape_and_cache) and runs pa_attention_varlen, one
+    launch for both kinds of rows; the same step with pa_prefill_chunk and
+    pa_decode as two launches is timed beside it."""
+    import numpy as np
+    import torch
+    from paged_attention_kv_block_amd import host, inputs, ops
+
+    d = inputs.mixed_step()
+    wl = d.wl
+    B, Hq, Hkv, D, bs = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_size, wl.block_size
+    seq_lens = d.seq_lens
+    chunks = np.asarray(wl.chunk_lens(), dtype=np.int64)
+    npre = int(np.sum(chunks > 1))          # the chunk sequences come first
+    assert np.all(chunks[:npre] > 1) and np.all(chunks[npre:] == 1)
+    msl = int(seq_lens.max())
+    P = 512 if a.partition_size is None else a.partition_size
+
+    def dev_tensor(arr):
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    t0 = time.perf_counter()
+    alloc = ops.Allocator(d.num_blocks, d.pool_order)
+    bt = host.decode_block_tables(alloc, seq_lens, bs)
+    qsl = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    new_slots = np.concatenate([ops.slot_mapping(bt[b], int(seq_lens[b]) - int(chunks[b]),
+                                                 int(chunks[b]), bs) for b in range(B)])
+    vplan, vnpre = ops.varlen_plan(qsl, seq_lens, msl, Hq, Hkv, P)
+    host_us = (time.perf_counter() - t0) * 1e6
+    dplan = ops.decode_plan(seq_lens[npre:], msl, P)
+
+    # the cache holds every token before the step; the step writes the rest
+    pool = torch.zeros((d.num_blocks, 2, Hkv, bs, D), dtype=torch.bfloat16, device=dev)
+    ks, vs, sl, nks, nvs = [], [], [], [], []
+    for b in range(B):
+        L, C = int(seq_lens[b]), int(chunks[b])
+        k, v = d.kv(b)
+        ks.append(k[:L - C])
+        vs.append(v[:L - C])
+        sl.append(ops.slot_mapping(bt[b], 0, L - C, bs))
+        nks.append(k[L - C:])
+        nvs.append(v[L - C:])
+    ops.reshape_and_cache(dev_tensor(np.concatenate(ks)), dev_tensor(np.concatenate(vs)),
+                          torch.from_numpy(np.concatenate(sl)).to(dev), pool)
+    del ks, vs
+    nk, nv = dev_tensor(np.concatenate(nks)), dev_tensor(np.concatenate(nvs))
+    slots_dev = torch.from_numpy(new_slots).to(dev)
+    q = dev_tensor(d.query())
+    T = q.shape[0]
+    Tpre = int(qsl[npre])
+    out = torch.empty_like(q)
+    qsl_dev = torch.from_numpy(qsl).to(dev)
+    qsl_pre = qsl_dev[:npre + 1]
+    bt_dev = torch.from_numpy(bt).to(dev)
+    sl_dev = torch.from_numpy(np.ascontiguousarray(seq_lens, dtype=np.int32)).to(dev)
+    vplan_dev = torch.from_numpy(vplan).to(dev)
+    dplan_dev = torch.from_numpy(dplan).to(dev)
+    ws = ops.decode_workspace(B, Hq, Hkv, D, msl, P, dev)
+    ws_dec = ops.decode_workspace(B - npre, Hq, Hkv, D, msl, P, dev)
+    scale = float(wl.scale)
+    msl_pre = int(seq_lens[:npre].max())
+    max_q = int(chunks[:npre].max())
+    torch.cuda.synchronize()
+
+    def varlen():
+        ops.attention_varlen(out, q, qsl_dev, pool, bt_dev, sl_dev, msl, scale, vplan_dev, P, ws)
+
+    def separate():
+        ops.prefill_chunk(out[:Tpre], q[:Tpre], qsl_pre, max_q, pool, bt_dev[:npre],
+                          sl_dev[:npre], msl_pre, scale)
+        ops.decode(out[Tpre:], q[Tpre:], pool, bt_dev[npre:], sl_dev[npre:], msl, scale, P,
+                   ws_dec, plan=dplan_dev)
+
+    def step():
+        ops.reshape_and_cache(nk, nv, slots_dev, pool)
+        varlen()
+
+    def step_separate():
+        ops.reshape_and_cache(nk, nv, slots_dev, pool)
+        separate()
+
+    def capture(fn, n):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        return g
+
+    def timed(g, n):
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n   # microseconds per step
+
+    g_warm = capture(step, max(1, a.warmup))
+    g_warm.replay()
+    torch.cuda.synchronize()
+    step_us = timed(capture(step, a.steps), a.steps)
+    sep_us = timed(capture(step_separate, a.steps), a.steps)
+    var_us = timed(capture(varlen, a.steps), a.steps)
+    two_us = timed(capture(separate, a.steps), a.steps)
+
+    kbytes = varlen_bytes(wl, seq_lens, chunks)
+    wbytes = 2 * 2 * int(chunks.sum()) * Hkv * D * 2        # read + write the new K and V rows
+    flops = prefill_flops(seq_lens, chunks, Hq, D)
+    value = (kbytes + wbytes) / (step_us * 1e-6) / 1e9
+    achieved = kbytes / (var_us * 1e-6) / 1e9
+    res = {
+        "metric": "paged-attn varlen step GB/s (decode rows + prefill chunks, one launch), 1 GPU",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(step_us * 1e-3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) keys/values/queries; no weights)",
+        "config": {
+            "workload": "mixed-step-llama3-8b", "sequences": B, "prefill_chunks": npre,
+            "chunk_tokens": int(chunks[:npre].sum()), "decode_rows": B - npre,
+            "num_q_heads": Hq, "num_kv_heads": Hkv, "head_size": D, "block_size": bs,
+            "context_tokens": int(seq_lens.sum()), "max_seq_len": msl, "partition_size": P,
+            "pool_blocks": d.num_blocks, "parallelism": "none (1 GPU)",
+        },
+        "host_metadata_us": round(host_us, 1),
+        "step_us_one_launch": round(step_us, 2),
+        "step_us_two_launches": round(sep_us, 2),
+        "attention_us_one_launch": round(var_us, 2),
+        "attention_us_two_launches": round(two_us, 2),
+        "attention_tflops": round(flops / (var_us * 1e-6) / 1e12, 2),
+        "roofline": {
+            "kernel": "pa_attention_varlen (varlen_kernel)",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": (load_traffic(source_hash(VARLEN_SOURCES), False, VARLEN_TRAFFIC)
+                        if P == 512 else None),
+            "algorithmic_bytes_per_launch": kbytes,
+            "algorithmic_flops_per_launch": flops,
+            "mfma_frac": round(flops / (var_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "avg_launch_us": round(var_us, 3),
+        },
+    }
+    if not a.no_cpu_baseline:
+        dt, cbytes, nseq = cpu_baseline_mixed(d, a.cpu_seconds)
+        res["cpu_baseline"] = {
+            "value": round(cbytes / dt / 1e9, 6),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"{nseq} sequences of the mixed step, chunk sequences and decode rows "
+                      f"alternating (write the step's keys/values, attend), fp64 numpy, BLAS "
+                      f"1 thread; {dt:.1f} s",
+        }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -342,6 +573,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=1,
                     help="workload index: decode 1, 2, 4 (0 = tiny); 3 = chunked prefill")
+    ap.add_argument("--mixed", action="store_true",
+                    help="a flattened continuous-batching step: 16 prefill chunks and 240 "
+                         "decode rows in one pa_attention_varlen launch")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="split-K partition in tokens (default: workload's, else 256/512)")
     ap.add_argument("--rotate-mb", type=int, default=768,
@@ -383,6 +617,8 @@ def main(argv=None):
         log(f"copy calibration: 5 copies of {n} bytes")
         return 0
 
+    if a.mixed:
+        return bench_mixed(a, dev)
     wl = inputs.workload(a.workload)
     d = inputs.draw(a.workload)
     if wl.kind == "prefill":

@@ -352,8 +352,8 @@ int pa_prefill_chunk(void* out, float* lse_out, const void* query,
  * become decode items (split into partitions of partition_size tokens
  * when that is non-zero and max_seq_len needs more than one), sequences
  * with C_b >= 2 rows become query tiles of 128 / G rows, C_b = 0 nothing.
- * Entries are (x << 16) | b, the query tiles first (x = tile), then the
- * decode items (x = partition), each kind longest first.
+ * Entries are (1 << 31) | (tile << 16) | b for a query tile and
+ * (partition << 16) | b for a decode item.
  *   query_start_loc [B+1] int32, host, [0] = 0, non-decreasing
  *   seq_lens        [B] int32, host, C_b <= seq_lens[b] <= max_seq_len
  *   plan            [capacity] int32, host (nullable when capacity is 0)
@@ -379,8 +379,8 @@ int pa_varlen_plan(const int32_t* query_start_loc, const int32_t* seq_lens,
  *                   built from (the kernel reads rows from it)
  *   seq_lens        [B] int32, device, likewise
  *   partition_size  as given to pa_varlen_plan
- *   plan, plan_entries, prefill_entries  device copy of pa_varlen_plan's
- *                   output and its two counts
+ *   plan, plan_entries  device copy of pa_varlen_plan's output and its
+ *                   entry count
  *   workspace       as pa_decode's, sized by pa_decode_workspace_bytes(B,
  *                   H_q, H_kv, D, max_seq_len, partition_size); calls
  *                   sharing a workspace must not run concurrently
@@ -395,8 +395,8 @@ int pa_attention_varlen(void* out, float* lse_out, const void* query,
                         int32_t num_kv_heads, int32_t head_size,
                         int32_t block_size, float scale, int32_t partition_size,
                         const int32_t* plan, int32_t plan_entries,
-                        int32_t prefill_entries, void* workspace,
-                        size_t workspace_bytes, int32_t dtype, void* stream);
+                        void* workspace, size_t workspace_bytes,
+                        int32_t dtype, void* stream);
 
 #ifdef __cplusplus
 }

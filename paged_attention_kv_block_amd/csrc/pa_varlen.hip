@@ -14,12 +14,19 @@
 // into partitions merged by the last workgroup to finish).
 //
 // A host plan (pa_varlen_plan) lists the work items: first the prefill
-// query tiles, longest first, then the decode (sequence, partition) items,
-// longest first.  The grid has one workgroup per (item, KV head), item-major,
-// so the dispatcher starts the heavy tiles first and the decode items fill
-// the compute units as tiles finish.  With the KV heads a multiple of the 8
-// XCDs, all tiles of one KV head run on one XCD and share the blocks they
-// stream (a common prefix included) through that XCD's L2.
+// query tiles, grouped by sequence, then the decode (sequence, partition)
+// items, longest first.  The grid has one workgroup per (item, KV head),
+// item-major, so the dispatcher starts the heavy tiles first and the decode
+// items fill the compute units as tiles finish.  With the KV heads a
+// multiple of the 8 XCDs, all tiles of one (sequence, KV head) run on one
+// XCD, one after another, and share the blocks they stream (a common prefix
+// included) through that XCD's L2.
+//
+// Both kinds of work are bound by the same per-CU path from memory (the
+// decode rows stream from HBM, the query tiles re-read their blocks from
+// L2 into LDS), so running them side by side does not make either faster:
+// the launch takes about as long as pa_prefill_chunk and pa_decode one
+// after the other, and saves the second launch and its host call.
 #include <algorithm>
 #include <vector>
 
@@ -39,11 +46,11 @@ union VarlenSmem {
   DecodeSmem<D, G, true, kVarlenWaves, false> dc;
 };
 
-// plan entries: (x << 16) | b with x the query tile (the first
-// prefill_entries entries) or the decode partition (the rest)
+// plan entries: (1 << 31) | (tile << 16) | b for a prefill query tile,
+// (part << 16) | b for a decode partition
 template <int D, int G>
 __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void varlen_kernel(const DecodeParams a, const int* __restrict__ qsl, int prefill_entries) {
+void varlen_kernel(const DecodeParams a, const int* __restrict__ qsl) {
   __shared__ VarlenSmem<D, G> sm;
   const int item = blockIdx.x / a.num_kv_heads;
   const int g = blockIdx.x % a.num_kv_heads;
@@ -51,7 +58,7 @@ void varlen_kernel(const DecodeParams a, const int* __restrict__ qsl, int prefil
   const int b = e & 0xFFFF;
   const int x = (e >> 16) & 0x7FFF;
   if (b >= a.B) return;  // not an entry of this batch
-  if (item < prefill_entries) {
+  if (e < 0) {
     prefill_tile<D, G>(sm.pf, static_cast<uint16_t*>(a.out), a.lse_out,
                        static_cast<const uint16_t*>(a.query), qsl,
                        reinterpret_cast<const uint16_t*>(a.cache), a.num_blocks, a.block_tables,
@@ -70,14 +77,13 @@ void varlen_kernel(const DecodeParams a, const int* __restrict__ qsl, int prefil
 }
 
 template <int D>
-static bool launch_varlen(int G, const DecodeParams& a, const int* qsl, int prefill_entries,
-                          hipStream_t s) {
+static bool launch_varlen(int G, const DecodeParams& a, const int* qsl, hipStream_t s) {
   const dim3 grid(a.num_items), block(kPrefillThreads);
   switch (G) {
-    case 1: hipLaunchKernelGGL((varlen_kernel<D, 1>), grid, block, 0, s, a, qsl, prefill_entries); return true;
-    case 2: hipLaunchKernelGGL((varlen_kernel<D, 2>), grid, block, 0, s, a, qsl, prefill_entries); return true;
-    case 4: hipLaunchKernelGGL((varlen_kernel<D, 4>), grid, block, 0, s, a, qsl, prefill_entries); return true;
-    case 8: hipLaunchKernelGGL((varlen_kernel<D, 8>), grid, block, 0, s, a, qsl, prefill_entries); return true;
+    case 1: hipLaunchKernelGGL((varlen_kernel<D, 1>), grid, block, 0, s, a, qsl); return true;
+    case 2: hipLaunchKernelGGL((varlen_kernel<D, 2>), grid, block, 0, s, a, qsl); return true;
+    case 4: hipLaunchKernelGGL((varlen_kernel<D, 4>), grid, block, 0, s, a, qsl); return true;
+    case 8: hipLaunchKernelGGL((varlen_kernel<D, 8>), grid, block, 0, s, a, qsl); return true;
     default: return false;
   }
 }
@@ -138,7 +144,19 @@ extern "C" int pa_varlen_plan(const int32_t* query_start_loc, const int32_t* seq
     if (p.x != q.x) return p.x < q.x;
     return p.b < q.b;
   };
-  std::stable_sort(pre.begin(), pre.end(), longest_first);
+  // Query tiles stay grouped by sequence (consecutive workgroups, and on
+  // one XCD per KV head when H_kv is a multiple of 8), so the tiles that
+  // re-read a sequence's blocks run together and find them in L2; the
+  // sequences go by their total work, longest first, and a sequence's
+  // tiles longest first.
+  std::vector<int64_t> seq_work(size_t(B), 0);
+  for (const Item& it : pre) seq_work[size_t(it.b)] += it.work;
+  std::stable_sort(pre.begin(), pre.end(), [&](const Item& p, const Item& q) {
+    const int64_t wp = seq_work[size_t(p.b)], wq = seq_work[size_t(q.b)];
+    if (wp != wq) return wp > wq;
+    if (p.b != q.b) return p.b < q.b;
+    return p.x > q.x;
+  });
   std::stable_sort(dec.begin(), dec.end(), longest_first);
   const int64_t n = int64_t(pre.size()) + int64_t(dec.size());
   if (num_entries) *num_entries = int32_t(std::min<int64_t>(n, 0x7FFFFFFF));
@@ -147,7 +165,7 @@ extern "C" int pa_varlen_plan(const int32_t* query_start_loc, const int32_t* seq
     return fail(PA_EINVAL, "pa_varlen_plan: %lld entries, capacity %d", (long long)n, capacity);
   if (n > 0 && !plan) return fail(PA_EINVAL, "pa_varlen_plan: NULL plan");
   size_t i = 0;
-  for (const Item& it : pre) plan[i++] = (it.x << 16) | it.b;
+  for (const Item& it : pre) plan[i++] = int32_t(0x80000000u | uint32_t(it.x << 16) | uint32_t(it.b));
   for (const Item& it : dec) plan[i++] = (it.x << 16) | it.b;
   return PA_OK;
 }
@@ -159,15 +177,12 @@ extern "C" int pa_attention_varlen(void* out, float* lse_out, const void* query,
                                    const int32_t* seq_lens, int32_t B, int32_t max_seq_len,
                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
                                    int32_t block_size, float scale, int32_t partition_size,
-                                   const int32_t* plan, int32_t plan_entries,
-                                   int32_t prefill_entries, void* workspace,
+                                   const int32_t* plan, int32_t plan_entries, void* workspace,
                                    size_t workspace_bytes, int32_t dtype, void* stream) {
   const char* fn = "pa_attention_varlen";
   if (B < 0 || num_blocks < 0 || max_seq_len < 0 || max_blocks_per_seq < 0 ||
-      total_query_tokens < 0 || plan_entries < 0 || prefill_entries < 0)
+      total_query_tokens < 0 || plan_entries < 0)
     return fail(PA_EINVAL, "%s: negative size", fn);
-  if (prefill_entries > plan_entries)
-    return fail(PA_EINVAL, "%s: %d prefill entries of %d", fn, prefill_entries, plan_entries);
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
     return fail(PA_EINVAL, "%s: H_q %d not a multiple of H_kv %d", fn, num_q_heads, num_kv_heads);
   if (dtype != PA_BF16)
@@ -234,8 +249,8 @@ extern "C" int pa_attention_varlen(void* out, float* lse_out, const void* query,
     a.ws_rec = base + w.rec_off;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const bool ok = head_size == 64 ? launch_varlen<64>(G, a, query_start_loc, prefill_entries, st)
-                                  : launch_varlen<128>(G, a, query_start_loc, prefill_entries, st);
+  const bool ok = head_size == 64 ? launch_varlen<64>(G, a, query_start_loc, st)
+                                  : launch_varlen<128>(G, a, query_start_loc, st);
   if (!ok) return fail(PA_ENOTSUP, "%s: group size %d", fn, G);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));

@@ -65,7 +65,7 @@ SIGNATURES = {
                                 _vp, _vp]),
     "pa_attention_varlen": (_c_int, [_vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _vp, _c_i32, _vp,
                                      _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _f, _c_i32,
-                                     _vp, _c_i32, _c_i32, _vp, _c_sz, _c_i32, _vp]),
+                                     _vp, _c_i32, _vp, _c_sz, _c_i32, _vp]),
 }
 
 _lib = None
@@ -413,7 +413,7 @@ def prefill_chunk(out, query, query_start_loc, max_query_len: int, kv_cache, blo
 def varlen_plan(query_start_loc_host, seq_lens_host, max_seq_len: int, num_q_heads: int,
                 num_kv_heads: int, partition_size: int = 0):
     """Host-built work list of pa_attention_varlen: (int32 entries, number of
-    prefill-tile entries at its front)."""
+    them that are prefill query tiles)."""
     qsl = np.ascontiguousarray(query_start_loc_host, dtype=np.int32)
     sl = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
     if qsl.size != sl.size + 1:
@@ -430,12 +430,12 @@ def varlen_plan(query_start_loc_host, seq_lens_host, max_seq_len: int, num_q_hea
 
 
 def attention_varlen(out, query, query_start_loc, kv_cache, block_tables, seq_lens,
-                     max_seq_len: int, scale: float, plan, prefill_entries: int,
-                     partition_size: int = 0, workspace=None, lse=None, stream=None) -> None:
+                     max_seq_len: int, scale: float, plan, partition_size: int = 0,
+                     workspace=None, lse=None, stream=None) -> None:
     """One launch over a flattened batch of decode rows and prefill chunks:
     out/query packed bf16 [T, H_q, D]; query_start_loc int32 [B+1]; plan an
-    int32 GPU tensor holding varlen_plan(...)[0] and prefill_entries its
-    second value, built from the same lengths and partition_size."""
+    int32 GPU tensor holding varlen_plan(...)[0], built from the same
+    lengths and partition_size."""
     _need_gpu(out, query, query_start_loc, kv_cache, block_tables, seq_lens, plan, workspace, lse)
     torch = _torch()
     N, _, Hkv, bs, D = kv_cache.shape
@@ -460,5 +460,5 @@ def attention_varlen(out, query, query_start_loc, kv_cache, block_tables, seq_le
                                      _ptr(kv_cache), N, _ptr(block_tables), block_tables.shape[1],
                                      _ptr(seq_lens), B, int(max_seq_len), Hq, Hkv, D, bs,
                                      float(scale), int(partition_size), _ptr(plan), plan.numel(),
-                                     int(prefill_entries), _ptr(workspace), ws_bytes,
+                                     _ptr(workspace), ws_bytes,
                                      _dtype_code(kv_cache), _stream(stream)))

@@ -138,6 +138,6 @@ class GpuSide:
                                       msl, partition_size, self.device)
         ops.attention_varlen(out, q, torch.from_numpy(qsl).to(self.device), self.pool, self.bt_dev,
                              self.seq_lens_dev, msl, float(wl.scale if scale is None else scale),
-                             torch.from_numpy(plan).to(self.device), npre, partition_size, ws, lse)
+                             torch.from_numpy(plan).to(self.device), partition_size, ws, lse)
         torch.cuda.synchronize()
         return out, lse

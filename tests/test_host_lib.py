@@ -366,13 +366,20 @@ def test_varlen_plan_orders_tiles_then_decode_items():
         plan, npre = ops.varlen_plan(qsl, sl, 1300, 8 * G, 8, P)
         pre, dec = _varlen_items(qsl, sl, 1300, G, P)
         assert npre == len(pre) and plan.size == len(pre) + len(dec)
-        got = [(int(e) & 0xFFFF, int(e) >> 16) for e in plan]
+        u = plan.view(np.uint32).astype(np.int64)
+        kinds = list(u >> 31)
+        got = [(int(e) & 0xFFFF, (int(e) >> 16) & 0x7FFF) for e in u]
+        assert kinds == [1] * npre + [0] * (plan.size - npre)   # the tiles come first
         assert sorted(got[:npre]) == sorted((b, x) for b, x, _ in pre)
         assert sorted(got[npre:]) == sorted((b, x) for b, x, _ in dec)
-        wp = {(b, x): w for b, x, w in pre}
         wd = {(b, x): w for b, x, w in dec}
-        assert [wp[e] for e in got[:npre]] == sorted(wp.values(), reverse=True)
         assert [wd[e] for e in got[npre:]] == sorted(wd.values(), reverse=True)
+        # tiles grouped by sequence, sequences by total work, tiles longest first
+        sw = {}
+        for b, x, w in pre:
+            sw[b] = sw.get(b, 0) + w
+        want = sorted(((b, x) for b, x, _ in pre), key=lambda e: (-sw[e[0]], e[0], -e[1]))
+        assert got[:npre] == want
 
 
 def test_varlen_plan_rejects_bad_metadata():
@@ -393,7 +400,7 @@ def test_varlen_plan_rejects_bad_metadata():
 
 def _varlen_status(**kw):
     args = dict(out=16, lse=None, q=16, qsl=16, T=4, cache=16, nb=4, bt=16, mbps=4, sl=16, B=1,
-                msl=64, hq=8, hkv=2, d=128, bs=16, scale=0.1, P=0, plan=16, plan_n=1, npre=0,
+                msl=64, hq=8, hkv=2, d=128, bs=16, scale=0.1, P=0, plan=16, plan_n=1,
                 ws=None, wsb=0, dtype=ops.PA_BF16)
     args.update(kw)
     L = ops.lib()
@@ -401,8 +408,7 @@ def _varlen_status(**kw):
                                args["cache"], args["nb"], args["bt"], args["mbps"], args["sl"],
                                args["B"], args["msl"], args["hq"], args["hkv"], args["d"],
                                args["bs"], args["scale"], args["P"], args["plan"],
-                               args["plan_n"], args["npre"], args["ws"], args["wsb"],
-                               args["dtype"], None)
+                               args["plan_n"], args["ws"], args["wsb"], args["dtype"], None)
     return st, L.pa_last_error().decode()
 
 
@@ -415,7 +421,6 @@ def _varlen_status(**kw):
     (dict(dtype=ops.PA_FP8), ops.PA_EINVAL),
     (dict(P=24), ops.PA_EINVAL),
     (dict(P=16), ops.PA_EINVAL),             # workspace missing
-    (dict(npre=2), ops.PA_EINVAL),           # more prefill entries than entries
     (dict(plan=None), ops.PA_EINVAL),
     (dict(plan=18), ops.PA_EINVAL),          # misaligned plan
     (dict(qsl=None), ops.PA_EINVAL),
