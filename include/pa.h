@@ -135,6 +135,53 @@ int pa_allocator_stats(const pa_allocator* a, const int32_t* seq_lens,
                        int64_t* tail_waste_tokens);
 
 /* ---------------------------------------------------------------------------
+ * Prefix cache on the allocator ("Im Inneren von vLLM", section
+ * "Fortgeschrittene Funktionen"; "vLLM: Ein tiefer Einblick ...", section
+ * "Tiefenanalyse": the KV cache of common prompt prefixes is kept and reused).
+ * The pages give no mechanism; the reading implemented here:
+ *   - only full blocks are cached; a block's keys and values depend on every
+ *     token up to its end, so a cached block is identified by that whole
+ *     token prefix (exact comparison, no hash collisions);
+ *   - a freed block (reference count 0) goes back to the free queue as
+ *     before but keeps its cached contents ("cached free") until
+ *     pa_allocator_allocate pops it, which evicts it from the cache;
+ *   - a lookup that hits a cached free block takes it out of the queue;
+ *   - the queue order decides eviction, so a sequence should free its
+ *     blocks last-to-first: a deeper block is only reachable through its
+ *     predecessors and is the one to go first.
+ * Host memory only; tokens are int32 token ids.
+ * ------------------------------------------------------------------------- */
+
+/* Turns the prefix cache on for blocks of block_size tokens.  Calling it
+ * again with the same block_size is a no-op; another value is PA_EINVAL. */
+int pa_prefix_cache_enable(pa_allocator* a, int32_t block_size);
+
+/* Longest cached prefix of tokens[0..num_tokens): walks the full blocks
+ * j = 0, 1, ... of the token list and stops at the first whose prefix is not
+ * cached.  Each hit block gains one reference (a cached free block leaves
+ * the free queue) and its id goes to out_ids[j]; *num_hit receives the
+ * count.  out_ids must hold num_tokens / block_size entries.  A caller that
+ * must compute at least one token passes num_tokens - 1. */
+int pa_prefix_cache_acquire(pa_allocator* a, const int32_t* tokens,
+                            int32_t num_tokens, int32_t* out_ids,
+                            int32_t* num_hit);
+
+/* Registers the full blocks of a sequence whose keys and values are now
+ * written: block_ids[j] (allocated, num_blocks >= num_tokens / block_size)
+ * holds tokens [j*bs, (j+1)*bs).  A prefix that is cached already keeps its
+ * block (block_ids[j] then stays uncached).  PA_EINVAL, with no state change,
+ * if an id is out of range, free, listed twice, or already caches another
+ * prefix. */
+int pa_prefix_cache_insert(pa_allocator* a, const int32_t* tokens,
+                           int32_t num_tokens, const int32_t* block_ids,
+                           int32_t num_blocks);
+
+/* cached_out[0..num_blocks) (nullable): 1 if the block caches a prefix.
+ * stats_out[3] (nullable): cached blocks, total hit blocks, total evictions. */
+int pa_prefix_cache_export(const pa_allocator* a, int32_t* cached_out,
+                           int64_t* stats_out);
+
+/* ---------------------------------------------------------------------------
  * Token -> slot ("Inside vLLM", section "LLM Engine & Engine Core": blocks
  * map tokens to their KV-cache blocks).  Host memory.
  * For each sequence b (in order) and i in [0, num_tokens[b]):

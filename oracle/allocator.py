@@ -16,6 +16,22 @@ The pages name the queue but not its policy.  Readings:
   * sharing a block (prefix reuse) raises its reference count; sharing a free
     block, or freeing more references than a block holds, is an invalid
     argument, detected for the whole request before anything changes.
+
+Prefix cache ([IM] "Fortgeschrittene Funktionen", [TE] "Tiefenanalyse": the
+KV cache of common prompt prefixes is stored and reused).  The pages give no
+mechanism.  Readings, written here as plainly as possible:
+  * only full blocks are cached; block j of a token list holds the keys and
+    values of tokens [j*bs, (j+1)*bs), which depend on every token before
+    them, so the cache key of that block is the whole prefix
+    tokens[0 : (j+1)*bs] (a tuple; Python's dict compares it exactly);
+  * a freed block keeps its cached contents while it waits in the queue;
+    allocate() popping it means new contents, so its key is dropped;
+  * acquire(tokens) walks j = 0, 1, ... and stops at the first uncached key;
+    each hit gains a reference, and a hit on a free block takes it out of
+    the queue;
+  * insert(tokens, ids) caches block ids[j] under key j unless that key is
+    cached already; an id that is free, repeated or caching another key is
+    an invalid argument, detected before anything changes.
 """
 from __future__ import annotations
 
@@ -40,6 +56,11 @@ class OracleAllocator:
         self.num_blocks = num_blocks
         self.free_block_queue = deque(order)
         self.refcount = [0] * num_blocks
+        self.cache_block_size = 0          # prefix cache off
+        self.cached = {}                   # prefix tuple -> block id
+        self.block_key = [None] * num_blocks
+        self.hits = 0
+        self.evictions = 0
 
     @property
     def num_free(self) -> int:
@@ -52,6 +73,10 @@ class OracleAllocator:
             raise NoFreeBlocks(f"need {n}, have {len(self.free_block_queue)}")
         ids = [self.free_block_queue.popleft() for _ in range(n)]
         for i in ids:
+            if self.block_key[i] is not None:   # cached free block: evicted
+                del self.cached[self.block_key[i]]
+                self.block_key[i] = None
+                self.evictions += 1
             self.refcount[i] = 1
         return ids
 
@@ -81,6 +106,60 @@ class OracleAllocator:
     def export(self):
         """(queue head..tail, refcounts) -- the whole allocator state."""
         return list(self.free_block_queue), list(self.refcount)
+
+    # prefix cache -----------------------------------------------------------
+    def enable_prefix_cache(self, block_size: int) -> None:
+        if block_size <= 0:
+            raise InvalidArgument("block_size <= 0")
+        if self.cache_block_size not in (0, block_size):
+            raise InvalidArgument("prefix cache enabled with another block size")
+        self.cache_block_size = block_size
+
+    def _key(self, tokens, j):
+        bs = self.cache_block_size
+        return tuple(int(t) for t in tokens[:(j + 1) * bs])
+
+    def acquire(self, tokens) -> list:
+        if not self.cache_block_size:
+            raise InvalidArgument("prefix cache not enabled")
+        hit = []
+        for j in range(len(tokens) // self.cache_block_size):
+            key = self._key(tokens, j)
+            if key not in self.cached:
+                break
+            b = self.cached[key]
+            if self.refcount[b] == 0:
+                self.free_block_queue.remove(b)
+            self.refcount[b] += 1
+            hit.append(b)
+        self.hits += len(hit)
+        return hit
+
+    def insert(self, tokens, ids) -> None:
+        if not self.cache_block_size:
+            raise InvalidArgument("prefix cache not enabled")
+        full = len(tokens) // self.cache_block_size
+        ids = [int(i) for i in ids]
+        if len(ids) < full:
+            raise InvalidArgument("fewer block ids than full blocks")
+        ids = ids[:full]
+        if len(set(ids)) != len(ids):
+            raise InvalidArgument("block listed twice")
+        for j, b in enumerate(ids):
+            if not (0 <= b < self.num_blocks) or self.refcount[b] == 0:
+                raise InvalidArgument(f"block {b} is not allocated")
+            if self.block_key[b] is not None and self.block_key[b] != self._key(tokens, j):
+                raise InvalidArgument(f"block {b} caches another prefix")
+        for j, b in enumerate(ids):
+            key = self._key(tokens, j)
+            if key not in self.cached:
+                self.cached[key] = b
+                self.block_key[b] = key
+
+    def export_prefix_cache(self):
+        """(cached flag per block, (cached blocks, hit blocks, evictions))."""
+        flags = [0 if k is None else 1 for k in self.block_key]
+        return flags, (len(self.cached), self.hits, self.evictions)
 
     def stats(self, seq_lens, block_size: int):
         """(blocks in use, tail waste in tokens): the last block of a sequence

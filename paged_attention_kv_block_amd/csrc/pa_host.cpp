@@ -56,21 +56,141 @@ extern "C" int64_t pa_num_blocks_for_budget(uint64_t budget_bytes,
 }
 
 // ---------------------------------------------------------------------------
-// Allocator: a ring buffer holds the free queue (head..tail), a refcount per
-// block id.  Every operation is O(n) in its argument count; capacity is the
-// pool size, so a block can never be queued twice.
+// Allocator.  The free queue is a doubly linked list threaded through the
+// block ids (push at the tail, pop at the head, and unlink of a cached free
+// block that a prefix lookup takes back), a refcount per block id.  Every
+// operation is O(n) in its argument count; a block is queued at most once.
+//
+// Prefix cache ("Im Inneren von vLLM", section "Fortgeschrittene
+// Funktionen": KV caches of common prompt prefixes are kept and reused).  A
+// full block's keys and values are a function of every token up to its end,
+// so a cached block is identified by that whole token prefix.  The prefixes
+// form a trie: a node is one full block of tokens under its parent node (the
+// root is -1), so node identity is prefix identity and needs no hash that
+// could collide.  A node holds the block that caches it, or -1 once that
+// block has been evicted; a node with neither a block nor children is
+// deleted, so node ids are never stale in a child's key.
 // ---------------------------------------------------------------------------
+namespace {
+
+struct NodeKey {
+  int32_t parent;
+  std::vector<int32_t> tokens;
+  bool operator==(const NodeKey& o) const {
+    return parent == o.parent && tokens == o.tokens;
+  }
+};
+
+// FNV-1a, 64-bit (Fowler, Noll, Vo): offset basis 14695981039346656037,
+// prime 1099511628211, over the key's bytes.  Only the bucket choice depends
+// on it; equality above is exact.
+struct NodeKeyHash {
+  size_t operator()(const NodeKey& k) const {
+    uint64_t h = 14695981039346656037ull;
+    auto mix = [&h](int32_t v) {
+      uint32_t u = uint32_t(v);
+      for (int i = 0; i < 4; ++i) {
+        h ^= (u >> (8 * i)) & 0xFFu;
+        h *= 1099511628211ull;
+      }
+    };
+    mix(k.parent);
+    for (int32_t t : k.tokens) mix(t);
+    return size_t(h);
+  }
+};
+
+struct Node {
+  int32_t parent = -1;
+  int32_t block = -1;     // block caching this prefix, -1: evicted
+  int32_t children = 0;   // live child nodes
+  std::vector<int32_t> tokens;
+};
+
+}  // namespace
+
 struct pa_allocator {
   int32_t n = 0;
-  std::vector<int32_t> ring;      // capacity n
-  int32_t head = 0, count = 0;    // queue = ring[head .. head+count) mod n
+  std::vector<int32_t> prev, next;  // queue links, -1 at the ends
+  std::vector<char> queued;
+  int32_t head = -1, tail = -1, count = 0;
   std::vector<int32_t> refcount;  // n
-  void push_tail(int32_t id) { ring[(head + count) % n] = id; ++count; }
-  int32_t pop_head() {
-    int32_t id = ring[head];
-    head = (head + 1) % n;
+
+  // prefix cache (block_size 0: not enabled)
+  int32_t cache_bs = 0;
+  std::vector<int32_t> block_node;  // node a block caches, or -1
+  std::vector<Node> nodes;
+  std::vector<int32_t> spare_nodes;
+  std::unordered_map<NodeKey, int32_t, NodeKeyHash> index;
+  int64_t cached = 0, hits = 0, evictions = 0;
+
+  void push_tail(int32_t id) {
+    prev[id] = tail;
+    next[id] = -1;
+    if (tail >= 0) next[tail] = id; else head = id;
+    tail = id;
+    queued[id] = 1;
+    ++count;
+  }
+  void unlink(int32_t id) {
+    if (prev[id] >= 0) next[prev[id]] = next[id]; else head = next[id];
+    if (next[id] >= 0) prev[next[id]] = prev[id]; else tail = prev[id];
+    prev[id] = next[id] = -1;
+    queued[id] = 0;
     --count;
+  }
+  int32_t pop_head() {
+    const int32_t id = head;
+    unlink(id);
     return id;
+  }
+
+  int32_t find_child(int32_t parent, const int32_t* toks) const {
+    NodeKey k{parent, std::vector<int32_t>(toks, toks + cache_bs)};
+    auto it = index.find(k);
+    return it == index.end() ? -1 : it->second;
+  }
+  int32_t child_or_new(int32_t parent, const int32_t* toks) {
+    NodeKey k{parent, std::vector<int32_t>(toks, toks + cache_bs)};
+    auto it = index.find(k);
+    if (it != index.end()) return it->second;
+    int32_t id;
+    if (!spare_nodes.empty()) {
+      id = spare_nodes.back();
+      spare_nodes.pop_back();
+    } else {
+      id = int32_t(nodes.size());
+      nodes.emplace_back();
+    }
+    Node& nd = nodes[id];
+    nd.parent = parent;
+    nd.block = -1;
+    nd.children = 0;
+    nd.tokens = k.tokens;
+    if (parent >= 0) ++nodes[parent].children;
+    index.emplace(std::move(k), id);
+    return id;
+  }
+  // deletes nodes that cache nothing and have no children, walking up
+  void prune(int32_t id) {
+    while (id >= 0 && nodes[id].block < 0 && nodes[id].children == 0) {
+      Node& nd = nodes[id];
+      index.erase(NodeKey{nd.parent, nd.tokens});
+      const int32_t parent = nd.parent;
+      if (parent >= 0) --nodes[parent].children;
+      nd.tokens.clear();
+      spare_nodes.push_back(id);
+      id = parent;
+    }
+  }
+  // a cached block leaves the cache (it is about to hold other contents)
+  void evict(int32_t id) {
+    const int32_t nd = block_node[id];
+    nodes[nd].block = -1;
+    block_node[id] = -1;
+    --cached;
+    ++evictions;
+    prune(nd);
   }
 };
 
@@ -84,8 +204,11 @@ extern "C" int pa_allocator_create(int32_t num_blocks,
   if (!a) return fail(PA_EINVAL, "pa_allocator_create: out of host memory");
   try {
     a->n = num_blocks;
-    a->ring.assign(num_blocks > 0 ? num_blocks : 1, 0);
+    a->prev.assign(num_blocks, -1);
+    a->next.assign(num_blocks, -1);
+    a->queued.assign(num_blocks, 0);
     a->refcount.assign(num_blocks, 0);
+    a->block_node.assign(num_blocks, -1);
   } catch (...) {
     delete a;
     return fail(PA_EINVAL, "pa_allocator_create: out of host memory");
@@ -120,6 +243,7 @@ extern "C" int pa_allocator_allocate(pa_allocator* a, int32_t n, int32_t* out_id
     return fail(PA_ENOBLOCKS, "pa_allocator_allocate: need %d blocks, %d free", n, a->count);
   for (int32_t i = 0; i < n; ++i) {
     const int32_t id = a->pop_head();
+    if (a->block_node[id] >= 0) a->evict(id);
     a->refcount[id] = 1;
     out_ids[i] = id;
   }
@@ -166,8 +290,10 @@ extern "C" int32_t pa_allocator_num_blocks(const pa_allocator* a) { return a ? a
 extern "C" int pa_allocator_export(const pa_allocator* a, int32_t* queue_out,
                                    int32_t* refcount_out) {
   if (!a) return fail(PA_EINVAL, "pa_allocator_export: NULL handle");
-  if (queue_out)
-    for (int32_t i = 0; i < a->count; ++i) queue_out[i] = a->ring[(a->head + i) % a->n];
+  if (queue_out) {
+    int32_t i = 0;
+    for (int32_t id = a->head; id >= 0; id = a->next[id]) queue_out[i++] = id;
+  }
   if (refcount_out && a->n > 0)
     std::memcpy(refcount_out, a->refcount.data(), sizeof(int32_t) * size_t(a->n));
   return PA_OK;
@@ -188,6 +314,107 @@ extern "C" int pa_allocator_stats(const pa_allocator* a, const int32_t* seq_lens
       w += (L + block_size - 1) / block_size * block_size - L;
     }
     *tail_waste_tokens = w;
+  }
+  return PA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// prefix cache
+// ---------------------------------------------------------------------------
+extern "C" int pa_prefix_cache_enable(pa_allocator* a, int32_t block_size) {
+  if (!a) return fail(PA_EINVAL, "pa_prefix_cache_enable: NULL handle");
+  if (block_size <= 0)
+    return fail(PA_EINVAL, "pa_prefix_cache_enable: block_size = %d", block_size);
+  if (a->cache_bs != 0 && a->cache_bs != block_size)
+    return fail(PA_EINVAL, "pa_prefix_cache_enable: already enabled with block_size %d",
+                a->cache_bs);
+  a->cache_bs = block_size;
+  return PA_OK;
+}
+
+extern "C" int pa_prefix_cache_acquire(pa_allocator* a, const int32_t* tokens,
+                                       int32_t num_tokens, int32_t* out_ids,
+                                       int32_t* num_hit) {
+  if (!a) return fail(PA_EINVAL, "pa_prefix_cache_acquire: NULL handle");
+  if (a->cache_bs == 0) return fail(PA_EINVAL, "pa_prefix_cache_acquire: cache not enabled");
+  if (!num_hit) return fail(PA_EINVAL, "pa_prefix_cache_acquire: num_hit is NULL");
+  if (num_tokens < 0 || (num_tokens > 0 && !tokens))
+    return fail(PA_EINVAL, "pa_prefix_cache_acquire: bad token list");
+  const int32_t full = num_tokens / a->cache_bs;
+  if (full > 0 && !out_ids) return fail(PA_EINVAL, "pa_prefix_cache_acquire: out_ids is NULL");
+  int32_t node = -1, h = 0;
+  for (int32_t j = 0; j < full; ++j) {
+    const int32_t child = a->find_child(node, tokens + int64_t(j) * a->cache_bs);
+    if (child < 0 || a->nodes[child].block < 0) break;
+    const int32_t id = a->nodes[child].block;
+    if (a->refcount[id] == 0) a->unlink(id);  // a cached free block is taken back
+    ++a->refcount[id];
+    out_ids[h++] = id;
+    node = child;
+  }
+  a->hits += h;
+  *num_hit = h;
+  return PA_OK;
+}
+
+extern "C" int pa_prefix_cache_insert(pa_allocator* a, const int32_t* tokens,
+                                      int32_t num_tokens, const int32_t* block_ids,
+                                      int32_t num_blocks) {
+  if (!a) return fail(PA_EINVAL, "pa_prefix_cache_insert: NULL handle");
+  if (a->cache_bs == 0) return fail(PA_EINVAL, "pa_prefix_cache_insert: cache not enabled");
+  if (num_tokens < 0 || (num_tokens > 0 && !tokens))
+    return fail(PA_EINVAL, "pa_prefix_cache_insert: bad token list");
+  const int32_t full = num_tokens / a->cache_bs;
+  if (num_blocks < full || (full > 0 && !block_ids))
+    return fail(PA_EINVAL, "pa_prefix_cache_insert: %d full blocks but %d block ids",
+                full, num_blocks);
+  // validate the whole request before any change
+  std::unordered_map<int32_t, int32_t> seen;
+  int32_t node = -1;
+  bool on_path = true;  // the trie already holds the prefix up to block j
+  for (int32_t j = 0; j < full; ++j) {
+    const int32_t id = block_ids[j];
+    if (id < 0 || id >= a->n)
+      return fail(PA_EINVAL, "pa_prefix_cache_insert: block %d out of range", id);
+    if (a->refcount[id] == 0)
+      return fail(PA_EINVAL, "pa_prefix_cache_insert: block %d is free", id);
+    if (!seen.emplace(id, j).second)
+      return fail(PA_EINVAL, "pa_prefix_cache_insert: block %d listed twice", id);
+    int32_t child = -1;
+    if (on_path) {
+      child = a->find_child(node, tokens + int64_t(j) * a->cache_bs);
+      on_path = child >= 0;
+      node = child;
+    }
+    if (a->block_node[id] >= 0 && a->block_node[id] != child)
+      return fail(PA_EINVAL,
+                  "pa_prefix_cache_insert: block %d already caches another prefix", id);
+  }
+  node = -1;
+  for (int32_t j = 0; j < full; ++j) {
+    const int32_t id = block_ids[j];
+    node = a->child_or_new(node, tokens + int64_t(j) * a->cache_bs);
+    Node& nd = a->nodes[node];
+    if (nd.block < 0) {  // first block to hold this prefix
+      nd.block = id;
+      a->block_node[id] = node;
+      ++a->cached;
+    }
+    // else: this prefix is cached already (by id itself, or by another block,
+    // which stays the cached copy; id then stays uncached)
+  }
+  return PA_OK;
+}
+
+extern "C" int pa_prefix_cache_export(const pa_allocator* a, int32_t* cached_out,
+                                      int64_t* stats_out) {
+  if (!a) return fail(PA_EINVAL, "pa_prefix_cache_export: NULL handle");
+  if (cached_out)
+    for (int32_t i = 0; i < a->n; ++i) cached_out[i] = a->block_node[i] >= 0 ? 1 : 0;
+  if (stats_out) {
+    stats_out[0] = a->cached;
+    stats_out[1] = a->hits;
+    stats_out[2] = a->evictions;
   }
   return PA_OK;
 }

@@ -241,3 +241,23 @@ def mixed_step(num_prefill: int = 16, prefill_context: int = 2560, chunk: int = 
     return custom("mixed-step", kind="prefill", seq_lens=seq_lens, chunk_lens=chunks,
                   num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_size=head_size,
                   seed=seed, index=index)
+
+
+def token_stream_rows(tokens, num_heads: int, head_size: int, dtype: str = "bf16",
+                      stream: int = 0, salt: int = 77) -> np.ndarray:
+    """Rows [len(tokens), num_heads, head_size] drawn N(0,1) where row t depends
+    only on tokens[0..t] (and the stream number): the seed of position t is
+    SeedSequence([seed word of position t-1, tokens[t], stream]).  Two token
+    lists with a common prefix get identical rows over that prefix, as keys
+    and values computed by a causal model would; prefix-cache tests draw
+    keys (stream 0), values (stream 1) and queries (stream 2) this way.
+    float32 for "f32", bf16 bit patterns (uint16) otherwise."""
+    out = np.empty((len(tokens), num_heads, head_size),
+                   dtype=np.float32 if dtype == "f32" else np.uint16)
+    word = salt
+    for t, tok in enumerate(tokens):
+        word = int(np.random.SeedSequence([word, int(tok)]).generate_state(1, np.uint64)[0])
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([word, stream])))
+        x = rng.standard_normal(size=(num_heads, head_size), dtype=np.float32)
+        out[t] = x if dtype == "f32" else round_to_bf16_bits(x)
+    return out

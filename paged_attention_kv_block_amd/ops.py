@@ -38,6 +38,10 @@ SIGNATURES = {
     "pa_allocator_num_blocks": (_c_i32, [_vp]),
     "pa_allocator_export": (_c_int, [_vp, _vp, _vp]),
     "pa_allocator_stats": (_c_int, [_vp, _vp, _c_i32, _c_i32, _vp, _vp]),
+    "pa_prefix_cache_enable": (_c_int, [_vp, _c_i32]),
+    "pa_prefix_cache_acquire": (_c_int, [_vp, _vp, _c_i32, _vp, _vp]),
+    "pa_prefix_cache_insert": (_c_int, [_vp, _vp, _c_i32, _vp, _c_i32]),
+    "pa_prefix_cache_export": (_c_int, [_vp, _vp, _vp]),
     "pa_slot_mapping": (_c_int, [_vp, _c_i32, _vp, _vp, _c_i32, _c_i32, _vp, _vp]),
     "pa_reshape_and_cache": (_c_int, [_vp, _vp, _vp, _c_i32, _vp, _c_i32, _c_i32, _c_i32,
                                       _c_i32, _c_i32, _vp]),
@@ -179,6 +183,32 @@ class Allocator:
         _check(lib().pa_allocator_stats(self._h, _np_ptr(sl), sl.size, int(block_size),
                                         ctypes.byref(used), ctypes.byref(waste)))
         return used.value, waste.value
+
+    # prefix cache ---------------------------------------------------------
+    def enable_prefix_cache(self, block_size: int) -> None:
+        _check(lib().pa_prefix_cache_enable(self._h, int(block_size)))
+        self._cache_bs = int(block_size)
+
+    def acquire_prefix(self, tokens) -> list:
+        """Ids of the cached blocks of the longest cached prefix (referenced)."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        out = np.empty(max(t.size // max(getattr(self, "_cache_bs", 1), 1), 1), dtype=np.int32)
+        hit = ctypes.c_int32()
+        _check(lib().pa_prefix_cache_acquire(self._h, _np_ptr(t), t.size, _np_ptr(out),
+                                             ctypes.byref(hit)))
+        return out[:hit.value].tolist()
+
+    def insert_prefix(self, tokens, block_ids) -> None:
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        ids = np.ascontiguousarray(block_ids, dtype=np.int32)
+        _check(lib().pa_prefix_cache_insert(self._h, _np_ptr(t), t.size, _np_ptr(ids), ids.size))
+
+    def export_prefix_cache(self):
+        """(cached flag per block, (cached blocks, hit blocks, evictions))."""
+        c = np.empty(max(self.num_blocks, 1), dtype=np.int32)
+        st = np.empty(3, dtype=np.int64)
+        _check(lib().pa_prefix_cache_export(self._h, _np_ptr(c), _np_ptr(st)))
+        return c[:self.num_blocks].tolist(), tuple(int(x) for x in st)
 
 
 def slot_mapping(block_tables: np.ndarray, start_pos, num_tokens, block_size: int) -> np.ndarray:
