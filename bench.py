@@ -566,6 +566,156 @@ def bench_mixed(a, dev):
     return 0
 
 
+def bench_spec(a, dev):
+    """A speculative-decoding verification step: every sequence of a decode
+    batch checks C = --spec-rows tokens at once (C - 1 draft tokens and the
+    one after them), i.e. a causal chunk of C query rows at the end of its
+    context.  The batch, heads and lengths are those of decode workload
+    --workload (lengths include the C new tokens).  The timed launch is
+    pa_decode_multi (the decode kernel with (row, head) matrix columns,
+    split-K as the workload's decode); beside it, on the same cache,
+    pa_attention_varlen and pa_prefill_chunk (the same rows as 128-row
+    query tiles) and, for scale, pa_decode with one row per sequence."""
+    import numpy as np
+    import torch
+    from paged_attention_kv_block_amd import host, inputs, ops
+
+    base = inputs.workload(a.workload)
+    if base.kind != "decode" or base.dtype != "bf16":
+        print("bench.py: --spec-rows needs a bf16 decode workload (1, 2 or 4)", file=sys.stderr)
+        return 2
+    C = int(a.spec_rows)
+    d0 = inputs.draw(a.workload)
+    B, Hq, Hkv, D, bs = base.num_seqs, base.num_q_heads, base.num_kv_heads, base.head_size, \
+        base.block_size
+    seq_lens = np.maximum(d0.seq_lens, C).astype(np.int32)
+    chunks = np.full(B, C, dtype=np.int64)
+    d = inputs.custom(f"spec-verify-{base.name}", kind="prefill", seq_lens=seq_lens,
+                      chunk_lens=chunks.tolist(), num_q_heads=Hq, num_kv_heads=Hkv,
+                      head_size=D, seed=3000 + a.workload, index=200 + a.workload)
+    msl = int(seq_lens.max())
+    P = default_partition(base) if a.partition_size is None else a.partition_size
+
+    def dev_tensor(arr):
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    alloc = ops.Allocator(d.num_blocks, d.pool_order)
+    bt = host.decode_block_tables(alloc, seq_lens, bs)
+    qsl = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    t0 = time.perf_counter()
+    vplan, _ = ops.varlen_plan(qsl, seq_lens, msl, Hq, Hkv, P)
+    host_us = (time.perf_counter() - t0) * 1e6
+    dplan = ops.decode_plan(seq_lens, msl, P)
+    pool0 = torch.zeros((d.num_blocks, 2, Hkv, bs, D), dtype=torch.bfloat16, device=dev)
+    for lo in range(0, B, 32):           # fill in slices to bound host memory
+        ks, vs, sl = [], [], []
+        for b in range(lo, min(B, lo + 32)):
+            k, v = d.kv(b)
+            ks.append(k)
+            vs.append(v)
+            sl.append(ops.slot_mapping(bt[b], 0, int(seq_lens[b]), bs))
+        ops.reshape_and_cache(dev_tensor(np.concatenate(ks)), dev_tensor(np.concatenate(vs)),
+                              torch.from_numpy(np.concatenate(sl)).to(dev), pool0)
+        del ks, vs
+    pool_bytes = pool0.numel() * pool0.element_size()
+    R = max(1, -(-a.rotate_mb * (1 << 20) // pool_bytes))
+    pools = [pool0] + [pool0.clone() for _ in range(R - 1)]
+    q = dev_tensor(d.query())
+    out = torch.empty_like(q)
+    q1 = q.view(B, C, Hq, D)[:, C - 1].contiguous()
+    out1 = torch.empty_like(q1)
+    qsl_dev = torch.from_numpy(qsl).to(dev)
+    bt_dev = torch.from_numpy(bt).to(dev)
+    sl_dev = torch.from_numpy(seq_lens).to(dev)
+    vplan_dev = torch.from_numpy(vplan).to(dev)
+    dplan_dev = torch.from_numpy(dplan).to(dev)
+    ws = ops.decode_workspace(B, Hq, Hkv, D, msl, P, dev)
+    ws_multi = ops.decode_multi_workspace(B, C, Hq, Hkv, D, msl, P, dev)
+    scale = float(base.scale)
+    torch.cuda.synchronize()
+
+    def multi(pool):
+        ops.decode_multi(out, q, pool, bt_dev, sl_dev, msl, scale, C, P, ws_multi, plan=dplan_dev)
+
+    def varlen(pool):
+        ops.attention_varlen(out, q, qsl_dev, pool, bt_dev, sl_dev, msl, scale, vplan_dev, P, ws)
+
+    def prefill(pool):
+        ops.prefill_chunk(out, q, qsl_dev, C, pool, bt_dev, sl_dev, msl, scale)
+
+    def decode1(pool):
+        ops.decode(out1, q1, pool, bt_dev, sl_dev, msl, scale, P, ws, plan=dplan_dev)
+
+    def timed(fn, n):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(min(n, R)):
+                fn(pools[i % R])
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(pools[i % R])
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    multi_us = timed(multi, a.steps)
+    var_us = timed(varlen, a.steps)
+    pre_us = timed(prefill, a.steps)
+    dec_us = timed(decode1, a.steps)
+    kbytes = varlen_bytes(d.wl, seq_lens, chunks)
+    flops = prefill_flops(seq_lens, chunks, Hq, D)
+    achieved = kbytes / (multi_us * 1e-6) / 1e9
+    res = {
+        "metric": "paged-attn speculative-verify step GB/s (C query rows per sequence), 1 GPU",
+        "value": round(achieved, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(multi_us * 1e-3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) keys/values/queries; no weights)",
+        "config": {
+            "workload": f"spec-verify-{base.name}", "batch": B, "rows_per_sequence": C,
+            "num_q_heads": Hq, "num_kv_heads": Hkv, "head_size": D, "block_size": bs,
+            "context_tokens": int(seq_lens.sum()), "max_seq_len": msl, "partition_size": P,
+            "pool_blocks": d.num_blocks, "pool_copies_rotated": R,
+            "parallelism": "none (1 GPU)",
+        },
+        "host_plan_us": round(host_us, 1),
+        "attention_us_decode_multi": round(multi_us, 2),
+        "attention_us_varlen": round(var_us, 2),
+        "attention_us_prefill_chunk": round(pre_us, 2),
+        "decode_us_one_row": round(dec_us, 2),
+        "roofline": {
+            "kernel": "pa_decode_multi (decode_kernel, multi-row)",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": kbytes,
+            "algorithmic_flops_per_launch": flops,
+            "avg_launch_us": round(multi_us, 3),
+        },
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -576,6 +726,9 @@ def main(argv=None):
     ap.add_argument("--mixed", action="store_true",
                     help="a flattened continuous-batching step: 16 prefill chunks and 240 "
                          "decode rows in one pa_attention_varlen launch")
+    ap.add_argument("--spec-rows", type=int, default=0,
+                    help="a speculative-decoding verification step: every sequence of decode "
+                         "workload --workload checks this many query rows at once")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="split-K partition in tokens (default: workload's, else 256/512)")
     ap.add_argument("--rotate-mb", type=int, default=768,
@@ -619,6 +772,8 @@ def main(argv=None):
 
     if a.mixed:
         return bench_mixed(a, dev)
+    if a.spec_rows > 0:
+        return bench_spec(a, dev)
     wl = inputs.workload(a.workload)
     d = inputs.draw(a.workload)
     if wl.kind == "prefill":

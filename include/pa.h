@@ -366,6 +366,37 @@ int pa_decode_append_fp8(void* out, float* lse_out, const void* query,
                          const int32_t* plan, int32_t plan_entries, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Several query rows per sequence on the decode path: sequence b's last
+ * `rows` tokens (already written to the cache) each attend causally to the
+ * tokens up to themselves, as in a chunk of pa_prefill_chunk.  This is the
+ * verification step of speculative decoding, which proposes several tokens
+ * and checks them in one pass ("vLLM: Ein tiefer Einblick ...", section
+ * "Tiefenanalyse", and "Im Inneren von vLLM", "Fortgeschrittene
+ * Funktionen": speculative decoding; "Inside vLLM", "LLM Engine & Engine
+ * Core": the attention is the standard transformer's).  Query row i of
+ * sequence b (0 <= i < rows) sits at position seq_lens[b] - rows + i:
+ *   o = softmax(scale * q K[0..pos]^T) V[0..pos]; a row before position 0
+ *   (seq_lens[b] < rows) gets o = 0 and lse = -inf.
+ *   out, query   [B * rows][H_q][D], bf16, device; row b * rows + i
+ *   lse_out      [B * rows][H_q] fp32, device, nullable
+ *   other arguments as pa_decode (plan: pa_decode_plan of the same seq_lens
+ *   and partition_size); workspace >= pa_decode_multi_workspace_bytes(...).
+ * A work item covers floor(16 / G) rows with their G heads (one matrix tile
+ * of 16 columns) over one partition; longer row sets take several items.
+ * rows in [1, 64]; rows > 1 needs a bf16 cache and G <= 16; rows == 1 is
+ * pa_decode.  Split-K needs B * H_kv * ceil(rows / floor(16 / G)) <= 65536. */
+size_t pa_decode_multi_workspace_bytes(int32_t B, int32_t rows, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_size,
+                                       int32_t max_seq_len, int32_t partition_size);
+int pa_decode_multi(void* out, float* lse_out, const void* query, const void* kv_cache,
+                    int32_t num_blocks, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t B,
+                    int32_t max_seq_len, int32_t rows, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                    float scale, int32_t partition_size, const int32_t* plan,
+                    int32_t plan_entries, void* workspace, size_t workspace_bytes,
+                    int32_t dtype, void* stream);
+
 /* Chunked prefill ("Im Inneren von vLLM", "Fortgeschrittene Funktionen":
  * long prompts are split into chunks; "Inside vLLM", "Generate function":
  * the batch is flattened into one sequence of tokens).  Sequence b owns the

@@ -12,6 +12,8 @@
 
 namespace pa {
 
+constexpr int kMaxMultiRows = 64;  // query rows per sequence of pa_decode_multi
+
 // Zero-fills a decode workspace (its arrival counters must start at zero).
 __global__ void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -23,7 +25,7 @@ __global__ void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
 // ---------------------------------------------------------------------------
 // Workgroups of one decode kernel variant that fit on the device at once
 // (cached per device and variant): the persistent grid never exceeds this.
-template <int D, int G, bool BF16, int NW, bool APPEND, bool KV8>
+template <int D, int G, bool BF16, int NW, bool APPEND, bool KV8, bool MULTI>
 static int resident_workgroups() {
   constexpr int kMaxDev = 64;
   static int cached[kMaxDev] = {0};
@@ -33,7 +35,8 @@ static int resident_workgroups() {
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<D, G, BF16, NW, APPEND, KV8>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu,
+                                                   decode_kernel<D, G, BF16, NW, APPEND, KV8, MULTI>,
                                                    NW * kWave, 0) != hipSuccess ||
       per_cu <= 0)
     per_cu = 1;
@@ -43,24 +46,27 @@ static int resident_workgroups() {
   return cached[dev];
 }
 
-template <int D, int G, bool BF16, int NW, bool APPEND, bool KV8>
+template <int D, int G, bool BF16, int NW, bool APPEND, bool KV8, bool MULTI>
 static void launch_decode_variant(const DecodeParams& a, hipStream_t s) {
-  auto k = decode_kernel<D, G, BF16, NW, APPEND, KV8>;
+  auto k = decode_kernel<D, G, BF16, NW, APPEND, KV8, MULTI>;
   // With a plan every item is real: one workgroup each, so the hardware
   // dispatcher balances them and overlaps one item's merge with another's
   // loads.  Without one, a persistent grid skips the empty virtual items.
   const int grid = a.plan ? a.num_items
                           : std::max(1, std::min(a.num_items,
-                                                 4 * resident_workgroups<D, G, BF16, NW, APPEND, KV8>()));
+                                                 4 * resident_workgroups<D, G, BF16, NW, APPEND, KV8,
+                                                                         MULTI>()));
   hipLaunchKernelGGL(k, dim3(grid), dim3(NW * kWave), 0, s, a);
 }
 
-template <int D, int G, bool BF16, int NW, bool KV8>
+template <int D, int G, bool BF16, int NW, bool KV8, bool MULTI>
 static void launch_decode_nw(const DecodeParams& a, hipStream_t s) {
-  if (a.new_k)
-    launch_decode_variant<D, G, BF16, NW, true, KV8>(a, s);
+  if constexpr (MULTI)
+    launch_decode_variant<D, G, BF16, NW, false, KV8, true>(a, s);
+  else if (a.new_k)
+    launch_decode_variant<D, G, BF16, NW, true, KV8, false>(a, s);
   else
-    launch_decode_variant<D, G, BF16, NW, false, KV8>(a, s);
+    launch_decode_variant<D, G, BF16, NW, false, KV8, false>(a, s);
 }
 
 // Compute units of the current device (cached per device).
@@ -82,16 +88,20 @@ static int device_cus() {
 // waves each (a long item's blocks spread over more SIMD slots); many items
 // get small workgroups, so that several items share a compute unit and one
 // item's start and merge latency hides behind the others' loads.
-template <int D, int G, bool BF16, bool KV8>
+template <int D, int G, bool BF16, bool KV8, bool MULTI = false>
 static void launch_decode(const DecodeParams& a, hipStream_t s) {
   const int64_t cus = device_cus();
   if (a.num_items < 2 * cus)
-    launch_decode_nw<D, G, BF16, 8, KV8>(a, s);
+    launch_decode_nw<D, G, BF16, 8, KV8, MULTI>(a, s);
   else if (a.num_items < 8 * cus)
-    launch_decode_nw<D, G, BF16, 4, KV8>(a, s);
+    launch_decode_nw<D, G, BF16, 4, KV8, MULTI>(a, s);
   else
-    launch_decode_nw<D, G, BF16, 2, KV8>(a, s);
+    launch_decode_nw<D, G, BF16, 2, KV8, MULTI>(a, s);
 }
+
+// Rows of one multi-row work item: as many of the sequence's query rows as
+// fit 16 matrix columns with their G heads each.
+inline int multi_rows_per_group(int G) { return G >= 16 ? 1 : 16 / G; }
 
 template <int D, bool BF16, bool KV8 = false>
 static bool dispatch_g(int G, const DecodeParams& a, hipStream_t s) {
@@ -118,6 +128,23 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int3
   const int64_t P = parts_for(max_seq_len, partition_size);
   if (P <= 1) return 0;
   return size_t(ws_layout(B, num_q_heads, num_kv_heads, head_size, P).total);
+}
+
+extern "C" size_t pa_decode_multi_workspace_bytes(int32_t B, int32_t rows, int32_t num_q_heads,
+                                                  int32_t num_kv_heads, int32_t head_size,
+                                                  int32_t max_seq_len, int32_t partition_size) {
+  if (B <= 0 || rows <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
+      num_q_heads % num_kv_heads || num_q_heads / num_kv_heads > 16)
+    return 0;
+  if (rows == 1)
+    return pa_decode_workspace_bytes(B, num_q_heads, num_kv_heads, head_size, max_seq_len,
+                                     partition_size);
+  const int64_t P = parts_for(max_seq_len, partition_size);
+  if (P <= 1) return 0;
+  const int rpg = multi_rows_per_group(num_q_heads / num_kv_heads);
+  const int64_t groups = (rows + rpg - 1) / rpg;
+  return size_t(ws_layout(int64_t(B) * groups, int64_t(16) * num_kv_heads, num_kv_heads,
+                          head_size, P).total);
 }
 
 extern "C" int pa_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
@@ -182,7 +209,8 @@ static int decode_call(const char* fn, void* out, float* lse_out, const void* qu
                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
                        int32_t block_size, float scale, float k_scale, float v_scale,
                        int32_t partition_size, const int32_t* plan, int32_t plan_entries,
-                       void* workspace, size_t workspace_bytes, int32_t dtype, void* stream) {
+                       void* workspace, size_t workspace_bytes, int32_t dtype, void* stream,
+                       int32_t rows = 1) {
   if (B < 0 || num_blocks < 0 || max_seq_len < 0 || max_blocks_per_seq < 0 || plan_entries < 0)
     return fail(PA_EINVAL, "%s: negative size", fn);
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
@@ -216,18 +244,29 @@ static int decode_call(const char* fn, void* out, float* lse_out, const void* qu
   if (plan && (B > 65535 || plan_entries == 0))
     return fail(PA_EINVAL, "%s: a plan needs B <= 65535 and at least one entry", fn);
   const int G = num_q_heads / num_kv_heads;
+  const bool multi = rows > 1;
+  if (rows < 1 || rows > kMaxMultiRows)
+    return fail(PA_EINVAL, "%s: rows %d outside [1, %d]", fn, rows, kMaxMultiRows);
+  if (multi && dtype != PA_BF16)
+    return fail(PA_ENOTSUP, "%s: several rows per sequence need a bf16 cache", fn);
+  if (multi && G > 16) return fail(PA_ENOTSUP, "%s: group size %d > 16", fn, G);
+  const int rpg = multi ? multi_rows_per_group(G) : 1;
+  const int groups = (rows + rpg - 1) / rpg;
   const int64_t P = parts_for(max_seq_len, partition_size);
   if (P > 65535) return fail(PA_EINVAL, "%s: too many partitions (%lld)", fn, (long long)P);
-  const int64_t items = (plan ? int64_t(plan_entries) : int64_t(B) * P) * num_kv_heads;
+  const int64_t per_group = plan ? int64_t(plan_entries) : int64_t(B) * P;
+  const int64_t items = per_group * groups * num_kv_heads;
   if (items > 0x7FFFFFFF) return fail(PA_ENOTSUP, "%s: too many work items", fn);
   const size_t need =
-      pa_decode_workspace_bytes(B, num_q_heads, num_kv_heads, head_size, max_seq_len, partition_size);
+      pa_decode_multi_workspace_bytes(B, rows, num_q_heads, num_kv_heads, head_size, max_seq_len,
+                                      partition_size);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PA_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes);
   if (need > 0 && (uintptr_t(workspace) & 255))
     return fail(PA_EINVAL, "%s: workspace must be 256-byte aligned", fn);
-  if (P > 1 && int64_t(B) * num_kv_heads > kCounterCap)
-    return fail(PA_ENOTSUP, "%s: split-K supports B * H_kv <= %lld", fn, (long long)kCounterCap);
+  if (P > 1 && int64_t(B) * num_kv_heads * groups > kCounterCap)
+    return fail(PA_ENOTSUP, "%s: split-K supports B * H_kv * column groups <= %lld", fn,
+                (long long)kCounterCap);
 
   DecodeParams a{};
   a.out = out;
@@ -250,15 +289,25 @@ static int decode_call(const char* fn, void* out, float* lse_out, const void* qu
   a.part_blocks = P > 1 ? partition_size / kBlockSize : 0;
   a.max_parts = int(P);
   a.num_items = int(items);
+  a.rows = rows;
+  a.group = G;
+  a.rows_per_group = rpg;
+  a.col_groups = groups;
+  a.items_per_group = int(per_group);
   if (P > 1) {
-    const WsLayout w = ws_layout(B, num_q_heads, num_kv_heads, head_size, P);
+    const WsLayout w = multi ? ws_layout(int64_t(B) * groups, int64_t(16) * num_kv_heads,
+                                         num_kv_heads, head_size, P)
+                             : ws_layout(B, num_q_heads, num_kv_heads, head_size, P);
     uint8_t* base = static_cast<uint8_t*>(workspace);
     a.ws_count = reinterpret_cast<int*>(base + w.count_off);
     a.ws_rec = base + w.rec_off;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   bool ok;
-  if (dtype == PA_FP8)
+  if (multi)
+    ok = head_size == 64 ? (launch_decode<64, 16, true, false, true>(a, st), true)
+                         : (launch_decode<128, 16, true, false, true>(a, st), true);
+  else if (dtype == PA_FP8)
     ok = head_size == 64 ? dispatch_g<64, true, true>(G, a, st)
                          : dispatch_g<128, true, true>(G, a, st);
   else if (dtype == PA_BF16)
@@ -340,3 +389,20 @@ extern "C" int pa_decode_append(void* out, float* lse_out, const void* query,
                      stream);
 }
 
+
+extern "C" int pa_decode_multi(void* out, float* lse_out, const void* query, const void* kv_cache,
+                               int32_t num_blocks, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t B,
+                               int32_t max_seq_len, int32_t rows, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                               float scale, int32_t partition_size, const int32_t* plan,
+                               int32_t plan_entries, void* workspace, size_t workspace_bytes,
+                               int32_t dtype, void* stream) {
+  if (dtype == PA_FP8)
+    return fail(PA_ENOTSUP, "pa_decode_multi: bf16 or fp32 caches only");
+  return decode_call("pa_decode_multi", out, lse_out, query, nullptr, nullptr, kv_cache,
+                     num_blocks, block_tables, max_blocks_per_seq, seq_lens, B, max_seq_len,
+                     num_q_heads, num_kv_heads, head_size, block_size, scale, 1.f, 1.f,
+                     partition_size, plan, plan_entries, workspace, workspace_bytes, dtype,
+                     stream, rows);
+}

@@ -420,6 +420,13 @@ struct DecodeParams {
   int part_blocks, max_parts, num_items;
   float scale_log2;       // scale * log2(e), times the key scale for an FP8 cache
   float k_scale, v_scale;  // FP8 cache: key / value scales
+  // Several query rows per sequence (the multi-row kernel variant only):
+  // sequence b's `rows` query rows are its last `rows` tokens, packed at
+  // rows b * rows ...; a work item covers `rows_per_group` of them for the
+  // `group` query heads of one KV head (columns = (row, head) pairs); there
+  // are col_groups items per (sequence, KV head, partition), and
+  // items_per_group items (plan entries or virtual (b, part)) per column group.
+  int rows, group, rows_per_group, col_groups, items_per_group;
 };
 
 // Append mode: the new token (position L - 1 of sequence b, KV head g)
@@ -678,10 +685,13 @@ __device__ __forceinline__ void append_new_token_fp8(MfmaBlock<D, true>& rg,
 // One block.  TAIL: only the first `valid` tokens (1 <= valid <= 16) are in
 // the sequence; the others get score -inf and their V rows are zeroed (they
 // may hold anything).
-template <int D, bool TAIL, bool KV8 = false>
+// MULTI: lane column n sees the block's tokens below `lim` (its own causal
+// limit, relative to the block's first token; may be <= 0 or >= 16).
+template <int D, bool TAIL, bool KV8 = false, bool MULTI = false>
 __device__ __forceinline__ void mfma_block(MfmaBlock<D, KV8>& cur, int valid,
                                            const u32x4 (&qb)[MfmaCfg<D>::KS], MfmaState<D>& st,
-                                           uint8_t* kt_lds, float scale_log2, int lane) {
+                                           uint8_t* kt_lds, float scale_log2, int lane,
+                                           int lim = 16) {
   using M = MfmaCfg<D, KV8>;
   const int n = lane & 15, grp = lane >> 4;
   // K tile -> LDS -> operand layout
@@ -713,12 +723,15 @@ __device__ __forceinline__ void mfma_block(MfmaBlock<D, KV8>& cur, int valid,
   for (int i = 0; i < 4; ++i) {
     float v = sc[i] * scale_log2;
     if constexpr (TAIL) v = 4 * grp + i < valid ? v : -INFINITY;
+    if constexpr (MULTI) v = 4 * grp + i < lim ? v : -INFINITY;
     x[i] = v;
   }
   const float t = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
   if (__builtin_amdgcn_ballot_w64(t > st.m_thr) != 0) {  // wave-uniform
     // max over the head's 16 tokens (lanes n, n + 16, n + 32, n + 48); it
-    // is finite: token 0 of the block is in the sequence
+    // is finite: token 0 of the block is in the sequence (MULTI: a column
+    // may see none of the block; its reference then starts at a finite
+    // -1e30, so the block's weights are exp2(-inf) = 0, never NaN)
     const float mb = allreduce_max_xor<4, 6>(t);
     const bool grow = mb > st.m_thr;
     const float alpha = grow ? __builtin_amdgcn_exp2f(st.m_run - mb) : 1.f;
@@ -779,10 +792,14 @@ __device__ __forceinline__ void mfma_block(MfmaBlock<D, KV8>& cur, int valid,
 // The bf16 block loop of one wave, then its (m, l) into sm.m / sm.l and its
 // unnormalised output rows into the LDS output stage; synchronises the
 // workgroup.
-template <int D, int G, int NW, bool APPEND, bool KV8 = false>
+// MULTI: column n is query row qrow + n / a.group, head g * a.group + n %
+// a.group, for n < ncols; that row sits at position L - a.rows + row_in_seq
+// and sees the tokens up to it.
+template <int D, int G, int NW, bool APPEND, bool KV8 = false, bool MULTI = false>
 __device__ __forceinline__ void mfma_blocks(const DecodeParams& a,
                                             DecodeSmem<D, G, true, NW, KV8>& sm, int b, int qrow,
-                                            int g, int L, int nblk, int blk_lo, int blk_hi) {
+                                            int g, int L, int nblk, int blk_lo, int blk_hi,
+                                            int row0 = 0, int ncols = G) {
   using M = MfmaCfg<D, KV8>;
   static_assert(G <= 16, "query heads per KV head");
   const uint8_t* __restrict__ cache = a.cache;
@@ -795,13 +812,25 @@ __device__ __forceinline__ void mfma_blocks(const DecodeParams& a,
 
   // Q^T operand: head n of this KV head (zero past G), d-chunks 4 s + grp
   u32x4 qb[M::KS];
+  int lim = L;  // MULTI: this lane column's causal limit (exclusive)
   {
-    const u32x4* qp = reinterpret_cast<const u32x4*>(a.query) +
-                      (int64_t(qrow) * H_q + g * G + (n < G ? n : 0)) * (D / 8);
+    int64_t qoff;
+    bool qvalid;
+    if constexpr (MULTI) {
+      const int gr = a.group;
+      const int nn = n < ncols ? n : 0;
+      qoff = (int64_t(qrow + nn / gr) * (num_kv_heads * gr) + g * gr + nn % gr) * (D / 8);
+      qvalid = n < ncols;
+      if (qvalid) lim = L - a.rows + row0 + n / gr + 1;
+    } else {
+      qoff = (int64_t(qrow) * H_q + g * G + (n < G ? n : 0)) * (D / 8);
+      qvalid = n < G;
+    }
+    const u32x4* qp = reinterpret_cast<const u32x4*>(a.query) + qoff;
 #pragma unroll
     for (int s = 0; s < M::KS; ++s) {
       const u32x4 v = qp[4 * s + grp];
-      qb[s] = n < G ? v : u32x4{0u, 0u, 0u, 0u};
+      qb[s] = qvalid ? v : u32x4{0u, 0u, 0u, 0u};
     }
   }
   const int64_t tile_bytes = int64_t(16) * M::RB;
@@ -810,8 +839,8 @@ __device__ __forceinline__ void mfma_blocks(const DecodeParams& a,
 
   uint8_t* kt_lds = sm.k + wave * M::TILE;
   MfmaState<D> st;
-  st.m_run = -INFINITY;
-  st.m_thr = -INFINITY;
+  st.m_run = MULTI ? -1e30f : -INFINITY;
+  st.m_thr = MULTI ? -1e30f : -INFINITY;
   st.l = 0.f;
 #pragma unroll
   for (int p = 0; p < M::NPV; ++p) st.o[p] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -845,7 +874,8 @@ __device__ __forceinline__ void mfma_blocks(const DecodeParams& a,
 #pragma unroll
       for (int s = 0; s < PD; ++s) {
         if (k0 + s < nfull)
-          mfma_block<D, false, KV8>(buf[s], 16, qb, st, kt_lds, scale_log2, lane);
+          mfma_block<D, false, KV8, MULTI>(buf[s], 16, qb, st, kt_lds, scale_log2, lane,
+                                           lim - 16 * (first + (k0 + s) * NW));
         buf[s] = load_mfma_block<D, KV8>(cache, __builtin_amdgcn_readlane(ids_next, s),
                                          block_bytes, g, num_kv_heads, tile_bytes, lane);
       }
@@ -862,7 +892,8 @@ __device__ __forceinline__ void mfma_blocks(const DecodeParams& a,
                                      block_bytes, tile_bytes, lane);
         }
       }
-      mfma_block<D, true, KV8>(buf[0], min(tail_valid, 16), qb, st, kt_lds, scale_log2, lane);
+      mfma_block<D, true, KV8, MULTI>(buf[0], min(tail_valid, 16), qb, st, kt_lds, scale_log2,
+                                      lane, lim - 16 * j_last);
     }
   }
 
@@ -1020,11 +1051,13 @@ __device__ __forceinline__ void valu_blocks(const DecodeParams& a, DecodeSmem<D,
 // [part * pb, min((part + 1) * pb, nblk))).  The query and output rows are
 // those of packed row `qrow` (b itself in a decode batch; the sequence's
 // first query row in a flattened batch).  Called by the whole workgroup.
-template <int D, int G, bool BF16, int NW, bool APPEND, bool KV8 = false>
+// MULTI (bf16 only): the item's columns are (query row, head) pairs of
+// column group cg (see DecodeParams); qrow is its first query row.
+template <int D, int G, bool BF16, int NW, bool APPEND, bool KV8 = false, bool MULTI = false>
 __device__ __forceinline__ void decode_item(const DecodeParams& a,
                                             DecodeSmem<D, G, BF16, NW, KV8>& sm,
                                             int b, int qrow, int g, int part, int L, int nblk,
-                                            int pb, int nparts) {
+                                            int pb, int nparts, int cg = 0) {
   void* __restrict__ out = a.out;
   float* __restrict__ lse_out = a.lse_out;
   const int num_kv_heads = a.num_kv_heads, max_parts = a.max_parts;
@@ -1036,8 +1069,23 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a,
   const int blk_hi = min(blk_lo + pb, nblk);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  static_assert(!MULTI || (BF16 && !APPEND), "multi-row items: bf16, no append");
+  int row0 = 0, ncols = G;  // MULTI: first row of the group within the sequence, live columns
+  if constexpr (MULTI) {
+    row0 = cg * a.rows_per_group;
+    ncols = min(a.rows_per_group, a.rows - row0) * a.group;
+  }
+  // output row of column h
+  auto out_row = [&](int h) -> int64_t {
+    if constexpr (MULTI)
+      return int64_t(qrow + h / a.group) * (num_kv_heads * a.group) + g * a.group + h % a.group;
+    else
+      return int64_t(qrow) * H_q + g * G + h;
+  };
+  const int slot = MULTI ? (b * num_kv_heads + g) * a.col_groups + cg : b * num_kv_heads + g;
   if constexpr (BF16)
-    mfma_blocks<D, G, NW, APPEND, KV8>(a, sm, b, qrow, g, L, nblk, blk_lo, blk_hi);
+    mfma_blocks<D, G, NW, APPEND, KV8, MULTI>(a, sm, b, qrow, g, L, nblk, blk_lo, blk_hi, row0,
+                                              ncols);
   else
     valu_blocks<D, G, NW, APPEND>(a, sm, b, qrow, g, L, nblk, blk_lo, blk_hi);
   float* o_lds = reinterpret_cast<float*>(sm.k);  // [wave][G][D]
@@ -1062,18 +1110,18 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a,
     }
   };
   if (single) {
-    for (int e = tid; e < G * D; e += NW * kWave) {
+    for (int e = tid; e < ncols * D; e += NW * kWave) {
       const int h = e / D, d = e % D;
       float M, lsum, acc;
       wave_merge(h, d, M, lsum, acc);
-      const int64_t row = int64_t(qrow) * H_q + g * G + h;
+      const int64_t row = out_row(h);
       store_out<BF16>(out, row * D + d, lsum > 0.f ? acc / lsum : 0.f);
       if (lse_out && d == 0) lse_out[row] = lsum > 0.f ? M * kLn2 + logf(lsum) : -INFINITY;
     }
     return;
   }
   // this partition's record: the outputs, then the maxima and sums
-  uint8_t* __restrict__ recs = a.ws_rec + int64_t(b * num_kv_heads + g) * max_parts * REC;
+  uint8_t* __restrict__ recs = a.ws_rec + int64_t(slot) * max_parts * REC;
   uint8_t* rec = recs + int64_t(part) * REC;
   constexpr int PER = BF16 ? 2 : 1;  // outputs per 4-byte store
   for (int e = tid; e < G * D / PER; e += NW * kWave) {
@@ -1106,20 +1154,19 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a,
   __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
   __syncthreads();
   if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(&ws_count[b * num_kv_heads + g], 1, __ATOMIC_RELAXED,
+    const int old = __hip_atomic_fetch_add(&ws_count[slot], 1, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
     sm.last = old == nparts - 1;
   }
   __syncthreads();
   if (!sm.last) return;
   if (tid == 0)  // ready for the next call
-    __hip_atomic_store(&ws_count[b * num_kv_heads + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&ws_count[slot], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // The partials of this KV head's G query-head rows, read through buffer
   // resources with the sc1 cache policy: like agent-scope atomic loads they
   // fetch past this XCD's L2 (which may hold stale lines from an earlier
   // call), but as plain loads many of them can be in flight at once.
-  const int64_t row0 = int64_t(qrow) * H_q + int64_t(g) * G;
   const __amdgpu_buffer_rsrc_t rr = ws_rsrc(reinterpret_cast<const float*>(recs), max_parts * REC);
   auto m_off = [&](int h, int p) { return p * REC + ML + h * 4; };
   auto l_off = [&](int h, int p) { return p * REC + ML + (G + h) * 4; };
@@ -1199,13 +1246,16 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a,
     for (int qi = 0; qi < QPT; ++qi) {
       const int quad = tid + qi * NT;
       const int h = quad / (D / 4), d4 = quad % (D / 4);
-      const int64_t row = row0 + h;
-      const float inv = 1.f / sm.W[h];
+      if (MULTI && h >= ncols) continue;
+      const int64_t row = out_row(h);
+      // a MULTI row before position 0 (seq_len < rows) sees nothing: W = 0
+      const float inv = (!MULTI || sm.W[h] > 0.f) ? 1.f / sm.W[h] : 0.f;
       store_out<BF16>(out, row * D + d4 * 4 + 0, acc[qi].x * inv);
       store_out<BF16>(out, row * D + d4 * 4 + 1, acc[qi].y * inv);
       store_out<BF16>(out, row * D + d4 * 4 + 2, acc[qi].z * inv);
       store_out<BF16>(out, row * D + d4 * 4 + 3, acc[qi].w * inv);
-      if (lse_out && d4 == 0) lse_out[row] = sm.M[h] * kLn2 + logf(sm.W[h]);
+      if (lse_out && d4 == 0)
+        lse_out[row] = (!MULTI || sm.W[h] > 0.f) ? sm.M[h] * kLn2 + logf(sm.W[h]) : -INFINITY;
     }
   }
 }
@@ -1222,26 +1272,35 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a,
 // items); head size 128 and fp32 need more registers than that.  An 8-wave
 // workgroup holds a compute unit alone at two or three waves per SIMD, so
 // its registers are left free for loads in flight.
+// The 16-column 2-wave variant of head size 128 (the multi-row kernel) is
+// held to two waves per SIMD, like the other 2-wave variants of that size.
 template <int D, int G, bool BF16, int NW>
-constexpr int decode_min_waves() { return NW == 4 && BF16 && D == 64 ? 3 : 1; }
+constexpr int decode_min_waves() {
+  return NW == 4 && BF16 && D == 64 ? 3 : (NW == 2 && BF16 && D == 128 && G == 16 ? 2 : 1);
+}
 template <int D, int G, bool BF16, int NW>
 constexpr int decode_max_waves() { return NW == 8 ? 2 : 8; }
 
-template <int D, int G, bool BF16, int NW, bool APPEND, bool KV8 = false>
+// MULTI: items are (column group, entry, KV head), column group slowest.
+template <int D, int G, bool BF16, int NW, bool APPEND, bool KV8 = false, bool MULTI = false>
 __global__ __launch_bounds__(NW * kWave)
 __attribute__((amdgpu_waves_per_eu(decode_min_waves<D, G, BF16, NW>(), decode_max_waves<D, G, BF16, NW>())))
 void decode_kernel(const DecodeParams a) {
   __shared__ DecodeSmem<D, G, BF16, NW, KV8> sm;
   for (int t = blockIdx.x; t < a.num_items; t += gridDim.x) {
     const int g = t % a.num_kv_heads;
+    int r = t / a.num_kv_heads, cg = 0;
+    if constexpr (MULTI) {
+      cg = r / a.items_per_group;
+      r -= cg * a.items_per_group;
+    }
     int b, part;
     if (a.plan) {
-      const int e = a.plan[t / a.num_kv_heads];
+      const int e = a.plan[r];
       b = e & 0xFFFF;
       part = (e >> 16) & 0xFFFF;
       if (b >= a.B) continue;  // not an entry of this batch
     } else {
-      const int r = t / a.num_kv_heads;
       b = r % a.B;
       part = r / a.B;
     }
@@ -1251,7 +1310,9 @@ void decode_kernel(const DecodeParams a) {
     const int pb = a.part_blocks > 0 ? a.part_blocks : (nblk > 0 ? nblk : 1);
     const int nparts = (nblk + pb - 1) / pb;
     if (part > 0 && part >= nparts) continue;
-    decode_item<D, G, BF16, NW, APPEND, KV8>(a, sm, b, b, g, part, L, nblk, pb, nparts);
+    const int qrow = MULTI ? b * a.rows + cg * a.rows_per_group : b;
+    decode_item<D, G, BF16, NW, APPEND, KV8, MULTI>(a, sm, b, qrow, g, part, L, nblk, pb, nparts,
+                                                    cg);
     __syncthreads();  // LDS is reused by the next item
   }
 }

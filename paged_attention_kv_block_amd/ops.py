@@ -62,6 +62,11 @@ SIGNATURES = {
     "pa_decode_append_fp8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _vp,
                                       _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _f, _f, _f,
                                       _c_i32, _vp, _c_i32, _vp, _c_sz, _vp]),
+    "pa_decode_multi_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                _c_i32]),
+    "pa_decode_multi": (_c_int, [_vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _vp, _c_i32, _c_i32,
+                                 _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _f, _c_i32, _vp, _c_i32,
+                                 _vp, _c_sz, _c_i32, _vp]),
     "pa_prefill_chunk": (_c_int, [_vp, _vp, _vp, _vp, _c_i32, _c_i32, _vp, _c_i32, _vp, _c_i32,
                                   _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _f,
                                   _c_i32, _vp]),
@@ -373,6 +378,57 @@ def decode(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int, scale
                                      "in the cache dtype")
     _check(lib().pa_decode_append(_ptr(out), _ptr(lse), _ptr(query), _ptr(new_key),
                                   _ptr(new_value), _ptr(kv_cache), *tail))
+
+
+def decode_multi_workspace_bytes(B: int, rows: int, num_q_heads: int, num_kv_heads: int,
+                                 head_size: int, max_seq_len: int, partition_size: int) -> int:
+    return int(lib().pa_decode_multi_workspace_bytes(B, rows, num_q_heads, num_kv_heads,
+                                                     head_size, max_seq_len, partition_size))
+
+
+def decode_multi_workspace(B: int, rows: int, num_q_heads: int, num_kv_heads: int,
+                           head_size: int, max_seq_len: int, partition_size: int,
+                           device="cuda", stream=None):
+    """A zeroed uint8 GPU workspace for decode_multi (at least 256 bytes)."""
+    torch = _torch()
+    n = decode_multi_workspace_bytes(B, rows, num_q_heads, num_kv_heads, head_size, max_seq_len,
+                                     partition_size)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    decode_workspace_init(ws, stream)
+    return ws
+
+
+def decode_multi(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int, scale: float,
+                 rows: int, partition_size: int = 0, workspace=None, lse=None, plan=None,
+                 stream=None) -> None:
+    """pa_decode_multi: every sequence's last `rows` tokens attend causally
+    (speculative-decoding verification).  out/query [B * rows, H_q, D];
+    lse fp32 [B * rows, H_q] or None; the other arguments as decode()."""
+    _need_gpu(out, query, kv_cache, block_tables, seq_lens, workspace, lse, plan)
+    torch = _torch()
+    N, _, Hkv, bs, D = kv_cache.shape
+    T, Hq, Dq = query.shape
+    B = seq_lens.numel()
+    if Dq != D or T != B * int(rows) or tuple(out.shape) != (T, Hq, D) \
+            or out.dtype != kv_cache.dtype or query.dtype != kv_cache.dtype:
+        raise PAError(PA_EINVAL, "out/query must be [B * rows, H_q, D] in the cache dtype")
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32 \
+            or block_tables.shape[0] != B:
+        raise PAError(PA_EINVAL, "block_tables/seq_lens must be int32 with B rows")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (T, Hq)):
+        raise PAError(PA_EINVAL, "lse must be fp32 [B * rows, H_q]")
+    for t in (out, query, kv_cache, block_tables, seq_lens, workspace, lse, plan):
+        if t is not None and not t.is_contiguous():
+            raise PAError(PA_EINVAL, "tensors must be contiguous")
+    if plan is not None and plan.dtype != torch.int32:
+        raise PAError(PA_EINVAL, "plan must be int32")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode_multi(_ptr(out), _ptr(lse), _ptr(query), _ptr(kv_cache), N,
+                                 _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), B,
+                                 int(max_seq_len), int(rows), Hq, Hkv, D, bs, float(scale),
+                                 int(partition_size), _ptr(plan),
+                                 0 if plan is None else plan.numel(), _ptr(workspace), ws_bytes,
+                                 _dtype_code(kv_cache), _stream(stream)))
 
 
 def decode_fp8(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int, scale: float,
