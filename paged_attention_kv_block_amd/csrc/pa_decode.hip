@@ -255,7 +255,9 @@ static int decode_call(const char* fn, void* out, float* lse_out, const void* qu
   const int64_t P = parts_for(max_seq_len, partition_size);
   if (P > 65535) return fail(PA_EINVAL, "%s: too many partitions (%lld)", fn, (long long)P);
   const int64_t per_group = plan ? int64_t(plan_entries) : int64_t(B) * P;
-  const int64_t items = per_group * groups * num_kv_heads;
+  // multi-row items come in runs of 8 per column group (see decode_kernel)
+  const int64_t items = multi ? (per_group * num_kv_heads + 7) / 8 * 8 * groups
+                              : per_group * num_kv_heads;
   if (items > 0x7FFFFFFF) return fail(PA_ENOTSUP, "%s: too many work items", fn);
   const size_t need =
       pa_decode_multi_workspace_bytes(B, rows, num_q_heads, num_kv_heads, head_size, max_seq_len,

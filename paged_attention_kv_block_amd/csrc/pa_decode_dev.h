@@ -1281,19 +1281,26 @@ constexpr int decode_min_waves() {
 template <int D, int G, bool BF16, int NW>
 constexpr int decode_max_waves() { return NW == 8 ? 2 : 8; }
 
-// MULTI: items are (column group, entry, KV head), column group slowest.
+// MULTI: the column groups of one (entry, KV head) item s are 8 item
+// indices apart, inside runs of 8 * col_groups indices: the dispatcher deals
+// workgroups to the 8 XCDs in turn, so they run on one XCD at about the same
+// time and the later ones can read the blocks from that XCD's L2.
 template <int D, int G, bool BF16, int NW, bool APPEND, bool KV8 = false, bool MULTI = false>
 __global__ __launch_bounds__(NW * kWave)
 __attribute__((amdgpu_waves_per_eu(decode_min_waves<D, G, BF16, NW>(), decode_max_waves<D, G, BF16, NW>())))
 void decode_kernel(const DecodeParams a) {
   __shared__ DecodeSmem<D, G, BF16, NW, KV8> sm;
   for (int t = blockIdx.x; t < a.num_items; t += gridDim.x) {
-    const int g = t % a.num_kv_heads;
-    int r = t / a.num_kv_heads, cg = 0;
+    int s = t, cg = 0;
     if constexpr (MULTI) {
-      cg = r / a.items_per_group;
-      r -= cg * a.items_per_group;
+      const int run = 8 * a.col_groups;
+      const int blk = t / run, rem = t - blk * run;
+      cg = rem >> 3;
+      s = blk * 8 + (rem & 7);
+      if (s >= a.items_per_group * a.num_kv_heads) continue;  // padding of the last run
     }
+    const int g = s % a.num_kv_heads;
+    const int r = s / a.num_kv_heads;
     int b, part;
     if (a.plan) {
       const int e = a.plan[r];
