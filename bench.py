@@ -48,6 +48,7 @@ METRIC = "paged-attn decode KV GB/s (% of HBM peak) + context-tokens/s, 1 GPU"
 TRAFFIC_FILES = {False: os.path.join(ROOT, "profiles", "decode_append_traffic.json"),
                  True: os.path.join(ROOT, "profiles", "decode_traffic.json")}
 VARLEN_TRAFFIC = os.path.join(ROOT, "profiles", "varlen_traffic.json")
+MULTI_TRAFFIC = os.path.join(ROOT, "profiles", "decode_multi_traffic.json")
 VARLEN_SOURCES = ["paged_attention_kv_block_amd/csrc/pa_varlen.hip",
                   "paged_attention_kv_block_amd/csrc/pa_decode_dev.h",
                   "paged_attention_kv_block_amd/csrc/pa_prefill_dev.h",
@@ -706,7 +707,8 @@ def bench_spec(a, dev):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": (load_traffic(source_hash(DECODE_SOURCES), False, MULTI_TRAFFIC)
+                        if a.workload == 2 and C == 4 and P == 512 else None),
             "algorithmic_bytes_per_launch": kbytes,
             "algorithmic_flops_per_launch": flops,
             "avg_launch_us": round(multi_us, 3),
