@@ -365,7 +365,7 @@ def cpu_baseline_mixed(d, min_seconds: float):
 
     wl = d.wl
     chunks = wl.chunk_lens()
-    npre = sum(1 for c in chunks if c > 1)
+    npre = sum(1 for c in chunks if c != chunks[-1])   # the decode sequences come last
     # alternate chunk sequences and decode rows so the sample has both kinds
     order = []
     for i in range(wl.num_seqs):
@@ -397,18 +397,22 @@ def bench_mixed(a, dev):
     length (Llama-3-8B-shaped heads).  The step writes the new tokens'
     keys/values (pa_reshape_and_cache) and runs pa_attention_varlen, one
     launch for both kinds of rows; the same step with pa_prefill_chunk and
-    pa_decode as two launches is timed beside it."""
+    pa_decode as two launches is timed beside it.  With --spec-rows C every
+    decode sequence has C rows (a speculative step): the varlen launch runs
+    them as multi-row decode items, and the second of the two launches is
+    pa_decode_multi."""
     import numpy as np
     import torch
     from paged_attention_kv_block_amd import host, inputs, ops
 
-    d = inputs.mixed_step()
+    Cd = max(1, int(a.spec_rows))          # rows per decode sequence
+    d = inputs.mixed_step(decode_rows=Cd)
     wl = d.wl
     B, Hq, Hkv, D, bs = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_size, wl.block_size
     seq_lens = d.seq_lens
     chunks = np.asarray(wl.chunk_lens(), dtype=np.int64)
-    npre = int(np.sum(chunks > 1))          # the chunk sequences come first
-    assert np.all(chunks[:npre] > 1) and np.all(chunks[npre:] == 1)
+    npre = int(np.sum(chunks != Cd))        # the chunk sequences come first
+    assert np.all(chunks[:npre] > Cd) and np.all(chunks[npre:] == Cd)
     msl = int(seq_lens.max())
     P = 512 if a.partition_size is None else a.partition_size
 
@@ -452,7 +456,8 @@ def bench_mixed(a, dev):
     vplan_dev = torch.from_numpy(vplan).to(dev)
     dplan_dev = torch.from_numpy(dplan).to(dev)
     ws = ops.decode_workspace(B, Hq, Hkv, D, msl, P, dev)
-    ws_dec = ops.decode_workspace(B - npre, Hq, Hkv, D, msl, P, dev)
+    ws_dec = (ops.decode_workspace(B - npre, Hq, Hkv, D, msl, P, dev) if Cd == 1 else
+              ops.decode_multi_workspace(B - npre, Cd, Hq, Hkv, D, msl, P, dev))
     scale = float(wl.scale)
     msl_pre = int(seq_lens[:npre].max())
     max_q = int(chunks[:npre].max())
@@ -464,8 +469,12 @@ def bench_mixed(a, dev):
     def separate():
         ops.prefill_chunk(out[:Tpre], q[:Tpre], qsl_pre, max_q, pool, bt_dev[:npre],
                           sl_dev[:npre], msl_pre, scale)
-        ops.decode(out[Tpre:], q[Tpre:], pool, bt_dev[npre:], sl_dev[npre:], msl, scale, P,
-                   ws_dec, plan=dplan_dev)
+        if Cd == 1:
+            ops.decode(out[Tpre:], q[Tpre:], pool, bt_dev[npre:], sl_dev[npre:], msl, scale, P,
+                       ws_dec, plan=dplan_dev)
+        else:
+            ops.decode_multi(out[Tpre:], q[Tpre:], pool, bt_dev[npre:], sl_dev[npre:], msl,
+                             scale, Cd, P, ws_dec, plan=dplan_dev)
 
     def step():
         ops.reshape_and_cache(nk, nv, slots_dev, pool)
@@ -525,8 +534,10 @@ def bench_mixed(a, dev):
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) keys/values/queries; no weights)",
         "config": {
-            "workload": "mixed-step-llama3-8b", "sequences": B, "prefill_chunks": npre,
-            "chunk_tokens": int(chunks[:npre].sum()), "decode_rows": B - npre,
+            "workload": "mixed-step-llama3-8b" + (f"-spec{Cd}" if Cd > 1 else ""),
+            "sequences": B, "prefill_chunks": npre,
+            "chunk_tokens": int(chunks[:npre].sum()), "decode_sequences": B - npre,
+            "rows_per_decode_sequence": Cd,
             "num_q_heads": Hq, "num_kv_heads": Hkv, "head_size": D, "block_size": bs,
             "context_tokens": int(seq_lens.sum()), "max_seq_len": msl, "partition_size": P,
             "pool_blocks": d.num_blocks, "parallelism": "none (1 GPU)",
@@ -545,7 +556,7 @@ def bench_mixed(a, dev):
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": (load_traffic(source_hash(VARLEN_SOURCES), False, VARLEN_TRAFFIC)
-                        if P == 512 else None),
+                        if P == 512 and Cd == 1 else None),
             "algorithmic_bytes_per_launch": kbytes,
             "algorithmic_flops_per_launch": flops,
             "mfma_frac": round(flops / (var_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),

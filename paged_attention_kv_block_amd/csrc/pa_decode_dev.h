@@ -793,13 +793,13 @@ __device__ __forceinline__ void mfma_block(MfmaBlock<D, KV8>& cur, int valid,
 // unnormalised output rows into the LDS output stage; synchronises the
 // workgroup.
 // MULTI: column n is query row qrow + n / a.group, head g * a.group + n %
-// a.group, for n < ncols; that row sits at position L - a.rows + row_in_seq
-// and sees the tokens up to it.
+// a.group, for n < ncols; that row sits at position L - rows + row_in_seq
+// (rows: the sequence's query rows) and sees the tokens up to it.
 template <int D, int G, int NW, bool APPEND, bool KV8 = false, bool MULTI = false>
 __device__ __forceinline__ void mfma_blocks(const DecodeParams& a,
                                             DecodeSmem<D, G, true, NW, KV8>& sm, int b, int qrow,
                                             int g, int L, int nblk, int blk_lo, int blk_hi,
-                                            int row0 = 0, int ncols = G) {
+                                            int row0 = 0, int ncols = G, int rows = 1) {
   using M = MfmaCfg<D, KV8>;
   static_assert(G <= 16, "query heads per KV head");
   const uint8_t* __restrict__ cache = a.cache;
@@ -821,7 +821,7 @@ __device__ __forceinline__ void mfma_blocks(const DecodeParams& a,
       const int nn = n < ncols ? n : 0;
       qoff = (int64_t(qrow + nn / gr) * (num_kv_heads * gr) + g * gr + nn % gr) * (D / 8);
       qvalid = n < ncols;
-      if (qvalid) lim = L - a.rows + row0 + n / gr + 1;
+      if (qvalid) lim = L - rows + row0 + n / gr + 1;
     } else {
       qoff = (int64_t(qrow) * H_q + g * G + (n < G ? n : 0)) * (D / 8);
       qvalid = n < G;
@@ -1052,12 +1052,13 @@ __device__ __forceinline__ void valu_blocks(const DecodeParams& a, DecodeSmem<D,
 // those of packed row `qrow` (b itself in a decode batch; the sequence's
 // first query row in a flattened batch).  Called by the whole workgroup.
 // MULTI (bf16 only): the item's columns are (query row, head) pairs of
-// column group cg (see DecodeParams); qrow is its first query row.
+// column group cg of the sequence's `rows` query rows (see DecodeParams);
+// qrow is the group's first query row.
 template <int D, int G, bool BF16, int NW, bool APPEND, bool KV8 = false, bool MULTI = false>
 __device__ __forceinline__ void decode_item(const DecodeParams& a,
                                             DecodeSmem<D, G, BF16, NW, KV8>& sm,
                                             int b, int qrow, int g, int part, int L, int nblk,
-                                            int pb, int nparts, int cg = 0) {
+                                            int pb, int nparts, int cg = 0, int rows = 1) {
   void* __restrict__ out = a.out;
   float* __restrict__ lse_out = a.lse_out;
   const int num_kv_heads = a.num_kv_heads, max_parts = a.max_parts;
@@ -1073,7 +1074,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a,
   int row0 = 0, ncols = G;  // MULTI: first row of the group within the sequence, live columns
   if constexpr (MULTI) {
     row0 = cg * a.rows_per_group;
-    ncols = min(a.rows_per_group, a.rows - row0) * a.group;
+    ncols = min(a.rows_per_group, rows - row0) * a.group;
   }
   // output row of column h
   auto out_row = [&](int h) -> int64_t {
@@ -1085,7 +1086,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a,
   const int slot = MULTI ? (b * num_kv_heads + g) * a.col_groups + cg : b * num_kv_heads + g;
   if constexpr (BF16)
     mfma_blocks<D, G, NW, APPEND, KV8, MULTI>(a, sm, b, qrow, g, L, nblk, blk_lo, blk_hi, row0,
-                                              ncols);
+                                              ncols, rows);
   else
     valu_blocks<D, G, NW, APPEND>(a, sm, b, qrow, g, L, nblk, blk_lo, blk_hi);
   float* o_lds = reinterpret_cast<float*>(sm.k);  // [wave][G][D]
@@ -1319,7 +1320,7 @@ void decode_kernel(const DecodeParams a) {
     if (part > 0 && part >= nparts) continue;
     const int qrow = MULTI ? b * a.rows + cg * a.rows_per_group : b;
     decode_item<D, G, BF16, NW, APPEND, KV8, MULTI>(a, sm, b, qrow, g, part, L, nblk, pb, nparts,
-                                                    cg);
+                                                    cg, a.rows);
     __syncthreads();  // LDS is reused by the next item
   }
 }

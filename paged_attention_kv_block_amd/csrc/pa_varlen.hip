@@ -44,10 +44,18 @@ template <int D, int G>
 union VarlenSmem {
   PrefillSmem<D, G> pf;
   DecodeSmem<D, G, true, kVarlenWaves, false> dc;
+  DecodeSmem<D, 16, true, kVarlenWaves, false> mc;
 };
 
+// A chunk this short runs on the multi-row decode path: 16 / G rows per
+// item, at most kShortGroups items per (sequence, KV head).
+constexpr int kShortGroups = 4;
+inline int varlen_rows_per_group(int G) { return 16 / G; }
+
 // plan entries: (1 << 31) | (tile << 16) | b for a prefill query tile,
-// (part << 16) | b for a decode partition
+// (part << 16) | b for a decode partition (part < 2^14), and
+// (1 << 30) | (cg << 16) | b for column group cg of a short chunk (one pass
+// over the sequence's blocks, no split-K)
 template <int D, int G>
 __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void varlen_kernel(const DecodeParams a, const int* __restrict__ qsl) {
@@ -69,6 +77,15 @@ void varlen_kernel(const DecodeParams a, const int* __restrict__ qsl) {
   int L = a.seq_lens[b];
   L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
   const int nblk = (L + 15) >> 4;
+  if (e & (1 << 30)) {  // column group of a short chunk
+    const int cg = x & 0x3FFF;
+    const int rows = qsl[b + 1] - qsl[b];
+    if (cg * a.rows_per_group >= rows) return;
+    decode_item<D, 16, true, kVarlenWaves, false, false, true>(
+        a, sm.mc, b, qsl[b] + cg * a.rows_per_group, g, 0, L, nblk, nblk > 0 ? nblk : 1, 1, cg,
+        rows);
+    return;
+  }
   const int pb = a.part_blocks > 0 ? a.part_blocks : (nblk > 0 ? nblk : 1);
   const int nparts = (nblk + pb - 1) / pb;
   if (x > 0 && x >= nparts) return;
@@ -111,9 +128,10 @@ extern "C" int pa_varlen_plan(const int32_t* query_start_loc, const int32_t* seq
   if (B > 0 && query_start_loc[0] != 0)
     return fail(PA_EINVAL, "pa_varlen_plan: query_start_loc[0] = %d", query_start_loc[0]);
   const int64_t P = parts_for(max_seq_len, partition_size);
-  if (P > 32767) return fail(PA_ENOTSUP, "pa_varlen_plan: too many partitions");
+  if (P > 16383) return fail(PA_ENOTSUP, "pa_varlen_plan: too many partitions");
   const int TQ = kPrefillRows / G;  // query tokens per prefill tile
-  // (work, b, x) of every item; work orders them
+  const int RPG = varlen_rows_per_group(G);
+  // (work, b, x) of every item; work orders them; x carries the multi-row flag
   struct Item { int64_t work; int32_t b, x; };
   std::vector<Item> pre, dec;
   for (int32_t b = 0; b < B; ++b) {
@@ -129,6 +147,11 @@ extern "C" int pa_varlen_plan(const int32_t* query_start_loc, const int32_t* seq
       const int32_t ptok = P > 1 ? partition_size : L;
       const int32_t np = (L + ptok - 1) / ptok;
       for (int32_t p = 0; p < np; ++p) dec.push_back({std::min(ptok, L - p * ptok), b, p});
+    } else if (Cb > 1 && (Cb + RPG - 1) / RPG <= kShortGroups) {
+      // a short chunk (e.g. the tokens of a speculative step): column groups
+      // of RPG rows on the decode path, each one pass over the L tokens
+      for (int32_t cg = 0; cg < int32_t((Cb + RPG - 1) / RPG); ++cg)
+        dec.push_back({L, b, (1 << 14) | cg});
     } else if (Cb > 1) {
       const int64_t tiles = (Cb + TQ - 1) / TQ;
       if (tiles > 32767) return fail(PA_ENOTSUP, "pa_varlen_plan: chunk of %lld rows", (long long)Cb);
@@ -166,7 +189,7 @@ extern "C" int pa_varlen_plan(const int32_t* query_start_loc, const int32_t* seq
   if (n > 0 && !plan) return fail(PA_EINVAL, "pa_varlen_plan: NULL plan");
   size_t i = 0;
   for (const Item& it : pre) plan[i++] = int32_t(0x80000000u | uint32_t(it.x << 16) | uint32_t(it.b));
-  for (const Item& it : dec) plan[i++] = (it.x << 16) | it.b;
+  for (const Item& it : dec) plan[i++] = int32_t((uint32_t(it.x) << 16) | uint32_t(it.b));
   return PA_OK;
 }
 
@@ -211,7 +234,7 @@ extern "C" int pa_attention_varlen(void* out, float* lse_out, const void* query,
   if (max_blocks_per_seq > (1 << 28))
     return fail(PA_ENOTSUP, "%s: max_blocks_per_seq %d too large", fn, max_blocks_per_seq);
   const int64_t P = parts_for(max_seq_len, partition_size);
-  if (P > 32767) return fail(PA_EINVAL, "%s: too many partitions (%lld)", fn, (long long)P);
+  if (P > 16383) return fail(PA_EINVAL, "%s: too many partitions (%lld)", fn, (long long)P);
   const int64_t items = int64_t(plan_entries) * num_kv_heads;
   if (items > 0x7FFFFFFF) return fail(PA_ENOTSUP, "%s: too many work items", fn);
   const size_t need =
@@ -242,6 +265,8 @@ extern "C" int pa_attention_varlen(void* out, float* lse_out, const void* query,
   a.part_blocks = P > 1 ? partition_size / kBlockSize : 0;
   a.max_parts = int(P);
   a.num_items = int(items);
+  a.group = G;                                  // short chunks' column groups
+  a.rows_per_group = varlen_rows_per_group(G);
   if (P > 1) {
     const WsLayout w = ws_layout(B, num_q_heads, num_kv_heads, head_size, P);
     uint8_t* base = static_cast<uint8_t*>(workspace);

@@ -224,7 +224,8 @@ def custom(name: str = "custom", *, kind: str = "decode", dtype: str = "bf16",
 
 def mixed_step(num_prefill: int = 16, prefill_context: int = 2560, chunk: int = 256,
                num_decode: int = 240, num_q_heads: int = 32, num_kv_heads: int = 8,
-               head_size: int = 128, seed: int = 11, index: int = 105) -> Draw:
+               head_size: int = 128, seed: int = 11, index: int = 105,
+               decode_rows: int = 1) -> Draw:
     """One flattened step of continuous batching, Llama-3-8B-shaped heads:
     `num_prefill` sequences each run a `chunk`-token causal prefill chunk
     after `prefill_context` cached tokens (the chunked-prefill workload's
@@ -232,12 +233,14 @@ def mixed_step(num_prefill: int = 16, prefill_context: int = 2560, chunk: int = 
     shared prefix), followed by `num_decode` sequences with one query row
     each, lengths log-normal (median 1024, sigma 1.0) clipped to [64, 8192]
     like the Llama-3-8B-shaped decode batch.  Packed query rows: the chunks
-    in sequence order, then the decode rows."""
+    in sequence order, then the decode rows.  decode_rows > 1 gives each
+    decode sequence that many rows (its last tokens, as a speculative step
+    checks them); the lengths stay the same draws."""
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
     x = rng.lognormal(mean=math.log(1024.0), sigma=1.0, size=num_decode)
     dec = np.clip(np.rint(x), 64, 8192).astype(np.int32)
     seq_lens = [prefill_context + chunk] * num_prefill + [int(v) for v in dec]
-    chunks = [chunk] * num_prefill + [1] * num_decode
+    chunks = [chunk] * num_prefill + [int(decode_rows)] * num_decode
     return custom("mixed-step", kind="prefill", seq_lens=seq_lens, chunk_lens=chunks,
                   num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_size=head_size,
                   seed=seed, index=index)

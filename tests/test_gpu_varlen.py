@@ -61,6 +61,13 @@ CASES = [
                                 num_kv_heads=1, head_size=64)),
     ("g4-d64-chunks-only", dict(seq_lens=(33, 64, 17), chunk_lens=(2, 64, 17), num_q_heads=16,
                                 num_kv_heads=4, head_size=64)),
+    # short chunks (speculative steps) on the multi-row decode items, beside
+    # decode rows and a tiled chunk: 1 to 4 column groups, L == C, L < 16
+    ("g8-d128-short-chunks", dict(seq_lens=(300, 45, 17, 1000, 64, 3, 520, 2),
+                                  chunk_lens=(4, 1, 2, 8, 40, 3, 1, 2), num_q_heads=16,
+                                  num_kv_heads=2, head_size=128)),
+    ("g2-d64-short-chunks", dict(seq_lens=(200, 31, 90, 700), chunk_lens=(20, 31, 1, 9),
+                                 num_q_heads=4, num_kv_heads=2, head_size=64)),
 ]
 
 
@@ -152,6 +159,18 @@ def test_every_row_written_and_repeatable():
     o2, l2 = g.varlen(32, workspace=ws)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1, l2)
+
+
+def test_mixed_step_with_speculative_rows_sampled():
+    """The mixed step with 4 rows per decode sequence (a speculative step):
+    the short chunks run as multi-row decode items in the same launch."""
+    d = inputs.mixed_step(decode_rows=4)
+    L = d.seq_lens
+    seqs = sorted({0, 15, 16 + int(np.argmax(L[16:])), 16 + int(np.argmin(L[16:])), 100})
+    from tests.gpu_setup import GpuSide
+    g = GpuSide(d, fill=False)
+    g.fill(seqs)
+    check_varlen(d, 512, seqs=seqs, g=g)
 
 
 def test_mixed_step_sampled():

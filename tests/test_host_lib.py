@@ -341,9 +341,12 @@ def test_decode_plan_lists_nonempty_partitions_longest_first():
 
 def _varlen_items(qsl, sl, msl, G, P):
     """Expected (kind, b, x, work) of a flattened batch, written out from the
-    plan's definition: chunks of C_b >= 2 rows in tiles of 128 / G rows, one
-    decode item per non-empty partition of a sequence with one row."""
+    plan's definition: one decode item per non-empty partition of a sequence
+    with one row; a chunk of C_b >= 2 rows that fits 4 groups of 16 / G rows
+    gives one multi-row decode item per group (x = 2^14 + group, work = the
+    sequence's tokens); longer chunks go in tiles of 128 / G rows."""
     TQ = 128 // G
+    RPG = 16 // G
     parts = 1 if P == 0 or msl <= P else -(-msl // P)
     pre, dec = [], []
     for b in range(len(sl)):
@@ -352,6 +355,9 @@ def _varlen_items(qsl, sl, msl, G, P):
             ptok = P if parts > 1 else L
             for p in range(-(-L // ptok)):
                 dec.append((b, p, min(ptok, L - p * ptok)))
+        elif C > 1 and -(-C // RPG) <= 4:
+            for cg in range(-(-C // RPG)):
+                dec.append((b, (1 << 14) + cg, L))
         elif C > 1:
             for t in range(-(-C // TQ)):
                 rows = min(TQ, C - t * TQ)
@@ -360,8 +366,8 @@ def _varlen_items(qsl, sl, msl, G, P):
 
 
 def test_varlen_plan_orders_tiles_then_decode_items():
-    qsl = np.array([0, 1, 40, 40, 41, 341, 342], np.int32)   # C = 1, 39, 0, 1, 300, 1
-    sl = np.array([700, 39, 5, 1, 900, 1300], np.int32)
+    qsl = np.array([0, 1, 40, 40, 41, 341, 342, 345, 352], np.int32)  # C = 1, 39, 0, 1, 300, 1, 3, 7
+    sl = np.array([700, 39, 5, 1, 900, 1300, 64, 500], np.int32)
     for G, P in [(4, 0), (8, 512), (1, 256), (2, 0)]:
         plan, npre = ops.varlen_plan(qsl, sl, 1300, 8 * G, 8, P)
         pre, dec = _varlen_items(qsl, sl, 1300, G, P)
