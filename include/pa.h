@@ -428,16 +428,21 @@ int pa_prefill_chunk(void* out, float* lse_out, const void* query,
  * function" and "LLM Engine & Engine Core": continuous batching over a
  * batch flattened into one sequence).  Sequences with C_b = 1 query row
  * become decode items (split into partitions of partition_size tokens
- * when that is non-zero and max_seq_len needs more than one), sequences
- * with C_b >= 2 rows become query tiles of 128 / G rows, C_b = 0 nothing.
- * Entries are (1 << 31) | (tile << 16) | b for a query tile and
- * (partition << 16) | b for a decode item.
+ * when that is non-zero and max_seq_len needs more than one); a short
+ * chunk, C_b >= 2 rows that fit 4 groups of 16 / G rows (e.g. the tokens a
+ * speculative step checks), becomes one multi-row decode item per group,
+ * each a single pass over the sequence's tokens (pa_decode_multi's tile);
+ * longer chunks become query tiles of 128 / G rows; C_b = 0 nothing.
+ * Entries are (1 << 31) | (tile << 16) | b for a query tile,
+ * (partition << 16) | b for a decode item (partition < 2^14) and
+ * (1 << 30) | (group << 16) | b for a short chunk's group.
  *   query_start_loc [B+1] int32, host, [0] = 0, non-decreasing
  *   seq_lens        [B] int32, host, C_b <= seq_lens[b] <= max_seq_len
  *   plan            [capacity] int32, host (nullable when capacity is 0)
  *   num_entries, num_prefill_entries  receive the entry counts (also when
  *                   capacity is too small: then PA_EINVAL)
- * G = num_q_heads / num_kv_heads in {1, 2, 4, 8}; B <= 65535. */
+ * G = num_q_heads / num_kv_heads in {1, 2, 4, 8}; B <= 65535; at most 16383
+ * partitions. */
 int pa_varlen_plan(const int32_t* query_start_loc, const int32_t* seq_lens,
                    int32_t B, int32_t max_seq_len, int32_t num_q_heads,
                    int32_t num_kv_heads, int32_t partition_size, int32_t* plan,
@@ -450,7 +455,8 @@ int pa_varlen_plan(const int32_t* query_start_loc, const int32_t* seq_lens,
  * causally to tokens 0..position through the block table; keys/values
  * already written); a sequence with one row gets exactly pa_decode's
  * result for it.  Chunks run on the prefill path (matrix-core tiles),
- * single rows on the decode path (optionally split-K), in one grid.
+ * single rows on the decode path (optionally split-K), short chunks on the
+ * decode path's multi-row tiles, in one grid.
  *   out, query      [total_query_tokens][H_q][D] bf16, device
  *   lse_out         [total_query_tokens][H_q] fp32, device, nullable
  *   query_start_loc [B+1] int32, device: the same values the plan was
