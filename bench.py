@@ -578,6 +578,36 @@ def bench_mixed(a, dev):
     return 0
 
 
+def cpu_baseline_spec(d, min_seconds: float):
+    """The fp64 oracle on this host over a bounded sample of a speculative
+    step: sequences spread over the batch in turn, each one's C rows as the
+    chunked-prefill definition gives them (its cache filled beforehand),
+    until min_seconds; returns (seconds, algorithmic bytes, sequences)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from tests.oracle_setup import OracleSide
+
+    wl = d.wl
+    B = wl.num_seqs
+    sample = sorted(set(int(x) for x in np.linspace(0, B - 1, min(B, 8))))
+    side = OracleSide(d, seqs=sample)
+    qsl = side.query_start_loc()
+    q = d.query()
+    chunks = wl.chunk_lens()
+    done, nbytes, t0 = 0, 0, time.perf_counter()
+    with threadpool_limits(1):
+        while True:
+            b = sample[done % len(sample)]
+            oracle.prefill_chunk(q, qsl, side.pool, side.block_tables, d.seq_lens, wl.scale,
+                                 seqs=[b])
+            nbytes += varlen_bytes(wl, [int(d.seq_lens[b])], [int(chunks[b])])
+            done += 1
+            if time.perf_counter() - t0 >= min_seconds:
+                break
+    return time.perf_counter() - t0, nbytes, done
+
+
 def bench_spec(a, dev):
     """A speculative-decoding verification step: every sequence of a decode
     batch checks C = --spec-rows tokens at once (C - 1 draft tokens and the
@@ -725,6 +755,16 @@ def bench_spec(a, dev):
             "avg_launch_us": round(multi_us, 3),
         },
     }
+    if not a.no_cpu_baseline:
+        dt, cbytes, nseq = cpu_baseline_spec(d, a.cpu_seconds)
+        res["cpu_baseline"] = {
+            "value": round(cbytes / dt / 1e9, 6),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"{nseq} sequences of the step in turn (up to 8 spread over the batch, "
+                      f"their {C} rows each), fp64 numpy, BLAS 1 thread; {dt:.1f} s",
+        }
     print(json.dumps(res), flush=True)
     return 0
 

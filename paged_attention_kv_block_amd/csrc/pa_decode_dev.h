@@ -563,9 +563,15 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
-// Non-temporal loads of one block's K and V operands (the cache is streamed
-// once per call).
-template <int D, bool KV8 = false>
+// Loads of one block's K and V operands: non-temporal when the cache is
+// streamed once per call (NT); ordinary loads when other workgroups on the
+// same XCD read the same blocks at about the same time (the column groups
+// of a multi-row item), so the lines stay in that XCD's L2 for them.
+template <class T>
+__device__ __forceinline__ T kv_load(const T* p, bool nt) {
+  return nt ? __builtin_nontemporal_load(p) : *p;
+}
+template <int D, bool KV8 = false, bool NT = true>
 __device__ __forceinline__ MfmaBlock<D, KV8> load_mfma_block(const uint8_t* __restrict__ cache,
                                                              int phys, int64_t block_bytes, int g,
                                                              int num_kv_heads, int64_t tile_bytes,
@@ -577,18 +583,18 @@ __device__ __forceinline__ MfmaBlock<D, KV8> load_mfma_block(const uint8_t* __re
   MfmaBlock<D, KV8> r;
   const u32x4* kt = reinterpret_cast<const u32x4*>(kbase);
 #pragma unroll
-  for (int j = 0; j < M::KLD; ++j) r.k[j] = __builtin_nontemporal_load(kt + j * kWave + lane);
+  for (int j = 0; j < M::KLD; ++j) r.k[j] = kv_load(kt + j * kWave + lane, NT);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint8_t* vp = vbase + (4 * grp + i) * M::RB + n * (M::VWD * 4);
     if constexpr (M::VWD == 1) {
-      r.v[i][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vp));
+      r.v[i][0] = kv_load(reinterpret_cast<const uint32_t*>(vp), NT);
     } else if constexpr (M::VWD == 2) {
-      const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vp));
+      const u32x2 x = kv_load(reinterpret_cast<const u32x2*>(vp), NT);
       r.v[i][0] = x.x;
       r.v[i][1] = x.y;
     } else {
-      const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp));
+      const u32x4 x = kv_load(reinterpret_cast<const u32x4*>(vp), NT);
       r.v[i][0] = x.x;
       r.v[i][1] = x.y;
       r.v[i][2] = x.z;
@@ -795,7 +801,9 @@ __device__ __forceinline__ void mfma_block(MfmaBlock<D, KV8>& cur, int valid,
 // MULTI: column n is query row qrow + n / a.group, head g * a.group + n %
 // a.group, for n < ncols; that row sits at position L - rows + row_in_seq
 // (rows: the sequence's query rows) and sees the tokens up to it.
-template <int D, int G, int NW, bool APPEND, bool KV8 = false, bool MULTI = false>
+// SHARED: ordinary (L2-allocating) loads, see load_mfma_block.
+template <int D, int G, int NW, bool APPEND, bool KV8 = false, bool MULTI = false,
+          bool SHARED = false>
 __device__ __forceinline__ void mfma_blocks(const DecodeParams& a,
                                             DecodeSmem<D, G, true, NW, KV8>& sm, int b, int qrow,
                                             int g, int L, int nblk, int blk_lo, int blk_hi,
@@ -863,7 +871,7 @@ __device__ __forceinline__ void mfma_blocks(const DecodeParams& a,
     MfmaBlock<D, KV8> buf[PD];
 #pragma unroll
     for (int s = 0; s < PD; ++s)
-      buf[s] = load_mfma_block<D, KV8>(cache, __builtin_amdgcn_readlane(ids_cur, s), block_bytes,
+      buf[s] = load_mfma_block<D, KV8, !SHARED>(cache, __builtin_amdgcn_readlane(ids_cur, s), block_bytes,
                                        g, num_kv_heads, tile_bytes, lane);
     const int j_last = first + (nmine - 1) * NW;
     const int tail_valid = L - j_last * 16;
@@ -876,7 +884,7 @@ __device__ __forceinline__ void mfma_blocks(const DecodeParams& a,
         if (k0 + s < nfull)
           mfma_block<D, false, KV8, MULTI>(buf[s], 16, qb, st, kt_lds, scale_log2, lane,
                                            lim - 16 * (first + (k0 + s) * NW));
-        buf[s] = load_mfma_block<D, KV8>(cache, __builtin_amdgcn_readlane(ids_next, s),
+        buf[s] = load_mfma_block<D, KV8, !SHARED>(cache, __builtin_amdgcn_readlane(ids_next, s),
                                          block_bytes, g, num_kv_heads, tile_bytes, lane);
       }
       ids_next = ids_after;
@@ -1054,7 +1062,8 @@ __device__ __forceinline__ void valu_blocks(const DecodeParams& a, DecodeSmem<D,
 // MULTI (bf16 only): the item's columns are (query row, head) pairs of
 // column group cg of the sequence's `rows` query rows (see DecodeParams);
 // qrow is the group's first query row.
-template <int D, int G, bool BF16, int NW, bool APPEND, bool KV8 = false, bool MULTI = false>
+template <int D, int G, bool BF16, int NW, bool APPEND, bool KV8 = false, bool MULTI = false,
+          bool SHARED = false>
 __device__ __forceinline__ void decode_item(const DecodeParams& a,
                                             DecodeSmem<D, G, BF16, NW, KV8>& sm,
                                             int b, int qrow, int g, int part, int L, int nblk,
@@ -1085,8 +1094,8 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a,
   };
   const int slot = MULTI ? (b * num_kv_heads + g) * a.col_groups + cg : b * num_kv_heads + g;
   if constexpr (BF16)
-    mfma_blocks<D, G, NW, APPEND, KV8, MULTI>(a, sm, b, qrow, g, L, nblk, blk_lo, blk_hi, row0,
-                                              ncols, rows);
+    mfma_blocks<D, G, NW, APPEND, KV8, MULTI, SHARED>(a, sm, b, qrow, g, L, nblk, blk_lo, blk_hi,
+                                                      row0, ncols, rows);
   else
     valu_blocks<D, G, NW, APPEND>(a, sm, b, qrow, g, L, nblk, blk_lo, blk_hi);
   float* o_lds = reinterpret_cast<float*>(sm.k);  // [wave][G][D]
@@ -1286,7 +1295,8 @@ constexpr int decode_max_waves() { return NW == 8 ? 2 : 8; }
 // indices apart, inside runs of 8 * col_groups indices: the dispatcher deals
 // workgroups to the 8 XCDs in turn, so they run on one XCD at about the same
 // time and the later ones can read the blocks from that XCD's L2.
-template <int D, int G, bool BF16, int NW, bool APPEND, bool KV8 = false, bool MULTI = false>
+template <int D, int G, bool BF16, int NW, bool APPEND, bool KV8 = false, bool MULTI = false,
+          bool SHARED = false>
 __global__ __launch_bounds__(NW * kWave)
 __attribute__((amdgpu_waves_per_eu(decode_min_waves<D, G, BF16, NW>(), decode_max_waves<D, G, BF16, NW>())))
 void decode_kernel(const DecodeParams a) {
@@ -1319,8 +1329,8 @@ void decode_kernel(const DecodeParams a) {
     const int nparts = (nblk + pb - 1) / pb;
     if (part > 0 && part >= nparts) continue;
     const int qrow = MULTI ? b * a.rows + cg * a.rows_per_group : b;
-    decode_item<D, G, BF16, NW, APPEND, KV8, MULTI>(a, sm, b, qrow, g, part, L, nblk, pb, nparts,
-                                                    cg, a.rows);
+    decode_item<D, G, BF16, NW, APPEND, KV8, MULTI, SHARED>(a, sm, b, qrow, g, part, L, nblk, pb,
+                                                            nparts, cg, a.rows);
     __syncthreads();  // LDS is reused by the next item
   }
 }
