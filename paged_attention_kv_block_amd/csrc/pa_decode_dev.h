@@ -567,9 +567,14 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
 // streamed once per call (NT); ordinary loads when other workgroups on the
 // same XCD read the same blocks at about the same time (the column groups
 // of a multi-row item), so the lines stay in that XCD's L2 for them.
-template <class T>
-__device__ __forceinline__ T kv_load(const T* p, bool nt) {
-  return nt ? __builtin_nontemporal_load(p) : *p;
+// (A compile-time choice: a select between the two loads of one address
+// is folded into a single load without the non-temporal hint.)
+template <bool NT, class T>
+__device__ __forceinline__ T kv_load(const T* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
 }
 template <int D, bool KV8 = false, bool NT = true>
 __device__ __forceinline__ MfmaBlock<D, KV8> load_mfma_block(const uint8_t* __restrict__ cache,
@@ -583,18 +588,18 @@ __device__ __forceinline__ MfmaBlock<D, KV8> load_mfma_block(const uint8_t* __re
   MfmaBlock<D, KV8> r;
   const u32x4* kt = reinterpret_cast<const u32x4*>(kbase);
 #pragma unroll
-  for (int j = 0; j < M::KLD; ++j) r.k[j] = kv_load(kt + j * kWave + lane, NT);
+  for (int j = 0; j < M::KLD; ++j) r.k[j] = kv_load<NT>(kt + j * kWave + lane);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint8_t* vp = vbase + (4 * grp + i) * M::RB + n * (M::VWD * 4);
     if constexpr (M::VWD == 1) {
-      r.v[i][0] = kv_load(reinterpret_cast<const uint32_t*>(vp), NT);
+      r.v[i][0] = kv_load<NT>(reinterpret_cast<const uint32_t*>(vp));
     } else if constexpr (M::VWD == 2) {
-      const u32x2 x = kv_load(reinterpret_cast<const u32x2*>(vp), NT);
+      const u32x2 x = kv_load<NT>(reinterpret_cast<const u32x2*>(vp));
       r.v[i][0] = x.x;
       r.v[i][1] = x.y;
     } else {
-      const u32x4 x = kv_load(reinterpret_cast<const u32x4*>(vp), NT);
+      const u32x4 x = kv_load<NT>(reinterpret_cast<const u32x4*>(vp));
       r.v[i][0] = x.x;
       r.v[i][1] = x.y;
       r.v[i][2] = x.z;
