@@ -60,17 +60,23 @@ static void launch_decode_variant(const DecodeParams& a, hipStream_t s) {
   hipLaunchKernelGGL(k, dim3(grid), dim3(NW * kWave), 0, s, a);
 }
 
-// Multi-row launches with several column groups use ordinary loads: the
-// groups of one item run on one XCD together and share its L2 (long
-// context, 4 rows at G = 8: 1.77 -> 1.30 ms); with one group non-temporal
-// loads stay ~1-4 % faster.
-template <int D, int G, bool BF16, int NW, bool KV8, bool MULTI>
+// Multi-row launches with several column groups and many items (the
+// 2-wave regime, ALLOW_SHARED) use ordinary loads: the groups of one item
+// run on one XCD together, and with that many workgroups in flight
+// non-temporal lines leave the XCD's L2 before the sibling group reads
+// them (long context, 4 rows at G = 8: 1.77 -> 1.32 ms).  With fewer
+// items (TinyLlama-shaped, 4 rows: 24.3 against 26.3 us) or one group,
+// non-temporal loads are faster.
+template <int D, int G, bool BF16, int NW, bool KV8, bool MULTI, bool ALLOW_SHARED = false>
 static void launch_decode_nw(const DecodeParams& a, hipStream_t s) {
   if constexpr (MULTI) {
-    if (a.col_groups > 1)
-      launch_decode_variant<D, G, BF16, NW, false, KV8, true, true>(a, s);
-    else
-      launch_decode_variant<D, G, BF16, NW, false, KV8, true, false>(a, s);
+    if constexpr (ALLOW_SHARED) {
+      if (a.col_groups > 1) {
+        launch_decode_variant<D, G, BF16, NW, false, KV8, true, true>(a, s);
+        return;
+      }
+    }
+    launch_decode_variant<D, G, BF16, NW, false, KV8, true, false>(a, s);
   } else if (a.new_k) {
     launch_decode_variant<D, G, BF16, NW, true, KV8, false, false>(a, s);
   } else {
@@ -105,7 +111,7 @@ static void launch_decode(const DecodeParams& a, hipStream_t s) {
   else if (a.num_items < 8 * cus)
     launch_decode_nw<D, G, BF16, 4, KV8, MULTI>(a, s);
   else
-    launch_decode_nw<D, G, BF16, 2, KV8, MULTI>(a, s);
+    launch_decode_nw<D, G, BF16, 2, KV8, MULTI, true>(a, s);
 }
 
 // Rows of one multi-row work item: as many of the sequence's query rows as
