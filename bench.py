@@ -49,6 +49,10 @@ TRAFFIC_FILES = {False: os.path.join(ROOT, "profiles", "decode_append_traffic.js
                  True: os.path.join(ROOT, "profiles", "decode_traffic.json")}
 VARLEN_TRAFFIC = os.path.join(ROOT, "profiles", "varlen_traffic.json")
 MULTI_TRAFFIC = os.path.join(ROOT, "profiles", "decode_multi_traffic.json")
+PREFILL_TRAFFIC = os.path.join(ROOT, "profiles", "prefill_traffic.json")
+PREFILL_SOURCES = ["paged_attention_kv_block_amd/csrc/pa_prefill.hip",
+                   "paged_attention_kv_block_amd/csrc/pa_prefill_dev.h",
+                   "paged_attention_kv_block_amd/csrc/pa_common.h"]
 VARLEN_SOURCES = ["paged_attention_kv_block_amd/csrc/pa_varlen.hip",
                   "paged_attention_kv_block_amd/csrc/pa_decode_dev.h",
                   "paged_attention_kv_block_amd/csrc/pa_prefill_dev.h",
@@ -322,7 +326,7 @@ def bench_prefill(a, d, dev):
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": load_traffic(source_hash(PREFILL_SOURCES), False, PREFILL_TRAFFIC),
             "algorithmic_flops_per_launch": flops,
             "avg_launch_us": round(pf_us, 3),
         },
