@@ -187,3 +187,75 @@ def test_tinyllama_shape_sampled():
     g.fill(seqs)
     check(d, 4, 0, True, seqs=seqs, o=o, g=g)
     check(d, 4, 256, True, seqs=seqs, o=o, g=g)
+
+
+def _graph_replays_match(step, out):
+    """Captures step() in a HIP graph after an eager warm-up and replays it
+    four times with eager work between replays; each replay must equal the
+    eager result bit for bit."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(4):
+        out.zero_()
+        _ = (eager.float() * 2).sum()            # unrelated eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), rep
+    return eager
+
+
+@pytest.mark.parametrize("rows,P", [(2, 64), (4, 64), (4, 0)])
+def test_multi_rows_in_a_hip_graph(rows, P):
+    """pa_decode_multi (split-K counters and records, one or two column
+    groups) captured in a HIP graph: every replay equals the eager call,
+    which matches the oracle."""
+    from paged_attention_kv_block_amd import ops
+    from tests.gpu_setup import GpuSide, to_device
+    d = _draw((300, 45, 17, 1000, 64, 130), rows, 32, 4, 64, seed=31)
+    o, g = OracleSide(d), GpuSide(d)
+    q = to_device(d.query(), d.wl)
+    out = torch.empty_like(q)
+    ws = ops.decode_multi_workspace(6, rows, 32, 4, 64, 1000, P)
+    plan = torch.from_numpy(ops.decode_plan(d.seq_lens, 1000, P)).cuda()
+
+    def step():
+        ops.decode_multi(out, q, g.pool, g.bt_dev, g.seq_lens_dev, 1000, float(d.wl.scale), rows,
+                         P, ws, plan=plan)
+
+    eager = _graph_replays_match(step, out)
+    ref, _ = o.prefill()
+    assert float(np.max(np.abs(_f64(eager) - ref))) <= TOL
+
+
+def test_varlen_short_chunks_in_a_hip_graph():
+    """A flattened batch with decode rows, short chunks (multi-row items) and
+    a tiled chunk, split-K 64, captured in a HIP graph."""
+    from paged_attention_kv_block_amd import ops
+    from tests.gpu_setup import GpuSide, to_device
+    d = inputs.custom(kind="prefill", seq_lens=(300, 45, 17, 1000, 64, 3),
+                      chunk_lens=(4, 1, 2, 8, 40, 3), num_q_heads=16, num_kv_heads=2,
+                      head_size=128, seed=32)
+    o, g = OracleSide(d), GpuSide(d)
+    q = to_device(d.query(), d.wl)
+    out = torch.empty_like(q)
+    qsl = g.query_start_loc()
+    plan, _ = ops.varlen_plan(qsl, d.seq_lens, 1000, 16, 2, 64)
+    plan = torch.from_numpy(plan).cuda()
+    qsl_dev = torch.from_numpy(qsl).cuda()
+    ws = ops.decode_workspace(6, 16, 2, 128, 1000, 64)
+
+    def step():
+        ops.attention_varlen(out, q, qsl_dev, g.pool, g.bt_dev, g.seq_lens_dev, 1000,
+                             float(d.wl.scale), plan, 64, ws)
+
+    eager = _graph_replays_match(step, out)
+    ref, _ = o.prefill()
+    assert float(np.max(np.abs(_f64(eager) - ref))) <= TOL
