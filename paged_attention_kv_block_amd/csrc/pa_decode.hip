@@ -103,12 +103,20 @@ static int device_cus() {
 // waves each (a long item's blocks spread over more SIMD slots); many items
 // get small workgroups, so that several items share a compute unit and one
 // item's start and merge latency hides behind the others' loads.
+// With many items, long items (whole sequences, or partitions of >= 1024
+// tokens) still run best on 4-wave workgroups, which keep more of one
+// item's blocks in flight; short partitions on 2-wave ones (measured on the
+// Llama-3-shaped batch: one pass 248 us with 4 waves against 282 us with 2;
+// 512-token partitions 258 against 265 us; long context, 1024-token
+// partitions: 990 against 1011 us).  FP8 and multi-row launches keep 2
+// waves there (the multi-row column groups' shared loads need it).
 template <int D, int G, bool BF16, bool KV8, bool MULTI = false>
 static void launch_decode(const DecodeParams& a, hipStream_t s) {
   const int64_t cus = device_cus();
+  const bool long_items = !KV8 && !MULTI && (a.part_blocks == 0 || a.part_blocks >= 64);
   if (a.num_items < 2 * cus)
     launch_decode_nw<D, G, BF16, 8, KV8, MULTI>(a, s);
-  else if (a.num_items < 8 * cus)
+  else if (a.num_items < 8 * cus || long_items)
     launch_decode_nw<D, G, BF16, 4, KV8, MULTI>(a, s);
   else
     launch_decode_nw<D, G, BF16, 2, KV8, MULTI, true>(a, s);
