@@ -295,6 +295,62 @@ def test_decode_workspace_size():
     assert L.pa_decode_workspace_init(128, 256, None) == ops.PA_EINVAL   # misaligned
 
 
+def _multi_status(**kw):
+    args = dict(out=16, lse=None, q=16, cache=16, nb=4, bt=16, mbps=4, sl=16, B=1, msl=64,
+                rows=4, hq=8, hkv=2, d=128, bs=16, scale=0.1, P=0, ws=None, wsb=0,
+                dtype=ops.PA_BF16)
+    args.update(kw)
+    L = ops.lib()
+    st = L.pa_decode_multi(args["out"], args["lse"], args["q"], args["cache"], args["nb"],
+                           args["bt"], args["mbps"], args["sl"], args["B"], args["msl"],
+                           args["rows"], args["hq"], args["hkv"], args["d"], args["bs"],
+                           args["scale"], args["P"], args.get("plan"), args.get("plan_n", 0),
+                           args["ws"], args["wsb"], args["dtype"], None)
+    return st, L.pa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=0), ops.PA_EINVAL),
+    (dict(rows=65), ops.PA_EINVAL),
+    (dict(dtype=ops.PA_F32), ops.PA_ENOTSUP),           # several rows need bf16
+    (dict(dtype=ops.PA_FP8), ops.PA_ENOTSUP),
+    (dict(hq=34, hkv=1), ops.PA_ENOTSUP),               # group 34 > 16
+    (dict(P=16), ops.PA_EINVAL),                        # workspace missing
+    (dict(P=16, ws=256, wsb=1024), ops.PA_EINVAL),      # workspace too small
+    (dict(hq=7), ops.PA_EINVAL),                        # the decode checks apply too
+    (dict(d=96), ops.PA_ENOTSUP),
+    (dict(msl=65), ops.PA_EINVAL),
+])
+def test_decode_multi_validation(kw, status):
+    st, msg = _multi_status(**kw)
+    assert st == status, msg
+    assert "pa_decode_multi" in msg
+
+
+def test_decode_multi_empty_batch_is_a_no_op():
+    assert _multi_status(B=0)[0] == ops.PA_OK
+
+
+def test_decode_multi_workspace_size():
+    """Records of 16 columns (floor(16 / G) rows with their G heads) per
+    (sequence, KV head, column group, partition), after the counter region;
+    one row is pa_decode's workspace."""
+    for B, Hq, Hkv, D, msl, P in [(4, 8, 2, 128, 100, 32), (64, 32, 4, 64, 2048, 256)]:
+        assert (ops.decode_multi_workspace_bytes(B, 1, Hq, Hkv, D, msl, P) ==
+                ops.decode_workspace_bytes(B, Hq, Hkv, D, msl, P))
+        G = Hq // Hkv
+        rpg = 16 // G
+        parts = -(-msl // P)
+        base = ops.decode_multi_workspace_bytes(B, 2, Hq, Hkv, D, 64, 64)
+        assert base == 0                                  # one partition: no workspace
+        for rows in (2, 4, 7):
+            groups = -(-rows // rpg)
+            n = ops.decode_multi_workspace_bytes(B, rows, Hq, Hkv, D, msl, P)
+            assert n >= B * Hkv * groups * parts * (16 * D * 4 + 128)
+            assert n < B * Hkv * groups * parts * (16 * D * 4 + 128) + 65536 * 4 + 256
+    assert ops.decode_multi_workspace_bytes(4, 2, 34, 1, 128, 100, 32) == 0   # G > 16
+
+
 def test_reshape_validation():
     L = ops.lib()
     assert L.pa_reshape_and_cache(16, 16, 16, 4, 16, 4, 16, 2, 80, ops.PA_BF16, None) == ops.PA_ENOTSUP
