@@ -192,12 +192,11 @@ class Allocator:
     # prefix cache ---------------------------------------------------------
     def enable_prefix_cache(self, block_size: int) -> None:
         _check(lib().pa_prefix_cache_enable(self._h, int(block_size)))
-        self._cache_bs = int(block_size)
 
     def acquire_prefix(self, tokens) -> list:
         """Ids of the cached blocks of the longest cached prefix (referenced)."""
         t = np.ascontiguousarray(tokens, dtype=np.int32)
-        out = np.empty(max(t.size // max(getattr(self, "_cache_bs", 1), 1), 1), dtype=np.int32)
+        out = np.empty(max(t.size, 1), dtype=np.int32)   # >= full blocks for any block size
         hit = ctypes.c_int32()
         _check(lib().pa_prefix_cache_acquire(self._h, _np_ptr(t), t.size, _np_ptr(out),
                                              ctypes.byref(hit)))
