@@ -122,9 +122,14 @@ static void launch_decode(const DecodeParams& a, hipStream_t s) {
     launch_decode_nw<D, G, BF16, 2, KV8, MULTI, true>(a, s);
 }
 
-// Rows of one multi-row work item: as many of the sequence's query rows as
-// fit 16 matrix columns with their G heads each.
-inline int multi_rows_per_group(int G) { return G >= 16 ? 1 : 16 / G; }
+// Columns of one multi-row work item: 16 (one matrix tile), or 32 (two tiles
+// sharing each K and V operand) at head size 64 when the rows need more
+// than one tile; an item holds as many of the sequence's query rows as fit
+// those columns with their G heads each.
+inline int multi_columns(int rows, int G, int head_size) {
+  return head_size == 64 && G <= 16 && rows > 16 / G ? 32 : 16;
+}
+inline int multi_rows_per_group(int G, int cols = 16) { return G >= cols ? 1 : cols / G; }
 
 template <int D, bool BF16, bool KV8 = false>
 static bool dispatch_g(int G, const DecodeParams& a, hipStream_t s) {
@@ -164,9 +169,11 @@ extern "C" size_t pa_decode_multi_workspace_bytes(int32_t B, int32_t rows, int32
                                      partition_size);
   const int64_t P = parts_for(max_seq_len, partition_size);
   if (P <= 1) return 0;
-  const int rpg = multi_rows_per_group(num_q_heads / num_kv_heads);
+  const int G = num_q_heads / num_kv_heads;
+  const int cols = multi_columns(rows, G, head_size);
+  const int rpg = multi_rows_per_group(G, cols);
   const int64_t groups = (rows + rpg - 1) / rpg;
-  return size_t(ws_layout(int64_t(B) * groups, int64_t(16) * num_kv_heads, num_kv_heads,
+  return size_t(ws_layout(int64_t(B) * groups, int64_t(cols) * num_kv_heads, num_kv_heads,
                           head_size, P).total);
 }
 
@@ -273,7 +280,8 @@ static int decode_call(const char* fn, void* out, float* lse_out, const void* qu
   if (multi && dtype != PA_BF16)
     return fail(PA_ENOTSUP, "%s: several rows per sequence need a bf16 cache", fn);
   if (multi && G > 16) return fail(PA_ENOTSUP, "%s: group size %d > 16", fn, G);
-  const int rpg = multi ? multi_rows_per_group(G) : 1;
+  const int cols = multi ? multi_columns(rows, G, head_size) : G;
+  const int rpg = multi ? multi_rows_per_group(G, cols) : 1;
   const int groups = (rows + rpg - 1) / rpg;
   const int64_t P = parts_for(max_seq_len, partition_size);
   if (P > 65535) return fail(PA_EINVAL, "%s: too many partitions (%lld)", fn, (long long)P);
@@ -320,7 +328,7 @@ static int decode_call(const char* fn, void* out, float* lse_out, const void* qu
   a.col_groups = groups;
   a.items_per_group = int(per_group);
   if (P > 1) {
-    const WsLayout w = multi ? ws_layout(int64_t(B) * groups, int64_t(16) * num_kv_heads,
+    const WsLayout w = multi ? ws_layout(int64_t(B) * groups, int64_t(cols) * num_kv_heads,
                                          num_kv_heads, head_size, P)
                              : ws_layout(B, num_q_heads, num_kv_heads, head_size, P);
     uint8_t* base = static_cast<uint8_t*>(workspace);
@@ -329,7 +337,9 @@ static int decode_call(const char* fn, void* out, float* lse_out, const void* qu
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   bool ok;
-  if (multi)
+  if (multi && cols == 32)
+    ok = (launch_decode<64, 32, true, false, true>(a, st), true);
+  else if (multi)
     ok = head_size == 64 ? (launch_decode<64, 16, true, false, true>(a, st), true)
                          : (launch_decode<128, 16, true, false, true>(a, st), true);
   else if (dtype == PA_FP8)

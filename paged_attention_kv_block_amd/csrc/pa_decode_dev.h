@@ -696,13 +696,14 @@ __device__ __forceinline__ void append_new_token_fp8(MfmaBlock<D, true>& rg,
 // One block.  TAIL: only the first `valid` tokens (1 <= valid <= 16) are in
 // the sequence; the others get score -inf and their V rows are zeroed (they
 // may hold anything).
-// MULTI: lane column n sees the block's tokens below `lim` (its own causal
-// limit, relative to the block's first token; may be <= 0 or >= 16).
-template <int D, bool TAIL, bool KV8 = false, bool MULTI = false>
+// MULTI: lane column n of tile c sees the block's tokens below lim[c] (its
+// own causal limit, relative to the block's first token; may be <= 0 or
+// >= 16).  CT tiles of 16 columns share the K operand and the V operand.
+template <int D, bool TAIL, bool KV8 = false, bool MULTI = false, int CT = 1>
 __device__ __forceinline__ void mfma_block(MfmaBlock<D, KV8>& cur, int valid,
-                                           const u32x4 (&qb)[MfmaCfg<D>::KS], MfmaState<D>& st,
-                                           uint8_t* kt_lds, float scale_log2, int lane,
-                                           int lim = 16) {
+                                           const u32x4 (&qbt)[CT][MfmaCfg<D>::KS],
+                                           MfmaState<D> (&stt)[CT], uint8_t* kt_lds,
+                                           float scale_log2, int lane, const int (&lim)[CT]) {
   using M = MfmaCfg<D, KV8>;
   const int n = lane & 15, grp = lane >> 4;
   // K tile -> LDS -> operand layout
@@ -726,6 +727,11 @@ __device__ __forceinline__ void mfma_block(MfmaBlock<D, KV8>& cur, int valid,
       ka[s] = *reinterpret_cast<const u32x4*>(src);
     }
   }
+  u32x2 pat[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+  const u32x4 (&qb)[MfmaCfg<D>::KS] = qbt[c];
+  MfmaState<D>& st = stt[c];
   f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < M::KS; ++s) sc = mfma_k32(ka[s], qb[s], sc);
@@ -734,7 +740,7 @@ __device__ __forceinline__ void mfma_block(MfmaBlock<D, KV8>& cur, int valid,
   for (int i = 0; i < 4; ++i) {
     float v = sc[i] * scale_log2;
     if constexpr (TAIL) v = 4 * grp + i < valid ? v : -INFINITY;
-    if constexpr (MULTI) v = 4 * grp + i < lim ? v : -INFINITY;
+    if constexpr (MULTI) v = 4 * grp + i < lim[c] ? v : -INFINITY;
     x[i] = v;
   }
   const float t = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
@@ -762,6 +768,8 @@ __device__ __forceinline__ void mfma_block(MfmaBlock<D, KV8>& cur, int valid,
   pa.y = pack_bf16x2(__builtin_amdgcn_exp2f(x[2] - st.m_run), __builtin_amdgcn_exp2f(x[3] - st.m_run));
   st.l = dot2_bf16(pa.x, 0x3F803F80u, st.l);  // the rounded values that multiply V
   st.l = dot2_bf16(pa.y, 0x3F803F80u, st.l);
+  pat[c] = pa;
+  }  // column tiles
   if constexpr (TAIL) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -781,8 +789,11 @@ __device__ __forceinline__ void mfma_block(MfmaBlock<D, KV8>& cur, int valid,
         const int p = 4 * w + 2 * c2;
         const u32x2 vlo = {fp8x2_to_bf16x2<false>(t01), fp8x2_to_bf16x2<false>(t23)};
         const u32x2 vhi = {fp8x2_to_bf16x2<true>(t01), fp8x2_to_bf16x2<true>(t23)};
-        st.o[p] = mfma_k16(pa, vlo, st.o[p]);
-        st.o[p + 1] = mfma_k16(pa, vhi, st.o[p + 1]);
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+          stt[c].o[p] = mfma_k16(pat[c], vlo, stt[c].o[p]);
+          stt[c].o[p + 1] = mfma_k16(pat[c], vhi, stt[c].o[p + 1]);
+        }
       }
     }
   } else {
@@ -794,7 +805,9 @@ __device__ __forceinline__ void mfma_block(MfmaBlock<D, KV8>& cur, int valid,
         u32x2 vb;
         vb.x = __builtin_amdgcn_perm(cur.v[1][w], cur.v[0][w], sel);  // tokens 4 grp + 0, + 1
         vb.y = __builtin_amdgcn_perm(cur.v[3][w], cur.v[2][w], sel);  // tokens 4 grp + 2, + 3
-        st.o[2 * w + hb] = mfma_k16(pa, vb, st.o[2 * w + hb]);
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+          stt[c].o[2 * w + hb] = mfma_k16(pat[c], vb, stt[c].o[2 * w + hb]);
       }
     }
   }
@@ -814,7 +827,9 @@ __device__ __forceinline__ void mfma_blocks(const DecodeParams& a,
                                             int g, int L, int nblk, int blk_lo, int blk_hi,
                                             int row0 = 0, int ncols = G, int rows = 1) {
   using M = MfmaCfg<D, KV8>;
-  static_assert(G <= 16, "query heads per KV head");
+  // columns in tiles of 16: G = 32 (multi-row items at head size 64) uses two
+  constexpr int CT = G > 16 ? 2 : 1;
+  static_assert(G <= 16 * CT && CT <= 2, "query heads per KV head");
   const uint8_t* __restrict__ cache = a.cache;
   const int num_blocks = a.num_blocks, num_kv_heads = a.num_kv_heads;
   const float scale_log2 = a.scale_log2;
@@ -824,26 +839,29 @@ __device__ __forceinline__ void mfma_blocks(const DecodeParams& a,
   const int n = lane & 15, grp = lane >> 4;
 
   // Q^T operand: head n of this KV head (zero past G), d-chunks 4 s + grp
-  u32x4 qb[M::KS];
-  int lim = L;  // MULTI: this lane column's causal limit (exclusive)
-  {
+  u32x4 qb[CT][M::KS];
+  int lim[CT];  // MULTI: this lane column's causal limit (exclusive), per tile
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    const int nc = n + 16 * c;  // the column this lane follows in tile c
+    lim[c] = L;
     int64_t qoff;
     bool qvalid;
     if constexpr (MULTI) {
       const int gr = a.group;
-      const int nn = n < ncols ? n : 0;
+      const int nn = nc < ncols ? nc : 0;
       qoff = (int64_t(qrow + nn / gr) * (num_kv_heads * gr) + g * gr + nn % gr) * (D / 8);
-      qvalid = n < ncols;
-      if (qvalid) lim = L - rows + row0 + n / gr + 1;
+      qvalid = nc < ncols;
+      if (qvalid) lim[c] = L - rows + row0 + nc / gr + 1;
     } else {
-      qoff = (int64_t(qrow) * H_q + g * G + (n < G ? n : 0)) * (D / 8);
-      qvalid = n < G;
+      qoff = (int64_t(qrow) * H_q + g * G + (nc < G ? nc : 0)) * (D / 8);
+      qvalid = nc < G;
     }
     const u32x4* qp = reinterpret_cast<const u32x4*>(a.query) + qoff;
 #pragma unroll
     for (int s = 0; s < M::KS; ++s) {
       const u32x4 v = qp[4 * s + grp];
-      qb[s] = qvalid ? v : u32x4{0u, 0u, 0u, 0u};
+      qb[c][s] = qvalid ? v : u32x4{0u, 0u, 0u, 0u};
     }
   }
   const int64_t tile_bytes = int64_t(16) * M::RB;
@@ -851,18 +869,23 @@ __device__ __forceinline__ void mfma_blocks(const DecodeParams& a,
   const int* bt_row = a.block_tables + int64_t(b) * a.max_blocks_per_seq;
 
   uint8_t* kt_lds = sm.k + wave * M::TILE;
-  MfmaState<D> st;
-  st.m_run = MULTI ? -1e30f : -INFINITY;
-  st.m_thr = MULTI ? -1e30f : -INFINITY;
-  st.l = 0.f;
+  MfmaState<D> st[CT];
 #pragma unroll
-  for (int p = 0; p < M::NPV; ++p) st.o[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < CT; ++c) {
+    st[c].m_run = MULTI ? -1e30f : -INFINITY;
+    st[c].m_thr = MULTI ? -1e30f : -INFINITY;
+    st[c].l = 0.f;
+#pragma unroll
+    for (int p = 0; p < M::NPV; ++p) st[c].o[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // Register ring of PD blocks in flight, block ids one group ahead; the
   // same scheme as the fp32 loop (see there).
   constexpr int PD = M::PD;
 #pragma unroll
-  for (int s = 0; s < M::KS; ++s) asm volatile("" ::"v"(qb[s]));
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int s = 0; s < M::KS; ++s) asm volatile("" ::"v"(qb[c][s]));
   const int first = blk_lo + wave;
   const int nmine = blk_hi > first ? (blk_hi - first + NW - 1) / NW : 0;
   if (nmine > 0) {
@@ -887,8 +910,12 @@ __device__ __forceinline__ void mfma_blocks(const DecodeParams& a,
 #pragma unroll
       for (int s = 0; s < PD; ++s) {
         if (k0 + s < nfull)
-          mfma_block<D, false, KV8, MULTI>(buf[s], 16, qb, st, kt_lds, scale_log2, lane,
-                                           lim - 16 * (first + (k0 + s) * NW));
+        {
+          int lr[CT];
+#pragma unroll
+          for (int c = 0; c < CT; ++c) lr[c] = lim[c] - 16 * (first + (k0 + s) * NW);
+          mfma_block<D, false, KV8, MULTI, CT>(buf[s], 16, qb, st, kt_lds, scale_log2, lane, lr);
+        }
         buf[s] = load_mfma_block<D, KV8, !SHARED>(cache, __builtin_amdgcn_readlane(ids_next, s),
                                          block_bytes, g, num_kv_heads, tile_bytes, lane);
       }
@@ -905,31 +932,42 @@ __device__ __forceinline__ void mfma_blocks(const DecodeParams& a,
                                      block_bytes, tile_bytes, lane);
         }
       }
-      mfma_block<D, true, KV8, MULTI>(buf[0], min(tail_valid, 16), qb, st, kt_lds, scale_log2,
-                                      lane, lim - 16 * j_last);
+      int lr[CT];
+#pragma unroll
+      for (int c = 0; c < CT; ++c) lr[c] = lim[c] - 16 * j_last;
+      mfma_block<D, true, KV8, MULTI, CT>(buf[0], min(tail_valid, 16), qb, st, kt_lds,
+                                          scale_log2, lane, lr);
     }
   }
 
   if constexpr (KV8) {  // values are codes times v_scale
 #pragma unroll
-    for (int p = 0; p < M::NPV; ++p) st.o[p] *= a.v_scale;
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int p = 0; p < M::NPV; ++p) st[c].o[p] *= a.v_scale;
   }
-  const float lsum = allreduce_sum<4, 6>(st.l);  // over the head's four lanes
-  if (lane < G) {
-    sm.m[wave][lane] = st.m_run;
-    sm.l[wave][lane] = lsum;
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    const float lsum = allreduce_sum<4, 6>(st[c].l);  // over the head's four lanes
+    if (lane < 16 && lane + 16 * c < G) {
+      sm.m[wave][lane + 16 * c] = st[c].m_run;
+      sm.l[wave][lane + 16 * c] = lsum;
+    }
   }
   __syncthreads();  // every wave is done with its K tile: reuse the LDS for o
   float* o_lds = reinterpret_cast<float*>(sm.k);  // [wave][G][D]
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int head = 4 * grp + i;
-    if (head < G) {
-      float* dst = o_lds + (wave * G + head) * D + M::NPV * n;
+  for (int c = 0; c < CT; ++c) {
 #pragma unroll
-      for (int p = 0; p < M::NPV; p += 4)
-        *reinterpret_cast<f32x4*>(dst + p) =
-            f32x4{st.o[p][i], st.o[p + 1][i], st.o[p + 2][i], st.o[p + 3][i]};
+    for (int i = 0; i < 4; ++i) {
+      const int head = 4 * grp + i + 16 * c;
+      if (head < G) {
+        float* dst = o_lds + (wave * G + head) * D + M::NPV * n;
+#pragma unroll
+        for (int p = 0; p < M::NPV; p += 4)
+          *reinterpret_cast<f32x4*>(dst + p) =
+              f32x4{st[c].o[p][i], st[c].o[p + 1][i], st[c].o[p + 2][i], st[c].o[p + 3][i]};
+      }
     }
   }
   __syncthreads();
@@ -1287,11 +1325,13 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a,
 // items); head size 128 and fp32 need more registers than that.  An 8-wave
 // workgroup holds a compute unit alone at two or three waves per SIMD, so
 // its registers are left free for loads in flight.
-// The 16-column 2-wave variant of head size 128 (the multi-row kernel) is
-// held to two waves per SIMD, like the other 2-wave variants of that size.
+// 2-wave variants with 16 or more columns (the multi-row kernel) are held to
+// two waves per SIMD, like the other 2-wave variants; the 4-wave head-size-64
+// variants with up to 16 columns to three (the 32-column one needs more).
 template <int D, int G, bool BF16, int NW>
 constexpr int decode_min_waves() {
-  return NW == 4 && BF16 && D == 64 ? 3 : (NW == 2 && BF16 && D == 128 && G == 16 ? 2 : 1);
+  return NW == 4 && BF16 && D == 64 && G <= 16 ? 3
+                                               : (NW == 2 && BF16 && G >= 16 ? 2 : 1);
 }
 template <int D, int G, bool BF16, int NW>
 constexpr int decode_max_waves() { return NW == 8 ? 2 : 8; }

@@ -332,22 +332,26 @@ def test_decode_multi_empty_batch_is_a_no_op():
 
 
 def test_decode_multi_workspace_size():
-    """Records of 16 columns (floor(16 / G) rows with their G heads) per
+    """Records of 16 columns (floor(16 / G) rows with their G heads), or 32 at
+    head size 64 when the rows need more than one 16-column tile, per
     (sequence, KV head, column group, partition), after the counter region;
     one row is pa_decode's workspace."""
-    for B, Hq, Hkv, D, msl, P in [(4, 8, 2, 128, 100, 32), (64, 32, 4, 64, 2048, 256)]:
+    for B, Hq, Hkv, D, msl, P in [(4, 8, 2, 128, 100, 32), (64, 32, 4, 64, 2048, 256),
+                                  (3, 16, 1, 64, 300, 32)]:
         assert (ops.decode_multi_workspace_bytes(B, 1, Hq, Hkv, D, msl, P) ==
                 ops.decode_workspace_bytes(B, Hq, Hkv, D, msl, P))
         G = Hq // Hkv
-        rpg = 16 // G
         parts = -(-msl // P)
         base = ops.decode_multi_workspace_bytes(B, 2, Hq, Hkv, D, 64, 64)
         assert base == 0                                  # one partition: no workspace
-        for rows in (2, 4, 7):
+        for rows in (2, 3, 4, 7):
+            cols = 32 if D == 64 and rows > 16 // G else 16
+            rpg = max(1, cols // G)
             groups = -(-rows // rpg)
+            rec = cols * D * 4 + 128
             n = ops.decode_multi_workspace_bytes(B, rows, Hq, Hkv, D, msl, P)
-            assert n >= B * Hkv * groups * parts * (16 * D * 4 + 128)
-            assert n < B * Hkv * groups * parts * (16 * D * 4 + 128) + 65536 * 4 + 256
+            assert n >= B * Hkv * groups * parts * rec, (B, rows, n)
+            assert n < B * Hkv * groups * parts * rec + 65536 * 4 + 256
     assert ops.decode_multi_workspace_bytes(4, 2, 34, 1, 128, 100, 32) == 0   # G > 16
 
 
