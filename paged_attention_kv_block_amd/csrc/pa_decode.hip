@@ -108,12 +108,15 @@ static int device_cus() {
 // item's blocks in flight; short partitions on 2-wave ones (measured on the
 // Llama-3-shaped batch: one pass 248 us with 4 waves against 282 us with 2;
 // 512-token partitions 258 against 265 us; long context, 1024-token
-// partitions: 990 against 1011 us).  FP8 and multi-row launches keep 2
-// waves there (the multi-row column groups' shared loads need it).
+// partitions: 990 against 1011 us; the same with 2 query rows per
+// sequence: 1027 against 1050 us).  FP8 launches (551 against 546 us) and
+// multi-row launches with several column groups (whose shared loads need
+// the 2-wave regime) keep 2 waves there.
 template <int D, int G, bool BF16, bool KV8, bool MULTI = false>
 static void launch_decode(const DecodeParams& a, hipStream_t s) {
   const int64_t cus = device_cus();
-  const bool long_items = !KV8 && !MULTI && (a.part_blocks == 0 || a.part_blocks >= 64);
+  const bool long_items = !KV8 && (!MULTI || a.col_groups == 1) &&
+                          (a.part_blocks == 0 || a.part_blocks >= 64);
   if (a.num_items < 2 * cus)
     launch_decode_nw<D, G, BF16, 8, KV8, MULTI>(a, s);
   else if (a.num_items < 8 * cus || long_items)
