@@ -614,6 +614,179 @@ def cpu_baseline_spec(d, min_seconds: float):
     return time.perf_counter() - t0, nbytes, done
 
 
+def bench_prefix_cache(a, dev):
+    """Prefix caching on the shared-prefix workload: 16 requests, each a
+    2816-token prompt made of a common 2048-token prefix and 768 tokens of
+    its own (32/8 heads, D 128, bf16).  Host: libpa's allocator with its
+    prefix cache serves the requests in turn (lookup of all but the last
+    token, allocation of the rest, registration of the full blocks), timed
+    per request.  Device: the prefill of the 16 prompts without the cache
+    (every request computes all its 2816 tokens over its own blocks) against
+    the same with it (the first request computes everything, the others only
+    their 768 tokens over the cached prefix blocks), each as one
+    pa_prefill_chunk launch; the rows both compute must agree."""
+    import numpy as np
+    import torch
+    from paged_attention_kv_block_amd import host, inputs, ops
+
+    d = inputs.draw(3)
+    wl = d.wl
+    B, Hq, Hkv, D, bs = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_size, wl.block_size
+    L = int(d.seq_lens[0])
+    pre = wl.prefix_tokens
+    nblk = -(-L // bs)
+    rng = np.random.default_rng(3003)
+    shared = rng.integers(0, 32000, size=pre)
+    tokens = [np.concatenate([shared, rng.integers(0, 32000, size=L - pre)]).astype(np.int32)
+              for _ in range(B)]
+    q_all = inputs.round_to_bf16_bits(
+        rng.standard_normal(size=(B, L, Hq, D), dtype=np.float32))   # every prompt position
+
+    def dev_tensor(arr):
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    # host: the prefix cache serves the requests in turn
+    ops.lib()
+    alloc = ops.Allocator(d.num_blocks, d.pool_order)
+    alloc.enable_prefix_cache(bs)
+    bt_c = np.full((B, nblk), -1, dtype=np.int32)
+    starts = []
+    t0 = time.perf_counter()
+    for b in range(B):
+        hits = alloc.acquire_prefix(tokens[b][:-1])
+        row = hits + alloc.allocate(nblk - len(hits))
+        alloc.insert_prefix(tokens[b], row)
+        bt_c[b] = row
+        starts.append(len(hits) * bs)
+    host_us = (time.perf_counter() - t0) * 1e6 / B
+    _, (cached_blocks, hit_blocks, evictions) = alloc.export_prefix_cache()
+
+    # without the cache: every request has its own blocks for all its tokens
+    n_u = int(np.ceil(1.1 * B * nblk))
+    alloc_u = ops.Allocator(n_u, np.random.default_rng(3004).permutation(n_u).astype(np.int32))
+    bt_u = host.decode_block_tables(alloc_u, [L] * B, bs)
+
+    def fill(pool, bt, first):
+        for b in range(B):
+            k, v = d.kv(b)
+            sl = ops.slot_mapping(bt[b], first[b], L - first[b], bs)
+            ops.reshape_and_cache(dev_tensor(k[first[b]:]), dev_tensor(v[first[b]:]),
+                                  torch.from_numpy(sl).to(dev), pool)
+
+    pool_c = torch.zeros((d.num_blocks, 2, Hkv, bs, D), dtype=torch.bfloat16, device=dev)
+    pool_u = torch.zeros((n_u, 2, Hkv, bs, D), dtype=torch.bfloat16, device=dev)
+    fill(pool_c, bt_c, starts)          # each request writes the tokens it computes
+    fill(pool_u, bt_u, [0] * B)
+    rows_c = [L - s0 for s0 in starts]
+    q_c = dev_tensor(np.concatenate([q_all[b, starts[b]:] for b in range(B)]))
+    q_u = dev_tensor(q_all.reshape(B * L, Hq, D))
+    out_c, out_u = torch.empty_like(q_c), torch.empty_like(q_u)
+    qsl_c = torch.from_numpy(np.concatenate([[0], np.cumsum(rows_c)]).astype(np.int32)).to(dev)
+    qsl_u = torch.from_numpy(np.arange(0, B * L + 1, L, dtype=np.int32)).to(dev)
+    sl_dev = torch.full((B,), L, dtype=torch.int32, device=dev)
+    btc_dev, btu_dev = torch.from_numpy(bt_c).to(dev), torch.from_numpy(bt_u).to(dev)
+    scale = float(wl.scale)
+    torch.cuda.synchronize()
+
+    def cached():
+        ops.prefill_chunk(out_c, q_c, qsl_c, max(rows_c), pool_c, btc_dev, sl_dev, L, scale)
+
+    def uncached():
+        ops.prefill_chunk(out_u, q_u, qsl_u, L, pool_u, btu_dev, sl_dev, L, scale)
+
+    def timed(fn, n):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    n = max(5, a.steps // 10)
+    c_us = timed(cached, n)
+    u_us = timed(uncached, n)
+    # the rows both launches compute (positions >= the cached prefix) agree
+    diff, exact = 0.0, True
+    off = 0
+    for b in range(B):
+        oc = out_c[off:off + rows_c[b]].float()
+        ou = out_u[b * L + starts[b]:(b + 1) * L].float()
+        diff = max(diff, float((oc - ou).abs().max()))
+        exact = exact and torch.equal(out_c[off:off + rows_c[b]].view(torch.int16),
+                                      out_u[b * L + starts[b]:(b + 1) * L].view(torch.int16))
+        off += rows_c[b]
+    assert diff <= 2e-2, diff
+    f_c = prefill_flops([L] * B, rows_c, Hq, D)
+    f_u = prefill_flops([L] * B, [L] * B, Hq, D)
+    achieved = f_c / (c_us * 1e-6) / 1e12
+    res = {
+        "metric": "prefix-cache prefill: prompt tokens served per second, 16 requests sharing a "
+                  "2048-token prefix, 1 GPU",
+        "value": round(B * L / (c_us * 1e-6), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": n,
+        "warmup": 1,
+        "ms_per_step": round(c_us * 1e-3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) keys/values/queries, random token ids; no weights)",
+        "config": {
+            "workload": "prefix-cache-shared-prefix-b16", "requests": B, "prompt_tokens": L,
+            "shared_prefix_tokens": pre, "num_q_heads": Hq, "num_kv_heads": Hkv,
+            "head_size": D, "block_size": bs, "parallelism": "none (1 GPU)",
+        },
+        "host_us_per_request": round(host_us, 1),
+        "prefix_cache": {"hit_blocks": hit_blocks, "cached_blocks": cached_blocks,
+                         "evictions": evictions, "computed_tokens": int(sum(rows_c)),
+                         "computed_tokens_without_cache": B * L},
+        "prefill_us_with_cache": round(c_us, 2),
+        "prefill_us_without_cache": round(u_us, 2),
+        "speedup": round(u_us / c_us, 3),
+        "shared_rows_max_abs_diff": diff,
+        "shared_rows_bit_identical": bool(exact),
+        "roofline": {
+            "kernel": "pa_prefill_chunk (prefill_chunk_kernel), with the cache",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": f_c,
+            "algorithmic_flops_without_cache": f_u,
+            "avg_launch_us": round(c_us, 3),
+        },
+    }
+    if not a.no_cpu_baseline:
+        dt, cflops, nseq = cpu_baseline_prefill(d, a.cpu_seconds)
+        res["cpu_baseline"] = {
+            "value": round(cflops / dt / 1e12, 8),
+            "unit": "TFLOP/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"{nseq} sequences of the shared-prefix chunked-prefill step (the same "
+                      f"attention definition, 256-row chunks over the cached prefix), fp64 "
+                      f"numpy, BLAS 1 thread; {dt:.1f} s",
+        }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def bench_spec(a, dev):
     """A speculative-decoding verification step: every sequence of a decode
     batch checks C = --spec-rows tokens at once (C - 1 draft tokens and the
@@ -786,6 +959,10 @@ def main(argv=None):
     ap.add_argument("--mixed", action="store_true",
                     help="a flattened continuous-batching step: 16 prefill chunks and 240 "
                          "decode rows in one pa_attention_varlen launch")
+    ap.add_argument("--prefix-cache", action="store_true",
+                    help="16 requests sharing a 2048-token prefix through the allocator's "
+                         "prefix cache: host cost per request and the prefill launch with "
+                         "and without the cache")
     ap.add_argument("--spec-rows", type=int, default=0,
                     help="a speculative-decoding verification step: every sequence of decode "
                          "workload --workload checks this many query rows at once")
@@ -832,6 +1009,8 @@ def main(argv=None):
 
     if a.mixed:
         return bench_mixed(a, dev)
+    if a.prefix_cache:
+        return bench_prefix_cache(a, dev)
     if a.spec_rows > 0:
         return bench_spec(a, dev)
     wl = inputs.workload(a.workload)
