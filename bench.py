@@ -1153,6 +1153,15 @@ def main(argv=None):
     torch.cuda.synchronize()
     dec_us = d0.elapsed_time(d1) * 1e3 / a.steps
 
+    # the same steps launched eagerly from the host (argument checks, ctypes
+    # call and dispatch per step), for the launch overhead the graph removes
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    for i in range(a.steps):
+        step(pools[i % R])
+    torch.cuda.synchronize()
+    eager_us = (time.perf_counter() - h0) * 1e6 / a.steps
+
     ctx = int(seq_lens.sum())
     kvb = 1 if fp8 else None
     dbytes = decode_bytes(wl, seq_lens, kvb)
@@ -1187,6 +1196,7 @@ def main(argv=None):
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "context_tokens_per_s": round(ctx / (ms_step * 1e-3), 1),
         "host_metadata_us": round(host_us, 1),
+        "step_us_eager_launches": round(eager_us, 2),   # no graph: host launch per step
         "roofline": {
             "kernel": ("pa_decode_fp8 (decode_kernel, FP8 cache)" if fp8 and a.unfused else
                        "pa_decode_append_fp8 (decode_kernel, FP8 cache, quantised cache write "
