@@ -984,7 +984,7 @@ def main(argv=None):
     a = ap.parse_args(argv)
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only; multi-GPU sharding is not "
+        print("bench.py: the library runs on one GPU only; multi-GPU sharding is not "
               "implemented (--gpus must be 1)", file=sys.stderr)
         return 2
 
