@@ -1153,6 +1153,21 @@ def main(argv=None):
     torch.cuda.synchronize()
     dec_us = d0.elapsed_time(d1) * 1e3 / a.steps
 
+    # a plain device copy of 1 GiB for a measured bandwidth beside the
+    # nominal peak (read + write bytes per copy; pools already rotated out)
+    cbuf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(cbuf)
+    cdst.copy_(cbuf)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        cdst.copy_(cbuf)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del cbuf, cdst
+
     # the same steps launched eagerly from the host (argument checks, ctypes
     # call and dispatch per step), for the launch overhead the graph removes
     torch.cuda.synchronize()
@@ -1197,6 +1212,7 @@ def main(argv=None):
         "context_tokens_per_s": round(ctx / (ms_step * 1e-3), 1),
         "host_metadata_us": round(host_us, 1),
         "step_us_eager_launches": round(eager_us, 2),   # no graph: host launch per step
+        "measured_copy_gbs": round(copy_gbs, 1),          # 1 GiB device copy, read + write
         "roofline": {
             "kernel": ("pa_decode_fp8 (decode_kernel, FP8 cache)" if fp8 and a.unfused else
                        "pa_decode_append_fp8 (decode_kernel, FP8 cache, quantised cache write "
