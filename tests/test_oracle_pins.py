@@ -347,6 +347,30 @@ def test_prefill_chunk_of_one_equals_decode():
     np.testing.assert_array_equal(p_lse, d_lse)
 
 
+def test_chunk_rows_equal_decodes_of_truncated_sequences():
+    """Speculative verification reads the last C tokens as a causal chunk:
+    row i of a chunk of C rows over L tokens must equal a one-row decode of
+    the same sequence truncated to L - C + i + 1 tokens (same block table,
+    same pool).  Pins the per-row causal limit, including rows whose limit
+    falls inside an earlier block than the last."""
+    C = 5
+    d = inputs.custom(kind="prefill", seq_lens=(20, 37, 16), chunk_lens=(C, C, C),
+                      num_q_heads=8, num_kv_heads=2, head_size=64, dtype="f32", seed=9)
+    side = OracleSide(d)
+    p_out, p_lse = side.prefill()
+    q = d.query()
+    for b, L in enumerate(d.seq_lens):
+        L = int(L)
+        for i in range(C):
+            lens = np.zeros(len(d.seq_lens), dtype=np.int32)
+            lens[b] = L - C + i + 1
+            qd = np.zeros((len(d.seq_lens),) + q.shape[1:], dtype=q.dtype)
+            qd[b] = q[b * C + i]
+            o, l = oracle.decode(qd, side.pool, side.block_tables, lens, d.wl.scale, seqs=[b])
+            np.testing.assert_array_equal(p_out[b * C + i], o[b])
+            np.testing.assert_array_equal(p_lse[b * C + i], l[b])
+
+
 def test_mha_is_gqa_with_group_one():
     """H_q == H_kv: each query head reads its own KV head."""
     d = inputs.custom(kind="decode", seq_lens=(21,), num_q_heads=3, num_kv_heads=3, head_size=64)
