@@ -47,6 +47,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 METRIC = "paged-attn decode KV GB/s (% of HBM peak) + context-tokens/s, 1 GPU"
 TRAFFIC_FILES = {False: os.path.join(ROOT, "profiles", "decode_append_traffic.json"),
                  True: os.path.join(ROOT, "profiles", "decode_traffic.json")}
+# counters of the fused decode launch of the larger workloads, at their own
+# partition sizes
+WORKLOAD_TRAFFIC = {2: os.path.join(ROOT, "profiles", "decode_append_traffic_llama3-8b.json"),
+                    4: os.path.join(ROOT, "profiles", "decode_append_traffic_long-context.json")}
 VARLEN_TRAFFIC = os.path.join(ROOT, "profiles", "varlen_traffic.json")
 MULTI_TRAFFIC = os.path.join(ROOT, "profiles", "decode_multi_traffic.json")
 PREFILL_TRAFFIC = os.path.join(ROOT, "profiles", "prefill_traffic.json")
@@ -1185,7 +1189,12 @@ def main(argv=None):
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = kbytes / (dec_us * 1e-6) / 1e9
     khash = source_hash(DECODE_SOURCES)
-    traffic = load_traffic(khash, a.unfused) if a.workload == 1 and P == 0 and not fp8 else None
+    traffic = None
+    if not fp8 and a.workload == 1 and P == 0:
+        traffic = load_traffic(khash, a.unfused)
+    elif (not fp8 and not a.unfused and a.workload in WORKLOAD_TRAFFIC
+          and P == default_partition(wl)):
+        traffic = load_traffic(khash, False, WORKLOAD_TRAFFIC[a.workload])
 
     res = {
         "metric": METRIC,
