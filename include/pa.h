@@ -110,6 +110,18 @@ void pa_allocator_destroy(pa_allocator* a);
  * no state change.  n == 0 is a no-op; n < 0 is PA_EINVAL. */
 int pa_allocator_allocate(pa_allocator* a, int32_t n, int32_t* out_ids);
 
+/* Block tables of a batch in one call ("Inside vLLM", "LLM Engine
+ * constructor": the CPU side holds the block tables for KV-cache
+ * indexing): sequences 0..B-1 in order each take ceil(seq_lens[b] /
+ * block_size) blocks from the head of the queue, exactly as that many
+ * pa_allocator_allocate calls would, and row b of block_tables ([B][width]
+ * int32, host) receives their ids followed by -1 padding.  All-or-nothing:
+ * PA_ENOBLOCKS if the batch needs more blocks than are free, PA_EINVAL if
+ * a sequence needs more than width blocks; either leaves the allocator and
+ * the table untouched. */
+int pa_allocator_build_tables(pa_allocator* a, const int32_t* seq_lens, int32_t B,
+                              int32_t block_size, int32_t width, int32_t* block_tables);
+
 /* Adds one reference to each listed (allocated) block.  PA_EINVAL, with no
  * state change, if any id is out of range or free. */
 int pa_allocator_share(pa_allocator* a, const int32_t* ids, int32_t n);

@@ -250,6 +250,39 @@ extern "C" int pa_allocator_allocate(pa_allocator* a, int32_t n, int32_t* out_id
   return PA_OK;
 }
 
+extern "C" int pa_allocator_build_tables(pa_allocator* a, const int32_t* seq_lens, int32_t B,
+                                         int32_t block_size, int32_t width,
+                                         int32_t* block_tables) {
+  if (!a) return fail(PA_EINVAL, "pa_allocator_build_tables: NULL handle");
+  if (B < 0 || block_size <= 0 || width < 0 || (B > 0 && (!seq_lens || !block_tables)))
+    return fail(PA_EINVAL, "pa_allocator_build_tables: bad arguments");
+  int64_t total = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    if (seq_lens[b] < 0)
+      return fail(PA_EINVAL, "pa_allocator_build_tables: seq_lens[%d] = %d", b, seq_lens[b]);
+    const int64_t n = (int64_t(seq_lens[b]) + block_size - 1) / block_size;
+    if (n > width)
+      return fail(PA_EINVAL, "pa_allocator_build_tables: sequence %d needs %lld blocks, "
+                  "rows hold %d", b, (long long)n, width);
+    total += n;
+  }
+  if (total > a->count)
+    return fail(PA_ENOBLOCKS, "pa_allocator_build_tables: need %lld blocks, %d free",
+                (long long)total, a->count);
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t n = (seq_lens[b] + block_size - 1) / block_size;
+    int32_t* row = block_tables + int64_t(b) * width;
+    for (int32_t j = 0; j < n; ++j) {
+      const int32_t id = a->pop_head();
+      if (a->block_node[id] >= 0) a->evict(id);
+      a->refcount[id] = 1;
+      row[j] = id;
+    }
+    for (int32_t j = n; j < width; ++j) row[j] = -1;
+  }
+  return PA_OK;
+}
+
 extern "C" int pa_allocator_share(pa_allocator* a, const int32_t* ids, int32_t n) {
   if (!a) return fail(PA_EINVAL, "pa_allocator_share: NULL handle");
   if (n < 0 || (n > 0 && !ids)) return fail(PA_EINVAL, "pa_allocator_share: bad id list");

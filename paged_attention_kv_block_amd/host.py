@@ -19,13 +19,11 @@ def blocks_for(tokens: int, block_size: int) -> int:
 
 def decode_block_tables(alloc: "ops.Allocator", seq_lens, block_size: int,
                         max_blocks: int | None = None) -> np.ndarray:
-    """Sequences 0..B-1 in order each take the blocks their tokens need."""
+    """Sequences 0..B-1 in order each take the blocks their tokens need (one
+    native call, pa_allocator_build_tables)."""
     need = [blocks_for(L, block_size) for L in seq_lens]
     width = max(need + [1]) if max_blocks is None else int(max_blocks)
-    bt = np.full((len(need), width), -1, dtype=np.int32)
-    for b, n in enumerate(need):
-        bt[b, :n] = alloc.allocate(n)
-    return bt
+    return alloc.build_tables(seq_lens, block_size, width)
 
 
 def prefill_block_tables(alloc: "ops.Allocator", num_seqs: int, prefix_tokens: int,

@@ -33,6 +33,7 @@ SIGNATURES = {
     "pa_allocator_destroy": (None, [_vp]),
     "pa_allocator_allocate": (_c_int, [_vp, _c_i32, _vp]),
     "pa_allocator_share": (_c_int, [_vp, _vp, _c_i32]),
+    "pa_allocator_build_tables": (_c_int, [_vp, _vp, _c_i32, _c_i32, _c_i32, _vp]),
     "pa_allocator_free": (_c_int, [_vp, _vp, _c_i32]),
     "pa_allocator_num_free": (_c_i32, [_vp]),
     "pa_allocator_num_blocks": (_c_i32, [_vp]),
@@ -159,6 +160,20 @@ class Allocator:
             raise NoFreeBlocks(st, lib().pa_last_error().decode())
         _check(st)
         return out[:max(int(n), 0)].tolist()
+
+    def build_tables(self, seq_lens, block_size: int, width: Optional[int] = None) -> np.ndarray:
+        """int32 [B, width] block tables of a batch, allocated in one call
+        (sequence order, -1 padding; width defaults to the longest row)."""
+        sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        need = -(-sl.astype(np.int64) // int(block_size)) if sl.size else np.zeros(0, np.int64)
+        w = int(max(int(need.max()) if sl.size else 0, 1)) if width is None else int(width)
+        out = np.empty((sl.size, max(w, 1)), dtype=np.int32)
+        st = lib().pa_allocator_build_tables(self._h, _np_ptr(sl), sl.size, int(block_size), w,
+                                             _np_ptr(out))
+        if st == PA_ENOBLOCKS:
+            raise NoFreeBlocks(st, lib().pa_last_error().decode())
+        _check(st)
+        return out[:, :w]
 
     def share(self, ids) -> None:
         a = np.ascontiguousarray(ids, dtype=np.int32)

@@ -154,6 +154,53 @@ def test_allocator_stats_match_oracle():
     assert c.stats(d.seq_lens, 16) == o.stats(d.seq_lens, 16)
 
 
+def test_build_tables_equals_allocate_calls():
+    """pa_allocator_build_tables is the batch form of one allocate per
+    sequence: same ids, same queue and refcounts, -1 padding, and with the
+    prefix cache on, the same evictions of cached free blocks."""
+    rng = np.random.default_rng(8)
+    N = 300
+    order = rng.permutation(N)
+    for trial in range(20):
+        lens = rng.integers(0, 120, size=int(rng.integers(0, 12))).tolist()
+        c = ops.Allocator(N, order)
+        o = oracle.OracleAllocator(N, order)
+        if trial % 2:
+            c.enable_prefix_cache(16)
+            o.enable_prefix_cache(16)
+            toks = rng.integers(0, 4, size=160).tolist()
+            ids = c.allocate(10)
+            assert ids == o.allocate(10)
+            c.insert_prefix(toks, ids)
+            o.insert(toks, ids)
+            c.free(ids[::-1])
+            o.free(ids[::-1])
+        width = max([-(-L // 16) for L in lens] + [1]) + 2
+        bt = c.build_tables(lens, 16, width)
+        want = np.full((len(lens), width), -1, dtype=np.int32)
+        for b, L in enumerate(lens):
+            n = -(-L // 16)
+            want[b, :n] = o.allocate(n)
+        np.testing.assert_array_equal(bt, want)
+        assert c.export() == o.export()
+        if trial % 2:
+            assert c.export_prefix_cache() == o.export_prefix_cache()
+
+
+def test_build_tables_is_all_or_nothing():
+    a = ops.Allocator(10, list(range(10))[::-1])
+    before = a.export()
+    with pytest.raises(ops.NoFreeBlocks):
+        a.build_tables([64, 64, 48], 16)        # 11 blocks > 10 free
+    assert a.export() == before
+    with pytest.raises(ops.PAError):
+        a.build_tables([64, 17], 16, width=1)    # a row too narrow
+    assert a.export() == before
+    bt = a.build_tables([0, 17, 16], 16)
+    np.testing.assert_array_equal(bt, [[-1, -1], [9, 8], [7, -1]])
+    assert a.num_free == 7
+
+
 def test_large_pool_allocator():
     """A pool of the size the pages mention (hundreds of thousands of blocks)."""
     N = 400_000
