@@ -195,13 +195,15 @@ def decode(query: np.ndarray, pool: np.ndarray, block_tables: np.ndarray,
 
 
 def prefill_chunk(query: np.ndarray, query_start_loc, pool: np.ndarray,
-                  block_tables: np.ndarray, seq_lens, scale: float, seqs=None):
+                  block_tables: np.ndarray, seq_lens, scale: float, seqs=None,
+                  k_scale: float = 1.0, v_scale: float = 1.0):
     """A causal chunk per sequence: the C_b = qsl[b+1] - qsl[b] query tokens of
     sequence b are its last C_b tokens (their keys/values already written);
     query i sits at position seq_len[b] - C_b + i and sees tokens 0..position.
 
     query is packed [sum C_b, H_q, D].  Returns out [sum C_b, H_q, D] and
-    lse [sum C_b, H_q] in float64."""
+    lse [sum C_b, H_q] in float64.  An FP8 pool holds codes: keys and values
+    are their values times k_scale / v_scale, as in decode()."""
     T, Hq, D = query.shape
     Hkv = pool.shape[2]
     G = Hq // Hkv
@@ -213,6 +215,7 @@ def prefill_chunk(query: np.ndarray, query_start_loc, pool: np.ndarray,
         C, L = hi - lo, int(seq_lens[b])
         assert 0 <= C <= L
         K, V = gather_kv(pool, block_tables[b], L)
+        K, V = K * float(k_scale), V * float(v_scale)
         for i in range(C):
             pos = L - C + i
             qi = to_f64(query[lo + i])

@@ -137,3 +137,25 @@ def test_fp8_decode_equals_pool_of_dequantised_values():
     o64, l64 = oracle.decode(q, deq, bt, lens, 0.125)       # float64 pool of the values
     np.testing.assert_allclose(o8, o64, rtol=0, atol=1e-12)
     np.testing.assert_allclose(l8, l64, rtol=0, atol=1e-12)
+
+
+def test_fp8_chunk_equals_pool_of_dequantised_values():
+    """prefill_chunk over FP8 codes with cache scales equals the same chunk over
+    a float64 pool holding code value x scale (the reading used for the rows
+    a speculative step checks over an FP8 cache)."""
+    rng = np.random.default_rng(10)
+    N, Hkv, D, bs = 6, 2, 64, 16
+    codes = rng.integers(0, 256, size=(N, 2, Hkv, bs, D), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38              # no NaN codes
+    ks, vs = 0.029, 0.017
+    deq = oracle.e4m3_decode_array(codes)
+    deq[:, 0] *= ks
+    deq[:, 1] *= vs
+    lens, C = [40, 17, 16], 3
+    q = rng.normal(size=(3 * C, 8, D)).astype(np.float32)
+    qsl = np.arange(0, 3 * C + 1, C)
+    bt = np.array([[0, 1, 2], [3, 4, -1], [5, -1, -1]], dtype=np.int32)
+    o8, l8 = oracle.prefill_chunk(q, qsl, codes, bt, lens, 0.125, k_scale=ks, v_scale=vs)
+    o64, l64 = oracle.prefill_chunk(q, qsl, deq, bt, lens, 0.125)
+    np.testing.assert_allclose(o8, o64, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l8, l64, rtol=0, atol=1e-12)
