@@ -350,12 +350,13 @@ def bench_prefill(a, d, dev):
     return 0
 
 
-def varlen_bytes(wl, seq_lens, chunk_lens) -> int:
+def varlen_bytes(wl, seq_lens, chunk_lens, kv_bytes=None) -> int:
     """Algorithmic bytes of one pa_attention_varlen launch: every context
     token's K/V once, query rows in, output rows out, the used block-table
-    entries, seq_lens and query_start_loc."""
+    entries, seq_lens and query_start_loc.  kv_bytes as decode_bytes."""
     db = wl.dtype_bytes
-    kv = int(sum(int(L) for L in seq_lens)) * 2 * wl.num_kv_heads * wl.head_size * db
+    kb = db if kv_bytes is None else kv_bytes
+    kv = int(sum(int(L) for L in seq_lens)) * 2 * wl.num_kv_heads * wl.head_size * kb
     rows = int(sum(int(C) for C in chunk_lens))
     qo = 2 * rows * wl.num_q_heads * wl.head_size * db
     bt = sum((int(L) + wl.block_size - 1) // wl.block_size for L in seq_lens) * 4
@@ -588,11 +589,12 @@ def bench_mixed(a, dev):
     return 0
 
 
-def cpu_baseline_spec(d, min_seconds: float):
+def cpu_baseline_spec(d, min_seconds: float, fp8_scales=None):
     """The fp64 oracle on this host over a bounded sample of a speculative
     step: sequences spread over the batch in turn, each one's C rows as the
-    chunked-prefill definition gives them (its cache filled beforehand),
-    until min_seconds; returns (seconds, algorithmic bytes, sequences)."""
+    chunked-prefill definition gives them (its cache filled beforehand,
+    quantised to FP8 codes with fp8_scales = (k, v) when given), until
+    min_seconds; returns (seconds, algorithmic bytes, sequences)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     import oracle
@@ -602,6 +604,13 @@ def cpu_baseline_spec(d, min_seconds: float):
     B = wl.num_seqs
     sample = sorted(set(int(x) for x in np.linspace(0, B - 1, min(B, 8))))
     side = OracleSide(d, seqs=sample)
+    ks = vs = 1.0
+    kvb = None
+    if fp8_scales is not None:
+        ks, vs = fp8_scales
+        kvb = 1
+        side.pool = np.stack([oracle.quantize(side.pool[:, 0], ks),
+                              oracle.quantize(side.pool[:, 1], vs)], axis=1)
     qsl = side.query_start_loc()
     q = d.query()
     chunks = wl.chunk_lens()
@@ -610,8 +619,8 @@ def cpu_baseline_spec(d, min_seconds: float):
         while True:
             b = sample[done % len(sample)]
             oracle.prefill_chunk(q, qsl, side.pool, side.block_tables, d.seq_lens, wl.scale,
-                                 seqs=[b])
-            nbytes += varlen_bytes(wl, [int(d.seq_lens[b])], [int(chunks[b])])
+                                 seqs=[b], k_scale=ks, v_scale=vs)
+            nbytes += varlen_bytes(wl, [int(d.seq_lens[b])], [int(chunks[b])], kvb)
             done += 1
             if time.perf_counter() - t0 >= min_seconds:
                 break
@@ -800,7 +809,10 @@ def bench_spec(a, dev):
     pa_decode_multi (the decode kernel with (row, head) matrix columns,
     split-K as the workload's decode); beside it, on the same cache,
     pa_attention_varlen and pa_prefill_chunk (the same rows as 128-row
-    query tiles) and, for scale, pa_decode with one row per sequence."""
+    query tiles) and, for scale, pa_decode with one row per sequence.
+    With --kv-cache fp8 the cache holds E4M3 codes (per-tensor scales) and
+    the timed launch is pa_decode_multi_fp8, beside pa_decode_fp8 with one
+    row per sequence."""
     import numpy as np
     import torch
     from paged_attention_kv_block_amd import host, inputs, ops
@@ -810,6 +822,7 @@ def bench_spec(a, dev):
         print("bench.py: --spec-rows needs a bf16 decode workload (1, 2 or 4)", file=sys.stderr)
         return 2
     C = int(a.spec_rows)
+    fp8 = a.kv_cache == "fp8"
     d0 = inputs.draw(a.workload)
     B, Hq, Hkv, D, bs = base.num_seqs, base.num_q_heads, base.num_kv_heads, base.head_size, \
         base.block_size
@@ -832,7 +845,16 @@ def bench_spec(a, dev):
     vplan, _ = ops.varlen_plan(qsl, seq_lens, msl, Hq, Hkv, P)
     host_us = (time.perf_counter() - t0) * 1e6
     dplan = ops.decode_plan(seq_lens, msl, P)
-    pool0 = torch.zeros((d.num_blocks, 2, Hkv, bs, D), dtype=torch.bfloat16, device=dev)
+    k_scale = v_scale = 1.0
+    if fp8:   # per-tensor scales mapping the largest |key| / |value| to 448
+        kmax = vmax = 0.0
+        for b in range(B):
+            k, v = d.kv(b)
+            kmax = max(kmax, float(np.max(np.abs((k.astype(np.uint32) << 16).view(np.float32)))))
+            vmax = max(vmax, float(np.max(np.abs((v.astype(np.uint32) << 16).view(np.float32)))))
+        k_scale, v_scale = max(kmax, 1e-3) / 448.0, max(vmax, 1e-3) / 448.0
+    pool0 = torch.zeros((d.num_blocks, 2, Hkv, bs, D),
+                        dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
     for lo in range(0, B, 32):           # fill in slices to bound host memory
         ks, vs, sl = [], [], []
         for b in range(lo, min(B, lo + 32)):
@@ -840,9 +862,13 @@ def bench_spec(a, dev):
             ks.append(k)
             vs.append(v)
             sl.append(ops.slot_mapping(bt[b], 0, int(seq_lens[b]), bs))
-        ops.reshape_and_cache(dev_tensor(np.concatenate(ks)), dev_tensor(np.concatenate(vs)),
-                              torch.from_numpy(np.concatenate(sl)).to(dev), pool0)
-        del ks, vs
+        kd, vd = dev_tensor(np.concatenate(ks)), dev_tensor(np.concatenate(vs))
+        sld = torch.from_numpy(np.concatenate(sl)).to(dev)
+        if fp8:
+            ops.reshape_and_cache_fp8(kd, vd, sld, pool0, k_scale, v_scale)
+        else:
+            ops.reshape_and_cache(kd, vd, sld, pool0)
+        del ks, vs, kd, vd
     pool_bytes = pool0.numel() * pool0.element_size()
     R = max(1, -(-a.rotate_mb * (1 << 20) // pool_bytes))
     pools = [pool0] + [pool0.clone() for _ in range(R - 1)]
@@ -861,7 +887,12 @@ def bench_spec(a, dev):
     torch.cuda.synchronize()
 
     def multi(pool):
-        ops.decode_multi(out, q, pool, bt_dev, sl_dev, msl, scale, C, P, ws_multi, plan=dplan_dev)
+        if fp8:
+            ops.decode_multi_fp8(out, q, pool, bt_dev, sl_dev, msl, scale, k_scale, v_scale, C, P,
+                                 ws_multi, plan=dplan_dev)
+        else:
+            ops.decode_multi(out, q, pool, bt_dev, sl_dev, msl, scale, C, P, ws_multi,
+                             plan=dplan_dev)
 
     def varlen(pool):
         ops.attention_varlen(out, q, qsl_dev, pool, bt_dev, sl_dev, msl, scale, vplan_dev, P, ws)
@@ -870,7 +901,11 @@ def bench_spec(a, dev):
         ops.prefill_chunk(out, q, qsl_dev, C, pool, bt_dev, sl_dev, msl, scale)
 
     def decode1(pool):
-        ops.decode(out1, q1, pool, bt_dev, sl_dev, msl, scale, P, ws, plan=dplan_dev)
+        if fp8:
+            ops.decode_fp8(out1, q1, pool, bt_dev, sl_dev, msl, scale, k_scale, v_scale, P, ws,
+                           plan=dplan_dev)
+        else:
+            ops.decode(out1, q1, pool, bt_dev, sl_dev, msl, scale, P, ws, plan=dplan_dev)
 
     def timed(fn, n):
         s = torch.cuda.Stream()
@@ -894,10 +929,10 @@ def bench_spec(a, dev):
         return e0.elapsed_time(e1) * 1e3 / n
 
     multi_us = timed(multi, a.steps)
-    var_us = timed(varlen, a.steps)
-    pre_us = timed(prefill, a.steps)
+    var_us = None if fp8 else timed(varlen, a.steps)      # no FP8 variant of these two
+    pre_us = None if fp8 else timed(prefill, a.steps)
     dec_us = timed(decode1, a.steps)
-    kbytes = varlen_bytes(d.wl, seq_lens, chunks)
+    kbytes = varlen_bytes(d.wl, seq_lens, chunks, 1 if fp8 else None)
     flops = prefill_flops(seq_lens, chunks, Hq, D)
     achieved = kbytes / (multi_us * 1e-6) / 1e9
     res = {
@@ -918,29 +953,33 @@ def bench_spec(a, dev):
             "num_q_heads": Hq, "num_kv_heads": Hkv, "head_size": D, "block_size": bs,
             "context_tokens": int(seq_lens.sum()), "max_seq_len": msl, "partition_size": P,
             "pool_blocks": d.num_blocks, "pool_copies_rotated": R,
+            "kv_cache": ("fp8-e4m3, per-tensor scales k %.6g v %.6g" % (k_scale, v_scale)
+                         if fp8 else "bf16"),
             "parallelism": "none (1 GPU)",
         },
         "host_plan_us": round(host_us, 1),
         "attention_us_decode_multi": round(multi_us, 2),
-        "attention_us_varlen": round(var_us, 2),
-        "attention_us_prefill_chunk": round(pre_us, 2),
+        "attention_us_varlen": None if var_us is None else round(var_us, 2),
+        "attention_us_prefill_chunk": None if pre_us is None else round(pre_us, 2),
         "decode_us_one_row": round(dec_us, 2),
         "roofline": {
-            "kernel": "pa_decode_multi (decode_kernel, multi-row)",
+            "kernel": ("pa_decode_multi_fp8 (decode_kernel, multi-row, FP8 cache)" if fp8
+                       else "pa_decode_multi (decode_kernel, multi-row)"),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": (load_traffic(source_hash(DECODE_SOURCES), False, MULTI_TRAFFIC)
-                        if a.workload == 2 and C == 4 and P == 512 else None),
+                        if a.workload == 2 and C == 4 and P == 512 and not fp8 else None),
             "algorithmic_bytes_per_launch": kbytes,
             "algorithmic_flops_per_launch": flops,
             "avg_launch_us": round(multi_us, 3),
         },
     }
     if not a.no_cpu_baseline:
-        dt, cbytes, nseq = cpu_baseline_spec(d, a.cpu_seconds)
+        dt, cbytes, nseq = cpu_baseline_spec(d, a.cpu_seconds,
+                                             (k_scale, v_scale) if fp8 else None)
         res["cpu_baseline"] = {
             "value": round(cbytes / dt / 1e9, 6),
             "unit": "GB/s",
@@ -982,7 +1021,8 @@ def main(argv=None):
     ap.add_argument("--kv-cache", choices=["native", "fp8"], default="native",
                     help="decode workloads: keep the cache in the workload dtype (default) "
                          "or in FP8 E4M3 with per-tensor scales (pa_decode_append_fp8; with "
-                         "--unfused pa_reshape_and_cache_fp8 + pa_decode_fp8)")
+                         "--unfused pa_reshape_and_cache_fp8 + pa_decode_fp8; with --spec-rows "
+                         "pa_decode_multi_fp8)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     a = ap.parse_args(argv)

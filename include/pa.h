@@ -394,9 +394,12 @@ int pa_decode_append_fp8(void* out, float* lse_out, const void* query,
  *   other arguments as pa_decode (plan: pa_decode_plan of the same seq_lens
  *   and partition_size); workspace >= pa_decode_multi_workspace_bytes(...).
  * A work item covers floor(16 / G) rows with their G heads (one matrix tile
- * of 16 columns) over one partition; longer row sets take several items.
- * rows in [1, 64]; rows > 1 needs a bf16 cache and G <= 16; rows == 1 is
- * pa_decode.  Split-K needs B * H_kv * ceil(rows / floor(16 / G)) <= 65536. */
+ * of 16 columns; at head size 64, when the rows need more than one tile,
+ * two tiles: floor(32 / G) rows) over one partition; longer row sets take
+ * several items.  rows in [1, 64]; rows > 1 needs a bf16 cache (an FP8
+ * cache goes through pa_decode_multi_fp8: dtype PA_FP8 here is PA_ENOTSUP)
+ * and G <= 16; rows == 1 is pa_decode.  Split-K needs
+ * B * H_kv * (items per (sequence, KV head)) <= 65536. */
 size_t pa_decode_multi_workspace_bytes(int32_t B, int32_t rows, int32_t num_q_heads,
                                        int32_t num_kv_heads, int32_t head_size,
                                        int32_t max_seq_len, int32_t partition_size);
@@ -408,6 +411,20 @@ int pa_decode_multi(void* out, float* lse_out, const void* query, const void* kv
                     float scale, int32_t partition_size, const int32_t* plan,
                     int32_t plan_entries, void* workspace, size_t workspace_bytes,
                     int32_t dtype, void* stream);
+
+/* pa_decode_multi over an FP8 (E4M3) cache with per-tensor key/value scales
+ * (as pa_decode_fp8): queries and outputs bf16, the cache uint8 codes whose
+ * values are code * k_scale / code * v_scale.  Other arguments, the
+ * workspace and the limits as pa_decode_multi; rows == 1 is pa_decode_fp8.
+ * k_scale, v_scale positive and finite (PA_EINVAL otherwise). */
+int pa_decode_multi_fp8(void* out, float* lse_out, const void* query, const void* kv_cache,
+                        int32_t num_blocks, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t B,
+                        int32_t max_seq_len, int32_t rows, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                        float scale, float k_scale, float v_scale, int32_t partition_size,
+                        const int32_t* plan, int32_t plan_entries, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /* Chunked prefill ("Im Inneren von vLLM", "Fortgeschrittene Funktionen":
  * long prompts are split into chunks; "Inside vLLM", "Generate function":

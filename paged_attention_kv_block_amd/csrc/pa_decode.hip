@@ -280,8 +280,8 @@ static int decode_call(const char* fn, void* out, float* lse_out, const void* qu
   const bool multi = rows > 1;
   if (rows < 1 || rows > kMaxMultiRows)
     return fail(PA_EINVAL, "%s: rows %d outside [1, %d]", fn, rows, kMaxMultiRows);
-  if (multi && dtype != PA_BF16)
-    return fail(PA_ENOTSUP, "%s: several rows per sequence need a bf16 cache", fn);
+  if (multi && dtype != PA_BF16 && dtype != PA_FP8)
+    return fail(PA_ENOTSUP, "%s: several rows per sequence need a bf16 or FP8 cache", fn);
   if (multi && G > 16) return fail(PA_ENOTSUP, "%s: group size %d > 16", fn, G);
   const int cols = multi ? multi_columns(rows, G, head_size) : G;
   const int rpg = multi ? multi_rows_per_group(G, cols) : 1;
@@ -340,7 +340,12 @@ static int decode_call(const char* fn, void* out, float* lse_out, const void* qu
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   bool ok;
-  if (multi && cols == 32)
+  if (multi && dtype == PA_FP8 && cols == 32)
+    ok = (launch_decode<64, 32, true, true, true>(a, st), true);
+  else if (multi && dtype == PA_FP8)
+    ok = head_size == 64 ? (launch_decode<64, 16, true, true, true>(a, st), true)
+                         : (launch_decode<128, 16, true, true, true>(a, st), true);
+  else if (multi && cols == 32)
     ok = (launch_decode<64, 32, true, false, true>(a, st), true);
   else if (multi)
     ok = head_size == 64 ? (launch_decode<64, 16, true, false, true>(a, st), true)
@@ -442,5 +447,21 @@ extern "C" int pa_decode_multi(void* out, float* lse_out, const void* query, con
                      num_blocks, block_tables, max_blocks_per_seq, seq_lens, B, max_seq_len,
                      num_q_heads, num_kv_heads, head_size, block_size, scale, 1.f, 1.f,
                      partition_size, plan, plan_entries, workspace, workspace_bytes, dtype,
+                     stream, rows);
+}
+
+extern "C" int pa_decode_multi_fp8(void* out, float* lse_out, const void* query,
+                                   const void* kv_cache, int32_t num_blocks,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* seq_lens, int32_t B, int32_t max_seq_len,
+                                   int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_size, int32_t block_size, float scale,
+                                   float k_scale, float v_scale, int32_t partition_size,
+                                   const int32_t* plan, int32_t plan_entries, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return decode_call("pa_decode_multi_fp8", out, lse_out, query, nullptr, nullptr, kv_cache,
+                     num_blocks, block_tables, max_blocks_per_seq, seq_lens, B, max_seq_len,
+                     num_q_heads, num_kv_heads, head_size, block_size, scale, k_scale, v_scale,
+                     partition_size, plan, plan_entries, workspace, workspace_bytes, PA_FP8,
                      stream, rows);
 }

@@ -68,6 +68,9 @@ SIGNATURES = {
     "pa_decode_multi": (_c_int, [_vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _vp, _c_i32, _c_i32,
                                  _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _f, _c_i32, _vp, _c_i32,
                                  _vp, _c_sz, _c_i32, _vp]),
+    "pa_decode_multi_fp8": (_c_int, [_vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _vp, _c_i32,
+                                     _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _f, _f, _f,
+                                     _c_i32, _vp, _c_i32, _vp, _c_sz, _vp]),
     "pa_prefill_chunk": (_c_int, [_vp, _vp, _vp, _vp, _c_i32, _c_i32, _vp, _c_i32, _vp, _c_i32,
                                   _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _f,
                                   _c_i32, _vp]),
@@ -443,6 +446,42 @@ def decode_multi(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int,
                                  int(partition_size), _ptr(plan),
                                  0 if plan is None else plan.numel(), _ptr(workspace), ws_bytes,
                                  _dtype_code(kv_cache), _stream(stream)))
+
+
+def decode_multi_fp8(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int,
+                     scale: float, k_scale: float, v_scale: float, rows: int,
+                     partition_size: int = 0, workspace=None, lse=None, plan=None,
+                     stream=None) -> None:
+    """pa_decode_multi_fp8: decode_multi over an FP8 cache (uint8
+    [N, 2, H_kv, 16, D] of E4M3 codes with per-tensor scales); out/query
+    bf16 [B * rows, H_q, D]."""
+    _need_gpu(out, query, kv_cache, block_tables, seq_lens, workspace, lse, plan)
+    torch = _torch()
+    N, _, Hkv, bs, D = kv_cache.shape
+    T, Hq, Dq = query.shape
+    B = seq_lens.numel()
+    if Dq != D or T != B * int(rows) or tuple(out.shape) != (T, Hq, D) \
+            or out.dtype != torch.bfloat16 or query.dtype != torch.bfloat16 \
+            or kv_cache.dtype != torch.uint8:
+        raise PAError(PA_EINVAL, "out/query must be bf16 [B * rows, H_q, D], kv_cache uint8")
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32 \
+            or block_tables.shape[0] != B:
+        raise PAError(PA_EINVAL, "block_tables/seq_lens must be int32 with B rows")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (T, Hq)):
+        raise PAError(PA_EINVAL, "lse must be fp32 [B * rows, H_q]")
+    for t in (out, query, kv_cache, block_tables, seq_lens, workspace, lse, plan):
+        if t is not None and not t.is_contiguous():
+            raise PAError(PA_EINVAL, "tensors must be contiguous")
+    if plan is not None and plan.dtype != torch.int32:
+        raise PAError(PA_EINVAL, "plan must be int32")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode_multi_fp8(_ptr(out), _ptr(lse), _ptr(query), _ptr(kv_cache), N,
+                                     _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
+                                     B, int(max_seq_len), int(rows), Hq, Hkv, D, bs,
+                                     float(scale), float(k_scale), float(v_scale),
+                                     int(partition_size), _ptr(plan),
+                                     0 if plan is None else plan.numel(), _ptr(workspace),
+                                     ws_bytes, _stream(stream)))
 
 
 def decode_fp8(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int, scale: float,

@@ -275,3 +275,81 @@ def test_decode_append_refuses_fp8_dtype():
     st = L.pa_decode_append(16, None, 16, 16, 16, 16, 1, 16, 1, 16, 1, 16, 8, 2, 64, 16, 0.125, 0,
                             None, 0, None, 0, ops.PA_FP8, None)
     assert st == ops.PA_EINVAL
+
+
+# ---------------------------------------------------------------------------
+# several query rows per sequence (pa_decode_multi_fp8)
+# ---------------------------------------------------------------------------
+def _multi_case(seq_lens, rows, Hq, Hkv, D, P=0, use_plan=False):
+    """Sequence b's last `rows` tokens attend causally over the FP8 pool:
+    the oracle's causal chunk of that length over its own FP8 pool with the
+    same scales (every sequence holds at least `rows` tokens)."""
+    from tests.gpu_setup import from_device, to_device
+    d = inputs.custom(kind="prefill", seq_lens=seq_lens, chunk_lens=[rows] * len(seq_lens),
+                      num_q_heads=Hq, num_kv_heads=Hkv, head_size=D, seed=9)
+    wl = d.wl
+    ks, vs = _data_scales(d)
+    o, g, opool, gpool = _fill_both(d, ks, vs)
+    np.testing.assert_array_equal(gpool.cpu().numpy(), opool)
+    q = to_device(d.query(), wl)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device="cuda")
+    msl = int(max(d.seq_lens))
+    ws = ops.decode_multi_workspace(wl.num_seqs, rows, Hq, Hkv, D, msl, P)
+    plan = torch.from_numpy(ops.decode_plan(d.seq_lens, msl, P)).cuda() if use_plan else None
+    ops.decode_multi_fp8(out, q, gpool, g.bt_dev, g.seq_lens_dev, msl, float(wl.scale), ks, vs,
+                         rows, P, ws, lse, plan)
+    torch.cuda.synchronize()
+    qsl = np.arange(wl.num_seqs + 1, dtype=np.int64) * rows
+    ref, ref_lse = oracle.prefill_chunk(d.query(), qsl, opool, o.block_tables, d.seq_lens,
+                                        wl.scale, k_scale=ks, v_scale=vs)
+    got = oracle.to_f64(from_device(out))
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(got_lse))
+    err = float(np.max(np.abs(got - ref)))
+    lerr = float(np.max(np.abs(got_lse - ref_lse)))
+    assert err <= TOL and lerr <= TOL, (rows, P, use_plan, err, lerr)
+    return err
+
+
+MULTI_CASES = [
+    # (name, seq_lens, rows, H_q, H_kv, D)
+    ("g8-d64-rows2", (2, 17, 33, 160, 300, 47), 2, 16, 2, 64),
+    ("g4-d128-rows3", (3, 15, 16, 31, 64, 200, 513), 3, 8, 2, 128),
+    ("g8-d128-rows4", (4, 16, 17, 100, 257), 4, 8, 1, 128),
+    ("g4-d64-rows16", (16, 17, 33, 100, 600), 16, 8, 2, 64),
+    ("g1-d64-rows5", (5, 6, 21, 80, 129), 5, 2, 2, 64),
+]
+
+
+@pytest.mark.parametrize("name,seq_lens,rows,Hq,Hkv,D", MULTI_CASES,
+                         ids=[c[0] for c in MULTI_CASES])
+@pytest.mark.parametrize("P,use_plan", [(0, False), (0, True), (32, True), (512, True)])
+def test_decode_multi_fp8(name, seq_lens, rows, Hq, Hkv, D, P, use_plan):
+    _multi_case(seq_lens, rows, Hq, Hkv, D, P=P, use_plan=use_plan)
+
+
+def test_decode_multi_fp8_one_row_is_decode_fp8():
+    """rows == 1 is pa_decode_fp8 itself: bit-identical outputs."""
+    from tests.gpu_setup import to_device
+    d = inputs.custom(kind="decode", seq_lens=(1, 15, 33, 100, 257), num_q_heads=32,
+                      num_kv_heads=4, head_size=64)
+    wl = d.wl
+    ks, vs = _data_scales(d)
+    o, g, opool, gpool = _fill_both(d, ks, vs)
+    q = to_device(d.query(), wl)
+    msl = int(max(d.seq_lens))
+    outs = []
+    for multi in (False, True):
+        out = torch.empty_like(q)
+        ws = ops.decode_workspace(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_size,
+                                  msl, 32, "cuda")
+        if multi:
+            ops.decode_multi_fp8(out, q, gpool, g.bt_dev, g.seq_lens_dev, msl, float(wl.scale),
+                                 ks, vs, 1, 32, ws)
+        else:
+            ops.decode_fp8(out, q, gpool, g.bt_dev, g.seq_lens_dev, msl, float(wl.scale), ks,
+                           vs, 32, ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])

@@ -378,6 +378,41 @@ def test_decode_multi_empty_batch_is_a_no_op():
     assert _multi_status(B=0)[0] == ops.PA_OK
 
 
+def _multi_fp8_status(**kw):
+    args = dict(out=16, lse=None, q=16, cache=16, nb=4, bt=16, mbps=4, sl=16, B=1, msl=64,
+                rows=4, hq=8, hkv=2, d=128, bs=16, scale=0.1, ks=0.01, vs=0.01, P=0, ws=None,
+                wsb=0)
+    args.update(kw)
+    L = ops.lib()
+    st = L.pa_decode_multi_fp8(args["out"], args["lse"], args["q"], args["cache"], args["nb"],
+                               args["bt"], args["mbps"], args["sl"], args["B"], args["msl"],
+                               args["rows"], args["hq"], args["hkv"], args["d"], args["bs"],
+                               args["scale"], args["ks"], args["vs"], args["P"], None, 0,
+                               args["ws"], args["wsb"], None)
+    return st, L.pa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=0), ops.PA_EINVAL),
+    (dict(rows=65), ops.PA_EINVAL),
+    (dict(ks=0.0), ops.PA_EINVAL),                       # scales positive and finite
+    (dict(vs=float("inf")), ops.PA_EINVAL),
+    (dict(ks=float("nan")), ops.PA_EINVAL),
+    (dict(hq=34, hkv=1), ops.PA_ENOTSUP),                # group 34 > 16
+    (dict(P=16), ops.PA_EINVAL),                         # workspace missing
+    (dict(d=96), ops.PA_ENOTSUP),
+    (dict(msl=65), ops.PA_EINVAL),
+])
+def test_decode_multi_fp8_validation(kw, status):
+    st, msg = _multi_fp8_status(**kw)
+    assert st == status, msg
+    assert "pa_decode_multi_fp8" in msg
+
+
+def test_decode_multi_fp8_empty_batch_is_a_no_op():
+    assert _multi_fp8_status(B=0)[0] == ops.PA_OK
+
+
 def test_decode_multi_workspace_size():
     """Records of 16 columns (floor(16 / G) rows with their G heads), or 32 at
     head size 64 when the rows need more than one 16-column tile, per
