@@ -26,10 +26,11 @@ def _pool_shape(d):
     return (d.num_blocks, 2, wl.num_kv_heads, wl.block_size, wl.head_size)
 
 
-def _data_scales(d):
-    """Per-tensor scales mapping the largest |key| / |value| to 448."""
+def _data_scales(d, seqs=None):
+    """Per-tensor scales mapping the largest |key| / |value| (of the selected
+    sequences, all by default) to 448."""
     ks = vs = 0.0
-    for b in range(d.wl.num_seqs):
+    for b in (range(d.wl.num_seqs) if seqs is None else seqs):
         k, v = d.kv(b)
         if k.size:
             ks = max(ks, float(np.max(np.abs(oracle.to_f64(k)))))
@@ -37,10 +38,11 @@ def _data_scales(d):
     return max(ks, 1e-3) / 448.0, max(vs, 1e-3) / 448.0
 
 
-def _fill_both(d, k_scale, v_scale):
+def _fill_both(d, k_scale, v_scale, seqs=None):
     """Oracle FP8 pool (oracle quantiser + scatter) and GPU FP8 pool
-    (pa_reshape_and_cache_fp8) of every cached token, block tables from the
-    two allocators (asserted equal)."""
+    (pa_reshape_and_cache_fp8) of every cached token of the selected
+    sequences (all by default; other slots keep the NaN code), block tables
+    from the two allocators (asserted equal)."""
     from tests.gpu_setup import GpuSide, to_device
     from tests.oracle_setup import OracleSide
     wl = d.wl
@@ -50,7 +52,7 @@ def _fill_both(d, k_scale, v_scale):
     opool = oracle.empty_pool(d.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_size,
                               np.uint8, fill=np.uint8(POISON))
     ks, vs, sl = [], [], []
-    for b in range(wl.num_seqs):
+    for b in (range(wl.num_seqs) if seqs is None else seqs):
         L = int(d.seq_lens[b])
         if L == 0:
             continue
@@ -353,3 +355,68 @@ def test_decode_multi_fp8_one_row_is_decode_fp8():
         outs.append(out)
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1])
+
+
+def test_decode_multi_fp8_llama3_shape_sampled():
+    """The Llama-3-8B-shaped decode batch at full size (256 sequences,
+    log-normal lengths to 8192) verifying 4 rows per sequence over the FP8
+    cache with split-K 512 and the plan, as bench.py times it; the oracle
+    checks the longest, the shortest and a few others (only their blocks are
+    written; the rest hold the NaN code)."""
+    from tests.gpu_setup import from_device, to_device
+    L = inputs.draw(2).seq_lens
+    rows, P = 4, 512
+    d = inputs.custom(kind="prefill", seq_lens=tuple(int(x) for x in L),
+                      chunk_lens=[rows] * len(L), num_q_heads=32, num_kv_heads=8,
+                      head_size=128, seed=2012)
+    wl = d.wl
+    seqs = sorted({int(np.argmax(L)), int(np.argmin(L)), 0, 77, 255})
+    ks, vs = _data_scales(d, seqs)
+    o, g, opool, gpool = _fill_both(d, ks, vs, seqs)
+    q = to_device(d.query(), wl)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    msl = int(max(L))
+    ws = ops.decode_multi_workspace(wl.num_seqs, rows, 32, 8, 128, msl, P)
+    plan = torch.from_numpy(ops.decode_plan(d.seq_lens, msl, P)).cuda()
+    ops.decode_multi_fp8(out, q, gpool, g.bt_dev, g.seq_lens_dev, msl, float(wl.scale), ks, vs,
+                         rows, P, ws, lse, plan)
+    torch.cuda.synchronize()
+    qsl = np.arange(wl.num_seqs + 1, dtype=np.int64) * rows
+    ref, ref_lse = oracle.prefill_chunk(d.query(), qsl, opool, o.block_tables, d.seq_lens,
+                                        wl.scale, seqs=seqs, k_scale=ks, v_scale=vs)
+    idx = np.array([b * rows + i for b in seqs for i in range(rows)])
+    got = oracle.to_f64(from_device(out))[idx]
+    gl = lse.cpu().numpy().astype(np.float64)[idx]
+    assert np.all(np.isfinite(got))
+    err = float(np.max(np.abs(got - ref[idx])))
+    lerr = float(np.max(np.abs(gl - ref_lse[idx])))
+    assert err <= TOL and lerr <= TOL, (err, lerr)
+
+
+@pytest.mark.parametrize("rows,P", [(4, 64), (2, 0)])
+def test_decode_multi_fp8_in_a_hip_graph(rows, P):
+    """pa_decode_multi_fp8 captured in a HIP graph: every replay (with eager
+    work between them) equals the eager call, which matches the oracle."""
+    from tests.gpu_setup import from_device, to_device
+    from tests.test_gpu_decode_multi import _graph_replays_match
+    seq_lens = (300, 45, 17, 1000, 64, 130)
+    d = inputs.custom(kind="prefill", seq_lens=seq_lens, chunk_lens=[rows] * len(seq_lens),
+                      num_q_heads=32, num_kv_heads=4, head_size=64, seed=33)
+    wl = d.wl
+    ks, vs = _data_scales(d)
+    o, g, opool, gpool = _fill_both(d, ks, vs)
+    q = to_device(d.query(), wl)
+    out = torch.empty_like(q)
+    ws = ops.decode_multi_workspace(6, rows, 32, 4, 64, 1000, P)
+    plan = torch.from_numpy(ops.decode_plan(d.seq_lens, 1000, P)).cuda()
+
+    def step():
+        ops.decode_multi_fp8(out, q, gpool, g.bt_dev, g.seq_lens_dev, 1000, float(wl.scale), ks,
+                             vs, rows, P, ws, plan=plan)
+
+    eager = _graph_replays_match(step, out)
+    qsl = np.arange(wl.num_seqs + 1, dtype=np.int64) * rows
+    ref, _ = oracle.prefill_chunk(d.query(), qsl, opool, o.block_tables, d.seq_lens, wl.scale,
+                                  k_scale=ks, v_scale=vs)
+    assert float(np.max(np.abs(oracle.to_f64(from_device(eager)) - ref))) <= TOL
