@@ -51,8 +51,14 @@ TRAFFIC_FILES = {False: os.path.join(ROOT, "profiles", "decode_append_traffic.js
 # partition sizes
 WORKLOAD_TRAFFIC = {2: os.path.join(ROOT, "profiles", "decode_append_traffic_llama3-8b.json"),
                     4: os.path.join(ROOT, "profiles", "decode_append_traffic_long-context.json")}
+# the same over the FP8 cache (pa_decode_append_fp8, each workload's own
+# partition size)
+FP8_TRAFFIC = {1: os.path.join(ROOT, "profiles", "decode_append_fp8_traffic_tinyllama-1.1b.json"),
+               2: os.path.join(ROOT, "profiles", "decode_append_fp8_traffic_llama3-8b.json"),
+               4: os.path.join(ROOT, "profiles", "decode_append_fp8_traffic_long-context.json")}
 VARLEN_TRAFFIC = os.path.join(ROOT, "profiles", "varlen_traffic.json")
 MULTI_TRAFFIC = os.path.join(ROOT, "profiles", "decode_multi_traffic.json")
+MULTI_FP8_TRAFFIC = os.path.join(ROOT, "profiles", "decode_multi_fp8_traffic.json")
 PREFILL_TRAFFIC = os.path.join(ROOT, "profiles", "prefill_traffic.json")
 PREFILL_SOURCES = ["paged_attention_kv_block_amd/csrc/pa_prefill.hip",
                    "paged_attention_kv_block_amd/csrc/pa_prefill_dev.h",
@@ -970,8 +976,9 @@ def bench_spec(a, dev):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": (load_traffic(source_hash(DECODE_SOURCES), False, MULTI_TRAFFIC)
-                        if a.workload == 2 and C == 4 and P == 512 and not fp8 else None),
+            "traffic": (load_traffic(source_hash(DECODE_SOURCES), False,
+                                     MULTI_FP8_TRAFFIC if fp8 else MULTI_TRAFFIC)
+                        if a.workload == 2 and C == 4 and P == 512 else None),
             "algorithmic_bytes_per_launch": kbytes,
             "algorithmic_flops_per_launch": flops,
             "avg_launch_us": round(multi_us, 3),
@@ -1235,6 +1242,8 @@ def main(argv=None):
     elif (not fp8 and not a.unfused and a.workload in WORKLOAD_TRAFFIC
           and P == default_partition(wl)):
         traffic = load_traffic(khash, False, WORKLOAD_TRAFFIC[a.workload])
+    elif fp8 and not a.unfused and a.workload in FP8_TRAFFIC and P == default_partition(wl):
+        traffic = load_traffic(khash, False, FP8_TRAFFIC[a.workload])
 
     res = {
         "metric": METRIC,
