@@ -420,3 +420,42 @@ def test_decode_multi_fp8_in_a_hip_graph(rows, P):
     ref, _ = oracle.prefill_chunk(d.query(), qsl, opool, o.block_tables, d.seq_lens, wl.scale,
                                   k_scale=ks, v_scale=vs)
     assert float(np.max(np.abs(oracle.to_f64(from_device(eager)) - ref))) <= TOL
+
+
+@pytest.mark.parametrize("seq_lens,rows,Hq,Hkv,D,P", [
+    ((1, 2, 3, 40, 0), 4, 8, 1, 64, 0),         # sequences shorter than rows, one empty
+    ((2, 5, 33, 70), 3, 16, 1, 64, 32),         # G = 16: one row per 16-column item
+    ((1, 7, 16, 300), 8, 4, 2, 128, 64),        # two column groups, split-K
+])
+def test_decode_multi_fp8_short_sequences(seq_lens, rows, Hq, Hkv, D, P):
+    """Rows before position 0 are zero with lse -inf; the others are the
+    oracle's causal chunk of the last min(rows, L) tokens."""
+    from tests.gpu_setup import from_device, to_device
+    d = inputs.custom(kind="prefill", seq_lens=seq_lens, chunk_lens=[rows] * len(seq_lens),
+                      num_q_heads=Hq, num_kv_heads=Hkv, head_size=D, seed=41)
+    wl = d.wl
+    ks, vs = _data_scales(d)
+    o, g, opool, gpool = _fill_both(d, ks, vs)
+    q = to_device(d.query(), wl)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device="cuda")
+    msl = int(max(d.seq_lens))
+    ws = ops.decode_multi_workspace(wl.num_seqs, rows, Hq, Hkv, D, msl, P)
+    ops.decode_multi_fp8(out, q, gpool, g.bt_dev, g.seq_lens_dev, msl, float(wl.scale), ks, vs,
+                         rows, P, ws, lse)
+    torch.cuda.synchronize()
+    got = oracle.to_f64(from_device(out))
+    gl = lse.cpu().numpy().astype(np.float64)
+    # the rows at positions >= 0, packed as a chunk of min(rows, L) per sequence
+    C = [min(rows, int(L)) for L in seq_lens]
+    idx = np.array([b * rows + i for b in range(len(seq_lens)) for i in range(rows - C[b], rows)],
+                   dtype=int)
+    early = np.setdiff1d(np.arange(len(seq_lens) * rows), idx)
+    assert np.all(got[early] == 0.0) and np.all(np.isneginf(gl[early]))
+    qsl = np.concatenate([[0], np.cumsum(C)]).astype(np.int64)
+    ref, ref_lse = oracle.prefill_chunk(d.query()[idx], qsl, opool, o.block_tables, d.seq_lens,
+                                        wl.scale, k_scale=ks, v_scale=vs)
+    assert np.all(np.isfinite(got[idx]))
+    err = float(np.max(np.abs(got[idx] - ref)))
+    lerr = float(np.max(np.abs(gl[idx] - ref_lse)))
+    assert err <= TOL and lerr <= TOL, (err, lerr)
