@@ -105,6 +105,7 @@ CASES = [
     ("g2-d128-rows8", (8, 9, 24, 200, 345), 8, 4, 2, 128),
     ("g4-d64-rows16", (16, 17, 33, 100, 600), 16, 8, 2, 64),
     ("g8-d64-short", (1, 2, 3, 40), 4, 8, 1, 64),        # sequences shorter than rows
+    ("g4-d128-empty", (0, 5, 0, 33, 1), 2, 8, 2, 128),  # empty sequences
 ]
 
 
