@@ -260,3 +260,21 @@ def test_varlen_short_chunks_in_a_hip_graph():
     eager = _graph_replays_match(step, out)
     ref, _ = o.prefill()
     assert float(np.max(np.abs(_f64(eager) - ref))) <= TOL
+
+
+def test_physical_permutation_is_bit_exact():
+    """The same sequences over another physical block assignment (the free
+    queue reversed) give bit-identical outputs and lse: the arithmetic order
+    depends on logical positions only."""
+    from tests.gpu_setup import GpuSide
+    lens = (40, 300, 77, 129, 5)
+    d1 = _draw(lens, 4, 16, 2, 64, seed=51)
+    d2 = _draw(lens, 4, 16, 2, 64, seed=51)
+    d2.pool_order = d2.pool_order[::-1].copy()
+    g1, g2 = GpuSide(d1), GpuSide(d2)
+    assert not np.array_equal(g1.block_tables, g2.block_tables)
+    for P, plan in ((0, False), (32, True)):
+        o1, l1 = _run(g1, 4, P, plan)
+        o2, l2 = _run(g2, 4, P, plan)
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), P
+        assert torch.equal(l1, l2), P

@@ -459,3 +459,40 @@ def test_decode_multi_fp8_short_sequences(seq_lens, rows, Hq, Hkv, D, P):
     err = float(np.max(np.abs(got[idx] - ref)))
     lerr = float(np.max(np.abs(gl[idx] - ref_lse)))
     assert err <= TOL and lerr <= TOL, (err, lerr)
+
+
+def test_fp8_physical_permutation_is_bit_exact():
+    """Over the FP8 cache too, another physical block assignment (the free
+    queue reversed) gives bit-identical one-row and multi-row outputs."""
+    from tests.gpu_setup import to_device
+    lens, rows = (40, 300, 77, 129, 5), 4
+    draws = [inputs.custom(kind="prefill", seq_lens=lens, chunk_lens=[rows] * len(lens),
+                           num_q_heads=16, num_kv_heads=2, head_size=128, seed=52)
+             for _ in range(2)]
+    draws[1].pool_order = draws[1].pool_order[::-1].copy()
+    ks, vs = _data_scales(draws[0])
+    sides = [_fill_both(d, ks, vs) for d in draws]
+    assert not np.array_equal(sides[0][1].block_tables, sides[1][1].block_tables)
+    wl = draws[0].wl
+    q = to_device(draws[0].query(), wl)
+    q1 = q.view(len(lens), rows, 16, 128)[:, rows - 1].contiguous()
+    msl = max(lens)
+    for P in (0, 32):
+        res = []
+        for (o, g, opool, gpool) in sides:
+            out = torch.empty_like(q)
+            lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+            ws = ops.decode_multi_workspace(len(lens), rows, 16, 2, 128, msl, P)
+            ops.decode_multi_fp8(out, q, gpool, g.bt_dev, g.seq_lens_dev, msl, float(wl.scale),
+                                 ks, vs, rows, P, ws, lse)
+            out1 = torch.empty_like(q1)
+            ws1 = ops.decode_workspace(len(lens), 16, 2, 128, msl, P, "cuda")
+            ops.decode_fp8(out1, q1, gpool, g.bt_dev, g.seq_lens_dev, msl, float(wl.scale), ks,
+                           vs, P, ws1)
+            res.append((out, lse, out1))
+        torch.cuda.synchronize()
+        for a, b in zip(res[0], res[1]):
+            assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32
+                               else a.view(torch.int16),
+                               b.view(torch.int32) if b.dtype == torch.float32
+                               else b.view(torch.int16)), P
