@@ -420,9 +420,12 @@ def decode_multi(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int,
                  stream=None) -> None:
     """pa_decode_multi: every sequence's last `rows` tokens attend causally
     (speculative-decoding verification).  out/query [B * rows, H_q, D];
-    lse fp32 [B * rows, H_q] or None; the other arguments as decode()."""
+    lse fp32 [B * rows, H_q] or None; the other arguments as decode().  An
+    FP8 cache goes through decode_multi_fp8 (it carries the scales)."""
     _need_gpu(out, query, kv_cache, block_tables, seq_lens, workspace, lse, plan)
     torch = _torch()
+    if kv_cache.dtype == torch.uint8:
+        raise PAError(PA_EINVAL, "an FP8 cache needs decode_multi_fp8 (its scales)")
     N, _, Hkv, bs, D = kv_cache.shape
     T, Hq, Dq = query.shape
     B = seq_lens.numel()

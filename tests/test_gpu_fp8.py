@@ -496,3 +496,14 @@ def test_fp8_physical_permutation_is_bit_exact():
                                else a.view(torch.int16),
                                b.view(torch.int32) if b.dtype == torch.float32
                                else b.view(torch.int16)), P
+
+
+def test_decode_multi_refuses_an_fp8_cache():
+    """decode_multi has no scales: an FP8 (uint8) cache is refused before
+    anything is launched, pointing at decode_multi_fp8."""
+    q = torch.zeros((4, 8, 64), dtype=torch.bfloat16, device="cuda")
+    pool = torch.zeros((4, 2, 2, 16, 64), dtype=torch.uint8, device="cuda")
+    bt = torch.zeros((2, 2), dtype=torch.int32, device="cuda")
+    sl = torch.full((2,), 4, dtype=torch.int32, device="cuda")
+    with pytest.raises(ops.PAError, match="decode_multi_fp8"):
+        ops.decode_multi(torch.empty_like(q), q, pool, bt, sl, 4, 0.125, 2)
