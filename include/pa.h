@@ -63,7 +63,10 @@ typedef enum {
 
 /* PA_FP8: an FP8 (OCP E4M3) KV cache with per-tensor key/value scales; the
  * queries and outputs around it are bf16 (pa_reshape_and_cache_fp8,
- * pa_decode_fp8). */
+ * pa_decode_fp8).  Passed as the dtype of an entry point without scales
+ * (pa_reshape_and_cache, pa_decode, pa_decode_append, pa_decode_multi,
+ * pa_prefill_chunk, pa_attention_varlen) it is PA_EINVAL: the *_fp8 entry
+ * points carry the scales. */
 typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8 = 2 } pa_dtype;
 
 /* Message of the last failing call on this thread ("" if none). */
@@ -397,7 +400,7 @@ int pa_decode_append_fp8(void* out, float* lse_out, const void* query,
  * of 16 columns; at head size 64, when the rows need more than one tile,
  * two tiles: floor(32 / G) rows) over one partition; longer row sets take
  * several items.  rows in [1, 64]; rows > 1 needs a bf16 cache (an FP8
- * cache goes through pa_decode_multi_fp8: dtype PA_FP8 here is PA_ENOTSUP)
+ * cache goes through pa_decode_multi_fp8: dtype PA_FP8 here is PA_EINVAL)
  * and G <= 16; rows == 1 is pa_decode.  Split-K needs
  * B * H_kv * (items per (sequence, KV head)) <= 65536. */
 size_t pa_decode_multi_workspace_bytes(int32_t B, int32_t rows, int32_t num_q_heads,

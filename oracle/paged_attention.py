@@ -225,18 +225,3 @@ def prefill_chunk(query: np.ndarray, query_start_loc, pool: np.ndarray,
                 out[lo + i, heads] = o
                 lse[lo + i, heads] = l
     return out, lse
-
-
-def context_tokens(seq_lens) -> int:
-    return int(sum(int(x) for x in seq_lens))
-
-
-def causal_flops(seq_lens, chunk_lens, num_q_heads: int, head_size: int) -> int:
-    """Algorithmic flops of a causal prefill chunk: 2 for the multiply-add of
-    q.k and 2 of p.v per (query head, visible key, dim)."""
-    tot = 0
-    for L, C in zip(seq_lens, chunk_lens):
-        ctx = int(L) - int(C)
-        tot += sum(ctx + i + 1 for i in range(int(C)))
-    return 4 * head_size * num_q_heads * tot
-

@@ -127,16 +127,25 @@ constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 // Einblick ...", section "Tiefenanalyse", lists FP8 among the engine's
 // quantisation formats without a format or scale: E4M3 with per-tensor
 // scales is the reading.
+// A NaN input (either sign) is stored as the code 0x7F: the clamp would
+// otherwise turn it into -448 or 448, a large finite key nothing can detect.
+// +-inf saturate to +-448 like any other out-of-range value.
 __device__ __forceinline__ float e4m3_input(uint32_t f32_bits, float scale) {
   const float q = __uint_as_float(f32_bits) / scale;
   return fminf(fmaxf(q, -448.f), 448.f);
+}
+__device__ __forceinline__ uint32_t e4m3_nan_byte(uint32_t f32_bits, uint32_t byte_mask) {
+  return (f32_bits & 0x7FFFFFFFu) > 0x7F800000u ? byte_mask : 0u;
 }
 __device__ __forceinline__ uint32_t quantize4_e4m3(uint32_t w0, uint32_t w1, float scale) {
   int r = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_input(w0 << 16, scale),
                                          e4m3_input(w0 & 0xFFFF0000u, scale), 0, false);
   r = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_input(w1 << 16, scale),
                                      e4m3_input(w1 & 0xFFFF0000u, scale), r, true);
-  return uint32_t(r);
+  const uint32_t nan = e4m3_nan_byte(w0 << 16, 0xFFu) | e4m3_nan_byte(w0 & 0xFFFF0000u, 0xFF00u) |
+                       e4m3_nan_byte(w1 << 16, 0xFF0000u) |
+                       e4m3_nan_byte(w1 & 0xFFFF0000u, 0xFF000000u);
+  return (uint32_t(r) & ~nan) | (0x7F7F7F7Fu & nan);
 }
 
 }  // namespace pa

@@ -442,7 +442,7 @@ extern "C" int pa_decode_multi(void* out, float* lse_out, const void* query, con
                                int32_t plan_entries, void* workspace, size_t workspace_bytes,
                                int32_t dtype, void* stream) {
   if (dtype == PA_FP8)
-    return fail(PA_ENOTSUP, "pa_decode_multi: bf16 or fp32 caches only");
+    return fail(PA_EINVAL, "pa_decode_multi: an FP8 cache needs pa_decode_multi_fp8 (its scales)");
   return decode_call("pa_decode_multi", out, lse_out, query, nullptr, nullptr, kv_cache,
                      num_blocks, block_tables, max_blocks_per_seq, seq_lens, B, max_seq_len,
                      num_q_heads, num_kv_heads, head_size, block_size, scale, 1.f, 1.f,

@@ -275,6 +275,13 @@ def _stream(stream=None) -> int:
 
 
 def _need_gpu(*ts):
+    """Every device argument (None = not given) must be a dense GPU tensor:
+    the library reads each as packed rows from its data pointer, so a strided
+    view (a slice of a fused QKV tensor, a transposed plan) would be read
+    wrongly rather than refused."""
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise PAError(PA_EINVAL, "tensors must be contiguous")
     for t in ts:
         if t is not None and not t.is_cuda:
             raise PAError(PA_EINVAL, "device arguments must be GPU tensors")
@@ -283,9 +290,6 @@ def _need_gpu(*ts):
 def reshape_and_cache(key, value, slot_mapping, kv_cache, stream=None) -> None:
     """key/value [T, H_kv, D]; slot_mapping int64 [T]; kv_cache [N, 2, H_kv, 16, D]."""
     _need_gpu(key, value, slot_mapping, kv_cache)
-    for t in (key, value, slot_mapping, kv_cache):
-        if not t.is_contiguous():
-            raise PAError(PA_EINVAL, "tensors must be contiguous")
     N, two, Hkv, bs, D = kv_cache.shape
     if two != 2 or key.shape != value.shape or tuple(key.shape[1:]) != (Hkv, D) \
             or key.dtype != kv_cache.dtype or value.dtype != kv_cache.dtype:
@@ -303,9 +307,6 @@ def reshape_and_cache_fp8(key, value, slot_mapping, kv_cache, k_scale: float, v_
     [N, 2, H_kv, 16, D] holding FP8 E4M3 codes (code * scale = value)."""
     torch = _torch()
     _need_gpu(key, value, slot_mapping, kv_cache)
-    for t in (key, value, slot_mapping, kv_cache):
-        if not t.is_contiguous():
-            raise PAError(PA_EINVAL, "tensors must be contiguous")
     N, two, Hkv, bs, D = kv_cache.shape
     if two != 2 or key.shape != value.shape or tuple(key.shape[1:]) != (Hkv, D) \
             or key.dtype != torch.bfloat16 or value.dtype != torch.bfloat16 \
@@ -375,9 +376,6 @@ def decode(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int, scale
         raise PAError(PA_EINVAL, "block_tables/seq_lens must be int32 with B rows")
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq)):
         raise PAError(PA_EINVAL, "lse must be fp32 [B, H_q]")
-    for t in (out, query, kv_cache, block_tables, seq_lens, workspace, lse):
-        if t is not None and not t.is_contiguous():
-            raise PAError(PA_EINVAL, "tensors must be contiguous")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if plan is not None and plan.dtype != torch.int32:
         raise PAError(PA_EINVAL, "plan must be int32")
@@ -437,9 +435,6 @@ def decode_multi(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int,
         raise PAError(PA_EINVAL, "block_tables/seq_lens must be int32 with B rows")
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (T, Hq)):
         raise PAError(PA_EINVAL, "lse must be fp32 [B * rows, H_q]")
-    for t in (out, query, kv_cache, block_tables, seq_lens, workspace, lse, plan):
-        if t is not None and not t.is_contiguous():
-            raise PAError(PA_EINVAL, "tensors must be contiguous")
     if plan is not None and plan.dtype != torch.int32:
         raise PAError(PA_EINVAL, "plan must be int32")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -472,9 +467,6 @@ def decode_multi_fp8(out, query, kv_cache, block_tables, seq_lens, max_seq_len: 
         raise PAError(PA_EINVAL, "block_tables/seq_lens must be int32 with B rows")
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (T, Hq)):
         raise PAError(PA_EINVAL, "lse must be fp32 [B * rows, H_q]")
-    for t in (out, query, kv_cache, block_tables, seq_lens, workspace, lse, plan):
-        if t is not None and not t.is_contiguous():
-            raise PAError(PA_EINVAL, "tensors must be contiguous")
     if plan is not None and plan.dtype != torch.int32:
         raise PAError(PA_EINVAL, "plan must be int32")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -507,9 +499,6 @@ def decode_fp8(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int, s
         raise PAError(PA_EINVAL, "block_tables/seq_lens must be int32 with B rows")
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq)):
         raise PAError(PA_EINVAL, "lse must be fp32 [B, H_q]")
-    for t in (out, query, kv_cache, block_tables, seq_lens, workspace, lse):
-        if t is not None and not t.is_contiguous():
-            raise PAError(PA_EINVAL, "tensors must be contiguous")
     if plan is not None and plan.dtype != torch.int32:
         raise PAError(PA_EINVAL, "plan must be int32")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -594,9 +583,6 @@ def attention_varlen(out, query, query_start_loc, kv_cache, block_tables, seq_le
         raise PAError(PA_EINVAL, "plan must be int32")
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (T, Hq)):
         raise PAError(PA_EINVAL, "lse must be fp32 [T, H_q]")
-    for t in (out, query, query_start_loc, kv_cache, block_tables, seq_lens, plan, workspace, lse):
-        if t is not None and not t.is_contiguous():
-            raise PAError(PA_EINVAL, "tensors must be contiguous")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pa_attention_varlen(_ptr(out), _ptr(lse), _ptr(query), _ptr(query_start_loc), T,
                                      _ptr(kv_cache), N, _ptr(block_tables), block_tables.shape[1],

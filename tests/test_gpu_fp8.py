@@ -87,16 +87,19 @@ def test_cache_write_bit_exact(scales, D):
 
 
 def test_cache_write_edge_values():
-    """Ties between neighbouring codes, saturation, subnormals, -0 (scale 1)."""
+    """Ties between neighbouring codes, saturation, subnormals, -0, +-inf
+    (saturate to +-448) and NaN of either sign (the NaN code 0x7F), scale 1."""
     from tests.gpu_setup import to_device
     special = np.array([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10, 2.0 ** -9, 464.0, 448.0,
                         496.0, 8192.0, -8192.0, -2.0 ** -12, 0.0, -0.0, 0.34375, 240.0, 232.0,
-                        2.0 ** -7, 17.0, -3.25, 0.015625], dtype=np.float32)
+                        2.0 ** -7, 17.0, -3.25, 0.015625, np.inf, -np.inf, np.nan,
+                        -np.float32(np.nan)], dtype=np.float32)
     D = 64
     row = np.resize(special, D).astype(np.float32)
     rows = np.stack([row, -row, row * 0.5, row * 3.0])              # 4 tokens
     bits = (rows.view(np.uint32) >> 16).astype(np.uint16)           # exact in bf16
-    assert np.array_equal((bits.astype(np.uint32) << 16).view(np.float32), rows)
+    assert np.array_equal((bits.astype(np.uint32) << 16).view(np.float32), rows, equal_nan=True)
+    assert np.isnan(rows).sum() >= 8 and np.isinf(rows).sum() >= 8
     key = bits.reshape(4, 1, D)
     val = bits[::-1].copy().reshape(4, 1, D)
     slots = np.array([0, 1, 17, -1], dtype=np.int64)                 # last token skipped

@@ -212,6 +212,50 @@ def test_large_pool_allocator():
     assert q[:3] == [N - 1, N - 2, N - 3] and max(rc) == 0
 
 
+def _recipe_tables(side, alloc, case, bs):
+    """Runs one case of the block-table fixture on the oracle or the library."""
+    if case["recipe"] == "decode":
+        L = case["seq_lens"]
+        width = max(-(-x // bs) for x in L)
+        if side == "oracle":
+            return oracle.build_decode_block_tables(alloc, L, bs, width)
+        return host.decode_block_tables(alloc, L, bs, width)
+    args = (alloc, case["num_seqs"], case["prefix_tokens"], case["own_tokens"], bs,
+            case["share_prefix"])
+    if side == "oracle":
+        return oracle.build_prefill_block_tables(*args)
+    return host.prefill_block_tables(*args)
+
+
+@pytest.mark.parametrize("side", ["oracle", "library"])
+def test_block_table_recipes_golden(side):
+    """Hand-derived tables, queues and refcounts of the decode and
+    shared-prefix recipes (tests/golden/block_table_recipes_n12.json): the
+    order of prefix shares, prefix copies and private allocations is fixed."""
+    g = _golden("block_table_recipes_n12.json")
+    for case in g["cases"]:
+        if side == "oracle":
+            a = oracle.OracleAllocator(g["num_blocks"], g["initial_order"])
+        else:
+            a = ops.Allocator(g["num_blocks"], g["initial_order"])
+        bt = _recipe_tables(side, a, case, g["block_size"])
+        np.testing.assert_array_equal(bt, np.array(case["table"], dtype=np.int32))
+        q, rc = a.export()
+        assert list(q) == case["queue"] and list(rc) == case["refcount"], case
+
+
+def test_block_table_recipe_golden_catches_interleaved_copies():
+    """A planted mistake in the oracle's prefix recipe (each unshared copy
+    followed at once by that sequence's private blocks) fails the fixture."""
+    g = _golden("block_table_recipes_n12.json")
+    case = next(c for c in g["cases"] if c["recipe"] == "prefill" and not c["share_prefix"])
+    a = oracle.OracleAllocator(g["num_blocks"], g["initial_order"])
+    npre = case["prefix_tokens"] // 16
+    nown = -(-case["own_tokens"] // 16)
+    wrong = [a.allocate(npre) + a.allocate(nown) for _ in range(case["num_seqs"])]
+    assert wrong != case["table"]
+
+
 @pytest.mark.parametrize("wl_index", [0, 1, 2, 3, 4])
 def test_block_tables_match_oracle(wl_index):
     d = inputs.draw(wl_index)
@@ -360,7 +404,7 @@ def _multi_status(**kw):
     (dict(rows=0), ops.PA_EINVAL),
     (dict(rows=65), ops.PA_EINVAL),
     (dict(dtype=ops.PA_F32), ops.PA_ENOTSUP),           # several rows need bf16
-    (dict(dtype=ops.PA_FP8), ops.PA_ENOTSUP),
+    (dict(dtype=ops.PA_FP8), ops.PA_EINVAL),            # needs pa_decode_multi_fp8
     (dict(hq=34, hkv=1), ops.PA_ENOTSUP),               # group 34 > 16
     (dict(P=16), ops.PA_EINVAL),                        # workspace missing
     (dict(P=16, ws=256, wsb=1024), ops.PA_EINVAL),      # workspace too small
@@ -459,6 +503,73 @@ def test_prefill_validation():
     st = L.pa_prefill_chunk(16, None, 16, 16, 4, 4, 16, 4, 16, 4, 16, 1, 64, 8, 2, 128, 16,
                             float("nan"), ops.PA_BF16, None)
     assert st == ops.PA_EINVAL, L.pa_last_error().decode()
+
+
+def test_fp8_dtype_refused_alike_by_every_entry_point_without_scales():
+    """An FP8 cache handed to an entry point that takes no scales is one and
+    the same argument error everywhere (the *_fp8 entry points carry them);
+    validation returns before anything is enqueued."""
+    L = ops.lib()
+    FP8, EINVAL = ops.PA_FP8, ops.PA_EINVAL
+    got = {
+        "pa_decode": _decode_status(dtype=FP8),
+        "pa_decode_append": _append_status(dtype=FP8),
+        "pa_decode_multi": _multi_status(dtype=FP8),
+        "pa_reshape_and_cache": (L.pa_reshape_and_cache(16, 16, 16, 4, 16, 4, 16, 2, 64, FP8,
+                                                        None), L.pa_last_error().decode()),
+        "pa_prefill_chunk": (L.pa_prefill_chunk(16, None, 16, 16, 4, 4, 16, 4, 16, 4, 16, 1, 64,
+                                                8, 2, 128, 16, 0.1, FP8, None),
+                             L.pa_last_error().decode()),
+        "pa_attention_varlen": _varlen_status(dtype=FP8),
+    }
+    for fn, (st, msg) in got.items():
+        assert st == EINVAL, (fn, st, msg)
+        assert fn in msg
+
+
+class _Strided:
+    """A CPU tensor view that is not contiguous (every other row)."""
+
+    @staticmethod
+    def rows(*shape, dtype=None):
+        import torch
+        full = torch.zeros((shape[0] * 2,) + tuple(shape[1:]), dtype=dtype or torch.bfloat16)
+        return full[::2]
+
+
+def test_binding_refuses_strided_tensors():
+    """A strided view (a slice of a fused QKV tensor, a sliced plan) would be
+    read as packed rows from its data pointer: every device wrapper refuses
+    it before anything reaches the library."""
+    import torch
+    bf, i32 = torch.bfloat16, torch.int32
+    q = _Strided.rows(4, 8, 64)
+    cache = torch.zeros((4, 2, 2, 16, 64), dtype=bf)
+    bt = torch.zeros((4, 4), dtype=i32)
+    sl = torch.ones(4, dtype=i32)
+    qsl = torch.arange(5, dtype=i32)
+    with pytest.raises(ops.PAError, match="contiguous"):
+        ops.prefill_chunk(torch.zeros((4, 8, 64), dtype=bf), q, qsl, 1, cache, bt, sl, 16, 0.1)
+    with pytest.raises(ops.PAError, match="contiguous"):
+        ops.prefill_chunk(torch.zeros((4, 8, 64), dtype=bf), torch.zeros((4, 8, 64), dtype=bf),
+                          qsl, 1, cache, bt[:, ::2], sl, 16, 0.1)
+    plan = torch.zeros(8, dtype=i32)[::2]
+    with pytest.raises(ops.PAError, match="contiguous"):
+        ops.decode(torch.zeros((4, 8, 64), dtype=bf), torch.zeros((4, 8, 64), dtype=bf), cache,
+                   bt, sl, 16, 0.1, 0, None, None, plan)
+    with pytest.raises(ops.PAError, match="contiguous"):
+        ops.decode_fp8(torch.zeros((4, 8, 64), dtype=bf), torch.zeros((4, 8, 64), dtype=bf),
+                       torch.zeros((4, 2, 2, 16, 64), dtype=torch.uint8), bt, sl, 16, 0.1, 1.0,
+                       1.0, 0, None, None, plan)
+    with pytest.raises(ops.PAError, match="contiguous"):
+        ops.decode_multi(torch.zeros((8, 8, 64), dtype=bf), torch.zeros((8, 8, 64), dtype=bf),
+                         cache, bt, sl, 16, 0.1, 2, 0, None, None, plan)
+    with pytest.raises(ops.PAError, match="contiguous"):
+        ops.attention_varlen(torch.zeros((4, 8, 64), dtype=bf), q, qsl, cache, bt, sl, 16, 0.1,
+                             torch.zeros(4, dtype=i32))
+    with pytest.raises(ops.PAError, match="contiguous"):
+        ops.reshape_and_cache(_Strided.rows(4, 2, 64), torch.zeros((4, 2, 64), dtype=bf),
+                              torch.zeros(4, dtype=torch.int64), cache)
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
