@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the paged-attention decode step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
 
 One step is the device half of a decode step of the engine for a batch of
 sequences: the new token's key/value of every sequence is written into its
@@ -10,20 +10,24 @@ context.  By default both happen in one launch (pa_decode_append; with
 split-K the partials are merged inside the same launch); --unfused runs
 pa_reshape_and_cache and pa_decode as two launches.  Host metadata (block
 tables from the free_block_queue allocator, slot mapping, the decode work
-plan) is built once before timing, as the engine's CPU side does ahead of
-the step, and its cost is reported separately.  The steps are replayed from
-a captured HIP graph, as the pages' engine replays pre-recorded graphs to cut
-launch overhead; the decode kernel's own duration is timed the same way from
-a graph of its launches alone (HIP events around the replays, on the stream
-the kernels run on).
+plan) is built before timing, as the engine's CPU side does ahead of the
+step, and its cost is reported separately: once from scratch, and as the
+incremental per-step update (one more token per sequence).  The steps are
+replayed from a captured HIP graph, as the pages' engine replays
+pre-recorded graphs to cut launch overhead; the decode kernel's own duration
+is timed the same way from a graph of its launches alone (HIP events around
+the replays, on the stream the kernels run on).
 
 Inputs are seeded synthetic draws (paged_attention_kv_block_amd.inputs) that
-are resident in HBM before timing.  The default workload is the
-TinyLlama-1.1B-shaped batch (64 sequences, 32/4 heads, head size 64, lengths
-uniform in [128, 2048], bf16).  Its pool (~79 MB) fits in the 256 MB
-Infinity Cache, so the step rotates over enough identical pool copies (>= 768
-MB) that each step reads its pool from HBM, as a real model's next visit to
-the same layer would.
+are resident in HBM before timing.  The default workload is the largest
+decode batch, the long-context one: 16 sequences of 32K-131K tokens (uniform),
+64/8 heads, head size 128, bf16, split-K over 1024-token partitions with the
+log-sum-exp merge (a 5.4 GB pool).  --workload 1 is the TinyLlama-1.1B-shaped
+batch (64 sequences, 32/4 heads, head size 64, lengths uniform in [128,
+2048]); its pool (~79 MB) fits in the 256 MB Infinity Cache, so the step
+rotates over enough identical pool copies (>= 768 MB) that each step reads
+its pool from HBM, as a real model's next visit to the same layer would.
+--workload 2 is the Llama-3-8B-shaped batch (256 sequences, split-K 512).
 
 Prints one JSON line: metric/value (algorithmic GB/s of the whole step),
 the HBM roofline of the dominant kernel (decode), and the fp64 CPU oracle
@@ -100,18 +104,19 @@ def decode_bytes(wl, seq_lens, kv_bytes=None) -> int:
     queries (1 for FP8)."""
     db = wl.dtype_bytes
     kb = db if kv_bytes is None else kv_bytes
+    n = len(seq_lens)
     kv = int(sum(int(L) for L in seq_lens)) * 2 * wl.num_kv_heads * wl.head_size * kb
-    qo = 2 * wl.num_seqs * wl.num_q_heads * wl.head_size * db
+    qo = 2 * n * wl.num_q_heads * wl.head_size * db
     bt = sum((int(L) + wl.block_size - 1) // wl.block_size for L in seq_lens) * 4
-    return kv + qo + bt + 4 * wl.num_seqs
+    return kv + qo + bt + 4 * n
 
 
-def cache_write_bytes(wl, kv_bytes=None) -> int:
+def cache_write_bytes(wl, kv_bytes=None, num_seqs=None) -> int:
     """Writing one new token per sequence into the cache: read its K and V
     rows, write them (as kv_bytes-wide elements for an FP8 cache)."""
     row = wl.num_kv_heads * wl.head_size * wl.dtype_bytes
     out_row = row if kv_bytes is None else wl.num_kv_heads * wl.head_size * kv_bytes
-    return wl.num_seqs * 2 * (row + out_row)
+    return (wl.num_seqs if num_seqs is None else num_seqs) * 2 * (row + out_row)
 
 
 def load_traffic(kernel_hash: str, unfused: bool, path=None):
@@ -128,24 +133,58 @@ def load_traffic(kernel_hash: str, unfused: bool, path=None):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(d, min_seconds: float, fp8_scales=None):
-    """The fp64 oracle (as it stands) on this host: the same step (write the
-    new tokens, decode) repeated until min_seconds of CPU time; BLAS limited
-    to one thread so `cores` is what it used.  fp8_scales = (k, v): the FP8
-    cache step (quantise the new tokens, decode the codes)."""
+def host_cores() -> int:
+    """CPU cores this process may run on (its affinity mask)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
+def oracle_sample(d, max_tokens: int, seed: int = 4242):
+    """A seeded subset of the batch's sequences for the CPU oracle: sequences
+    in a seeded random order until their context tokens reach max_tokens
+    (at least one sequence); all of them when the batch is that small."""
+    import numpy as np
+    L = d.seq_lens
+    if int(L.sum()) <= max_tokens:
+        return list(range(len(L)))
+    picked, tot = [], 0
+    for b in np.random.default_rng(seed).permutation(len(L)):
+        picked.append(int(b))
+        tot += int(L[b])
+        if tot >= max_tokens:
+            break
+    return sorted(picked)
+
+
+def cpu_baseline(d, min_seconds: float, fp8_scales=None, max_tokens: int = 200_000):
+    """The fp64 oracle (as it stands) on this host: the decode step (write the
+    new token, decode) of a seeded sample of the batch's sequences (the whole
+    batch when it holds at most max_tokens context tokens), repeated until
+    min_seconds of CPU time; BLAS limited to one thread, so one core is what
+    it uses.  fp8_scales = (k, v): the FP8 cache step (quantise the new
+    tokens, decode the codes).  Returns (seconds per pass, passes, sample)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     import oracle
     from tests.oracle_setup import OracleSide
 
     wl = d.wl
-    side = OracleSide(d)   # allocator, tables and the full cache (setup, untimed)
+    seqs = oracle_sample(d, max_tokens)
+    # allocator, tables and the sample's cache (setup, untimed)
+    side = OracleSide(d, seqs=seqs, fill_pool=fp8_scales is None)
     if fp8_scales is not None:
-        side.pool = np.stack([oracle.quantize(side.pool[:, 0], fp8_scales[0]),
-                              oracle.quantize(side.pool[:, 1], fp8_scales[1])], axis=1)
+        ks, vs = fp8_scales
+        side.pool = oracle.empty_pool(d.num_blocks, wl.num_kv_heads, wl.block_size,
+                                      wl.head_size, np.uint8, fill=np.uint8(0x7F))
+        for b in seqs:
+            k, v = d.kv(b)
+            oracle.reshape_and_cache(side.pool, oracle.quantize(k, ks), oracle.quantize(v, vs),
+                                     side.slots_for(b, 0, int(d.seq_lens[b])))
     q = d.query()
     new_k, new_v, slots = [], [], []
-    for b in range(wl.num_seqs):
+    for b in seqs:
         L = int(d.seq_lens[b])
         k, v = d.kv(b)
         new_k.append(k[L - 1])
@@ -157,18 +196,46 @@ def cpu_baseline(d, min_seconds: float, fp8_scales=None):
         while True:
             if fp8_scales is None:
                 oracle.reshape_and_cache(side.pool, new_k, new_v, slots)
-                oracle.decode(q, side.pool, side.block_tables, d.seq_lens, wl.scale)
+                oracle.decode(q, side.pool, side.block_tables, d.seq_lens, wl.scale, seqs=seqs)
             else:
                 ks, vs = fp8_scales
                 oracle.reshape_and_cache(side.pool, oracle.quantize(new_k, ks),
                                          oracle.quantize(new_v, vs), slots)
-                oracle.decode(q, side.pool, side.block_tables, d.seq_lens, wl.scale,
+                oracle.decode(q, side.pool, side.block_tables, d.seq_lens, wl.scale, seqs=seqs,
                               k_scale=ks, v_scale=vs)
             reps += 1
             if time.perf_counter() - t0 >= min_seconds:
                 break
     dt = (time.perf_counter() - t0) / reps
-    return dt, reps
+    return dt, reps, seqs
+
+
+def host_step_us(d, partition_size: int, steps: int = 200) -> float:
+    """Host metadata of one decode step, updated incrementally as the engine's
+    CPU side does it between steps: every running sequence gains one token;
+    a sequence whose new token starts a block takes one block from the
+    free_block_queue (libpa allocator) into its table row; the new tokens'
+    slots and the work plan are rebuilt.  Average over `steps` consecutive
+    steps, in microseconds (the uploads of the changed rows are not
+    included)."""
+    import numpy as np
+    from paged_attention_kv_block_amd import host, ops
+    bs = d.wl.block_size
+    L = np.ascontiguousarray(d.seq_lens, dtype=np.int32).copy()
+    width = int(max(-(-int(x) // bs) for x in L)) + steps // bs + 2
+    extra = int(sum(-(-(int(x) + steps) // bs) - -(-int(x) // bs) for x in L))
+    alloc = ops.Allocator(max(d.num_blocks, int(sum(-(-int(x) // bs) for x in L)) + extra),
+                          None)
+    bt = host.decode_block_tables(alloc, L, bs, width)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        cross = np.flatnonzero(L % bs == 0)       # the new token opens a block
+        if cross.size:
+            bt[cross, L[cross] // bs] = alloc.allocate(int(cross.size))
+        ops.slot_mapping(bt, L, 1, bs)
+        L += 1
+        ops.decode_plan(L, int(L.max()), partition_size)
+    return (time.perf_counter() - t0) * 1e6 / steps
 
 
 def prefill_flops(seq_lens, chunk_lens, num_q_heads: int, head_size: int) -> int:
@@ -329,7 +396,8 @@ def bench_prefill(a, d, dev):
             "shared_prefix_tokens": wl.prefix_tokens, "max_seq_len": msl,
             "pool_blocks": d.num_blocks, "pool_copies_rotated": R, "parallelism": "none (1 GPU)",
         },
-        "host_metadata_us": round(host_us, 1),
+        "host_metadata_us": round(host_us, 1),            # from scratch: allocator, tables
+        "host_step_us": round(step_host_us, 2),           # per step, incremental update
         "roofline": {
             "kernel": "pa_prefill_chunk (prefill_chunk_kernel)",
             "bound": "mfma",
@@ -559,7 +627,8 @@ def bench_mixed(a, dev):
             "context_tokens": int(seq_lens.sum()), "max_seq_len": msl, "partition_size": P,
             "pool_blocks": d.num_blocks, "parallelism": "none (1 GPU)",
         },
-        "host_metadata_us": round(host_us, 1),
+        "host_metadata_us": round(host_us, 1),            # from scratch: allocator, tables
+        "host_step_us": round(step_host_us, 2),           # per step, incremental update
         "step_us_one_launch": round(step_us, 2),
         "step_us_two_launches": round(sep_us, 2),
         "attention_us_one_launch": round(var_us, 2),
@@ -1004,8 +1073,9 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=1,
-                    help="workload index: decode 1, 2, 4 (0 = tiny); 3 = chunked prefill")
+    ap.add_argument("--workload", type=int, default=4,
+                    help="workload index: decode 1, 2, 4 (0 = tiny); 3 = chunked prefill; "
+                         "default 4, the long-context batch (the largest decode workload)")
     ap.add_argument("--mixed", action="store_true",
                     help="a flattened continuous-batching step: 16 prefill chunks and 240 "
                          "decode rows in one pa_attention_varlen launch")
@@ -1091,6 +1161,7 @@ def main(argv=None):
     new_slots = ops.slot_mapping(bt, seq_lens - 1, 1, bs)
     plan = ops.decode_plan(seq_lens, msl, P)
     host_us = (time.perf_counter() - t0) * 1e6
+    step_host_us = host_step_us(d, P)
 
     # ---- device inputs: cache holds tokens 0..L-2; the step writes token L-1
     pool_shape = (d.num_blocks, 2, Hkv, bs, D)
@@ -1268,7 +1339,8 @@ def main(argv=None):
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "context_tokens_per_s": round(ctx / (ms_step * 1e-3), 1),
-        "host_metadata_us": round(host_us, 1),
+        "host_metadata_us": round(host_us, 1),            # from scratch: allocator, tables
+        "host_step_us": round(step_host_us, 2),           # per step, incremental update
         "step_us_eager_launches": round(eager_us, 2),   # no graph: host launch per step
         "measured_copy_gbs": round(copy_gbs, 1),          # 1 GiB device copy, read + write
         "roofline": {
@@ -1289,15 +1361,24 @@ def main(argv=None):
         },
     }
     if not a.no_cpu_baseline:
-        dt, reps = cpu_baseline(d, a.cpu_seconds, (k_scale, v_scale) if fp8 else None)
+        dt, reps, seqs = cpu_baseline(d, a.cpu_seconds, (k_scale, v_scale) if fp8 else None)
+        sub = d.seq_lens[seqs]
+        sample_bytes = decode_bytes(wl, sub, kvb) + cache_write_bytes(wl, kvb, len(seqs))
+        sctx = int(sub.sum())
+        what = (f"the whole {wl.name} step" if len(seqs) == B else
+                f"{len(seqs)} of the {B} sequences of the {wl.name} step (seeded choice: "
+                f"sequences {seqs}, lengths {[int(x) for x in sub]})")
         res["cpu_baseline"] = {
-            "value": round(step_bytes / dt / 1e9, 4),
+            "value": round(sample_bytes / dt / 1e9, 4),
             "unit": "GB/s",
             "cores": 1,
+            "host_cores": host_cores(),
+            "blas_threads": 1,
+            "context_tokens_per_s": round(sctx / dt, 1),
             "kind": "oracle",
-            "sample": f"the whole {wl.name} step (write {B} new tokens, decode {B} sequences, "
-                      f"{ctx} context tokens) repeated {reps}x; fp64 numpy, BLAS 1 thread; "
-                      f"{dt * 1e3:.1f} ms per step",
+            "sample": f"{what}: write the new tokens, decode ({sctx} context tokens), "
+                      f"repeated {reps}x; fp64 numpy on one core (BLAS 1 thread); "
+                      f"{dt * 1e3:.1f} ms per pass",
         }
     print(json.dumps(res), flush=True)
     return 0

@@ -47,12 +47,16 @@ def check_pool(o, g):
         np.testing.assert_array_equal(got, o.pool)
 
 
-def run_decode_case(d, partition_size=None, seqs=None, check_pool_bits=True, use_plan=False):
+def run_decode_case(d, partition_size=None, seqs=None, check_pool_bits=True, use_plan=False,
+                    full_pool=False):
+    """seqs limits the oracle's attention to a sample of sequences; with
+    full_pool the oracle still fills every sequence, so the whole GPU pool is
+    compared bit for bit (its scatter is a cheap host loop)."""
     GpuSide, _ = _gpu()
-    o = OracleSide(d, seqs=seqs)
+    o = OracleSide(d, seqs=None if full_pool else seqs)
     g = GpuSide(d)
     check_tables(o, g)
-    if check_pool_bits and seqs is None:
+    if check_pool_bits and (seqs is None or full_pool):
         check_pool(o, g)
     out, lse = g.decode(partition_size=partition_size, use_plan=use_plan)
     ref, ref_lse = o.decode(seqs=seqs)
@@ -160,8 +164,17 @@ def test_llama3_workload_sampled():
     d = inputs.draw(2)
     L = d.seq_lens
     seqs = sorted({int(np.argmax(L)), int(np.argmin(L)), 0, 1, 100, 255})
-    run_decode_case(d, partition_size=512, seqs=seqs, use_plan=True)
+    run_decode_case(d, partition_size=512, seqs=seqs, use_plan=True, full_pool=True)
     run_decode_case(d, partition_size=512, seqs=seqs[:3], use_plan=False)
+
+
+def test_llama3_workload_more_sequences():
+    """The same launch on 24 more sequences spread over the length range
+    (every 11th by length), so the sample covers one to sixteen partitions."""
+    d = inputs.draw(2)
+    order = np.argsort(d.seq_lens, kind="stable")
+    seqs = sorted(int(x) for x in order[::11][:24])
+    run_decode_case(d, partition_size=512, seqs=seqs, use_plan=True)
 
 
 def test_long_context_workload_sampled():
@@ -243,7 +256,10 @@ def test_workspace_reused_across_calls_and_shapes():
 def test_decode_step_in_a_hip_graph():
     """The decode step (cache write + split-K decode) captured in a HIP graph
     and replayed several times, with eager work between replays: every
-    replay matches the eager result bit for bit."""
+    replay matches the eager result bit for bit, and the eager result
+    matches the oracle's reshape_and_cache of the same new K/V followed by
+    its decode (pool bit for bit, outputs within the bf16 bar)."""
+    import oracle
     from paged_attention_kv_block_amd import ops
     from tests.gpu_setup import GpuSide, to_device
     d = inputs.draw(1)
@@ -255,6 +271,13 @@ def test_decode_step_in_a_hip_graph():
     newk = torch.zeros((wl.num_seqs, wl.num_kv_heads, wl.head_size), dtype=torch.bfloat16, device="cuda")
     newv = torch.ones_like(newk)
     slots = torch.from_numpy(ops.slot_mapping(g.block_tables, L - 1, 1, 16)).cuda()
+    o = OracleSide(d)
+    zero = np.zeros((wl.num_seqs, wl.num_kv_heads, wl.head_size), dtype=np.uint16)
+    one = np.full_like(zero, 0x3F80)                     # bf16 1.0
+    oracle.reshape_and_cache(o.pool, zero, one,
+                             np.array([o.slots_for(b, int(L[b]) - 1, 1)[0]
+                                       for b in range(wl.num_seqs)]))
+    ref, _ = o.decode()
     ws = ops.decode_workspace(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_size, msl, 256)
     out = torch.empty_like(q)
 
@@ -269,6 +292,9 @@ def test_decode_step_in_a_hip_graph():
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     eager = out.clone()
+    check_pool(o, g)
+    err = np.max(np.abs(out_f64(eager) - ref))
+    assert err <= TOL["bf16"], err
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step()
@@ -278,6 +304,7 @@ def test_decode_step_in_a_hip_graph():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), rep
+    check_pool(o, g)
 
 
 def test_split_k_partials_never_stale():

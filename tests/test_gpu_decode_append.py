@@ -21,9 +21,11 @@ pytestmark = [pytest.mark.gpu,
 TOL = {"f32": 1e-5, "bf16": 2e-2}
 
 
-def _append_case(d, P=0, use_plan=False, rounds=1):
-    from tests.gpu_setup import GpuSide, from_device, to_device, empty_pool
-    import oracle
+def _prepare(d):
+    """Oracle side with every token cached; GPU side with every token but
+    each sequence's last (its slot keeps the NaN poison); the new tokens'
+    K/V as GPU tensors."""
+    from tests.gpu_setup import GpuSide, to_device, empty_pool
     wl = d.wl
     bs = wl.block_size
     o = OracleSide(d)
@@ -48,19 +50,14 @@ def _append_case(d, P=0, use_plan=False, rounds=1):
                               torch.from_numpy(np.concatenate(sl).astype(np.int64)).cuda(), g.pool)
     new_k = to_device(np.stack(nk), wl)
     new_v = to_device(np.stack(nv), wl)
+    return o, g, new_k, new_v
 
-    q = to_device(d.query(), wl)
-    out = torch.empty_like(q)
-    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
-    msl = int(max(d.seq_lens)) if wl.num_seqs else 0
-    ws = ops.decode_workspace(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_size, msl, P,
-                              "cuda")
-    plan = torch.from_numpy(ops.decode_plan(d.seq_lens, msl, P)).cuda() if use_plan else None
-    for _ in range(rounds):  # a repeated call rewrites the same values
-        ops.decode(out, q, g.pool, g.bt_dev, g.seq_lens_dev, msl, float(wl.scale), P, ws, lse,
-                   plan, new_key=new_k, new_value=new_v)
-    torch.cuda.synchronize()
 
+def _check(d, o, g, out, lse):
+    """Pool bit for bit against the oracle's; outputs and lse within the bar."""
+    from tests.gpu_setup import from_device
+    import oracle
+    wl = d.wl
     got_pool = from_device(g.pool)
     if got_pool.dtype == np.float32:
         np.testing.assert_array_equal(got_pool.view(np.uint32), o.pool.view(np.uint32))
@@ -77,6 +74,24 @@ def _append_case(d, P=0, use_plan=False, rounds=1):
     assert err <= tol, f"max abs error {err} > {tol}"
     assert lerr <= tol, f"lse max abs error {lerr} > {tol}"
     return err
+
+
+def _append_case(d, P=0, use_plan=False, rounds=1):
+    from tests.gpu_setup import to_device
+    wl = d.wl
+    o, g, new_k, new_v = _prepare(d)
+    q = to_device(d.query(), wl)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    msl = int(max(d.seq_lens)) if wl.num_seqs else 0
+    ws = ops.decode_workspace(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_size, msl, P,
+                              "cuda")
+    plan = torch.from_numpy(ops.decode_plan(d.seq_lens, msl, P)).cuda() if use_plan else None
+    for _ in range(rounds):  # a repeated call rewrites the same values
+        ops.decode(out, q, g.pool, g.bt_dev, g.seq_lens_dev, msl, float(wl.scale), P, ws, lse,
+                   plan, new_key=new_k, new_value=new_v)
+    torch.cuda.synchronize()
+    return _check(d, o, g, out, lse)
 
 
 @pytest.mark.parametrize("P", [0, 16, 48])
@@ -125,3 +140,45 @@ def test_many_items():
     d = inputs.custom(kind="decode", seq_lens=tuple(int(x) for x in lens), num_q_heads=32,
                       num_kv_heads=8, head_size=128, seed=11)
     _append_case(d, P=0, use_plan=True)
+
+
+@pytest.mark.parametrize("P", [0, 256])
+def test_fused_step_in_a_hip_graph(P):
+    """The fused decode step bench.py replays (pa_decode_append with the
+    plan; split-K or one pass) captured in a HIP graph: the first replay
+    writes the new tokens and matches the oracle (pool bit for bit, outputs
+    within the bar); later replays, with eager work between them, rewrite
+    the same values and equal it bit for bit."""
+    from tests.gpu_setup import to_device
+    d = inputs.draw(1)
+    wl = d.wl
+    o, g, new_k, new_v = _prepare(d)
+    q = to_device(d.query(), wl)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    msl = int(max(d.seq_lens))
+    ws = ops.decode_workspace(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_size, msl, P)
+    plan = torch.from_numpy(ops.decode_plan(d.seq_lens, msl, P)).cuda()
+    # warm-up of the same launch on a copy of the pool, outside the capture
+    ops.decode(torch.empty_like(out), q, g.pool.clone(), g.bt_dev, g.seq_lens_dev, msl,
+               float(wl.scale), P, ws, None, plan, new_key=new_k, new_value=new_v)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):      # captured only: nothing runs yet
+        ops.decode(out, q, g.pool, g.bt_dev, g.seq_lens_dev, msl, float(wl.scale), P, ws, lse,
+                   plan, new_key=new_k, new_value=new_v)
+    torch.cuda.synchronize()
+    first = None
+    for rep in range(4):
+        out.fill_(float("nan"))
+        _ = (q.float() * 2).sum()                # unrelated eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        if first is None:
+            _check(d, o, g, out, lse)
+            first = (out.clone(), lse.clone())
+        else:
+            assert torch.equal(out.view(torch.int16), first[0].view(torch.int16)), rep
+            assert torch.equal(lse, first[1]), rep

@@ -198,22 +198,34 @@ def test_decode_fp8_needs_its_entry_point():
 # ---------------------------------------------------------------------------
 # decode with the new token's cache write fused (pa_decode_append_fp8)
 # ---------------------------------------------------------------------------
-def _append_case(d, P=0, use_plan=False, rounds=1):
+def _append_case(d, P=0, use_plan=False, rounds=1, seqs=None, check=None):
     """GPU pool: every token but each sequence's last through
     pa_reshape_and_cache_fp8, the last written by pa_decode_append_fp8.
-    Oracle pool: every token through the oracle quantiser."""
+    Oracle pool: every token through the oracle quantiser.  ``seqs`` limits
+    both pools to a sample of sequences (the others' new token is zero on
+    both sides, their other slots keep the NaN code), ``check`` the oracle's
+    attention to a sample; the pools are compared whole either way."""
     from tests.gpu_setup import GpuSide, from_device, to_device
     from tests.oracle_setup import OracleSide
     wl = d.wl
-    ks, vs = _data_scales(d)
+    ks, vs = _data_scales(d, seqs)
     o = OracleSide(d, fill_pool=False)
     g = GpuSide(d, fill=False)
     np.testing.assert_array_equal(g.block_tables, o.block_tables)
     opool = oracle.empty_pool(d.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_size,
                               np.uint8, fill=np.uint8(POISON))
     keys, vals, sl, nk, nv = [], [], [], [], []
+    filled = set(range(wl.num_seqs) if seqs is None else seqs)
+    z = np.zeros((wl.num_kv_heads, wl.head_size), dtype=np.uint16)
     for b in range(wl.num_seqs):
         L = int(d.seq_lens[b])
+        if b not in filled:
+            if L > 0:
+                zq = oracle.quantize(z[None], 1.0)
+                oracle.reshape_and_cache(opool, zq, zq, o.slots_for(b, L - 1, 1))
+            nk.append(z)
+            nv.append(z)
+            continue
         k, v = d.kv(b)
         if L > 0:
             oracle.reshape_and_cache(opool, oracle.quantize(k, ks), oracle.quantize(v, vs),
@@ -222,7 +234,6 @@ def _append_case(d, P=0, use_plan=False, rounds=1):
             keys.append(k[:L - 1])
             vals.append(v[:L - 1])
             sl.append(ops.slot_mapping(g.block_tables[b], 0, L - 1, wl.block_size))
-        z = np.zeros((wl.num_kv_heads, wl.head_size), dtype=np.uint16)
         nk.append(k[L - 1] if L > 0 else z)
         nv.append(v[L - 1] if L > 0 else z)
     gpool = torch.full(_pool_shape(d), POISON, dtype=torch.uint8, device="cuda")
@@ -244,17 +255,73 @@ def _append_case(d, P=0, use_plan=False, rounds=1):
                        ws, lse, plan, new_key=new_k, new_value=new_v)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(gpool.cpu().numpy(), opool)
+    if check is None:
+        check = None if seqs is None else sorted(filled)
+    rows = list(range(wl.num_seqs)) if check is None else list(check)
     ref, ref_lse = oracle.decode(d.query(), opool, o.block_tables, d.seq_lens, wl.scale,
-                                 k_scale=ks, v_scale=vs)
-    got = oracle.to_f64(from_device(out))
+                                 seqs=check, k_scale=ks, v_scale=vs)
+    got = oracle.to_f64(from_device(out))[rows]
+    ref, ref_lse = ref[rows], ref_lse[rows]
     assert np.all(np.isfinite(got))
     err = np.max(np.abs(got - ref))
-    got_lse = lse.cpu().numpy().astype(np.float64)
+    got_lse = lse.cpu().numpy().astype(np.float64)[rows]
     both_empty = np.isneginf(got_lse) & np.isneginf(ref_lse)
     lerr = np.max(np.abs(np.where(both_empty, 0.0, got_lse - np.where(both_empty, 0.0, ref_lse))))
     assert err <= TOL, f"max abs error {err} > {TOL}"
     assert lerr <= TOL, f"lse max abs error {lerr} > {TOL}"
     return err
+
+
+# Many short ragged sequences, so that the FP8 launches take their 4-wave
+# (from 2 items per compute unit) and 2-wave (from 8) workgroup variants,
+# which have register budgets of their own.
+MANY = [
+    ("many-g8-d64-b300", 300, 32, 4, 64),     # 1 200 items: 4-wave workgroups
+    ("many-g8-d64-b600", 600, 32, 4, 64),     # 2 400 items: 2-wave workgroups
+    ("many-g4-d128-b600", 600, 32, 8, 128),   # 4 800 items
+]
+
+
+def _many(B, hq, hkv, D):
+    rng = np.random.default_rng(B + D + 1)
+    lens = rng.integers(1, 97, B)
+    lens[:3] = (1, 16, 17)
+    return inputs.custom(kind="decode", seq_lens=tuple(int(x) for x in lens), num_q_heads=hq,
+                         num_kv_heads=hkv, head_size=D, seed=B + 1)
+
+
+@pytest.mark.parametrize("name,B,hq,hkv,D", MANY, ids=[m[0] for m in MANY])
+@pytest.mark.parametrize("P,use_plan", [(0, True), (0, False), (32, True)])
+def test_decode_fp8_many_items(name, B, hq, hkv, D, P, use_plan):
+    _decode_case(_many(B, hq, hkv, D), P=P, use_plan=use_plan)
+
+
+@pytest.mark.parametrize("name,B,hq,hkv,D", MANY, ids=[m[0] for m in MANY])
+@pytest.mark.parametrize("P,use_plan", [(0, True), (0, False), (32, True)])
+def test_decode_append_fp8_many_items(name, B, hq, hkv, D, P, use_plan):
+    _append_case(_many(B, hq, hkv, D), P=P, use_plan=use_plan)
+
+
+def test_decode_append_fp8_llama3_workload():
+    """The Llama-3-shaped batch at full size in the launch bench.py times
+    (split-K 512, plan): every sequence in both pools (compared whole), the
+    oracle's attention on a sample spread over the length range."""
+    d = inputs.draw(2)
+    order = np.argsort(d.seq_lens, kind="stable")
+    check = sorted({int(x) for x in order[::16]} | {int(order[0]), int(order[-1])})
+    err = _append_case(d, P=512, use_plan=True, check=check)
+    print("llama3 fp8 append max err", err)
+
+
+def test_decode_append_fp8_long_context_workload():
+    """The long-context batch at full size (16 sequences of 32K-131K tokens)
+    in the launch bench.py times (split-K 1024, plan): the longest and the
+    shortest sequence in both pools; the others' new token only."""
+    d = inputs.draw(4)
+    L = d.seq_lens
+    seqs = sorted({int(np.argmax(L)), int(np.argmin(L))})
+    err = _append_case(d, P=1024, use_plan=True, seqs=seqs)
+    print("long-context fp8 append max err", err)
 
 
 @pytest.mark.parametrize("name,kw", CASES[:4], ids=[c[0] for c in CASES[:4]])

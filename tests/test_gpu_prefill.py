@@ -23,13 +23,16 @@ def _f64(t):
     return oracle.to_f64(from_device(t))
 
 
-def run_prefill_case(d, seqs=None, check_pool=True):
+def run_prefill_case(d, seqs=None, check_pool=True, full_pool=False):
+    """seqs limits the oracle's attention to a sample of sequences; with
+    full_pool the oracle still fills every sequence and the whole GPU pool
+    is compared bit for bit."""
     from tests.gpu_setup import GpuSide, from_device
-    o = OracleSide(d, seqs=seqs)
+    o = OracleSide(d, seqs=None if full_pool else seqs)
     g = GpuSide(d)
     np.testing.assert_array_equal(g.block_tables, o.block_tables)
     assert g.alloc.export() == o.alloc.export()
-    if check_pool and seqs is None:
+    if check_pool and (seqs is None or full_pool):
         np.testing.assert_array_equal(from_device(g.pool), o.pool)
     out, lse = g.prefill()
     ref, ref_lse = o.prefill(seqs=seqs)
@@ -92,9 +95,10 @@ def test_shared_prefix_equals_unshared_copies_bit_exact():
 
 
 def test_chunked_prefill_workload_sampled():
-    """The 16-sequence shared-prefix workload at full size; the oracle checks
-    the first and last sequence (all 256 queries, all heads)."""
-    run_prefill_case(inputs.draw(3), seqs=[0, 15])
+    """The 16-sequence shared-prefix workload at full size: the whole pool
+    bit for bit; the oracle's attention on four sequences (all 256 queries,
+    all heads)."""
+    run_prefill_case(inputs.draw(3), seqs=[0, 5, 10, 15], full_pool=True)
 
 
 def test_chunked_prefill_workload_shared_vs_copies():
