@@ -365,6 +365,30 @@ int pa_decode_fp8(void* out, float* lse_out, const void* query,
                   int32_t plan_entries, void* workspace, size_t workspace_bytes,
                   void* stream);
 
+/* pa_decode_append without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Its split-K counters and
+ * partial records live in a static device array of
+ * PA_NOALLOC_SCRATCH_BYTES bytes inside the library, one per device the
+ * library runs on, held until the process ends; the call allocates
+ * nothing.  Inputs, outputs and errors as pa_decode_append; additionally
+ * PA_EINVAL when the split-K layout (pa_decode_workspace_bytes of the same
+ * sizes) exceeds PA_NOALLOC_SCRATCH_BYTES, and PA_EHIP when the runtime
+ * cannot resolve the array's device address.  The first call on a device
+ * clears the array's counters on `stream` (a fill kernel); every completed
+ * call leaves them at zero.  All calls on one device share the array:
+ * calls that overlap on one GPU (two streams, two threads) race and give
+ * wrong results. */
+#define PA_NOALLOC_SCRATCH_BYTES (128u << 20)
+int pa_decode_append_noalloc(void* out, float* lse_out, const void* query,
+                             const void* new_key, const void* new_value, void* kv_cache,
+                             int32_t num_blocks, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t B,
+                             int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_size, int32_t block_size, float scale,
+                             int32_t partition_size, const int32_t* plan, int32_t plan_entries,
+                             int32_t dtype, void* stream);
+
 /* pa_decode_append for an FP8 cache: the new token of every sequence is
  * quantised exactly as pa_reshape_and_cache_fp8 does (new_key/new_value
  * bf16 [B][H_kv][D], 16-byte aligned; k_scale/v_scale), written to its slot

@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <vector>
 
 #include "pa.h"
@@ -19,6 +20,15 @@ __global__ void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
 }
+
+// Scratch of pa_decode_append_noalloc: the split-K arrival counters and
+// partial records of its launches live in this file-scope device array
+// instead of a caller workspace.  Each device the library runs on holds its
+// own copy until the process ends.  Host code never takes its address
+// directly (in host code the name is only a stand-in): noalloc_scratch()
+// asks the runtime for the device address, once per device.
+constexpr size_t kNoallocScratchBytes = PA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
 
 // ---------------------------------------------------------------------------
 // host side
@@ -464,4 +474,71 @@ extern "C" int pa_decode_multi_fp8(void* out, float* lse_out, const void* query,
                      num_q_heads, num_kv_heads, head_size, block_size, scale, k_scale, v_scale,
                      partition_size, plan, plan_entries, workspace, workspace_bytes, PA_FP8,
                      stream, rows);
+}
+
+// Device address of this device's scratch array, looked up once per device
+// (with that device current), and its arrival counters cleared on the
+// caller's stream by a fill kernel at that first call: every completed
+// call leaves them at zero again.  nullptr on a runtime error.
+static uint8_t* noalloc_scratch(hipStream_t stream) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static uint8_t* ptrs[kMaxDev] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    fail(PA_EHIP, "pa_decode_append_noalloc: no current device (or more than %d)", kMaxDev);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev]) return ptrs[dev];
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) {
+    fail(PA_EHIP, "pa_decode_append_noalloc: hipGetSymbolAddress(scratch) failed: %s",
+         hipGetErrorString(e));
+    return nullptr;
+  }
+  const int64_t n = ws_layout(1, 1, 1, 64, 1).rec_off / 4;   // the counter region
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((n + 255) / 256), dim3(256), 0, stream,
+                     static_cast<uint32_t*>(p), n);
+  const hipError_t le = hipGetLastError();
+  if (le != hipSuccess) {
+    fail(PA_EHIP, "pa_decode_append_noalloc: clearing the scratch failed: %s",
+         hipGetErrorString(le));
+    return nullptr;
+  }
+  ptrs[dev] = static_cast<uint8_t*>(p);
+  return ptrs[dev];
+}
+
+extern "C" int pa_decode_append_noalloc(void* out, float* lse_out, const void* query,
+                                        const void* new_key, const void* new_value,
+                                        void* kv_cache, int32_t num_blocks,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* seq_lens, int32_t B, int32_t max_seq_len,
+                                        int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_size, int32_t block_size, float scale,
+                                        int32_t partition_size, const int32_t* plan,
+                                        int32_t plan_entries, int32_t dtype, void* stream) {
+  const char* fn = "pa_decode_append_noalloc";
+  if (dtype == PA_FP8)
+    return fail(PA_EINVAL, "%s: an FP8 cache needs pa_decode_append_fp8 (its scales)", fn);
+  if (B > 0 && (!new_key || !new_value)) return fail(PA_EINVAL, "%s: NULL new_key/new_value", fn);
+  if (B < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 || partition_size < 0)
+    return fail(PA_EINVAL, "%s: bad sizes", fn);
+  const size_t need = pa_decode_workspace_bytes(B, num_q_heads, num_kv_heads, head_size,
+                                                max_seq_len, partition_size);
+  if (need > kNoallocScratchBytes)
+    return fail(PA_EINVAL, "%s: split-K needs %zu bytes of scratch, the static scratch holds %zu "
+                "(fewer sequences or partitions, or pa_decode_append with a workspace)",
+                fn, need, kNoallocScratchBytes);
+  uint8_t* ws = nullptr;
+  if (need > 0 && B > 0) {
+    ws = noalloc_scratch(reinterpret_cast<hipStream_t>(stream));
+    if (!ws) return PA_EHIP;
+  }
+  return decode_call(fn, out, lse_out, query, new_key, new_value, kv_cache, num_blocks,
+                     block_tables, max_blocks_per_seq, seq_lens, B, max_seq_len, num_q_heads,
+                     num_kv_heads, head_size, block_size, scale, 1.f, 1.f, partition_size, plan,
+                     plan_entries, ws, ws ? kNoallocScratchBytes : 0, dtype, stream);
 }

@@ -57,6 +57,9 @@ SIGNATURES = {
     "pa_decode_append": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _vp,
                                   _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _f, _c_i32,
                                   _vp, _c_i32, _vp, _c_sz, _c_i32, _vp]),
+    "pa_decode_append_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _vp,
+                                          _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _f,
+                                          _c_i32, _vp, _c_i32, _c_i32, _vp]),
     "pa_decode_fp8": (_c_int, [_vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _vp, _c_i32, _c_i32,
                                _c_i32, _c_i32, _c_i32, _c_i32, _f, _f, _f, _c_i32, _vp, _c_i32,
                                _vp, _c_sz, _vp]),
@@ -393,6 +396,42 @@ def decode(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int, scale
                                      "in the cache dtype")
     _check(lib().pa_decode_append(_ptr(out), _ptr(lse), _ptr(query), _ptr(new_key),
                                   _ptr(new_value), _ptr(kv_cache), *tail))
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20   # PA_NOALLOC_SCRATCH_BYTES
+
+
+def decode_append_noalloc(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int,
+                          scale: float, new_key, new_value, partition_size: int = 0, lse=None,
+                          plan=None, stream=None) -> None:
+    """pa_decode_append_noalloc: decode(..., new_key=, new_value=) without a
+    workspace; split-K runs in the library's static device scratch
+    (NOALLOC_SCRATCH_BYTES per device, shared by all such calls on a device:
+    calls that overlap on one GPU race)."""
+    _need_gpu(out, query, kv_cache, block_tables, seq_lens, lse, plan, new_key, new_value)
+    torch = _torch()
+    N, _, Hkv, bs, D = kv_cache.shape
+    B, Hq, Dq = query.shape
+    if Dq != D or tuple(out.shape) != (B, Hq, D) or out.dtype != kv_cache.dtype \
+            or query.dtype != kv_cache.dtype:
+        raise PAError(PA_EINVAL, "shape/dtype mismatch between out/query and kv_cache")
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32 \
+            or block_tables.shape[0] != B or seq_lens.numel() != B:
+        raise PAError(PA_EINVAL, "block_tables/seq_lens must be int32 with B rows")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq)):
+        raise PAError(PA_EINVAL, "lse must be fp32 [B, H_q]")
+    if plan is not None and plan.dtype != torch.int32:
+        raise PAError(PA_EINVAL, "plan must be int32")
+    for t in (new_key, new_value):
+        if tuple(t.shape) != (B, Hkv, D) or t.dtype != kv_cache.dtype:
+            raise PAError(PA_EINVAL, "new_key/new_value must be [B, H_kv, D] in the cache dtype")
+    _check(lib().pa_decode_append_noalloc(_ptr(out), _ptr(lse), _ptr(query), _ptr(new_key),
+                                          _ptr(new_value), _ptr(kv_cache), N, _ptr(block_tables),
+                                          block_tables.shape[1], _ptr(seq_lens), B,
+                                          int(max_seq_len), Hq, Hkv, D, bs, float(scale),
+                                          int(partition_size), _ptr(plan),
+                                          0 if plan is None else plan.numel(),
+                                          _dtype_code(kv_cache), _stream(stream)))
 
 
 def decode_multi_workspace_bytes(B: int, rows: int, num_q_heads: int, num_kv_heads: int,
