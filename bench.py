@@ -396,8 +396,7 @@ def bench_prefill(a, d, dev):
             "shared_prefix_tokens": wl.prefix_tokens, "max_seq_len": msl,
             "pool_blocks": d.num_blocks, "pool_copies_rotated": R, "parallelism": "none (1 GPU)",
         },
-        "host_metadata_us": round(host_us, 1),            # from scratch: allocator, tables
-        "host_step_us": round(step_host_us, 2),           # per step, incremental update
+        "host_metadata_us": round(host_us, 1),
         "roofline": {
             "kernel": "pa_prefill_chunk (prefill_chunk_kernel)",
             "bound": "mfma",
@@ -627,8 +626,7 @@ def bench_mixed(a, dev):
             "context_tokens": int(seq_lens.sum()), "max_seq_len": msl, "partition_size": P,
             "pool_blocks": d.num_blocks, "parallelism": "none (1 GPU)",
         },
-        "host_metadata_us": round(host_us, 1),            # from scratch: allocator, tables
-        "host_step_us": round(step_host_us, 2),           # per step, incremental update
+        "host_metadata_us": round(host_us, 1),
         "step_us_one_launch": round(step_us, 2),
         "step_us_two_launches": round(sep_us, 2),
         "attention_us_one_launch": round(var_us, 2),

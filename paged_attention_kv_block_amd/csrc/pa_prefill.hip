@@ -1,9 +1,9 @@
 // pa_prefill_chunk host side: argument checks and launches.  The kernel and
-// the design notes are in pa_prefill_dev.h.
+// the design notes are in pa_prefill_wide_dev.h.
 #include "pa.h"
 #include "pa_common.h"
 #include "pa_internal.h"
-#include "pa_prefill_dev.h"
+#include "pa_prefill_wide_dev.h"
 
 namespace pa {
 
@@ -14,11 +14,11 @@ static bool launch_prefill(int G, int max_query_len, int B, hipStream_t s, uint1
                            float sc) {
 #define PA_PREFILL_CASE(GG)                                                                     \
   case GG: {                                                                                    \
-    const int tiles = (max_query_len + PrefillCfg<D, GG>::TQ - 1) / PrefillCfg<D, GG>::TQ;      \
+    const int tiles = (max_query_len + WideCfg<D, GG>::TQ - 1) / WideCfg<D, GG>::TQ;            \
     const int groups = B * hkv;                                                                 \
-    hipLaunchKernelGGL((prefill_chunk_kernel<D, GG>), dim3(tiles * groups),                     \
-                       dim3(kPrefillThreads), 0, s, out, lse, q, qsl, cache, nb, bt, mbps, sl,  \
-                       msl, hkv, sc, tiles, groups);                                            \
+    hipLaunchKernelGGL((prefill_wide_kernel<D, GG>), dim3(tiles * groups), dim3(kWideThreads),  \
+                       0, s, out, lse, q, qsl, cache, nb, bt, mbps, sl, msl, hkv, sc, tiles,    \
+                       groups);                                                                 \
     return true;                                                                                \
   }
   switch (G) {
