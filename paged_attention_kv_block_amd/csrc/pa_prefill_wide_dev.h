@@ -484,7 +484,8 @@ __device__ __forceinline__ void wide_tile(
   // the ring)
   int* wave_flags = reinterpret_cast<int*>(smem + kWideBufs * C::BUF);
   const bool flag = pass(std::false_type{});
-  if (lane == 0) wave_flags[wave] = __builtin_amdgcn_ballot_w64(flag) != 0;
+  const bool wave_flag = __builtin_amdgcn_ballot_w64(flag) != 0;   // all lanes take part
+  if (lane == 0) wave_flags[wave] = wave_flag;
   wait_lgkmcnt0();
   ring_barrier();
   bool redo = false;

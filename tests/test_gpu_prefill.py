@@ -122,3 +122,44 @@ def test_unit_values_give_unit_output():
     g.pool[:, 1] = 1.0
     out, _ = g.prefill()
     np.testing.assert_array_equal(_f64(out), 1.0)
+
+
+def _scaled_late_keys(d, start, factor):
+    """Keys of every token at or after `start` multiplied by `factor` (rounded
+    back to bf16) on both sides: those keys' scores exceed the reference a
+    tile takes from its first step by far more than any fixed slack, so the
+    kernel must move its softmax reference (the oracle, in float64, takes
+    the row max directly)."""
+    import oracle
+    orig = d.kv
+
+    def kv(b):
+        k, v = orig(b)
+        kf = oracle.to_f64(k).astype(np.float32)
+        kf[start:] *= np.float32(factor)
+        return (kf.view(np.uint32) >> 16).astype(np.uint16), v
+    d.kv = kv
+    return d
+
+
+@pytest.mark.parametrize("D,G", [(128, 4), (64, 2)])
+def test_scores_far_above_the_first_step(D, G):
+    """A late key's score exceeds the first step's by ~2^90 in the log2
+    domain: the workgroup redoes the tile with the rescaling pass and still
+    matches the oracle (the softmax is then dominated by those keys)."""
+    d = inputs.custom(kind="prefill", seq_lens=(300, 200, 97), chunk_lens=(180, 200, 60),
+                      num_q_heads=2 * G, num_kv_heads=2, head_size=D, seed=31)
+    run_prefill_case(_scaled_late_keys(d, 150, 48.0))
+
+
+def test_scores_far_above_in_one_sequence_only():
+    """Only one sequence needs the rescaling pass; the others' tiles keep
+    the fast pass (both in one launch)."""
+    d = inputs.custom(kind="prefill", seq_lens=(260, 260), chunk_lens=(200, 200), num_q_heads=8,
+                      num_kv_heads=2, head_size=128, seed=32)
+    orig = d.kv
+    scaled = _scaled_late_keys(inputs.custom(kind="prefill", seq_lens=(260, 260),
+                                             chunk_lens=(200, 200), num_q_heads=8,
+                                             num_kv_heads=2, head_size=128, seed=32), 150, 48.0)
+    d.kv = lambda b: scaled.kv(b) if b == 1 else orig(b)
+    run_prefill_case(d)
