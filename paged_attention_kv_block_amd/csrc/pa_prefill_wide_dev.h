@@ -296,6 +296,17 @@ __device__ __forceinline__ void wide_tile(
     }
     return grow;
   };
+  // mask(): the causal mask alone (the fast pass checks no maxima)
+  auto mask = [&](int s, f32x16 (&x)[C::NC], auto mask_tag) __attribute__((always_inline)) {
+    if constexpr (decltype(mask_tag)::value) {
+      const int key0 = s * C::KSTEP + 4 * hl;
+#pragma unroll
+      for (int nc = 0; nc < C::NC; ++nc)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          x[nc][e] = key0 + 8 * (e >> 2) + (e & 3) <= row_pos[nc] ? x[nc][e] : -INFINITY;
+    }
+  };
   // rescale(): rows whose max grew past the threshold move their reference
   // and scale their accumulators (rescaling pass only)
   auto rescale = [&]() __attribute__((always_inline)) {
@@ -376,19 +387,20 @@ __device__ __forceinline__ void wide_tile(
     ring_barrier();
   };
 
-  // One pass over the tile's keys.  The fast pass never rescales: every
-  // row's reference is the exact max of step 0 (which holds key 0, visible
-  // to every query; padding rows take 0), a score above it by up to 2^64
-  // is harmless (P stays far inside the fp32 and bf16 range and keeps its
-  // relative precision), and a step whose score exceeds that only raises a
-  // flag.  A flag anywhere in the workgroup makes every wave redo the tile
-  // with the rescaling pass (reference moved whenever a score exceeds it by
-  // 2^8, as in prefill_tile).  So the fast pass's steps are straight-line
-  // code: K operands of step s + 1 first, the softmax of step s while they
-  // arrive, then both matrix products.
+  // One pass over the tile's keys.  The fast pass never rescales and
+  // checks no maxima: every row's reference is the exact max of step 0
+  // (which holds key 0, visible to every query; padding rows take 0), and a
+  // later score above it is harmless as long as P, the denominators and the
+  // accumulators stay finite (bf16 and fp32 keep their relative precision
+  // up to 2^127).  If any of them overflowed, the wave raises a flag at the
+  // end, and a flag anywhere in the workgroup makes every wave redo the
+  // tile with the rescaling pass (reference moved whenever a score exceeds
+  // it by 2^8, as in prefill_tile).  So the fast pass's steps are
+  // straight-line code: K operands of step s + 1 first, the softmax of step
+  // s while they arrive, then both matrix products.
   auto pass = [&](auto slow_tag) __attribute__((always_inline)) -> bool {
     constexpr bool SLOW = decltype(slow_tag)::value;
-    const float slack = SLOW ? kPrefillSlack : 64.f;
+    const float slack = kPrefillSlack;   // used by the rescaling pass only
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
@@ -425,11 +437,10 @@ __device__ __forceinline__ void wide_tile(
       head(s);
       u32x4 ka[C::KS];
       read_k(s + 1, ka);
-      const bool grow = check(s, cur, mask_tag);
       if constexpr (SLOW) {
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) rescale();
+        if (__builtin_amdgcn_ballot_w64(check(s, cur, mask_tag)) != 0) rescale();
       } else {
-        flag |= grow;
+        mask(s, cur, mask_tag);
       }
       u32x4 pb[C::NC][2];
       probs(cur, pb);
@@ -454,11 +465,10 @@ __device__ __forceinline__ void wide_tile(
       head(s);
       if (s + 1 < wave_steps) scores(s + 1, sb);
       if (s < wave_steps) {
-        const bool grow = check(s, sa, mask_tag);
         if constexpr (SLOW) {
-          if (__builtin_amdgcn_ballot_w64(grow) != 0) rescale();
+          if (__builtin_amdgcn_ballot_w64(check(s, sa, mask_tag)) != 0) rescale();
         } else {
-          flag |= grow;
+          mask(s, sa, mask_tag);
         }
         u32x4 pb[C::NC][2];
         probs(sa, pb);
@@ -477,6 +487,24 @@ __device__ __forceinline__ void wide_tile(
     full_steps(e2, std::true_type{});
     while (s < nsteps) other_step(std::true_type{});
     wait_vmcnt<0>();   // every load has landed before the ring is reused or released
+    if constexpr (!SLOW) {
+      // A score far above its row's reference overflows P, the denominator
+      // or the accumulators to inf (or NaN): one sum per row shows it.
+#pragma unroll
+      for (int nc = 0; nc < C::NC; ++nc) {
+        float t = l_part[nc];
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) t += acc[dt][nc][e];
+        // the bits pass through an empty asm: this file is built without
+        // NaN semantics, under which the compiler would reduce the exponent
+        // test to |t| == inf and miss a NaN
+        uint32_t tb = __float_as_uint(t);
+        __asm__ __volatile__("" : "+v"(tb));
+        flag |= (tb & 0x7F800000u) == 0x7F800000u;
+      }
+    }
     return flag;
   };
 
