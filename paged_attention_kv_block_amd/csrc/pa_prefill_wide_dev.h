@@ -253,6 +253,13 @@ __device__ __forceinline__ void wide_tile(
 
   // S^T of a step for both column tiles: its K operands from the ring slot
   // (read_k), then the matrix products (mfma_s)
+  // (the *_at forms take the ring slot as a compile-time constant, so its
+  // offset folds into the LDS instructions' immediate field)
+  auto read_k_at = [&](auto slot_tag, u32x4 (&ka)[C::KS]) __attribute__((always_inline)) {
+    const uint8_t* slot = smem + decltype(slot_tag)::value * C::BUF;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) ka[ks] = *reinterpret_cast<const u32x4*>(slot + kofs[ks]);
+  };
   auto read_k = [&](int s, u32x4 (&ka)[C::KS]) __attribute__((always_inline)) {
     const uint8_t* slot = smem + (s & (kWideBufs - 1)) * C::BUF;
 #pragma unroll
@@ -341,8 +348,8 @@ __device__ __forceinline__ void wide_tile(
       pb[nc][1] = u32x4{pw[4], pw[5], pw[6], pw[7]};
     }
   };
-  auto mfma_pv = [&](int s, const u32x4 (&pb)[C::NC][2]) __attribute__((always_inline)) {
-    const uint8_t* slot = smem + (s & (kWideBufs - 1)) * C::BUF;
+  auto mfma_pv_slot = [&](const uint8_t* slot, const u32x4 (&pb)[C::NC][2])
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
@@ -355,6 +362,12 @@ __device__ __forceinline__ void wide_tile(
 #pragma unroll
         for (int nc = 0; nc < C::NC; ++nc) acc[dt][nc] = mfma32x32x16(a, pb[nc][kh], acc[dt][nc]);
       }
+  };
+  auto mfma_pv = [&](int s, const u32x4 (&pb)[C::NC][2]) __attribute__((always_inline)) {
+    mfma_pv_slot(smem + (s & (kWideBufs - 1)) * C::BUF, pb);
+  };
+  auto mfma_pv_at = [&](auto slot_tag, const u32x4 (&pb)[C::NC][2]) __attribute__((always_inline)) {
+    mfma_pv_slot(smem + decltype(slot_tag)::value * C::BUF, pb);
   };
 
   // V rows at and past kend in the last step's slot may hold unwritten
@@ -432,11 +445,15 @@ __device__ __forceinline__ void wide_tile(
     }
     bool flag = false;
     int s = 0;
-    auto full_step = [&](f32x16 (&cur)[C::NC], f32x16 (&nxt)[C::NC], auto mask_tag)
-        __attribute__((always_inline)) {
+    // a full step (S^T of step s + 1 and P V of step s); SL: the ring slot
+    // of step s when known at compile time (-1: computed from s)
+    auto full_step = [&](f32x16 (&cur)[C::NC], f32x16 (&nxt)[C::NC], auto mask_tag,
+                         auto slot_tag) __attribute__((always_inline)) {
+      constexpr int SL = decltype(slot_tag)::value;
       head(s);
       u32x4 ka[C::KS];
-      read_k(s + 1, ka);
+      if constexpr (SL >= 0) read_k_at(std::integral_constant<int, (SL + 1) & (kWideBufs - 1)>{}, ka);
+      else read_k(s + 1, ka);
       if constexpr (SLOW) {
         if (__builtin_amdgcn_ballot_w64(check(s, cur, mask_tag)) != 0) rescale();
       } else {
@@ -445,18 +462,29 @@ __device__ __forceinline__ void wide_tile(
       u32x4 pb[C::NC][2];
       probs(cur, pb);
       mfma_s(ka, nxt);
-      mfma_pv(s, pb);
+      if constexpr (SL >= 0) mfma_pv_at(slot_tag, pb);
+      else mfma_pv(s, pb);
       tail(s);
       ++s;
     };
-    // full steps in pairs, so the two score buffers swap roles without copies
+    using Dyn = std::integral_constant<int, -1>;
+    // full steps: singles up to a multiple of the ring size, then groups of
+    // four with static slots (the score buffers also swap roles without
+    // copies), then singles
     auto full_steps = [&](int end, auto mask_tag) __attribute__((always_inline)) {
-      for (; s + 1 < end;) {
-        full_step(sa, sb, mask_tag);
-        full_step(sb, sa, mask_tag);
+      while (s < end && (s & (kWideBufs - 1)) != 0) {
+        full_step(sa, sb, mask_tag, Dyn{});
+#pragma unroll
+        for (int nc = 0; nc < C::NC; ++nc) sa[nc] = sb[nc];
       }
-      if (s < end) {
-        full_step(sa, sb, mask_tag);
+      for (; s + kWideBufs - 1 < end;) {
+        full_step(sa, sb, mask_tag, std::integral_constant<int, 0>{});
+        full_step(sb, sa, mask_tag, std::integral_constant<int, 1>{});
+        full_step(sa, sb, mask_tag, std::integral_constant<int, 2>{});
+        full_step(sb, sa, mask_tag, std::integral_constant<int, 3>{});
+      }
+      while (s < end) {
+        full_step(sa, sb, mask_tag, Dyn{});
 #pragma unroll
         for (int nc = 0; nc < C::NC; ++nc) sa[nc] = sb[nc];
       }
