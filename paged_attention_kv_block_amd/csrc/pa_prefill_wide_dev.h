@@ -348,20 +348,35 @@ __device__ __forceinline__ void wide_tile(
       pb[nc][1] = u32x4{pw[4], pw[5], pw[6], pw[7]};
     }
   };
-  auto mfma_pv_slot = [&](const uint8_t* slot, const u32x4 (&pb)[C::NC][2])
-      __attribute__((always_inline)) {
+  // V^T operands of a step from its ring slot (read_v_slot), then
+  // O^T += V^T P^T (mfma_pv_ops)
+  auto read_v_slot = [&](const uint8_t* slot, u32x4 (&va)[C::DT][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
-        const uint8_t* va = slot + vofs[dt] + (16 * kh) * C::RB;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(PA_LDS_PTR(i16x4, va));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(PA_LDS_PTR(i16x4, va + 8 * C::RB));
+        const uint8_t* p = slot + vofs[dt] + (16 * kh) * C::RB;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(PA_LDS_PTR(i16x4, p));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(PA_LDS_PTR(i16x4, p + 8 * C::RB));
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        const u32x4 a = {l2[0], l2[1], h2[0], h2[1]};
-#pragma unroll
-        for (int nc = 0; nc < C::NC; ++nc) acc[dt][nc] = mfma32x32x16(a, pb[nc][kh], acc[dt][nc]);
+        va[dt][kh] = u32x4{l2[0], l2[1], h2[0], h2[1]};
       }
+  };
+  auto mfma_pv_ops = [&](const u32x4 (&va)[C::DT][2], const u32x4 (&pb)[C::NC][2])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int nc = 0; nc < C::NC; ++nc)
+          acc[dt][nc] = mfma32x32x16(va[dt][kh], pb[nc][kh], acc[dt][nc]);
+  };
+  auto mfma_pv_slot = [&](const uint8_t* slot, const u32x4 (&pb)[C::NC][2])
+      __attribute__((always_inline)) {
+    u32x4 va[C::DT][2];
+    read_v_slot(slot, va);
+    mfma_pv_ops(va, pb);
   };
   auto mfma_pv = [&](int s, const u32x4 (&pb)[C::NC][2]) __attribute__((always_inline)) {
     mfma_pv_slot(smem + (s & (kWideBufs - 1)) * C::BUF, pb);
@@ -451,9 +466,20 @@ __device__ __forceinline__ void wide_tile(
                          auto slot_tag) __attribute__((always_inline)) {
       constexpr int SL = decltype(slot_tag)::value;
       head(s);
+      // every LDS operand read of the step first (K of step s + 1, V of
+      // step s), held there by a scheduling barrier: the softmax below
+      // then covers their latency instead of each product waiting on its
+      // own read
       u32x4 ka[C::KS];
-      if constexpr (SL >= 0) read_k_at(std::integral_constant<int, (SL + 1) & (kWideBufs - 1)>{}, ka);
-      else read_k(s + 1, ka);
+      u32x4 va[C::DT][2];
+      if constexpr (SL >= 0) {
+        read_k_at(std::integral_constant<int, (SL + 1) & (kWideBufs - 1)>{}, ka);
+        read_v_slot(smem + SL * C::BUF, va);
+      } else {
+        read_k(s + 1, ka);
+        read_v_slot(smem + (s & (kWideBufs - 1)) * C::BUF, va);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (SLOW) {
         if (__builtin_amdgcn_ballot_w64(check(s, cur, mask_tag)) != 0) rescale();
       } else {
@@ -462,8 +488,7 @@ __device__ __forceinline__ void wide_tile(
       u32x4 pb[C::NC][2];
       probs(cur, pb);
       mfma_s(ka, nxt);
-      if constexpr (SL >= 0) mfma_pv_at(slot_tag, pb);
-      else mfma_pv(s, pb);
+      mfma_pv_ops(va, pb);
       tail(s);
       ++s;
     };
