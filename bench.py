@@ -65,6 +65,7 @@ MULTI_TRAFFIC = os.path.join(ROOT, "profiles", "decode_multi_traffic.json")
 MULTI_FP8_TRAFFIC = os.path.join(ROOT, "profiles", "decode_multi_fp8_traffic.json")
 PREFILL_TRAFFIC = os.path.join(ROOT, "profiles", "prefill_traffic.json")
 PREFILL_SOURCES = ["paged_attention_kv_block_amd/csrc/pa_prefill.hip",
+                   "paged_attention_kv_block_amd/csrc/pa_prefill_wide_dev.h",
                    "paged_attention_kv_block_amd/csrc/pa_prefill_dev.h",
                    "paged_attention_kv_block_amd/csrc/pa_common.h"]
 VARLEN_SOURCES = ["paged_attention_kv_block_amd/csrc/pa_varlen.hip",
@@ -398,7 +399,7 @@ def bench_prefill(a, d, dev):
         },
         "host_metadata_us": round(host_us, 1),
         "roofline": {
-            "kernel": "pa_prefill_chunk (prefill_chunk_kernel)",
+            "kernel": "pa_prefill_chunk (prefill_wide_kernel)",
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -415,6 +416,8 @@ def bench_prefill(a, d, dev):
             "value": round(cflops / dt / 1e12, 8),
             "unit": "TFLOP/s",
             "cores": 1,
+            "host_cores": host_cores(),
+            "blas_threads": 1,
             "kind": "oracle",
             "sample": f"{nseq} of the {B} sequences of the {wl.name} step (write the chunk's "
                       f"keys/values, attend), fp64 numpy, BLAS 1 thread; {dt:.1f} s",
@@ -653,6 +656,8 @@ def bench_mixed(a, dev):
             "value": round(cbytes / dt / 1e9, 6),
             "unit": "GB/s",
             "cores": 1,
+            "host_cores": host_cores(),
+            "blas_threads": 1,
             "kind": "oracle",
             "sample": f"{nseq} sequences of the mixed step, chunk sequences and decode rows "
                       f"alternating (write the step's keys/values, attend), fp64 numpy, BLAS "
@@ -846,7 +851,7 @@ def bench_prefix_cache(a, dev):
         "shared_rows_max_abs_diff": diff,
         "shared_rows_bit_identical": bool(exact),
         "roofline": {
-            "kernel": "pa_prefill_chunk (prefill_chunk_kernel), with the cache",
+            "kernel": "pa_prefill_chunk (prefill_wide_kernel), with the cache",
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -864,6 +869,8 @@ def bench_prefix_cache(a, dev):
             "value": round(cflops / dt / 1e12, 8),
             "unit": "TFLOP/s",
             "cores": 1,
+            "host_cores": host_cores(),
+            "blas_threads": 1,
             "kind": "oracle",
             "sample": f"{nseq} sequences of the shared-prefix chunked-prefill step (the same "
                       f"attention definition, 256-row chunks over the cached prefix), fp64 "
@@ -1058,6 +1065,8 @@ def bench_spec(a, dev):
             "value": round(cbytes / dt / 1e9, 6),
             "unit": "GB/s",
             "cores": 1,
+            "host_cores": host_cores(),
+            "blas_threads": 1,
             "kind": "oracle",
             "sample": f"{nseq} sequences of the step in turn (up to 8 spread over the batch, "
                       f"their {C} rows each), fp64 numpy, BLAS 1 thread; {dt:.1f} s",
