@@ -66,11 +66,10 @@ MULTI_FP8_TRAFFIC = os.path.join(ROOT, "profiles", "decode_multi_fp8_traffic.jso
 PREFILL_TRAFFIC = os.path.join(ROOT, "profiles", "prefill_traffic.json")
 PREFILL_SOURCES = ["paged_attention_kv_block_amd/csrc/pa_prefill.hip",
                    "paged_attention_kv_block_amd/csrc/pa_prefill_wide_dev.h",
-                   "paged_attention_kv_block_amd/csrc/pa_prefill_dev.h",
                    "paged_attention_kv_block_amd/csrc/pa_common.h"]
 VARLEN_SOURCES = ["paged_attention_kv_block_amd/csrc/pa_varlen.hip",
                   "paged_attention_kv_block_amd/csrc/pa_decode_dev.h",
-                  "paged_attention_kv_block_amd/csrc/pa_prefill_dev.h",
+                  "paged_attention_kv_block_amd/csrc/pa_prefill_wide_dev.h",
                   "paged_attention_kv_block_amd/csrc/pa_common.h"]
 DECODE_SOURCES = ["paged_attention_kv_block_amd/csrc/pa_decode.hip",
                   "paged_attention_kv_block_amd/csrc/pa_decode_dev.h",

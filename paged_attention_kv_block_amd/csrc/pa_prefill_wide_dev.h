@@ -1,21 +1,23 @@
-// pa_prefill_chunk device code: causal chunked prefill over a paged KV cache
-// with 64 query rows per wave on the gfx950 32x32x16 bf16 matrix
-// instructions.
+// Causal chunked prefill over a paged KV cache on the gfx950 32x32x16 bf16
+// matrix instructions: the device code of pa_prefill_chunk, and of the
+// chunk rows of pa_attention_varlen.
 //
-// What is computed is the same as prefill_tile in pa_prefill_dev.h ("Im
-// Inneren von vLLM", section "Fortgeschrittene Funktionen": chunked prefill
-// and prefix caching; "Inside vLLM", section "Generate function": the batch
-// is one flattened token sequence): sequence b owns packed query rows
-// [qsl[b], qsl[b+1]); query i of its C_b chunk tokens sits at position
-// p = seq_len[b] - C_b + i and attends to tokens 0..p through the block
-// table with scaled-dot-product softmax attention.
+// What is computed: "Im Inneren von vLLM: Anatomie eines Hochdurchsatz-LLM-
+// Inferenzsystems", section "Fortgeschrittene Funktionen" (chunked prefill:
+// long prompts are cut into chunks; prefix caching: KV of shared prompt
+// prefixes is reused) and "Inside vLLM: Anatomy of a High-Throughput LLM
+// Inference System", section "Generate function" (the batch is flattened
+// into one sequence of tokens).  Sequence b owns packed query rows
+// [qsl[b], qsl[b+1]); these C_b queries are its last C_b tokens, and query i
+// at position p = seq_len[b] - C_b + i attends to tokens 0..p through the
+// block table (scaled-dot-product softmax attention, the standard
+// transformer's, cited in "Inside vLLM", "LLM Engine & Engine Core").
 //
-// Design (MFMA-bound; the narrower tile reads 16 KiB of LDS operands per
-// 32 rows and 32 keys, which saturates the LDS before the matrix cores):
-//   * one workgroup of 4 waves (one per SIMD, accumulators in AGPRs) per
-//     (query tile, KV head, sequence); a tile is 256 (token, head) rows of
-//     the G query heads sharing the KV head, token-major, 64 rows per wave
-//     in two 32-row column tiles;
+// Design (MFMA-bound: ~1400 flop per distinct KV byte):
+//   * one workgroup of 4 waves (one per SIMD, about 250 registers each, two
+//     workgroups per compute unit) per (query tile, KV head, sequence); a
+//     tile is 128 (token, head) rows of the G query heads sharing the KV
+//     head, token-major, 32 rows per wave;
 //   * keys advance 32 per step (two cache blocks).  Every step's K and V
 //     tiles travel from memory straight into a 4-step LDS ring (buffer
 //     loads with the LDS destination, no registers), issued three steps
@@ -30,11 +32,15 @@
 //   * the V^T operand comes from the row-major V tile through the
 //     transposing LDS read (ds_read_b64_tr_b16), 4 keys of one head
 //     dimension per lane per read;
-//   * online softmax in the log2 domain; the reference max moves only when
-//     a score exceeds it by 2^8, checked against each lane's own 16 scores,
-//     so the cross-lane row max and the rescale run only then; the causal
+//   * online softmax in the log2 domain, in two passes of which the second
+//     rarely runs: the fast pass fixes each row's reference at the exact
+//     max of the first step and never rescales; if a later score is so far
+//     above it that P, the denominator or the accumulators overflow, the
+//     workgroup redoes the tile with a pass that moves the reference
+//     whenever a score exceeds it by 2^8 and rescales the row.  The causal
 //     mask is applied only on steps that reach the diagonal of the wave's
-//     rows; steps past the wave's last row are skipped.
+//     rows; steps past the wave's last row are skipped; the denominator
+//     sums the same bf16-rounded P that multiplies V.
 #pragma once
 
 #include <type_traits>
@@ -42,10 +48,10 @@
 #include "pa.h"
 #include "pa_common.h"
 #include "pa_internal.h"
-#include "pa_prefill_dev.h"
 
 namespace pa {
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -54,11 +60,15 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 constexpr int kWideWaves = 4;
 constexpr int kWideThreads = kWideWaves * kWave;
 constexpr int kWideBufs = 4;  // LDS ring of K/V steps
+constexpr int kWideRows = kWideWaves * 32;  // (token, head) rows per workgroup
+constexpr float kLog2eP = 1.4426950408889634f;
+constexpr float kLn2P = 0.6931471805599453f;
+constexpr float kPrefillSlack = 8.f;  // log2 units a row max may exceed the reference
 
 template <int D, int G>
 struct WideCfg {
   static constexpr int RW = 32;                   // query rows per wave
-  static constexpr int ROWS = kWideWaves * RW;    // rows per workgroup
+  static constexpr int ROWS = kWideRows;          // rows per workgroup
   static constexpr int TQ = ROWS / G;             // query tokens per tile
   static constexpr int NC = RW / 32;              // 32-row column tiles per wave
   static constexpr int KSTEP = 32;                // keys per step
@@ -74,6 +84,7 @@ struct WideCfg {
   static constexpr int ROWS_PER_WL = kWave / CPR;
   static_assert(WL % LOADS == 0 && LOAD_WAVES <= kWideWaves, "load split");
   static_assert(16 % ROWS_PER_WL == 0, "a wave-load stays inside one cache block");
+  static_assert(ROWS == kWideWaves * RW, "rows per workgroup");
 };
 
 // Physical 16-byte chunk of logical chunk c in row r (an involution).  K:
@@ -159,7 +170,7 @@ __device__ __forceinline__ void wide_tile(
   const int hl = lane >> 5;                     // half of the wave
   const int ln = lane & 31;                     // query row within a 32-row column tile
 
-  // ---- this wave's rows: r = 64 wave + 32 nc + ln -> (token r / G, head r % G)
+  // ---- this wave's rows: r = RW wave + 32 nc + ln -> (token r / G, head r % G)
   int row_pos[C::NC];   // absolute position of the row's query, -1 if the row is padding
   u32x4 qt[C::NC][C::KS];
 #pragma unroll
@@ -423,7 +434,7 @@ __device__ __forceinline__ void wide_tile(
   // up to 2^127).  If any of them overflowed, the wave raises a flag at the
   // end, and a flag anywhere in the workgroup makes every wave redo the
   // tile with the rescaling pass (reference moved whenever a score exceeds
-  // it by 2^8, as in prefill_tile).  So the fast pass's steps are
+  // it by 2^8).  So the fast pass's steps are
   // straight-line code: K operands of step s + 1 first, the softmax of step
   // s while they arrive, then both matrix products.
   auto pass = [&](auto slow_tag) __attribute__((always_inline)) -> bool {

@@ -8,8 +8,8 @@
 // Engine Core"; "Im Inneren von vLLM", "Fortgeschrittene Funktionen" for
 // chunked prefill).  Both kinds of rows compute the same causal attention
 // over the sequence's cached tokens; what differs is the shape of the work:
-// a chunk of C_b >= 2 rows is a dense contraction (prefill_tile: MFMA over
-// 128 (token, head) rows per workgroup), a single row is a stream over the
+// a chunk of C_b >= 2 rows is a dense contraction (wide_tile, the prefill
+// tile: MFMA over 128 (token, head) rows per workgroup), a single row is a stream over the
 // sequence's blocks (decode_item: the matrix-core decode, optionally split
 // into partitions merged by the last workgroup to finish).
 //
@@ -34,15 +34,16 @@
 #include "pa_common.h"
 #include "pa_internal.h"
 #include "pa_decode_dev.h"
-#include "pa_prefill_dev.h"
+#include "pa_prefill_wide_dev.h"
 
 namespace pa {
 
-constexpr int kVarlenWaves = kPrefillWaves;  // decode items run with the prefill workgroup
+constexpr int kVarlenWaves = kWideWaves;  // decode items run with the prefill workgroup
 
 template <int D, int G>
 union VarlenSmem {
-  PrefillSmem<D, G> pf;
+  // the prefill tile's LDS ring and vote words
+  __attribute__((aligned(1024))) uint8_t pf[kWideBufs * WideCfg<D, G>::BUF + 64];
   DecodeSmem<D, G, true, kVarlenWaves, false> dc;
   DecodeSmem<D, 16, true, kVarlenWaves, false> mc;
 };
@@ -57,7 +58,7 @@ inline int varlen_rows_per_group(int G) { return 16 / G; }
 // (1 << 30) | (cg << 16) | b for column group cg of a short chunk (one pass
 // over the sequence's blocks, no split-K)
 template <int D, int G>
-__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void varlen_kernel(const DecodeParams a, const int* __restrict__ qsl) {
   __shared__ VarlenSmem<D, G> sm;
   const int item = blockIdx.x / a.num_kv_heads;
@@ -67,11 +68,11 @@ void varlen_kernel(const DecodeParams a, const int* __restrict__ qsl) {
   const int x = (e >> 16) & 0x7FFF;
   if (b >= a.B) return;  // not an entry of this batch
   if (e < 0) {
-    prefill_tile<D, G>(sm.pf, static_cast<uint16_t*>(a.out), a.lse_out,
-                       static_cast<const uint16_t*>(a.query), qsl,
-                       reinterpret_cast<const uint16_t*>(a.cache), a.num_blocks, a.block_tables,
-                       a.max_blocks_per_seq, a.seq_lens, a.max_seq_len, a.num_kv_heads,
-                       a.scale_log2, b, g, x);
+    wide_tile<D, G>(sm.pf, static_cast<uint16_t*>(a.out), a.lse_out,
+                    static_cast<const uint16_t*>(a.query), qsl,
+                    reinterpret_cast<const uint16_t*>(a.cache), a.num_blocks, a.block_tables,
+                    a.max_blocks_per_seq, a.seq_lens, a.max_seq_len, a.num_kv_heads,
+                    a.scale_log2, b, g, x);
     return;
   }
   int L = a.seq_lens[b];
@@ -95,7 +96,7 @@ void varlen_kernel(const DecodeParams a, const int* __restrict__ qsl) {
 
 template <int D>
 static bool launch_varlen(int G, const DecodeParams& a, const int* qsl, hipStream_t s) {
-  const dim3 grid(a.num_items), block(kPrefillThreads);
+  const dim3 grid(a.num_items), block(kWideThreads);
   switch (G) {
     case 1: hipLaunchKernelGGL((varlen_kernel<D, 1>), grid, block, 0, s, a, qsl); return true;
     case 2: hipLaunchKernelGGL((varlen_kernel<D, 2>), grid, block, 0, s, a, qsl); return true;
@@ -129,7 +130,7 @@ extern "C" int pa_varlen_plan(const int32_t* query_start_loc, const int32_t* seq
     return fail(PA_EINVAL, "pa_varlen_plan: query_start_loc[0] = %d", query_start_loc[0]);
   const int64_t P = parts_for(max_seq_len, partition_size);
   if (P > 16383) return fail(PA_ENOTSUP, "pa_varlen_plan: too many partitions");
-  const int TQ = kPrefillRows / G;  // query tokens per prefill tile
+  const int TQ = kWideRows / G;  // query tokens per prefill tile
   const int RPG = varlen_rows_per_group(G);
   // (work, b, x) of every item; work orders them; x carries the multi-row flag
   struct Item { int64_t work; int32_t b, x; };
