@@ -1074,6 +1074,141 @@ def bench_spec(a, dev):
     return 0
 
 
+def bench_graphs(a, dev):
+    """Decode steps replayed from the graphs captured per warm-up batch size
+    (pa_decode_graphs_*), at several batch sizes B up to the workload's:
+    each replay takes the smallest captured size that fits and pads the
+    rest with seq_len 0.  --layers L stacks L layers (each its own cache,
+    queries and new K/V; the block tables and lengths shared), as a model's
+    decode step runs attention once per layer.  Beside each: the same step
+    issued eagerly (pa_decode_append per layer without a plan, as the graphs
+    hold it), one ctypes call per launch.  Timed per step from the host loop
+    (wall clock: what a serving loop sees) and on the device (HIP events).
+    Cache copies rotate as in the decode line: one graph set per copy."""
+    import numpy as np
+    import torch
+    from paged_attention_kv_block_amd import host, inputs, ops
+    wl = inputs.workload(a.workload)
+    d = inputs.draw(a.workload)
+    if wl.kind != "decode" or wl.dtype != "bf16":
+        print("bench.py: --graphs needs a bf16 decode workload", file=sys.stderr)
+        return 2
+    B, Hq, Hkv, D, bs = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_size, wl.block_size
+    P = default_partition(wl) if a.partition_size is None else a.partition_size
+    NL = max(1, int(a.layers))
+    seq_lens = d.seq_lens
+    msl = int(seq_lens.max())
+
+    def dev_tensor(arr):
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    alloc = ops.Allocator(d.num_blocks, d.pool_order)
+    bt = host.decode_block_tables(alloc, seq_lens, bs)
+    pool0 = torch.zeros((d.num_blocks, 2, Hkv, bs, D), dtype=torch.bfloat16, device=dev)
+    ks, vs, sl, new_k, new_v = [], [], [], [], []
+    for b in range(B):
+        L = int(seq_lens[b])
+        k, v = d.kv(b)
+        ks.append(k[:L - 1])
+        vs.append(v[:L - 1])
+        sl.append(ops.slot_mapping(bt[b], 0, L - 1, bs))
+        new_k.append(k[L - 1])
+        new_v.append(v[L - 1])
+    ops.reshape_and_cache(dev_tensor(np.concatenate(ks)), dev_tensor(np.concatenate(vs)),
+                          torch.from_numpy(np.concatenate(sl)).to(dev), pool0)
+    del ks, vs
+    pool_bytes = pool0.numel() * pool0.element_size()
+    R = max(1, -(-a.rotate_mb * (1 << 20) // (pool_bytes * NL)))
+    pools = [pool0] + [pool0.clone() for _ in range(R * NL - 1)]   # set r, layer l: r * NL + l
+    q = dev_tensor(d.query()).unsqueeze(0).repeat(NL, 1, 1, 1).contiguous()
+    nk = dev_tensor(np.stack(new_k)).unsqueeze(0).repeat(NL, 1, 1, 1).contiguous()
+    nv = dev_tensor(np.stack(new_v)).unsqueeze(0).repeat(NL, 1, 1, 1).contiguous()
+    bt_dev = torch.from_numpy(bt).to(dev)
+    lens_dev = torch.from_numpy(np.ascontiguousarray(seq_lens, dtype=np.int32)).to(dev)
+    sl_dev = lens_dev.clone()
+    out = torch.empty_like(q)
+    ws = ops.decode_workspace(B, Hq, Hkv, D, msl, P, dev)
+    scale = float(wl.scale)
+    sizes = sorted({1 << i for i in range(16) if (1 << i) < B} | {B})
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sets = [ops.DecodeGraphs(out, q, nk, nv, pools[r * NL:(r + 1) * NL], bt_dev, sl_dev, msl,
+                                 scale, sizes, P, ws) for r in range(R)]
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    def timed(fn, Bx):
+        for i in range(max(1, a.warmup)):
+            fn(Bx, i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        h0 = time.perf_counter()
+        e0.record()
+        for i in range(a.steps):
+            fn(Bx, i)
+        e1.record()
+        h1 = time.perf_counter()
+        torch.cuda.synchronize()
+        h2 = time.perf_counter()
+        return ((h1 - h0) * 1e6 / a.steps, (h2 - h0) * 1e6 / a.steps,
+                e0.elapsed_time(e1) * 1e3 / a.steps)
+
+    def replay(Bx, i):
+        sets[i % R].replay(Bx)
+
+    def eager(Bx, i):
+        r = i % R
+        for layer in range(NL):
+            ops.decode(out[layer, :Bx], q[layer, :Bx], pools[r * NL + layer], bt_dev[:Bx],
+                       sl_dev[:Bx], msl, scale, P, ws, new_key=nk[layer, :Bx],
+                       new_value=nv[layer, :Bx])
+
+    rows = []
+    for Bx in sorted({1, max(1, B // 8), max(1, B // 4) + 1, B // 2, B}):
+        sl_dev.copy_(lens_dev)           # replays zero the padding lengths
+        torch.cuda.synchronize()
+        g_issue, g_wall, g_dev = timed(replay, Bx)
+        sl_dev.copy_(lens_dev)
+        torch.cuda.synchronize()
+        e_issue, e_wall, e_dev = timed(eager, Bx)
+        Bc = min(s for s in sizes if s >= Bx)
+        step_bytes = NL * (decode_bytes(wl, seq_lens[:Bx]) + cache_write_bytes(wl, None, Bx))
+        rows.append({"batch": Bx, "graph_batch": Bc,
+                     "graph_step_us": round(g_dev, 2), "graph_host_issue_us": round(g_issue, 2),
+                     "graph_wall_us": round(g_wall, 2),
+                     "eager_step_us": round(e_dev, 2), "eager_host_issue_us": round(e_issue, 2),
+                     "eager_wall_us": round(e_wall, 2),
+                     "graph_gbs": round(step_bytes / (g_dev * 1e-6) / 1e9, 1),
+                     "eager_gbs": round(step_bytes / (e_dev * 1e-6) / 1e9, 1)})
+        log(f"graphs: B={Bx} (graph {Bc}), {NL} layer(s): replay {g_dev:.2f} us/step on the "
+            f"device, {g_issue:.2f} us host issue; eager {e_dev:.2f} / {e_issue:.2f} us")
+    full = rows[-1]
+    for s_ in sets:
+        s_.close()
+    res = {
+        "metric": "paged-attn decode step GB/s replayed from graphs per warm-up batch size, 1 GPU",
+        "value": full["graph_gbs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(full["graph_step_us"] * 1e-3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) keys/values/queries; no weights)",
+        "config": {"workload": wl.name + "-graphs", "batch": B, "layers": NL,
+                   "num_q_heads": Hq, "num_kv_heads": Hkv, "head_size": D, "block_size": bs,
+                   "max_seq_len": msl, "partition_size": P, "warmup_batch_sizes": sizes,
+                   "cache_sets_rotated": R, "parallelism": "none (1 GPU)"},
+        "by_batch": rows,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -1092,6 +1227,12 @@ def main(argv=None):
     ap.add_argument("--spec-rows", type=int, default=0,
                     help="a speculative-decoding verification step: every sequence of decode "
                          "workload --workload checks this many query rows at once")
+    ap.add_argument("--graphs", action="store_true",
+                    help="decode workload --workload replayed from graphs captured per warm-up "
+                         "batch size (pa_decode_graphs_*) at several batch sizes, beside eager "
+                         "launches")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="with --graphs: attention layers per decode step (one cache each)")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="split-K partition in tokens (default: workload's, else 256/512)")
     ap.add_argument("--rotate-mb", type=int, default=768,
@@ -1140,6 +1281,8 @@ def main(argv=None):
         return bench_prefix_cache(a, dev)
     if a.spec_rows > 0:
         return bench_spec(a, dev)
+    if a.graphs:
+        return bench_graphs(a, dev)
     wl = inputs.workload(a.workload)
     d = inputs.draw(a.workload)
     if wl.kind == "prefill":

@@ -538,6 +538,72 @@ int pa_attention_varlen(void* out, float* lse_out, const void* query,
                         void* workspace, size_t workspace_bytes,
                         int32_t dtype, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Decode-step graphs for warm-up batch sizes ("Inside vLLM", section "LLM
+ * Engine constructor": the engine captures a graph of the forward pass for
+ * each of a list of warm-up batch sizes and replays it during decoding).
+ * ------------------------------------------------------------------------- */
+typedef struct pa_decode_graphs pa_decode_graphs;
+
+/* Captures, once per size Bc in batch_sizes (num_sizes entries, each in
+ * [1, 65535]; duplicates ignored), the attention of a decode step over
+ * num_layers layers: pa_decode_append for layer 0, 1, ... in order, each with
+ * B = Bc on the first Bc rows of that layer's buffers and no plan (its
+ * fixed grid walks every (sequence, partition up to max_seq_len) pair and
+ * skips the empty ones on the device, so one graph serves any lengths up to
+ * max_seq_len).  Capture runs on `stream`, which must not be the null
+ * stream; the graphs are instantiated at once.  The buffers are the
+ * caller's, static, device memory, sized for the largest size Bmax and
+ * layer-major:
+ *   out, query        [num_layers][Bmax][H_q][D] dtype
+ *   lse_out           [num_layers][Bmax][H_q] fp32, nullable
+ *   new_key, new_value [num_layers][Bmax][H_kv][D] dtype
+ *   kv_caches         host array of num_layers device pointers, each a
+ *                     cache of num_blocks blocks as pa_decode_append's
+ *   block_tables      [Bmax][max_blocks_per_seq] int32, shared by the layers
+ *   seq_lens          [Bmax] int32, shared by the layers
+ *   workspace         as pa_decode_append's for Bmax sequences (shared by
+ *                     the layers, which run one after another), zeroed by
+ *                     pa_decode_workspace_init before the first replay.
+ * dtype is PA_BF16 or PA_F32.  The addresses are recorded: the buffers must
+ * stay allocated, and their contents at replay time are what a replay
+ * reads.  Argument errors are PA_EINVAL here or pa_decode_append's (checked
+ * at capture); PA_EHIP if capture or instantiation fails.  *handle receives
+ * an object owned by the library (pa_decode_graphs_destroy); nothing is
+ * launched. */
+int pa_decode_graphs_create(void* out, float* lse_out, const void* query,
+                            const void* new_key, const void* new_value,
+                            void* const* kv_caches, int32_t num_layers, int32_t num_blocks,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            int32_t* seq_lens, int32_t max_seq_len, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                            float scale, int32_t partition_size, void* workspace,
+                            size_t workspace_bytes, int32_t dtype,
+                            const int32_t* batch_sizes, int32_t num_sizes, void* stream,
+                            pa_decode_graphs** handle);
+
+/* One decode step of B sequences (0 <= B <= Bmax) whose rows 0..B-1 the
+ * caller has written into the static buffers (every layer's): on `stream`
+ * (any stream of the capturing device), writes seq_lens[B..Bc) = 0 with a
+ * fill kernel, where Bc is the smallest captured size >= B, then launches
+ * graph Bc.  Padding rows B..Bc-1 get a zero output row and lse -inf in
+ * every layer and write nothing into the caches; rows from Bc on are not
+ * touched.  *graph_batch
+ * (nullable) receives Bc (0 for B = 0, which launches nothing).
+ * PA_EINVAL for B outside [0, Bmax] or another current device.  Replays of
+ * one handle share its buffers and workspace: they must not overlap. */
+int pa_decode_graphs_replay(pa_decode_graphs* handle, int32_t B, void* stream,
+                            int32_t* graph_batch);
+
+/* Number of captured sizes (-1 for a NULL handle); the first `capacity` of
+ * them, ascending, into batch_sizes (nullable). */
+int32_t pa_decode_graphs_count(const pa_decode_graphs* handle, int32_t* batch_sizes,
+                               int32_t capacity);
+
+/* Releases the graphs (the caller's buffers are untouched).  NULL is a
+ * no-op. */
+void pa_decode_graphs_destroy(pa_decode_graphs* handle);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libpa.so")
 HOST_LIB = os.path.join(PKG, "libpa_host.so")
 
 HIP_SOURCES = ["pa_host.cpp", "pa_cache.hip", "pa_decode.hip", "pa_prefill.hip",
-               "pa_varlen.hip"]
+               "pa_varlen.hip", "pa_graphs.hip"]
 # Per-source flags.  The prefill kernel never lets a NaN reach a max or an
 # exponent (scores of keys that may be unwritten are replaced by -inf with a
 # select first, and their V rows are zeroed), so it drops the NaN-quieting

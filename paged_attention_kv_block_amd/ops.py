@@ -82,6 +82,13 @@ SIGNATURES = {
     "pa_attention_varlen": (_c_int, [_vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _vp, _c_i32, _vp,
                                      _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _f, _c_i32,
                                      _vp, _c_i32, _vp, _c_sz, _c_i32, _vp]),
+    "pa_decode_graphs_create": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _vp,
+                                         _c_i32, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _f,
+                                         _c_i32, _vp, _c_sz, _c_i32, _vp, _c_i32, _vp,
+                                         ctypes.POINTER(_vp)]),
+    "pa_decode_graphs_replay": (_c_int, [_vp, _c_i32, _vp, _vp]),
+    "pa_decode_graphs_count": (_c_i32, [_vp, _vp, _c_i32]),
+    "pa_decode_graphs_destroy": (None, [_vp]),
 }
 
 _lib = None
@@ -629,3 +636,86 @@ def attention_varlen(out, query, query_start_loc, kv_cache, block_tables, seq_le
                                      float(scale), int(partition_size), _ptr(plan), plan.numel(),
                                      _ptr(workspace), ws_bytes,
                                      _dtype_code(kv_cache), _stream(stream)))
+
+
+class DecodeGraphs:
+    """pa_decode_graphs_*: the attention of a decode step over a stack of
+    layers (pa_decode_append per layer) captured once per warm-up batch size
+    over static buffers sized for the largest one.
+
+    kv_caches: a list of L caches [N, 2, H_kv, 16, D] (or one cache: L = 1);
+    out/query [L, Bmax, H_q, D] (or [Bmax, H_q, D] for L = 1);
+    new_key/new_value [L, Bmax, H_kv, D] (or [Bmax, H_kv, D]); block_tables
+    int32 [Bmax, max_blocks]; seq_lens int32 [Bmax]; lse fp32 [L, Bmax, H_q]
+    (or [Bmax, H_q]) or None; workspace as decode() for Bmax sequences.  The
+    object keeps these tensors alive: the graphs read them at their recorded
+    addresses.  replay(B) runs a step over their first B rows and returns the
+    captured size it used."""
+
+    def __init__(self, out, query, new_key, new_value, kv_caches, block_tables, seq_lens,
+                 max_seq_len: int, scale: float, batch_sizes: Sequence[int],
+                 partition_size: int = 0, workspace=None, lse=None, stream=None):
+        caches = list(kv_caches) if isinstance(kv_caches, (list, tuple)) else [kv_caches]
+        _need_gpu(out, query, new_key, new_value, block_tables, seq_lens, workspace, lse,
+                  *caches)
+        torch = _torch()
+        Ls = len(caches)
+        N, _, Hkv, bs, D = caches[0].shape
+        for c in caches:
+            if tuple(c.shape) != tuple(caches[0].shape) or c.dtype != caches[0].dtype:
+                raise PAError(PA_EINVAL, "every layer's cache must have one shape and dtype")
+        lead = (Ls,) if query.dim() == 4 else ()
+        if query.dim() == 3 and Ls != 1:
+            raise PAError(PA_EINVAL, "several layers need [L, Bmax, ...] buffers")
+        Bmax, Hq, Dq = query.shape[-3:]
+        if (query.dim() == 4 and query.shape[0] != Ls) or Dq != D \
+                or tuple(out.shape) != lead + (Bmax, Hq, D) \
+                or out.dtype != caches[0].dtype or query.dtype != caches[0].dtype:
+            raise PAError(PA_EINVAL, "shape/dtype mismatch between out/query and the caches")
+        if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32 \
+                or block_tables.shape[0] != Bmax or seq_lens.numel() != Bmax:
+            raise PAError(PA_EINVAL, "block_tables/seq_lens must be int32 with Bmax rows")
+        if lse is not None and (lse.dtype != torch.float32
+                                or tuple(lse.shape) != lead + (Bmax, Hq)):
+            raise PAError(PA_EINVAL, "lse must be fp32 [(L,) Bmax, H_q]")
+        for t in (new_key, new_value):
+            if tuple(t.shape) != lead + (Bmax, Hkv, D) or t.dtype != caches[0].dtype:
+                raise PAError(PA_EINVAL, "new_key/new_value must be [(L,) Bmax, H_kv, D] in the "
+                                         "cache dtype")
+        sizes = np.ascontiguousarray(batch_sizes, dtype=np.int32)
+        if sizes.size == 0 or int(sizes.max()) != Bmax:
+            raise PAError(PA_EINVAL, "the largest batch size must equal the buffers' rows")
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        self._keep = (out, query, new_key, new_value, caches, block_tables, seq_lens,
+                      workspace, lse)
+        ptrs = (_vp * Ls)(*[c.data_ptr() for c in caches])
+        h = _vp()
+        _check(lib().pa_decode_graphs_create(
+            _ptr(out), _ptr(lse), _ptr(query), _ptr(new_key), _ptr(new_value), ptrs, Ls, N,
+            _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), int(max_seq_len), Hq, Hkv,
+            D, bs, float(scale), int(partition_size), _ptr(workspace), ws_bytes,
+            _dtype_code(caches[0]), _np_ptr(sizes), sizes.size, _stream(stream),
+            ctypes.byref(h)))
+        self._h = h
+
+    def batch_sizes(self) -> list:
+        n = lib().pa_decode_graphs_count(self._h, None, 0)
+        a = np.zeros(max(n, 0), dtype=np.int32)
+        lib().pa_decode_graphs_count(self._h, _np_ptr(a), a.size)
+        return [int(x) for x in a]
+
+    def replay(self, B: int, stream=None) -> int:
+        got = ctypes.c_int32(0)
+        _check(lib().pa_decode_graphs_replay(self._h, int(B), _stream(stream), ctypes.byref(got)))
+        return got.value
+
+    def close(self) -> None:
+        if self._h is not None and self._h.value:
+            lib().pa_decode_graphs_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

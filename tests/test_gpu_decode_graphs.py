@@ -1,0 +1,148 @@
+"""GPU parity of the decode-step graphs captured per warm-up batch size
+(pa_decode_graphs_*: "Inside vLLM", section "LLM Engine constructor").
+
+One set of graphs (batch sizes 16, 32, 64) over static buffers of 64 rows on
+the TinyLlama-shaped workload, for one layer and for a stack of three.  Each
+replay takes B sequences drawn from the workload (a random subset, each a
+few tokens shorter than drawn, so the new token overwrites a cached one),
+fresh queries and new K/V per layer; the oracle writes the same new K/V
+with its reshape_and_cache and attends with its decode.
+Every replay is checked: real rows within the bf16 bar of the oracle, padding
+rows (B..Bc-1) exactly zero with lse -inf, rows from Bc on untouched, the
+pool bit for bit, and the captured size the smallest that fits.  Eager work
+and a synchronisation separate the replays.
+"""
+import numpy as np
+import pytest
+import torch
+
+from paged_attention_kv_block_amd import inputs
+from tests.conftest import gpu_available
+from tests.oracle_setup import OracleSide
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+TOL = 2e-2   # bf16 outputs and fp32 lse, as the other decode tests
+SIZES = (16, 32, 64)
+
+
+def _bf16(rng, shape):
+    return inputs.round_to_bf16_bits(rng.standard_normal(size=shape, dtype=np.float32))
+
+
+@pytest.mark.parametrize("P,layers", [(0, 1), (256, 1), (256, 3)])
+def test_replays_by_batch_size_match_the_oracle(P, layers):
+    """Layer l > 0 holds the layer-0 cache with its K and V halves swapped
+    (the oracle and the GPU apply the same swap), so a layer that read
+    another layer's cache or rows would fail."""
+    import oracle
+    from paged_attention_kv_block_amd import ops
+    from tests.gpu_setup import GpuSide, from_device, to_device
+    d = inputs.draw(1)
+    wl = d.wl
+    Bmax, Hq, Hkv, D = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_size
+    assert Bmax == max(SIZES)
+    o, g = OracleSide(d), GpuSide(d)
+    msl = int(d.seq_lens.max())
+    mbps = g.block_tables.shape[1]
+    dev = "cuda"
+    o_pools = [o.pool] + [o.pool[:, ::-1].copy() for _ in range(layers - 1)]
+    g_pools = [g.pool] + [g.pool.flip(1).contiguous() for _ in range(layers - 1)]
+    q_s = torch.zeros((layers, Bmax, Hq, D), dtype=torch.bfloat16, device=dev)
+    nk_s = torch.zeros((layers, Bmax, Hkv, D), dtype=torch.bfloat16, device=dev)
+    nv_s = torch.zeros_like(nk_s)
+    out_s = torch.zeros_like(q_s)
+    lse_s = torch.zeros((layers, Bmax, Hq), dtype=torch.float32, device=dev)
+    bt_s = torch.zeros((Bmax, mbps), dtype=torch.int32, device=dev)
+    sl_s = torch.zeros(Bmax, dtype=torch.int32, device=dev)
+    ws = ops.decode_workspace(Bmax, Hq, Hkv, D, msl, P)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        graphs = ops.DecodeGraphs(out_s, q_s, nk_s, nv_s, g_pools, bt_s, sl_s, msl,
+                                  float(wl.scale), SIZES, P, ws, lse_s)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert graphs.batch_sizes() == list(SIZES)
+
+    rng = np.random.default_rng(4242 + P + layers)
+    for rep, B in enumerate((16, 20, 33, 64, 5, 64, 1)):
+        seqs = np.sort(rng.choice(Bmax, size=B, replace=False))
+        lens = np.maximum(d.seq_lens[seqs] - rng.integers(0, 3, size=B), 1).astype(np.int32)
+        slots = np.array([o.slots_for(int(s), int(L) - 1, 1)[0] for s, L in zip(seqs, lens)])
+        refs = []
+        for layer in range(layers):
+            q = _bf16(rng, (B, Hq, D))
+            nk, nv = _bf16(rng, (B, Hkv, D)), _bf16(rng, (B, Hkv, D))
+            oracle.reshape_and_cache(o_pools[layer], nk, nv, slots)
+            refs.append(oracle.decode(q, o_pools[layer], o.block_tables[seqs], lens, wl.scale))
+            q_s[layer, :B] = to_device(q, wl)
+            nk_s[layer, :B] = to_device(nk, wl)
+            nv_s[layer, :B] = to_device(nv, wl)
+        Bc = min(s for s in SIZES if s >= B)
+        bt_s[:B] = torch.from_numpy(g.block_tables[seqs]).to(dev)
+        sl_s[:B] = torch.from_numpy(lens).to(dev)
+        sl_s[B:] = 7           # stale lengths: the replay clears B..Bc-1
+        out_s.fill_(float("nan"))
+        lse_s.fill_(float("nan"))
+        _ = (q_s.float() * 2).sum()   # unrelated eager work before the replay
+        torch.cuda.synchronize()
+        print(f"replay {rep}: B={B} P={P} layers={layers}", flush=True)
+        assert graphs.replay(B) == Bc
+        torch.cuda.synchronize()
+
+        for layer, (ref, ref_lse) in enumerate(refs):
+            got = oracle.to_f64(from_device(out_s[layer, :B]))
+            err = float(np.max(np.abs(got - ref)))
+            lerr = float(np.max(np.abs(lse_s[layer, :B].cpu().numpy() - ref_lse)))
+            assert err <= TOL and lerr <= TOL, (rep, B, layer, err, lerr)
+            if Bc > B:
+                assert torch.all(out_s[layer, B:Bc] == 0), (rep, layer)
+                assert torch.all(lse_s[layer, B:Bc] == float("-inf")), (rep, layer)
+            assert torch.all(torch.isnan(out_s[layer, Bc:].float())), (rep, layer)
+            np.testing.assert_array_equal(from_device(g_pools[layer]), o_pools[layer])
+        assert torch.all(sl_s[B:Bc] == 0), rep
+        assert torch.all(sl_s[Bc:] == 7), rep
+    graphs.close()
+
+
+def test_replay_edges():
+    """B = 0 launches nothing; B above the largest size and a closed set are
+    refused; create refuses a workspace too small for the largest size."""
+    from paged_attention_kv_block_amd import ops
+    from tests.gpu_setup import GpuSide
+    d = inputs.draw(1)
+    wl = d.wl
+    Bmax, Hq, Hkv, D = 32, wl.num_q_heads, wl.num_kv_heads, wl.head_size
+    g = GpuSide(d)
+    msl = int(d.seq_lens.max())
+    dev = "cuda"
+    q_s = torch.zeros((Bmax, Hq, D), dtype=torch.bfloat16, device=dev)
+    nk_s = torch.zeros((Bmax, Hkv, D), dtype=torch.bfloat16, device=dev)
+    out_s = torch.full_like(q_s, 3.0)
+    bt_s = torch.zeros((Bmax, g.block_tables.shape[1]), dtype=torch.int32, device=dev)
+    sl_s = torch.zeros(Bmax, dtype=torch.int32, device=dev)
+    small = ops.decode_workspace(16, Hq, Hkv, D, msl, 256)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        with pytest.raises(ops.PAError) as e:
+            ops.DecodeGraphs(out_s, q_s, nk_s, nk_s, g.pool, bt_s, sl_s, msl, float(wl.scale),
+                             (8, 32), 256, small)
+        assert e.value.status == ops.PA_EINVAL
+        graphs = ops.DecodeGraphs(out_s, q_s, nk_s, nk_s, g.pool, bt_s, sl_s, msl,
+                                  float(wl.scale), (8, 32))
+    torch.cuda.synchronize()
+    assert graphs.replay(0) == 0
+    torch.cuda.synchronize()
+    assert torch.all(out_s == 3.0)
+    with pytest.raises(ops.PAError) as e:
+        graphs.replay(33)
+    assert e.value.status == ops.PA_EINVAL
+    with pytest.raises(ops.PAError) as e:
+        graphs.replay(-1)
+    assert e.value.status == ops.PA_EINVAL
+    assert graphs.replay(3) == 8     # lengths all 0: rows 0..7 zero, rows 8.. untouched
+    torch.cuda.synchronize()
+    assert torch.all(out_s[:8] == 0) and torch.all(out_s[8:] == 3.0)
+    graphs.close()

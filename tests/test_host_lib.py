@@ -696,3 +696,43 @@ def test_varlen_validation(kw, status):
 def test_varlen_empty_batch_is_a_no_op():
     assert _varlen_status(B=0)[0] == ops.PA_OK
     assert _varlen_status(plan=None, plan_n=0)[0] == ops.PA_OK
+
+
+def test_decode_graphs_refuse_bad_arguments_before_any_device_call():
+    """pa_decode_graphs_create checks its arguments before it touches the
+    device (capture and instantiation come last); replay, count and destroy
+    take a NULL handle safely."""
+    import ctypes
+    L = ops.lib()
+    EINVAL = ops.PA_EINVAL
+    sizes = np.array([4, 8], dtype=np.int32)
+    h = ctypes.c_void_p()
+
+    caches = (ctypes.c_void_p * 2)(16, 16)
+
+    def create(handle=True, sizes_=sizes, n=None, stream=16, seq_lens=16, P=0, ws_bytes=0,
+               layers=2, dtype=ops.PA_BF16, out=16):
+        return L.pa_decode_graphs_create(
+            out, None, 16, 16, 16, caches, layers, 4, 16, 4, seq_lens, 64, 8, 4, 64, 16, 0.125,
+            P, None, ws_bytes, dtype, None if sizes_ is None else sizes_.ctypes.data,
+            len(sizes_) if n is None else n, stream, ctypes.byref(h) if handle else None)
+
+    assert create(handle=False) == EINVAL and "NULL handle" in L.pa_last_error().decode()
+    assert create(layers=0) == EINVAL and "no layers" in L.pa_last_error().decode()
+    assert create(dtype=ops.PA_FP8) == EINVAL
+    assert create(out=None) == EINVAL and "NULL pointer" in L.pa_last_error().decode()
+    assert create(n=0) == EINVAL and "no batch sizes" in L.pa_last_error().decode()
+    assert create(sizes_=np.array([0, 8], np.int32)) == EINVAL
+    assert create(sizes_=np.array([8, 65536], np.int32)) == EINVAL
+    assert create(stream=None) == EINVAL and "null stream" in L.pa_last_error().decode()
+    assert create(seq_lens=None) == EINVAL
+    # split-K over 64 tokens at P = 16 needs a workspace for batch 8
+    need = L.pa_decode_workspace_bytes(8, 8, 4, 64, 64, 16)
+    assert need > 0
+    assert create(P=16, ws_bytes=need - 1) == EINVAL
+    assert "workspace" in L.pa_last_error().decode()
+    assert h.value is None
+    got = ctypes.c_int32(5)
+    assert L.pa_decode_graphs_replay(None, 1, None, ctypes.byref(got)) == EINVAL
+    assert L.pa_decode_graphs_count(None, None, 0) == -1
+    L.pa_decode_graphs_destroy(None)
