@@ -210,14 +210,16 @@ def cpu_baseline(d, min_seconds: float, fp8_scales=None, max_tokens: int = 200_0
     return dt, reps, seqs
 
 
-def host_step_us(d, partition_size: int, steps: int = 200) -> float:
+def host_step_us(d, partition_size: int, steps: int = 200, native: bool = True) -> float:
     """Host metadata of one decode step, updated incrementally as the engine's
     CPU side does it between steps: every running sequence gains one token;
     a sequence whose new token starts a block takes one block from the
     free_block_queue (libpa allocator) into its table row; the new tokens'
-    slots and the work plan are rebuilt.  Average over `steps` consecutive
-    steps, in microseconds (the uploads of the changed rows are not
-    included)."""
+    slots and the work plan are rebuilt.  native: one pa_decode_step_prepare
+    call per step; otherwise the same step composed in Python from the
+    allocator, slot-mapping and plan calls.  Average over `steps`
+    consecutive steps, in microseconds (the uploads of the changed rows are
+    not included)."""
     import numpy as np
     from paged_attention_kv_block_amd import host, ops
     bs = d.wl.block_size
@@ -227,14 +229,24 @@ def host_step_us(d, partition_size: int, steps: int = 200) -> float:
     alloc = ops.Allocator(max(d.num_blocks, int(sum(-(-int(x) // bs) for x in L)) + extra),
                           None)
     bt = host.decode_block_tables(alloc, L, bs, width)
+    msl = int(L.max()) + steps
+    slots = np.zeros(L.size, np.int64)
+    parts = 1 if partition_size <= 0 else -(-msl // partition_size)
+    plan = np.zeros(L.size * parts, np.int32)
     t0 = time.perf_counter()
-    for _ in range(steps):
-        cross = np.flatnonzero(L % bs == 0)       # the new token opens a block
-        if cross.size:
-            bt[cross, L[cross] // bs] = alloc.allocate(int(cross.size))
-        ops.slot_mapping(bt, L, 1, bs)
-        L += 1
-        ops.decode_plan(L, int(L.max()), partition_size)
+    if native:
+        st = ops.DecodeStep(alloc, bt, L, bs, msl, partition_size)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            st.prepare()
+    else:
+        for _ in range(steps):
+            cross = np.flatnonzero(L % bs == 0)       # the new token opens a block
+            if cross.size:
+                bt[cross, L[cross] // bs] = alloc.allocate(int(cross.size))
+            ops.slot_mapping(bt, L, 1, bs)
+            L += 1
+            ops.decode_plan(L, msl, partition_size)
     return (time.perf_counter() - t0) * 1e6 / steps
 
 
@@ -1311,6 +1323,7 @@ def main(argv=None):
     plan = ops.decode_plan(seq_lens, msl, P)
     host_us = (time.perf_counter() - t0) * 1e6
     step_host_us = host_step_us(d, P)
+    step_host_us_py = host_step_us(d, P, native=False)
 
     # ---- device inputs: cache holds tokens 0..L-2; the step writes token L-1
     pool_shape = (d.num_blocks, 2, Hkv, bs, D)
@@ -1489,7 +1502,8 @@ def main(argv=None):
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "context_tokens_per_s": round(ctx / (ms_step * 1e-3), 1),
         "host_metadata_us": round(host_us, 1),            # from scratch: allocator, tables
-        "host_step_us": round(step_host_us, 2),           # per step, incremental update
+        "host_step_us": round(step_host_us, 2),           # per step, incremental, one native call
+        "host_step_us_python": round(step_host_us_py, 2),  # the same composed in Python
         "step_us_eager_launches": round(eager_us, 2),   # no graph: host launch per step
         "measured_copy_gbs": round(copy_gbs, 1),          # 1 GiB device copy, read + write
         "roofline": {

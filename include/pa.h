@@ -286,6 +286,34 @@ int pa_decode_plan(const int32_t* seq_lens, int32_t B, int32_t max_seq_len,
                    int32_t partition_size, int32_t* plan, int32_t capacity,
                    int32_t* num_entries);
 
+/* The host half of one decode step in one call ("Inside vLLM", section
+ * "LLM Engine & Engine Core": the KV-cache manager allocates blocks from
+ * the free_block_queue as sequences grow; section "LLM Engine constructor":
+ * the CPU side prepares the step's attention metadata).  Every sequence b
+ * gains one token at position p = seq_lens[b]: if p % block_size == 0 the
+ * token opens a block, which is taken from the head of the allocator's
+ * queue (sequences in order, exactly as one pa_allocator_allocate of that
+ * many blocks) into block_tables[b][p / block_size]; slots[b] receives
+ * block_tables[b][p / block_size] * block_size + p % block_size, and
+ * seq_lens[b] becomes p + 1.  With plan non-NULL, plan receives
+ * pa_decode_plan of the new lengths (max_seq_len, partition_size) and
+ * *num_entries (nullable) its length.
+ *   block_tables [B][max_blocks_per_seq] int32, host, updated in place
+ *   seq_lens     [B] int32, host, updated in place
+ *   slots        [B] int64, host (written)
+ *   plan         [plan_capacity] int32, host, nullable
+ * All-or-nothing: nothing changes when a call fails.  PA_EINVAL if a new
+ * token reaches max_seq_len or beyond the table, if the entry a new block
+ * goes to already holds one (>= 0), if a token that does not open a block
+ * finds none, or if the plan needs more than plan_capacity entries;
+ * PA_ENOBLOCKS if fewer blocks are free than the step opens.  Host memory
+ * only. */
+int pa_decode_step_prepare(pa_allocator* allocator, int32_t* block_tables,
+                           int32_t max_blocks_per_seq, int32_t* seq_lens, int32_t B,
+                           int32_t block_size, int32_t max_seq_len,
+                           int32_t partition_size, int64_t* slots, int32_t* plan,
+                           int32_t plan_capacity, int32_t* num_entries);
+
 /* Decode attention: one query token per sequence, the last of its seq_len
  * cached tokens (already written), attends to all of them through its block
  * table; grouped-query heads share KV heads.  The attention itself is the

@@ -207,44 +207,6 @@ extern "C" int pa_decode_workspace_init(void* workspace, size_t workspace_bytes,
   return PA_OK;
 }
 
-extern "C" int pa_decode_plan(const int32_t* seq_lens, int32_t B, int32_t max_seq_len,
-                              int32_t partition_size, int32_t* plan, int32_t capacity,
-                              int32_t* num_entries) {
-  if (B < 0 || max_seq_len < 0 || partition_size < 0 || partition_size % kBlockSize || capacity < 0)
-    return fail(PA_EINVAL, "pa_decode_plan: bad sizes");
-  if (B > 65535) return fail(PA_ENOTSUP, "pa_decode_plan: B %d > 65535", B);
-  if (B > 0 && !seq_lens) return fail(PA_EINVAL, "pa_decode_plan: NULL seq_lens");
-  const int64_t P = parts_for(max_seq_len, partition_size);
-  if (P > 65535) return fail(PA_ENOTSUP, "pa_decode_plan: too many partitions");
-  // (tokens, b, part) of every non-empty partition; a sequence of length 0
-  // still gets one item (its output row is zero)
-  struct Item { int32_t tokens, b, part; };
-  std::vector<Item> items;
-  items.reserve(size_t(B) * 2);
-  for (int32_t b = 0; b < B; ++b) {
-    int32_t L = seq_lens[b];
-    if (L < 0 || L > max_seq_len)
-      return fail(PA_EINVAL, "pa_decode_plan: seq_lens[%d] = %d outside [0, %d]", b, L, max_seq_len);
-    const int32_t ptok = P > 1 ? partition_size : std::max(L, 1);
-    const int32_t np = L == 0 ? 1 : (L + ptok - 1) / ptok;
-    for (int32_t p = 0; p < np; ++p) items.push_back({std::min(ptok, L - p * ptok), b, p});
-  }
-  // longest first; among equal sizes partition-major, so items running at
-  // the same time belong to different sequences (their split-K arrival
-  // counters differ).  Workgroups take items round robin.
-  std::stable_sort(items.begin(), items.end(), [](const Item& x, const Item& y) {
-    if (x.tokens != y.tokens) return x.tokens > y.tokens;
-    if (x.part != y.part) return x.part < y.part;
-    return x.b < y.b;
-  });
-  if (num_entries) *num_entries = int32_t(items.size());
-  if (int64_t(items.size()) > capacity)
-    return fail(PA_EINVAL, "pa_decode_plan: %zu entries, capacity %d", items.size(), capacity);
-  if (!items.empty() && !plan) return fail(PA_EINVAL, "pa_decode_plan: NULL plan");
-  for (size_t i = 0; i < items.size(); ++i) plan[i] = (items[i].part << 16) | items[i].b;
-  return PA_OK;
-}
-
 static int decode_call(const char* fn, void* out, float* lse_out, const void* query,
                        const void* new_key, const void* new_value, const void* kv_cache,
                        int32_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -1,15 +1,18 @@
 // Host half of libpa: status messages, closed forms, the block allocator
-// (free_block_queue) and the token -> slot mapping.  Plain C++17, no HIP:
+// (free_block_queue), the token -> slot mapping, the decode work plan and
+// the host half of a decode step.  Plain C++17, no HIP:
 // it also builds with g++ alone for host sanitizer runs.
 //
 // "Inside vLLM: Anatomy of a High-Throughput LLM Inference System",
 // section "LLM Engine & Engine Core": the KV-cache manager keeps a
 // free_block_queue; blocks map a sequence's tokens to where their keys and
 // values live.  Section "LLM Engine constructor": the block-bytes formula.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <new>
+#include <utility>
 #include <unordered_map>
 #include <vector>
 
@@ -489,5 +492,166 @@ extern "C" int pa_slot_mapping(const int32_t* block_tables, int32_t max_blocks_p
     }
   }
   if (total) *total = k;
+  return PA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// decode work plan and the host half of a decode step
+// ---------------------------------------------------------------------------
+namespace {
+
+// Partitions of max_seq_len tokens (1 when there is no split).
+int64_t plan_parts(int32_t max_seq_len, int32_t partition_size) {
+  if (partition_size <= 0 || max_seq_len <= 0) return 1;
+  return (int64_t(max_seq_len) + partition_size - 1) / partition_size;
+}
+
+// Division by a positive divisor fixed for a call: shifts when it is a
+// power of two (block sizes and partition sizes usually are), else the
+// plain operators.
+struct Divisor {
+  int32_t d;
+  int shift = -1;
+  explicit Divisor(int32_t v) : d(v) {
+    if (v > 0 && (v & (v - 1)) == 0) shift = __builtin_ctz(uint32_t(v));
+  }
+  int32_t div(int32_t x) const { return shift >= 0 ? x >> shift : x / d; }
+  int32_t mod(int32_t x) const { return shift >= 0 ? x & (d - 1) : x % d; }
+};
+
+// Entries of one sequence of length L (an empty sequence still gets one,
+// its zero output row).
+inline int64_t plan_items(int32_t L, int64_t P, const Divisor& part) {
+  if (P <= 1 || L == 0) return 1;
+  return part.div(L + part.d - 1);
+}
+
+// Writes the plan of lengths L[0..B) (validated by the caller) into plan:
+// entries (part << 16) | b ordered by tokens descending, then part, then b.
+// Without a split every sequence is one item of L tokens.  With one, the
+// full partitions (partition_size tokens, more than any other item) come
+// first in (part, b) order, listed part by part over the sequences that
+// still have one; then each sequence's last, shorter partition (or its
+// single empty item).  Those are ordered by one sort of 64-bit keys
+// (tokens inverted, part, b), which is the entry itself in the low bits.
+void write_plan(const int32_t* L, int32_t B, int64_t P, const Divisor& part, int32_t* plan) {
+  static thread_local std::vector<uint64_t> tail;
+  static thread_local std::vector<std::pair<int32_t, int32_t>> active;   // (b, full partitions)
+  tail.clear();
+  auto key = [](int32_t tokens, int32_t part, int32_t b) {
+    return (uint64_t(uint32_t(0x7FFFFFFF - tokens)) << 32) | (uint64_t(uint32_t(part)) << 16) |
+           uint64_t(uint32_t(b));
+  };
+  int64_t k = 0;
+  if (P <= 1) {
+    for (int32_t b = 0; b < B; ++b) tail.push_back(key(L[b], 0, b));
+  } else {
+    active.clear();
+    for (int32_t b = 0; b < B; ++b) {
+      const int32_t full = part.div(L[b]), rem = part.mod(L[b]);
+      if (full > 0) active.emplace_back(b, full);
+      if (rem > 0 || L[b] == 0) tail.push_back(key(rem, full, b));
+    }
+    for (int32_t p = 0; !active.empty(); ++p) {
+      size_t keep = 0;
+      for (const auto& bf : active) {
+        plan[k++] = int32_t(uint32_t(p) << 16 | uint32_t(bf.first));
+        if (bf.second > p + 1) active[keep++] = bf;
+      }
+      active.resize(keep);
+    }
+  }
+  std::sort(tail.begin(), tail.end());
+  for (uint64_t e : tail) plan[k++] = int32_t(uint32_t(e));
+}
+
+}  // namespace
+
+extern "C" int pa_decode_plan(const int32_t* seq_lens, int32_t B, int32_t max_seq_len,
+                              int32_t partition_size, int32_t* plan, int32_t capacity,
+                              int32_t* num_entries) {
+  if (B < 0 || max_seq_len < 0 || partition_size < 0 || partition_size % 16 || capacity < 0)
+    return fail(PA_EINVAL, "pa_decode_plan: bad sizes");
+  if (B > 65535) return fail(PA_ENOTSUP, "pa_decode_plan: B %d > 65535", B);
+  if (B > 0 && !seq_lens) return fail(PA_EINVAL, "pa_decode_plan: NULL seq_lens");
+  const int64_t P = plan_parts(max_seq_len, partition_size);
+  if (P > 65535) return fail(PA_ENOTSUP, "pa_decode_plan: too many partitions");
+  const Divisor part(partition_size > 0 ? partition_size : 1);
+  int64_t n = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t L = seq_lens[b];
+    if (L < 0 || L > max_seq_len)
+      return fail(PA_EINVAL, "pa_decode_plan: seq_lens[%d] = %d outside [0, %d]", b, L, max_seq_len);
+    n += plan_items(L, P, part);
+  }
+  if (num_entries) *num_entries = int32_t(n);
+  if (n > capacity)
+    return fail(PA_EINVAL, "pa_decode_plan: %lld entries, capacity %d", (long long)n, capacity);
+  if (n > 0 && !plan) return fail(PA_EINVAL, "pa_decode_plan: NULL plan");
+  write_plan(seq_lens, B, P, part, plan);
+  return PA_OK;
+}
+
+extern "C" int pa_decode_step_prepare(pa_allocator* a, int32_t* block_tables,
+                                      int32_t max_blocks_per_seq, int32_t* seq_lens, int32_t B,
+                                      int32_t block_size, int32_t max_seq_len,
+                                      int32_t partition_size, int64_t* slots, int32_t* plan,
+                                      int32_t plan_capacity, int32_t* num_entries) {
+  const char* fn = "pa_decode_step_prepare";
+  if (num_entries) *num_entries = 0;
+  if (!a) return fail(PA_EINVAL, "%s: NULL allocator", fn);
+  if (B < 0 || block_size <= 0 || max_blocks_per_seq < 0 || max_seq_len < 0 ||
+      partition_size < 0 || partition_size % 16 || plan_capacity < 0)
+    return fail(PA_EINVAL, "%s: bad sizes", fn);
+  if (B > 65535) return fail(PA_ENOTSUP, "%s: B %d > 65535", fn, B);
+  if (B > 0 && (!block_tables || !seq_lens || !slots)) return fail(PA_EINVAL, "%s: NULL array", fn);
+  const int64_t P = plan_parts(max_seq_len, partition_size);
+  if (plan && P > 65535) return fail(PA_ENOTSUP, "%s: too many partitions", fn);
+  const Divisor blk(block_size), part(partition_size > 0 ? partition_size : 1);
+  // validate everything before changing anything
+  int64_t need = 0, n = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t p = seq_lens[b];   // position of the new token
+    if (p < 0 || p >= max_seq_len)
+      return fail(PA_EINVAL, "%s: sequence %d: new token at %d, max_seq_len %d", fn, b, p,
+                  max_seq_len);
+    const int32_t j = blk.div(p);
+    if (j >= max_blocks_per_seq)
+      return fail(PA_EINVAL, "%s: sequence %d: position %d beyond its table", fn, b, p);
+    const int32_t id = block_tables[int64_t(b) * max_blocks_per_seq + j];
+    if (blk.mod(p) == 0) {
+      if (id >= 0)
+        return fail(PA_EINVAL, "%s: sequence %d: table entry %d already holds block %d", fn, b,
+                    j, id);
+      ++need;
+    } else if (id < 0 || id >= a->n) {
+      return fail(PA_EINVAL, "%s: sequence %d: position %d has no block", fn, b, p);
+    }
+    if (plan) n += plan_items(p + 1, P, part);
+  }
+  if (plan) {
+    if (num_entries) *num_entries = int32_t(n);
+    if (n > plan_capacity)
+      return fail(PA_EINVAL, "%s: %lld plan entries, capacity %d", fn, (long long)n,
+                  plan_capacity);
+  }
+  if (need > a->count)
+    return fail(PA_ENOBLOCKS, "%s: need %lld blocks, %d free", fn, (long long)need, a->count);
+  // blocks for the sequences whose new token opens one, in sequence order
+  // (as one pa_allocator_allocate of that many blocks)
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t p = seq_lens[b];
+    int32_t* row = block_tables + int64_t(b) * max_blocks_per_seq;
+    const int32_t j = blk.div(p), off = blk.mod(p);
+    if (off == 0) {
+      const int32_t id = a->pop_head();
+      if (a->block_node[id] >= 0) a->evict(id);
+      a->refcount[id] = 1;
+      row[j] = id;
+    }
+    slots[b] = int64_t(row[j]) * block_size + off;
+    seq_lens[b] = p + 1;
+  }
+  if (plan) write_plan(seq_lens, B, P, part, plan);
   return PA_OK;
 }

@@ -51,6 +51,8 @@ SIGNATURES = {
     "pa_decode_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "pa_decode_workspace_init": (_c_int, [_vp, _c_sz, _vp]),
     "pa_decode_plan": (_c_int, [_vp, _c_i32, _c_i32, _c_i32, _vp, _c_i32, _vp]),
+    "pa_decode_step_prepare": (_c_int, [_vp, _vp, _c_i32, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
+                                        _vp, _vp, _c_i32, _vp]),
     "pa_decode": (_c_int, [_vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _vp, _c_i32, _c_i32,
                            _c_i32, _c_i32, _c_i32, _c_i32, _f, _c_i32, _vp, _c_i32, _vp, _c_sz,
                            _c_i32, _vp]),
@@ -362,6 +364,71 @@ def decode_plan(seq_lens_host, max_seq_len: int, partition_size: int) -> np.ndar
     _check(lib().pa_decode_plan(_np_ptr(sl), sl.size, int(max_seq_len), int(partition_size),
                                 _np_ptr(out), out.size, ctypes.byref(n)))
     return out[:n.value]
+
+
+def decode_step_prepare(allocator: "Allocator", block_tables: np.ndarray, seq_lens: np.ndarray,
+                        block_size: int, max_seq_len: int, partition_size: int,
+                        slots: np.ndarray, plan: Optional[np.ndarray] = None) -> int:
+    """pa_decode_step_prepare: one token more for every sequence (a block
+    from the free queue where the token opens one), the new tokens' slots and
+    the decode plan of the new lengths, in one native call.  block_tables
+    (int32 [B, width]) and seq_lens (int32 [B]) are updated in place; slots
+    (int64 [B]) and plan (int32, any capacity, or None) are written.
+    Returns the number of plan entries."""
+    for arr, dt, nd in ((block_tables, np.int32, 2), (seq_lens, np.int32, 1), (slots, np.int64, 1)):
+        if not isinstance(arr, np.ndarray) or arr.dtype != dt or arr.ndim != nd \
+                or not arr.flags.c_contiguous or not arr.flags.writeable:
+            raise PAError(PA_EINVAL, "block_tables/seq_lens/slots must be writable C-contiguous "
+                                     "int32 [B, width] / int32 [B] / int64 [B] arrays")
+    B = seq_lens.size
+    if block_tables.shape[0] != B or slots.size != B:
+        raise PAError(PA_EINVAL, "block_tables, seq_lens and slots need B rows")
+    if plan is not None and (plan.dtype != np.int32 or not plan.flags.c_contiguous
+                             or not plan.flags.writeable):
+        raise PAError(PA_EINVAL, "plan must be a writable C-contiguous int32 array")
+    n = ctypes.c_int32()
+    _check(lib().pa_decode_step_prepare(
+        allocator._h, _np_ptr(block_tables), block_tables.shape[1], _np_ptr(seq_lens), B,
+        int(block_size), int(max_seq_len), int(partition_size), _np_ptr(slots),
+        None if plan is None else _np_ptr(plan), 0 if plan is None else plan.size,
+        ctypes.byref(n)))
+    return n.value
+
+
+class DecodeStep:
+    """The host half of successive decode steps over fixed arrays: the
+    arguments of pa_decode_step_prepare are checked and marshalled once, and
+    each prepare() is one native call.  block_tables (int32 [B, width]) and
+    seq_lens (int32 [B]) are updated in place; after prepare(), slots (int64
+    [B]) holds the new tokens' slots and plan[:n] the decode plan, n being
+    the value returned."""
+
+    def __init__(self, allocator: "Allocator", block_tables: np.ndarray, seq_lens: np.ndarray,
+                 block_size: int, max_seq_len: int, partition_size: int):
+        for arr, nd in ((block_tables, 2), (seq_lens, 1)):
+            if not isinstance(arr, np.ndarray) or arr.dtype != np.int32 or arr.ndim != nd \
+                    or not arr.flags.c_contiguous or not arr.flags.writeable:
+                raise PAError(PA_EINVAL, "block_tables/seq_lens must be writable C-contiguous "
+                                         "int32 [B, width] / [B] arrays")
+        B = seq_lens.size
+        if block_tables.shape[0] != B:
+            raise PAError(PA_EINVAL, "block_tables and seq_lens need B rows")
+        parts = 1 if partition_size <= 0 or max_seq_len <= 0 else -(-int(max_seq_len) //
+                                                                      int(partition_size))
+        self.block_tables, self.seq_lens = block_tables, seq_lens
+        self.slots = np.zeros(B, np.int64)
+        self.plan = np.zeros(max(1, B * parts), np.int32)
+        self._allocator = allocator
+        self._n = ctypes.c_int32()
+        self._fn = lib().pa_decode_step_prepare
+        self._args = (allocator._h, _np_ptr(block_tables), block_tables.shape[1],
+                      _np_ptr(seq_lens), B, int(block_size), int(max_seq_len),
+                      int(partition_size), _np_ptr(self.slots), _np_ptr(self.plan),
+                      self.plan.size, ctypes.byref(self._n))
+
+    def prepare(self) -> int:
+        _check(self._fn(*self._args))
+        return self._n.value
 
 
 def decode(out, query, kv_cache, block_tables, seq_lens, max_seq_len: int, scale: float,

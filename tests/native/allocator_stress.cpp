@@ -3,7 +3,8 @@
 // tests/test_native_sanitized.py (host code only).  After every operation
 // the exported state must be consistent: the free queue holds exactly the
 // blocks with no reference, each once; the cached flags agree with the
-// cached-block count.  Exit status 0 on success.
+// cached-block count.  Then decode steps through pa_decode_step_prepare.
+// Exit status 0 on success.
 #include <cstdio>
 #include <random>
 #include <vector>
@@ -88,6 +89,56 @@ int main() {
       if (const int e = check_state(a, n)) {
         std::fprintf(stderr, "round %d step %d: state check %d\n", round, step, e);
         return 20 + e;
+      }
+    }
+    pa_allocator_destroy(a);
+  }
+  // decode steps: every sequence grows by one token per step through
+  // pa_decode_step_prepare (blocks at block crossings, slots, plan); when
+  // the queue runs dry the step must change nothing, and the longest
+  // sequence is then finished (its blocks freed, its row and length reset)
+  for (int round = 0; round < 6; ++round) {
+    const int n = 30 + 11 * round, bs = 16, B = 5 + round, width = 64, msl = width * bs;
+    pa_allocator* a = nullptr;
+    if (pa_allocator_create(n, nullptr, &a) != PA_OK) return 40;
+    std::vector<int32_t> lens(B), bt(size_t(B) * width, -1), plan(size_t(B) * 70);
+    std::vector<int64_t> slots(B);
+    for (int b = 0; b < B; ++b) lens[b] = int32_t(rng() % 40);
+    if (pa_allocator_build_tables(a, lens.data(), B, bs, width, bt.data()) != PA_OK) return 41;
+    for (int step = 0; step < 400; ++step) {
+      std::vector<int32_t> q0(n), rc0(n), bt0 = bt, lens0 = lens;
+      pa_allocator_export(a, q0.data(), rc0.data());
+      int32_t entries = 0;
+      const int st = pa_decode_step_prepare(a, bt.data(), width, lens.data(), B, bs, msl, 64,
+                                            slots.data(), plan.data(), int32_t(plan.size()),
+                                            &entries);
+      if (st == PA_ENOBLOCKS) {
+        std::vector<int32_t> q1(n), rc1(n);
+        pa_allocator_export(a, q1.data(), rc1.data());
+        if (q1 != q0 || rc1 != rc0 || bt != bt0 || lens != lens0) return 42;
+        int longest = 0;
+        for (int b = 1; b < B; ++b) longest = lens[b] > lens[longest] ? b : longest;
+        std::vector<int32_t> ids;
+        for (int j = 0; j < width && bt[size_t(longest) * width + j] >= 0; ++j) {
+          ids.push_back(bt[size_t(longest) * width + j]);
+          bt[size_t(longest) * width + j] = -1;
+        }
+        if (!ids.empty() && pa_allocator_free(a, ids.data(), int32_t(ids.size())) != PA_OK)
+          return 43;
+        lens[longest] = 0;
+      } else if (st != PA_OK) {
+        std::fprintf(stderr, "decode round %d step %d: status %d\n", round, step, st);
+        return 44;
+      } else {
+        for (int b = 0; b < B; ++b) {
+          const int32_t p = lens[b] - 1;
+          if (slots[b] != int64_t(bt[size_t(b) * width + p / bs]) * bs + p % bs) return 45;
+        }
+        if (entries <= 0 || entries > int32_t(plan.size())) return 46;
+      }
+      if (const int e = check_state(a, n)) {
+        std::fprintf(stderr, "decode round %d step %d: state check %d\n", round, step, e);
+        return 50 + e;
       }
     }
     pa_allocator_destroy(a);

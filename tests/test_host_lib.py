@@ -736,3 +736,136 @@ def test_decode_graphs_refuse_bad_arguments_before_any_device_call():
     assert L.pa_decode_graphs_replay(None, 1, None, ctypes.byref(got)) == EINVAL
     assert L.pa_decode_graphs_count(None, None, 0) == -1
     L.pa_decode_graphs_destroy(None)
+
+
+def _plan_by_rule(lens, max_seq_len, P):
+    """The decode plan written out from its rule: one item per (sequence,
+    partition) with tokens, one (empty) item for a sequence of length 0,
+    ordered by tokens descending, then partition, then sequence."""
+    parts = 1 if P <= 0 or max_seq_len <= 0 else -(-max_seq_len // P)
+    items = []
+    for b, L in enumerate(int(x) for x in lens):
+        ptok = P if parts > 1 else max(L, 1)
+        n = 1 if L == 0 else -(-L // ptok)
+        for p in range(n):
+            items.append((min(ptok, L - p * ptok), p, b))
+    items.sort(key=lambda t: (-t[0], t[1], t[2]))
+    return [(p << 16) | b for _, p, b in items]
+
+
+@pytest.mark.parametrize("P", [0, 16, 32, 512])
+def test_decode_plan_follows_its_ordering_rule(P):
+    rng = np.random.default_rng(77 + P)
+    for trial in range(20):
+        B = int(rng.integers(1, 300))
+        msl = int(rng.integers(1, 4000))
+        lens = rng.integers(0, msl + 1, size=B).astype(np.int32)
+        lens[rng.random(B) < 0.1] = 0
+        if P:
+            k = rng.random(B) < 0.2            # whole partitions
+            lens[k] = np.minimum((lens[k] // P) * P, msl)
+        got = ops.decode_plan(lens, msl, P)
+        assert [int(x) for x in got] == _plan_by_rule(lens, msl, P), (trial, B, msl)
+
+
+@pytest.mark.parametrize("P,bs", [(0, 16), (64, 16), (32, 8)])
+def test_decode_step_prepare_equals_the_oracle_step(P, bs):
+    """Forty steps of pa_decode_step_prepare against the same step done by
+    the oracle: its allocator pops the new blocks (sequences in order), its
+    slot mapping gives the new tokens' slots, and the plan follows the rule;
+    tables, lengths, slots, plan and the allocator state agree every step."""
+    rng = np.random.default_rng(5 + P + bs)
+    B, steps = 37, 40
+    lens0 = rng.integers(1, 200, size=B).astype(np.int32)
+    lens0[:5] = [bs, 2 * bs, bs - 1, 1, 3 * bs]              # block boundaries
+    N = int(sum(-(-(int(L) + steps) // bs) for L in lens0)) + 9
+    order = rng.permutation(N).astype(np.int32)
+    width = int(max(-(-(int(L) + steps) // bs) for L in lens0))
+    msl = int(lens0.max()) + steps
+    ca = ops.Allocator(N, order)
+    oa = oracle.OracleAllocator(N, order)
+    bt = host.decode_block_tables(ca, lens0, bs, width)
+    obt = oracle.build_decode_block_tables(oa, lens0, bs, width)
+    np.testing.assert_array_equal(bt, obt)
+    lens, olens = lens0.copy(), lens0.copy()
+    slots = np.zeros(B, np.int64)
+    plan = np.zeros(B * (msl // 16 + 2), np.int32)
+    for step in range(steps):
+        n = ops.decode_step_prepare(ca, bt, lens, bs, msl, P, slots, plan)
+        opens = [b for b in range(B) if olens[b] % bs == 0]
+        ids = oa.allocate(len(opens))
+        for b, i in zip(opens, ids):
+            obt[b, olens[b] // bs] = i
+        oslots = [oracle.slot_mapping(obt[b], int(olens[b]), 1, bs)[0] for b in range(B)]
+        olens += 1
+        np.testing.assert_array_equal(bt, obt)
+        np.testing.assert_array_equal(lens, olens)
+        assert [int(s) for s in slots] == [int(s) for s in oslots], step
+        assert [int(x) for x in plan[:n]] == _plan_by_rule(olens, msl, P), step
+        assert ca.export() == oa.export()
+
+
+def test_decode_step_prepare_is_all_or_nothing():
+    """Each refusal leaves the tables, lengths, allocator and outputs as
+    they were."""
+    bs = 16
+    lens0 = np.array([16, 5, 32, 31], np.int32)     # sequences 0 and 2 open a block
+    ca = ops.Allocator(12, None)
+    bt0 = host.decode_block_tables(ca, lens0, bs, 4)
+    state0 = ca.export()
+
+    def attempt(bt, lens, msl=1000, plan=None, alloc=ca):
+        slots = np.full(lens.size, -7, np.int64)
+        with pytest.raises(ops.PAError) as e:
+            ops.decode_step_prepare(alloc, bt, lens, bs, msl, 32, slots, plan)
+        assert (slots == -7).all()
+        return e.value.status
+
+    bt, lens = bt0.copy(), lens0.copy()
+    assert attempt(bt, lens, msl=32) == ops.PA_EINVAL             # sequence 2 reaches 32
+    bad = bt0.copy()
+    bad[0, 1] = 3                                                   # entry already holds a block
+    assert attempt(bad, lens) == ops.PA_EINVAL
+    bad = bt0.copy()
+    bad[1, 0] = -1                                                  # token 5 finds no block
+    assert attempt(bad, lens) == ops.PA_EINVAL
+    assert attempt(bt, lens, plan=np.zeros(2, np.int32)) == ops.PA_EINVAL   # capacity
+    np.testing.assert_array_equal(bt, bt0)
+    np.testing.assert_array_equal(lens, lens0)
+    assert ca.export() == state0
+    taken = ca.allocate(ca.num_free - 1)                            # one block left, two needed
+    state1 = ca.export()
+    assert attempt(bt, lens) == ops.PA_ENOBLOCKS
+    np.testing.assert_array_equal(bt, bt0)
+    np.testing.assert_array_equal(lens, lens0)
+    assert ca.export() == state1
+    ca.free(taken)
+    slots = np.zeros(4, np.int64)
+    plan = np.zeros(16, np.int32)
+    assert ops.decode_step_prepare(ca, bt, lens, bs, 1000, 32, slots, plan) == 5
+    assert list(lens) == [17, 6, 33, 32]
+
+
+def test_decode_step_object_equals_the_function():
+    """ops.DecodeStep (arguments marshalled once) gives the same tables,
+    lengths, slots and plans as ops.decode_step_prepare step after step."""
+    bs, P, steps = 16, 32, 30
+    rng = np.random.default_rng(9)
+    lens0 = rng.integers(1, 100, size=11).astype(np.int32)
+    order = rng.permutation(200).astype(np.int32)
+    a1, a2 = ops.Allocator(200, order), ops.Allocator(200, order)
+    bt1 = host.decode_block_tables(a1, lens0, bs, 12)
+    bt2 = host.decode_block_tables(a2, lens0, bs, 12)
+    l1, l2 = lens0.copy(), lens0.copy()
+    st = ops.DecodeStep(a1, bt1, l1, bs, 400, P)
+    slots = np.zeros(11, np.int64)
+    plan = np.zeros(11 * 13, np.int32)
+    for _ in range(steps):
+        n1 = st.prepare()
+        n2 = ops.decode_step_prepare(a2, bt2, l2, bs, 400, P, slots, plan)
+        assert n1 == n2
+        np.testing.assert_array_equal(st.plan[:n1], plan[:n2])
+        np.testing.assert_array_equal(st.slots, slots)
+        np.testing.assert_array_equal(bt1, bt2)
+        np.testing.assert_array_equal(l1, l2)
+    assert a1.export() == a2.export()
