@@ -328,9 +328,11 @@ int pa_decode_step_prepare(pa_allocator* allocator, int32_t* block_tables,
  *   partition_size  0: one pass per (sequence, KV head); otherwise a
  *                multiple of block_size: the context is split into
  *                partitions of that many tokens, each processed by its own
- *                workgroup; the last workgroup of a (sequence, KV head) to
- *                finish combines the partials with a log-sum-exp weighted
- *                sum (split-K, one kernel launch).
+ *                workgroup, and the partials are combined with a
+ *                log-sum-exp weighted sum (split-K): by the last workgroup
+ *                of each (sequence, KV head) to finish, or, for partitions
+ *                of 1024 tokens or more, by a second launch on the same
+ *                stream.
  *   plan, plan_entries  device copy of pa_decode_plan's output for these
  *                seq_lens and partition_size, or NULL / 0: then every
  *                (sequence, partition up to max_seq_len) pair is visited and

@@ -148,6 +148,41 @@ inline int multi_columns(int rows, int G, int head_size) {
 }
 inline int multi_rows_per_group(int G, int cols = 16) { return G >= cols ? 1 : cols / G; }
 
+// The split-K merge launch after a decode launch with defer_merge: one
+// workgroup per (sequence, KV head), or four (each a quarter of the output
+// columns) when there are fewer than two slots per compute unit, so that
+// a few long sequences' merges still spread over the chip.
+template <int D, bool BF16>
+static bool launch_merge(int G, const DecodeParams& a, hipStream_t s) {
+  const int64_t slots = int64_t(a.B) * a.num_kv_heads;
+  const bool split = slots < 2 * device_cus();
+  const dim3 block(kMergeWaves * kWave);
+#define PA_MERGE_CASE(GG)                                                                    \
+  case GG:                                                                                   \
+    if (split)                                                                               \
+      hipLaunchKernelGGL((merge_kernel<D, GG, BF16, 4>), dim3(slots * 4), block, 0, s, a);    \
+    else                                                                                     \
+      hipLaunchKernelGGL((merge_kernel<D, GG, BF16, 1>), dim3(slots), block, 0, s, a);        \
+    return true;
+  switch (G) {
+    PA_MERGE_CASE(1)
+    PA_MERGE_CASE(2)
+    PA_MERGE_CASE(4)
+    PA_MERGE_CASE(8)
+    case 16:
+      if constexpr (D == 64) {
+        if (split)
+          hipLaunchKernelGGL((merge_kernel<D, 16, BF16, 4>), dim3(slots * 4), block, 0, s, a);
+        else
+          hipLaunchKernelGGL((merge_kernel<D, 16, BF16, 1>), dim3(slots), block, 0, s, a);
+        return true;
+      }
+      return false;
+    default: return false;
+  }
+#undef PA_MERGE_CASE
+}
+
 template <int D, bool BF16, bool KV8 = false>
 static bool dispatch_g(int G, const DecodeParams& a, hipStream_t s) {
   switch (G) {
@@ -306,6 +341,15 @@ static int decode_call(const char* fn, void* out, float* lse_out, const void* qu
   a.rows_per_group = rpg;
   a.col_groups = groups;
   a.items_per_group = int(per_group);
+  // One-row split-K over long partitions (>= 1024 tokens): the items only
+  // write their records and a second launch merges them.  A workgroup that
+  // merges in place first waits for its records' stores and an arrival
+  // count, idle while the other items stream; with long items that idle
+  // time costs more than the second launch (long-context batch, 1024-token
+  // partitions: 986 -> 958 us).  Short partitions keep the in-place merge
+  // (Llama-3-shaped batch, 512-token partitions: 257 us in place, 260 us
+  // with the second launch).
+  a.defer_merge = P > 1 && !multi && B > 0 && partition_size >= 64 * kBlockSize;
   if (P > 1) {
     const WsLayout w = multi ? ws_layout(int64_t(B) * groups, int64_t(cols) * num_kv_heads,
                                          num_kv_heads, head_size, P)
@@ -334,6 +378,15 @@ static int decode_call(const char* fn, void* out, float* lse_out, const void* qu
   else
     ok = head_size == 64 ? dispatch_g<64, false>(G, a, st) : dispatch_g<128, false>(G, a, st);
   if (!ok) return fail(PA_ENOTSUP, "%s: group size %d with head_size %d", fn, G, head_size);
+  if (a.defer_merge) {
+    const bool bf16_recs = dtype != PA_F32;   // FP8 caches run the bf16 path
+    const bool merged = head_size == 64
+                            ? (bf16_recs ? launch_merge<64, true>(G, a, st)
+                                         : launch_merge<64, false>(G, a, st))
+                            : (bf16_recs ? launch_merge<128, true>(G, a, st)
+                                         : launch_merge<128, false>(G, a, st));
+    if (!merged) return fail(PA_ENOTSUP, "%s: group size %d with head_size %d", fn, G, head_size);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return PA_OK;

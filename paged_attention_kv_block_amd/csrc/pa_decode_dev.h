@@ -427,6 +427,9 @@ struct DecodeParams {
   // are col_groups items per (sequence, KV head, partition), and
   // items_per_group items (plan entries or virtual (b, part)) per column group.
   int rows, group, rows_per_group, col_groups, items_per_group;
+  // 1: split items only write their records, and a second launch
+  // (merge_kernel) merges them; 0: the last item of a slot to finish merges
+  int defer_merge;
 };
 
 // Append mode: the new token (position L - 1 of sequence b, KV head g)
@@ -1098,6 +1101,163 @@ __device__ __forceinline__ void valu_blocks(const DecodeParams& a, DecodeSmem<D,
   __syncthreads();
 }
 
+// Merges the split-K records of one (sequence, KV head[, column group]) into
+// its output rows: M = max_p m_p, W = sum_p 2^(m_p - M) l_p and
+// O = sum_p 2^(m_p - M) l_p o_p / W per head.  Called by the whole
+// workgroup (NW waves); sm supplies M[G], W[G] and the scratch k[] (at
+// least NW * 64 * 16 bytes).  recs: the nparts records of the slot.  With
+// QSPLIT > 1 the slot's G * D / 4 output quads are shared by QSPLIT
+// workgroups and this one writes those of part qs.
+template <int D, int G, bool BF16, int NW, bool MULTI, int QSPLIT = 1, int MB = 8, class SM,
+          class OutRow>
+__device__ __forceinline__ void merge_records(const DecodeParams& a, SM& sm,
+                                              const uint8_t* __restrict__ recs, int nparts,
+                                              int ncols, OutRow out_row, int qs = 0) {
+  void* __restrict__ out = a.out;
+  float* __restrict__ lse_out = a.lse_out;
+  const int max_parts = a.max_parts;
+  constexpr int REC = int(ws_record_bytes(G, D));
+  constexpr int ML = G * D * (BF16 ? 2 : 4);  // offset of the maxima within a record
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  // The partials of this KV head's G query-head rows, read through buffer
+  // resources with the sc1 cache policy: like agent-scope atomic loads they
+  // fetch past this XCD's L2 (which may hold stale lines from an earlier
+  // call), but as plain loads many of them can be in flight at once.
+  const __amdgpu_buffer_rsrc_t rr = ws_rsrc(reinterpret_cast<const float*>(recs), max_parts * REC);
+  auto m_off = [&](int h, int p) { return p * REC + ML + h * 4; };
+  auto l_off = [&](int h, int p) { return p * REC + ML + (G + h) * 4; };
+
+  // O = sum_p w_p o_p / W with w_p = 2^(m_p - M) l_p, M = max_p m_p and
+  // W = sum_p w_p.  Each thread owns 16-byte quads of the output rows; when
+  // there are more threads than quads, S threads share a quad and take
+  // every S-th partition, and their sums meet in LDS.  Partials are loaded
+  // MB at a time.
+  constexpr int NT = NW * kWave;
+  constexpr int Q = G * D / 4 / QSPLIT;   // quads of this workgroup
+  static_assert(Q >= 1 && (G * D / 4) % QSPLIT == 0, "quad split");
+  constexpr int S = NT > Q ? NT / Q : 1;
+  constexpr int QPT = Q > NT ? Q / NT : 1;
+  static_assert(NT * 16 <= int(sizeof(sm.k)), "LDS too small for the subset sums");
+  float* lds = reinterpret_cast<float*>(sm.k);
+  const int sub = S > 1 ? tid / Q : 0;
+  f32x4 acc[QPT];
+#pragma unroll
+  for (int qi = 0; qi < QPT; ++qi) acc[qi] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // partitions [p0, p0 + pc) with weight(h, p - p0)
+  auto accumulate = [&](int p0, int pc, auto weight) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qi = 0; qi < QPT; ++qi) {
+      const int quad = qs * Q + (S > 1 ? tid % Q : tid) + qi * NT;
+      const int h = quad / (D / 4), d4 = quad % (D / 4);
+      for (int pp = sub; pp < pc; pp += S * MB) {
+        f32x4 v[MB];
+        float w[MB];
+#pragma unroll
+        for (int j = 0; j < MB; ++j) {
+          const int p = pp + j * S;
+          const int pl = p < pc ? p : pc - 1;  // in range; weight 0 past the chunk
+          if constexpr (BF16)
+            v[j] = ws_load_bf16x4(rr, (p0 + pl) * REC + (h * D + d4 * 4) * 2);
+          else
+            v[j] = ws_load4(rr, (p0 + pl) * REC + (h * D + d4 * 4) * 4);
+          w[j] = p < pc ? weight(h, pl) : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < MB; ++j) acc[qi] += w[j] * v[j];
+      }
+    }
+  };
+  // maxima and sums of every partition fit LDS at once: one pass of loads
+  // stages them, the weights replace the maxima in place, and no record
+  // field is read twice
+  constexpr int FCAP = int(sizeof(sm.k) / sizeof(float)) / (2 * G);
+  if (nparts <= FCAP) {
+    const int n = nparts * 2 * G;          // [p][m_0..m_{G-1}, l_0..l_{G-1}]
+    for (int i0 = tid; i0 < n; i0 += 4 * NT) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * NT;
+        v[u] = i < n ? ws_load(rr, (i / (2 * G)) * REC + ML + (i % (2 * G)) * 4) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i0 + u * NT < n) lds[i0 + u * NT] = v[u];
+    }
+    __syncthreads();
+    for (int h = wave; h < G; h += NW) {   // one wave per head
+      float M = -INFINITY;
+      for (int p = lane; p < nparts; p += kWave) M = fmaxf(M, lds[p * 2 * G + h]);
+      M = allreduce_max<0, 6>(M);
+      float W = 0.f;
+      for (int p = lane; p < nparts; p += kWave) {
+        const float w = exp2f(lds[p * 2 * G + h] - M) * lds[p * 2 * G + G + h];
+        lds[p * 2 * G + h] = w;
+        W += w;
+      }
+      W = allreduce_sum<0, 6>(W);
+      if (lane == 0) { sm.M[h] = M; sm.W[h] = W; }
+    }
+    __syncthreads();
+    accumulate(0, nparts, [&](int h, int p) { return lds[p * 2 * G + h]; });
+    __syncthreads();
+  } else {
+    // per head: M and W over all partitions (one wave per head), then the
+    // weights staged through LDS in chunks of WCAP partitions per head
+    for (int h = wave; h < G; h += NW) {
+      float M = -INFINITY;
+      for (int p = lane; p < nparts; p += kWave) M = fmaxf(M, ws_load(rr, m_off(h, p)));
+      M = allreduce_max<0, 6>(M);
+      float W = 0.f;
+      for (int p = lane; p < nparts; p += kWave)
+        W += exp2f(ws_load(rr, m_off(h, p)) - M) * ws_load(rr, l_off(h, p));
+      W = allreduce_sum<0, 6>(W);
+      if (lane == 0) { sm.M[h] = M; sm.W[h] = W; }
+    }
+    __syncthreads();
+    constexpr int WCAP = int(sizeof(sm.k) / sizeof(float)) / G;
+    for (int p0 = 0; p0 < nparts; p0 += WCAP) {
+      const int pc = min(WCAP, nparts - p0);
+      for (int idx = tid; idx < G * pc; idx += NT) {
+        const int h = idx / pc, pp = idx % pc;
+        lds[h * WCAP + pp] =
+            exp2f(ws_load(rr, m_off(h, p0 + pp)) - sm.M[h]) * ws_load(rr, l_off(h, p0 + pp));
+      }
+      __syncthreads();
+      accumulate(p0, pc, [&](int h, int p) { return lds[h * WCAP + p]; });
+      __syncthreads();
+    }
+  }
+  if constexpr (S > 1) {
+    f32x4* red = reinterpret_cast<f32x4*>(sm.k);  // [S][Q]
+    red[tid] = acc[0];
+    __syncthreads();
+    if (sub == 0) {
+#pragma unroll
+      for (int t = 1; t < S; ++t) acc[0] += red[t * Q + tid];
+    }
+  }
+  if (sub == 0) {
+#pragma unroll
+    for (int qi = 0; qi < QPT; ++qi) {
+      const int quad = qs * Q + tid + qi * NT;
+      const int h = quad / (D / 4), d4 = quad % (D / 4);
+      if (MULTI && h >= ncols) continue;
+      const int64_t row = out_row(h);
+      // a MULTI row before position 0 (seq_len < rows) sees nothing: W = 0
+      const float inv = (!MULTI || sm.W[h] > 0.f) ? 1.f / sm.W[h] : 0.f;
+      store_out<BF16>(out, row * D + d4 * 4 + 0, acc[qi].x * inv);
+      store_out<BF16>(out, row * D + d4 * 4 + 1, acc[qi].y * inv);
+      store_out<BF16>(out, row * D + d4 * 4 + 2, acc[qi].z * inv);
+      store_out<BF16>(out, row * D + d4 * 4 + 3, acc[qi].w * inv);
+      if (lse_out && d4 == 0)
+        lse_out[row] = (!MULTI || sm.W[h] > 0.f) ? sm.M[h] * kLn2 + logf(sm.W[h]) : -INFINITY;
+    }
+  }
+}
+
 // One work item: KV head g of sequence b, partition `part` (blocks
 // [part * pb, min((part + 1) * pb, nblk))).  The query and output rows are
 // those of packed row `qrow` (b itself in a decode batch; the sequence's
@@ -1198,6 +1358,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a,
   __syncthreads();
   if (tid < 2 * G)  // the maxima and sums in one store
     coherent_store(reinterpret_cast<float*>(rec + ML) + tid, tid < G ? sm.M[tid] : sm.W[tid - G]);
+  if (a.defer_merge) return;  // merge_kernel combines the records after this launch
 
   // ---- split-K: the last workgroup of this (sequence, KV head) to finish
   // merges all partitions.  Partials are written and read with accesses that
@@ -1216,101 +1377,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a,
   if (tid == 0)  // ready for the next call
     __hip_atomic_store(&ws_count[slot], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  // The partials of this KV head's G query-head rows, read through buffer
-  // resources with the sc1 cache policy: like agent-scope atomic loads they
-  // fetch past this XCD's L2 (which may hold stale lines from an earlier
-  // call), but as plain loads many of them can be in flight at once.
-  const __amdgpu_buffer_rsrc_t rr = ws_rsrc(reinterpret_cast<const float*>(recs), max_parts * REC);
-  auto m_off = [&](int h, int p) { return p * REC + ML + h * 4; };
-  auto l_off = [&](int h, int p) { return p * REC + ML + (G + h) * 4; };
-
-  // per head: M = max_p m_p and W = sum_p 2^(m_p - M) l_p (one wave per head)
-  for (int h = wave; h < G; h += NW) {
-    float M = -INFINITY;
-    for (int p = lane; p < nparts; p += kWave) M = fmaxf(M, ws_load(rr, m_off(h, p)));
-    M = allreduce_max<0, 6>(M);
-    float W = 0.f;
-    for (int p = lane; p < nparts; p += kWave)
-      W += exp2f(ws_load(rr, m_off(h, p)) - M) * ws_load(rr, l_off(h, p));
-    W = allreduce_sum<0, 6>(W);
-    if (lane == 0) { sm.M[h] = M; sm.W[h] = W; }
-  }
-  __syncthreads();
-
-  // O = sum_p w_p o_p / W with w_p = 2^(m_p - M) l_p.  Each thread owns
-  // 16-byte quads of the output rows; when there are more threads than
-  // quads, S threads share a quad and take every S-th partition, and their
-  // sums meet in LDS.  Partials are loaded MB at a time; the weights are
-  // staged through LDS in chunks of WCAP partitions per head.
-  constexpr int NT = NW * kWave;
-  constexpr int Q = G * D / 4;
-  constexpr int S = NT > Q ? NT / Q : 1;
-  constexpr int QPT = Q > NT ? Q / NT : 1;
-  constexpr int MB = 8;
-  constexpr int WCAP = int(sizeof(sm.k) / sizeof(float)) / G;
-  static_assert(NT * 16 <= int(sizeof(sm.k)), "LDS too small for the subset sums");
-  float* wbuf = reinterpret_cast<float*>(sm.k);
-  const int sub = S > 1 ? tid / Q : 0;
-  f32x4 acc[QPT];
-#pragma unroll
-  for (int qi = 0; qi < QPT; ++qi) acc[qi] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int p0 = 0; p0 < nparts; p0 += WCAP) {
-    const int pc = min(WCAP, nparts - p0);
-    for (int idx = tid; idx < G * pc; idx += NT) {
-      const int h = idx / pc, pp = idx % pc;
-      wbuf[h * WCAP + pp] = exp2f(ws_load(rr, m_off(h, p0 + pp)) - sm.M[h]) * ws_load(rr, l_off(h, p0 + pp));
-    }
-    __syncthreads();
-#pragma unroll
-    for (int qi = 0; qi < QPT; ++qi) {
-      const int quad = (S > 1 ? tid % Q : tid) + qi * NT;
-      const int h = quad / (D / 4), d4 = quad % (D / 4);
-      const float* wh = wbuf + h * WCAP;
-      for (int pp = sub; pp < pc; pp += S * MB) {
-        f32x4 v[MB];
-        float w[MB];
-#pragma unroll
-        for (int j = 0; j < MB; ++j) {
-          const int p = pp + j * S;
-          const int pl = p < pc ? p : pc - 1;  // in range; weight 0 past the chunk
-          if constexpr (BF16)
-            v[j] = ws_load_bf16x4(rr, (p0 + pl) * REC + (h * D + d4 * 4) * 2);
-          else
-            v[j] = ws_load4(rr, (p0 + pl) * REC + (h * D + d4 * 4) * 4);
-          w[j] = p < pc ? wh[pl] : 0.f;
-        }
-#pragma unroll
-        for (int j = 0; j < MB; ++j) acc[qi] += w[j] * v[j];
-      }
-    }
-    __syncthreads();
-  }
-  if constexpr (S > 1) {
-    f32x4* red = reinterpret_cast<f32x4*>(sm.k);  // [S][Q]
-    red[tid] = acc[0];
-    __syncthreads();
-    if (sub == 0) {
-#pragma unroll
-      for (int t = 1; t < S; ++t) acc[0] += red[t * Q + tid];
-    }
-  }
-  if (sub == 0) {
-#pragma unroll
-    for (int qi = 0; qi < QPT; ++qi) {
-      const int quad = tid + qi * NT;
-      const int h = quad / (D / 4), d4 = quad % (D / 4);
-      if (MULTI && h >= ncols) continue;
-      const int64_t row = out_row(h);
-      // a MULTI row before position 0 (seq_len < rows) sees nothing: W = 0
-      const float inv = (!MULTI || sm.W[h] > 0.f) ? 1.f / sm.W[h] : 0.f;
-      store_out<BF16>(out, row * D + d4 * 4 + 0, acc[qi].x * inv);
-      store_out<BF16>(out, row * D + d4 * 4 + 1, acc[qi].y * inv);
-      store_out<BF16>(out, row * D + d4 * 4 + 2, acc[qi].z * inv);
-      store_out<BF16>(out, row * D + d4 * 4 + 3, acc[qi].w * inv);
-      if (lse_out && d4 == 0)
-        lse_out[row] = (!MULTI || sm.W[h] > 0.f) ? sm.M[h] * kLn2 + logf(sm.W[h]) : -INFINITY;
-    }
-  }
+  merge_records<D, G, BF16, NW, MULTI>(a, sm, recs, nparts, ncols, out_row);
 }
 
 
@@ -1378,6 +1445,36 @@ void decode_kernel(const DecodeParams a) {
                                                             nparts, cg, a.rows);
     __syncthreads();  // LDS is reused by the next item
   }
+}
+
+// Split-K merge as its own launch (decode launches with defer_merge): one
+// workgroup per (slot, quad part), slot = b * H_kv + g; slots whose
+// sequence fits one partition were written by their single item.  The
+// records were written by the previous launch on the stream, so they are
+// complete when this one starts.
+constexpr int kMergeWaves = 4;
+
+template <int G>
+struct MergeSmem {
+  __attribute__((aligned(16))) uint8_t k[16384];
+  float M[G], W[G];
+};
+
+template <int D, int G, bool BF16, int QSPLIT>
+__global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(const DecodeParams a) {
+  __shared__ MergeSmem<G> sm;
+  const int slot = blockIdx.x / QSPLIT, qs = blockIdx.x % QSPLIT;
+  const int b = slot / a.num_kv_heads, g = slot % a.num_kv_heads;
+  int L = a.seq_lens[b];
+  L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+  const int nblk = (L + 15) >> 4;
+  const int pb = a.part_blocks > 0 ? a.part_blocks : (nblk > 0 ? nblk : 1);
+  const int nparts = (nblk + pb - 1) / pb;
+  if (nparts <= 1) return;
+  const int H_q = a.num_kv_heads * G;
+  auto out_row = [&](int h) -> int64_t { return int64_t(b) * H_q + g * G + h; };
+  const uint8_t* recs = a.ws_rec + int64_t(slot) * a.max_parts * ws_record_bytes(G, D);
+  merge_records<D, G, BF16, kMergeWaves, false, QSPLIT, 16>(a, sm, recs, nparts, G, out_row, qs);
 }
 
 }  // namespace pa

@@ -134,6 +134,44 @@ def test_decode_many_items(name, B, hq, hkv, D, P, use_plan):
     run_decode_case(d, partition_size=P, use_plan=use_plan)
 
 
+# Split-K over partitions of 1024 tokens or more: the decode launch only
+# writes its records and a second launch merges them (one workgroup per
+# (sequence, KV head), or four per slot when there are fewer slots than two
+# per compute unit).  Sequences at, just above and well past a partition
+# boundary, one-token rows, every group size and both cache dtypes.
+LONGPART = [
+    ("bf16-g8-d128", dict(seq_lens=(1, 1023, 1024, 1025, 2049, 3000), num_q_heads=64,
+                          num_kv_heads=8, head_size=128)),
+    ("bf16-g16-d64", dict(seq_lens=(1024, 2500, 17), num_q_heads=32, num_kv_heads=2,
+                          head_size=64)),
+    ("bf16-g1-d64", dict(seq_lens=(4097, 1030), num_q_heads=2, num_kv_heads=2, head_size=64)),
+    ("bf16-g4-d64", dict(seq_lens=(2048, 2047, 1), num_q_heads=16, num_kv_heads=4,
+                         head_size=64)),
+    ("f32-g4-d128", dict(seq_lens=(1500, 2100), num_q_heads=8, num_kv_heads=2, head_size=128,
+                         dtype="f32")),
+    ("f32-g2-d64", dict(seq_lens=(3100, 5), num_q_heads=4, num_kv_heads=2, head_size=64,
+                        dtype="f32")),
+]
+
+
+@pytest.mark.parametrize("name,kw", LONGPART, ids=[e[0] for e in LONGPART])
+@pytest.mark.parametrize("P,use_plan", [(1024, False), (1024, True), (2048, True)])
+def test_decode_merge_launch(name, kw, P, use_plan):
+    run_decode_case(inputs.custom(kind="decode", **kw), partition_size=P, use_plan=use_plan)
+
+
+@pytest.mark.parametrize("use_plan", [False, True])
+def test_decode_merge_launch_many_slots(use_plan):
+    """640 (sequence, KV head) slots, more than two per compute unit: one
+    merge workgroup per slot."""
+    rng = np.random.default_rng(31)
+    lens = rng.integers(1, 2600, 160)
+    lens[:4] = (1, 1024, 1025, 2599)
+    d = inputs.custom(kind="decode", seq_lens=tuple(int(x) for x in lens), num_q_heads=32,
+                      num_kv_heads=4, head_size=64, seed=160)
+    run_decode_case(d, partition_size=1024, use_plan=use_plan)
+
+
 def test_zero_length_row():
     GpuSide, _ = _gpu()
     d = inputs.custom(kind="decode", seq_lens=(0, 20, 0), num_q_heads=8, num_kv_heads=2,
@@ -307,10 +345,12 @@ def test_decode_step_in_a_hip_graph():
     check_pool(o, g)
 
 
-def test_split_k_partials_never_stale():
+@pytest.mark.parametrize("P", [128, 1024])
+def test_split_k_partials_never_stale(P):
     """Two different inputs of the same shape alternate through one
     workspace: the partials of call n+1 occupy the addresses call n used, so
-    a merge that read a stale partial would differ from the first result."""
+    a merge that read a stale partial would differ from the first result
+    (P 128: the merge in the decode launch; P 1024: the merge launch)."""
     from paged_attention_kv_block_amd import ops
     from tests.gpu_setup import GpuSide, to_device
     d = inputs.draw(1)
@@ -319,12 +359,12 @@ def test_split_k_partials_never_stale():
     msl = int(d.seq_lens.max())
     qa = to_device(d.query(), wl)
     qb = -qa
-    ws = ops.decode_workspace(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_size, msl, 128)
+    ws = ops.decode_workspace(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_size, msl, P)
     outs = {}
     for it in range(12):
         for name, q in (("a", qa), ("b", qb)):
             out = torch.empty_like(q)
-            ops.decode(out, q, g.pool, g.bt_dev, g.seq_lens_dev, msl, float(wl.scale), 128, ws)
+            ops.decode(out, q, g.pool, g.bt_dev, g.seq_lens_dev, msl, float(wl.scale), P, ws)
             torch.cuda.synchronize()
             if name not in outs:
                 outs[name] = out

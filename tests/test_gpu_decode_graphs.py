@@ -31,7 +31,7 @@ def _bf16(rng, shape):
     return inputs.round_to_bf16_bits(rng.standard_normal(size=shape, dtype=np.float32))
 
 
-@pytest.mark.parametrize("P,layers", [(0, 1), (256, 1), (256, 3)])
+@pytest.mark.parametrize("P,layers", [(0, 1), (256, 1), (256, 3), (1024, 2)])
 def test_replays_by_batch_size_match_the_oracle(P, layers):
     """Layer l > 0 holds the layer-0 cache with its K and V halves swapped
     (the oracle and the GPU apply the same swap), so a layer that read

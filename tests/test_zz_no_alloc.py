@@ -49,6 +49,24 @@ def _case(d, P):
 
 @pytest.mark.gpu
 @pytest.mark.skipif(not gpu_available(), reason="needs a GPU")
+def test_noalloc_with_the_merge_launch():
+    """1024-token partitions (records merged by a second launch, which reads
+    them from the static scratch as well): bit for bit again, twice, the
+    second call smaller."""
+    import torch
+    big = inputs.draw(1)
+    small = inputs.custom(kind="decode", seq_lens=(1100, 5, 2100), num_q_heads=8,
+                          num_kv_heads=2, head_size=128, seed=4)
+    for d in (big, small):
+        (o1, l1, p1), (o2, l2, p2) = _case(d, 1024)
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), d.wl.name
+        assert torch.equal(l1, l2), d.wl.name
+        assert torch.equal(p1.view(torch.int16), p2.view(torch.int16)), d.wl.name
+        assert not torch.isnan(o2.float()).any()
+
+
+@pytest.mark.gpu
+@pytest.mark.skipif(not gpu_available(), reason="needs a GPU")
 def test_noalloc_equals_workspace_entry_point_twice():
     import torch
     big = inputs.draw(1)                                   # 64 sequences, G 8, D 64
